@@ -1,0 +1,138 @@
+"""Pins for the oracle's matrix-vector and matrix-matrix products.
+
+The dequantizers are pinned by the hand-worked blocks; these tests pin the
+products built on them: exact rational brute force on tiny shapes, a library
+float64 product, and closed forms that a transposed operand, a dropped term or
+a wrong index would break.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+
+
+def _round_to_f32(fr: Fraction) -> np.float32:
+    """Correctly rounded (nearest, ties to even) float32 of an exact rational."""
+    approx = np.float32(float(fr))
+    best = None
+    cands = [approx, np.nextafter(approx, np.float32(np.inf)), np.nextafter(approx, np.float32(-np.inf))]
+    for c in cands:
+        dist = abs(Fraction(float(c)) - fr)
+        key = (dist, int(np.array([c]).view(np.uint32)[0]) & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def _ulp_distance(a: np.float32, b: np.float32) -> int:
+    ia = int(np.array([a], np.float32).view(np.int32)[0])
+    ib = int(np.array([b], np.float32).view(np.int32)[0])
+    ia = ia if ia >= 0 else -(ia & 0x7FFFFFFF)
+    ib = ib if ib >= 0 else -(ib & 0x7FFFFFFF)
+    return abs(ia - ib)
+
+
+@pytest.mark.parametrize("fmt,m,k,n", [(0, 3, 32, 2), (0, 4, 64, 3), (1, 2, 256, 2), (1, 3, 256, 1)])
+def test_brute_force_exact_rationals(orc, fmt, m, k, n):
+    rng = np.random.default_rng(100 + m * k + n)
+    w = (rng.standard_normal((m, k)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((n, k)).astype(np.float32)
+    buf = orc.quantize(fmt, w)
+    what = orc.dequantize(fmt, buf, m, k)
+    y = orc.matvec(fmt, buf, m, k, x)
+    exact_hits = 0
+    for t in range(n):
+        for i in range(m):
+            fr = sum(Fraction(float(what[i, c])) * Fraction(float(x[t, c])) for c in range(k))
+            ref = _round_to_f32(fr)
+            dist = _ulp_distance(y[t, i], ref)
+            assert dist <= 1, (t, i, y[t, i], ref)
+            exact_hits += dist == 0
+    assert exact_hits >= (m * n + 1) // 2
+
+
+@pytest.mark.parametrize("fmt,m,k", [(0, 37, 320), (1, 19, 512), (0, 5, 2048)])
+def test_matches_numpy_float64(orc, fmt, m, k):
+    w = synth.weights(21, m, k)
+    x = synth.activations(22, 3, k)
+    buf = orc.quantize(fmt, w)
+    what = orc.dequantize(fmt, buf, m, k).astype(np.float64)
+    y = orc.matvec(fmt, buf, m, k, x)
+    ref = x.astype(np.float64) @ what.T
+    assert np.allclose(y, ref.astype(np.float32), rtol=1e-6, atol=1e-9)
+    # float64 result before rounding agrees closely
+    v, ad = orc.matvec_one(fmt, buf, m, k, x, 2, m - 1)
+    assert abs(v - ref[2, m - 1]) <= 1e-12 * ad
+
+
+def test_closed_forms_q4_0(orc):
+    m, k = 6, 96
+    w = synth.weights(31, m, k)
+    buf = orc.quantize(0, w)
+    what = orc.dequantize(0, buf, m, k)
+    # x = 1: row sums of the dequantized matrix (rows, not columns)
+    y1 = orc.matvec(0, buf, m, k, np.ones((1, k), np.float32))[0]
+    assert np.allclose(y1, what.astype(np.float64).sum(axis=1), rtol=1e-12, atol=0)
+    assert not np.allclose(y1[:min(m, k)], what.astype(np.float64).sum(axis=0)[:min(m, k)])
+    # one-hot x = e_j returns column j exactly
+    for j in (0, 17, 31, 32, 95):
+        e = np.zeros((1, k), np.float32)
+        e[0, j] = 1.0
+        assert np.array_equal(orc.matvec(0, buf, m, k, e)[0], what[:, j])
+    # all codes 8 -> y = 0 exactly, whatever the scales and x
+    allc8 = buf.copy()
+    allc8[: m * k // 2] = 0x88
+    x = synth.activations(32, 2, k)
+    assert not orc.matvec(0, allc8, m, k, x).any()
+    # scaling x by 2^k scales y exactly
+    y = orc.matvec(0, buf, m, k, x)
+    y8 = orc.matvec(0, buf, m, k, x * np.float32(8.0))
+    assert np.array_equal(y8, y * np.float32(8.0))
+
+
+def test_closed_forms_q4_k(orc):
+    m, k = 3, 512
+    w = synth.weights(41, m, k)
+    buf = orc.quantize(1, w)
+    what = orc.dequantize(1, buf, m, k)
+    for j in (0, 33, 100, 255, 256, 511):
+        e = np.zeros((1, k), np.float32)
+        e[0, j] = 1.0
+        assert np.array_equal(orc.matvec(1, buf, m, k, e)[0], what[:, j])
+    # q = 0 everywhere and m = 0 everywhere -> y = 0
+    z = buf.copy().reshape(-1, 144)
+    z[:, 16:] = 0
+    z[:, 4:16] = 0
+    assert not orc.matvec(1, z.reshape(-1), m, k, synth.activations(42, 2, k)).any()
+
+
+def test_threads_do_not_change_result(orc):
+    m, k = 50, 256
+    w = synth.weights(51, m, k)
+    x = synth.activations(52, 2, k)
+    buf = orc.quantize(0, w)
+    assert np.array_equal(orc.matvec(0, buf, m, k, x, threads=1), orc.matvec(0, buf, m, k, x, threads=7))
+
+
+def test_matmul_bf16(orc):
+    torch = pytest.importorskip("torch")
+    m, k, n = 9, 128, 5
+    w = synth.weights(61, m, k)
+    xb = synth.bf16_bits(synth.activations(62, n, k))
+    buf = orc.quantize(0, w)
+    what = orc.dequantize(0, buf, m, k)
+    xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).double().numpy()
+    y = orc.matmul(0, buf, m, k, xb)
+    assert np.allclose(y, (xf @ what.astype(np.float64).T).astype(np.float32), rtol=1e-6, atol=1e-9)
+    # bf16-rounded weights: against torch's bf16 cast of the dequantized matrix
+    wb = torch.from_numpy(what).to(torch.bfloat16).double().numpy()
+    yb = orc.matmul(0, buf, m, k, xb, round_w_bf16=True)
+    assert np.allclose(yb, (xf @ wb.T).astype(np.float32), rtol=1e-6, atol=1e-9)
+    # identity X gives bf16(W_hat)^T exactly
+    eye = synth.bf16_bits(np.eye(k, dtype=np.float32))
+    yi = orc.matmul(0, buf, m, k, eye, round_w_bf16=True)
+    assert np.array_equal(yi, wb.T.astype(np.float32))
+    yi = orc.matmul(0, buf, m, k, eye)
+    assert np.array_equal(yi, what.T)
