@@ -1,0 +1,148 @@
+/*
+ * q4.h -- C ABI of the Q4 weight-matrix product library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What the library computes: the matrix products of LLM decode and prefill
+ * with weights block-quantized to 4 bits, dequantized inside the product --
+ * in registers for the decode matrix-vector product, through shared memory
+ * (LDS) for the prefill matrix-matrix product (Llamas on the Web, technical
+ * summary, Methodology section 3, "integrated dequantization"). Weight
+ * formats are flat byte buffers decoded by a per-format routine chosen at
+ * compile time (same section, "extensibility"); all memory is allocated by
+ * the caller ahead of time (Methodology section 1, "static allocation").
+ *
+ * Conventions for every entry point:
+ *   - The caller owns every buffer. The library allocates no memory and keeps
+ *     no state between calls (the graph handle below is caller-owned state),
+ *     so calls are reentrant.
+ *   - Matrices are row-major. W is logically [m][k] (k = input dimension,
+ *     m = output dimension), quantized along k. Activations are token-major:
+ *     x[n][k], y[n][m].
+ *   - Device entry points validate every argument first. On any error they
+ *     return a negative status, enqueue nothing and leave y untouched; only
+ *     then do they make a HIP call. Faults during execution surface at the
+ *     caller's next synchronization.
+ *   - Device work is enqueued on the given HIP stream (NULL = null stream);
+ *     the call returns without synchronizing.
+ *   - No exception or abort crosses the ABI.
+ *
+ * Weight buffer layouts (produced by q4_quantize_ref):
+ *   Q4_0, m x k, k % 32 == 0, m*k*9/16 bytes, "plane-split":
+ *     bytes [0, m*k/2): nibble plane. Block (r, b) (row r, weights
+ *       32b..32b+31) occupies 16 bytes at (r*k/32 + b)*16; byte j holds the
+ *       code of weight j in its low nibble and of weight j+16 in its high
+ *       nibble (llama.cpp's order inside a block).
+ *     bytes [m*k/2, m*k*9/16): scale plane. The fp16 scale d of block (r, b)
+ *       is at m*k/2 + (r*k/32 + b)*2, little-endian.
+ *     Weight value: (q - 8) * d. This moves the same bytes as llama.cpp's
+ *     18-byte array-of-blocks layout, but every 16-byte group is 16-byte
+ *     aligned for 128-bit loads.
+ *   Q4_K, m x k, k % 256 == 0, m*(k/256)*144 bytes: row-major 144-byte
+ *     super-blocks of 256 weights: [0,2) fp16 d, [2,4) fp16 dmin, [4,16)
+ *     twelve bytes S packing eight 6-bit scales sc and eight 6-bit mins mn
+ *     (sub-block j < 4: sc = S[j] & 63, mn = S[j+4] & 63; j >= 4:
+ *     sc = (S[j+4] & 15) | (S[j-4] >> 6) << 4, mn = (S[j+4] >> 4) |
+ *     (S[j] >> 6) << 4), [16,144) nibbles: four 32-byte chunks; byte i of
+ *     chunk c holds weight 64c+i (low nibble) and 64c+32+i (high nibble).
+ *     Weight value of sub-block j: d*sc_j*q - dmin*mn_j.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats: legacy Q4_0 and the K-quant Q4_K (llama.cpp families the
+ * technical summary names: problem statement item 3; q4_k_m in its results). */
+typedef enum { Q4_FMT_Q4_0 = 0, Q4_FMT_Q4_K = 1 } q4_format;
+
+/* Status codes. */
+enum {
+    Q4_OK = 0,
+    Q4_EINVAL = -1,       /* bad size, null pointer, k not a whole number of blocks, short buffer */
+    Q4_EUNSUPPORTED = -2, /* n outside 1..8 for gemv; unknown format; size beyond the 32-bit offsets */
+    Q4_EALIGN = -3,       /* w or x not 16-byte aligned, y not 4-byte aligned */
+    Q4_ENONFINITE = -4,   /* NaN or Inf among the weights given to the quantizer */
+    Q4_ERANGE = -5,       /* a block scale that rounds to a non-finite fp16 */
+    Q4_EHIP = -6          /* the HIP runtime reported a launch or capture error */
+};
+
+/* Bytes of the quantized buffer for an m x k matrix; 0 if k is not a
+ * positive multiple of the block (32 for Q4_0, 256 for Q4_K), m < 0, or the
+ * format is unknown. Host only; no device work. */
+size_t q4_weight_bytes(int fmt, int64_t m, int64_t k);
+
+/* Host quantizer: float32 W[m][k] (host memory) -> packed buffer `out`
+ * (host memory, at least q4_weight_bytes(fmt, m, k) bytes).
+ * Q4_0 block: d = fp16_rne(max|w| / 7) (binary32 division); codes
+ *   q = clamp(round_half_away(w / d) + 8, 0, 15), all 8 when d == 0.
+ * Q4_K super-block (min/max reading, evaluated in float64): per sub-block
+ *   lo = min(0, min w), hi = max w, s = (hi - lo)/15, mu = -lo;
+ *   d = fp16_rne(max s / 63), dmin = fp16_rne(max mu / 63);
+ *   sc = clamp(round_half_away(s/d), 0, 63), mn = clamp(round_half_away(mu/dmin), 0, 63);
+ *   q = clamp(round_half_away((w + dmin*mn)/(d*sc)), 0, 15) (0 where a divisor is 0).
+ * Blocks are quantized row by row; the status is that of the first failing
+ * block in row-major order (Q4_ENONFINITE for NaN/Inf, Q4_ERANGE for a scale
+ * that overflows fp16), and `out` is then unspecified.
+ * (16-bit weights to 4 bits per parameter: MicroLLM Lab post, "Seven models,
+ * all in Q4".) */
+int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, size_t out_bytes);
+
+/* Decode product y[t][i] = sum_k w_hat[i][k] * x[t][k] for t < n, fp32 out.
+ * w: device, quantized as above, 16-byte aligned; x: device float32 [n][k],
+ * 16-byte aligned; y: device float32 [n][m], 4-byte aligned, fully written.
+ * n must be 1..8 (decode batch); m == 0 is a successful no-op.
+ * Weights are dequantized in registers and never written back (Llamas on the
+ * Web, technical summary, Methodology section 3). x is rounded to fp16 after
+ * an exact power-of-two scaling by its largest magnitude; products and sums
+ * are fp32. */
+int q4_gemv(int fmt, const void *w, const float *x, float *y,
+            int64_t m, int64_t k, int64_t n, void *hip_stream);
+
+/* Prefill product Y[t][i] = sum_k bf16_rne(w_hat[i][k]) * X[t][k], fp32 out.
+ * w: device, quantized as above (Q4_0 or Q4_K), 16-byte aligned; x_bf16: device bf16 bit
+ * patterns [n][k], 16-byte aligned; y: device float32 [n][m], 4-byte aligned.
+ * n >= 1 (any token count). Weight tiles are dequantized to bf16 into LDS
+ * and reused across the token tile by bf16 matrix-core (MFMA) instructions
+ * with fp32 accumulation (Methodology section 3: dequantize into shared
+ * memory and reuse for the matrix-matrix product). */
+int q4_gemm(int fmt, const void *w, const uint16_t *x_bf16, float *y,
+            int64_t m, int64_t k, int64_t n, void *hip_stream);
+
+/* One decode product of a layer stack. */
+typedef struct {
+    const void *w;   /* device weights */
+    const float *x;  /* device [n][k] */
+    float *y;        /* device [n][m] */
+    int64_t m, k;
+} q4_gemv_op;
+
+/* Enqueue count decode products back-to-back on one stream with no host
+ * synchronization in between (the runtime batches kernel submissions and
+ * avoids CPU-GPU synchronization: Llamas on the Web, technical summary,
+ * Methodology section 2, "execution scheduling"). Every op is validated
+ * before the first launch; on error nothing is enqueued. */
+int q4_gemv_sequence(int fmt, const q4_gemv_op *ops, int count, int64_t n, void *hip_stream);
+
+/* The same sequence captured once into a HIP graph and replayed with one
+ * launch per step (no per-step launch setup: compiled pipelines are cached
+ * after the first pass, same section). *graph_out receives a caller-owned
+ * handle; the op pointers are baked into the graph. */
+typedef struct q4_graph q4_graph;
+int q4_graph_create(int fmt, const q4_gemv_op *ops, int count, int64_t n, void *hip_stream,
+                    q4_graph **graph_out);
+int q4_graph_launch(q4_graph *graph, void *hip_stream);
+int q4_graph_destroy(q4_graph *graph);
+
+/* Static string for a status code. */
+const char *q4_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

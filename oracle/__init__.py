@@ -189,10 +189,11 @@ def _row_split(m: int, threads: int):
 
 
 def matvec(fmt: int, buf: np.ndarray, m: int, k: int, x: np.ndarray, threads: int = 1,
-           absdot: bool = False):
+           absdot: bool = False, rows=None):
     """y[n][m] = fp32(sum_k w_hat * x) in float64; rows split over ``threads`` threads.
 
-    Returns y, or (y, sum_k |w_hat*x|) with ``absdot``.
+    Returns y, or (y, sum_k |w_hat*x|) with ``absdot``. ``rows`` (a list of
+    (r0, r1) ranges) restricts the work to those rows; the others stay 0.
     """
     buf = np.ascontiguousarray(buf, dtype=np.uint8)
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -211,12 +212,22 @@ def matvec(fmt: int, buf: np.ndarray, m: int, k: int, x: np.ndarray, threads: in
         else:
             L.oracle_matvec(fmt, _p(buf, _u8p), m, k, _p(x, _f32p), n, _p(y, _f32p), r0, r1)
 
-    _parallel(run, _row_split(m, threads))
+    ranges = _row_split(m, threads) if rows is None else _split_ranges(rows, threads)
+    _parallel(run, ranges)
     return (y, ad) if absdot else y
 
 
+def _split_ranges(rows, threads):
+    out = []
+    per = max(1, sum(r1 - r0 for r0, r1 in rows) // max(1, threads))
+    for r0, r1 in rows:
+        for a in range(r0, r1, per):
+            out.append((a, min(r1, a + per)))
+    return out
+
+
 def matmul(fmt: int, buf: np.ndarray, m: int, k: int, x_bf16: np.ndarray, round_w_bf16: bool = False,
-           threads: int = 1, absdot: bool = False):
+           threads: int = 1, absdot: bool = False, rows=None):
     """Y[n][m] = fp32(sum_k w_eff * X) in float64, X given as bf16 bit patterns."""
     buf = np.ascontiguousarray(buf, dtype=np.uint8)
     x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
@@ -230,7 +241,8 @@ def matmul(fmt: int, buf: np.ndarray, m: int, k: int, x_bf16: np.ndarray, round_
         L.oracle_matmul(fmt, _p(buf, _u8p), m, k, _p(x_bf16, _u16p), n, _p(y, _f32p),
                         1 if round_w_bf16 else 0, _p(ad, _f64p) if absdot else None, r0, r1)
 
-    _parallel(run, _row_split(m, threads))
+    ranges = _row_split(m, threads) if rows is None else _split_ranges(rows, threads)
+    _parallel(run, ranges)
     return (y, ad) if absdot else y
 
 

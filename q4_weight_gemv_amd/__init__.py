@@ -1,0 +1,159 @@
+"""Python binding of the Q4 weight-matrix product library (gfx950 / MI355X).
+
+Argument marshalling only: every entry point forwards to the C ABI declared
+in ``include/q4.h`` (the in-tree ``libq4gemv.so``), which runs the products in
+hand-written HIP kernels. PyTorch supplies device memory and streams. There
+is no fallback path: if the library is missing, import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libq4gemv.so")
+
+Q4_FMT_Q4_0 = 0
+Q4_FMT_Q4_K = 1
+
+Q4_OK = 0
+Q4_EINVAL = -1
+Q4_EUNSUPPORTED = -2
+Q4_EALIGN = -3
+Q4_ENONFINITE = -4
+Q4_ERANGE = -5
+Q4_EHIP = -6
+
+BLOCK = {Q4_FMT_Q4_0: 32, Q4_FMT_Q4_K: 256}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m q4_weight_gemv_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class q4_gemv_op(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("m", ctypes.c_int64), ("k", ctypes.c_int64)]
+
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_SIGS = {
+    "q4_weight_bytes": (ctypes.c_size_t, [ctypes.c_int, _i64, _i64]),
+    "q4_quantize_ref": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i64, _vp, ctypes.c_size_t]),
+    "q4_gemv": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q4_gemm": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q4_gemv_sequence": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_gemv_op), ctypes.c_int, _i64, _vp]),
+    "q4_graph_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_gemv_op), ctypes.c_int, _i64, _vp,
+                                        ctypes.POINTER(_vp)]),
+    "q4_graph_launch": (ctypes.c_int, [_vp, _vp]),
+    "q4_graph_destroy": (ctypes.c_int, [_vp]),
+    "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTS = tuple(_SIGS)
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {q4_strerror(status)} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != Q4_OK:
+        raise Q4Error(status, where)
+
+
+def q4_strerror(status: int) -> str:
+    return _lib.q4_strerror(status).decode()
+
+
+def q4_weight_bytes(fmt: int, m: int, k: int) -> int:
+    return int(_lib.q4_weight_bytes(fmt, m, k))
+
+
+def q4_quantize_ref(fmt: int, w: np.ndarray) -> np.ndarray:
+    """Host quantizer: float32 W[m][k] -> packed uint8 buffer (layout in include/q4.h)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D [m][k]")
+    m, k = w.shape
+    nbytes = q4_weight_bytes(fmt, m, k)
+    out = np.zeros(max(nbytes, 1), dtype=np.uint8)
+    _check(_lib.q4_quantize_ref(fmt, w.ctypes.data, m, k, out.ctypes.data, nbytes), "q4_quantize_ref")
+    return out[:nbytes]
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def q4_gemv(fmt: int, w, x, y, m: int, k: int, stream=None) -> None:
+    """y[n][m] = W_hat x for n = x.shape[0] tokens (1..8); torch device tensors."""
+    n = x.shape[0] if x.dim() == 2 else 1
+    _check(_lib.q4_gemv(fmt, w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k, n, _stream_ptr(stream)), "q4_gemv")
+
+
+def q4_gemm(fmt: int, w, x_bf16, y, m: int, k: int, stream=None) -> None:
+    """Y[n][m] = bf16(W_hat) X for bf16 X[n][k] (torch bfloat16/int16 device tensor)."""
+    n = x_bf16.shape[0]
+    _check(_lib.q4_gemm(fmt, w.data_ptr(), x_bf16.data_ptr(), y.data_ptr(), m, k, n, _stream_ptr(stream)),
+           "q4_gemm")
+
+
+def _ops_array(ops):
+    arr = (q4_gemv_op * len(ops))()
+    for i, (w, x, y, m, k) in enumerate(ops):
+        arr[i] = q4_gemv_op(w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k)
+    return arr
+
+
+def q4_gemv_sequence(fmt: int, ops, n: int, stream=None) -> None:
+    """Enqueue decode products back-to-back; ops = [(w, x, y, m, k), ...]."""
+    arr = _ops_array(ops)
+    _check(_lib.q4_gemv_sequence(fmt, arr, len(ops), n, _stream_ptr(stream)), "q4_gemv_sequence")
+
+
+class Q4Graph:
+    """A captured decode step: q4_graph_create / q4_graph_launch / q4_graph_destroy."""
+
+    def __init__(self, fmt: int, ops, n: int, stream=None):
+        self._ops = list(ops)  # keep the tensors alive: their pointers are in the graph
+        arr = _ops_array(self._ops)
+        h = ctypes.c_void_p(None)
+        _check(_lib.q4_graph_create(fmt, arr, len(self._ops), n, _stream_ptr(stream), ctypes.byref(h)),
+               "q4_graph_create")
+        self._h = h
+
+    def launch(self, stream=None) -> None:
+        _check(_lib.q4_graph_launch(self._h, _stream_ptr(stream)), "q4_graph_launch")
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            _check(_lib.q4_graph_destroy(self._h), "q4_graph_destroy")
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def raw():
+    """The ctypes library handle (tests call entry points with raw pointers)."""
+    return _lib

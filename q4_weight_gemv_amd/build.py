@@ -1,0 +1,71 @@
+"""Build the in-tree shared library ``libq4gemv.so`` for gfx950 with hipcc.
+
+Every .hip source is compiled for gfx950 only; the host quantizer (.cpp) is
+compiled as plain C++ with floating-point contraction off. Run directly
+(``python -m q4_weight_gemv_amd.build``) or through ``__graft_entry__.build()``.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OBJ = os.path.join(ROOT, "_build", "obj")
+LIB = os.path.join(HERE, "libq4gemv.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+COMMON = ["-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter", f"-I{INCLUDE}", f"-I{CSRC}"]
+# Packed fp32 VALU forms are kept out of the device code.
+DEVICE = ["-O3", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-ffp-contract=fast", "-munsafe-fp-atomics"]
+# -O2 for the host quantizer: clang's -O3 loop passes take many minutes on it.
+HOST_ONLY = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-pthread"]
+
+SOURCES = [
+    ("q4_host.cpp", "host"),
+    ("q4_gemv.hip", "device"),
+    ("q4_gemm.hip", "device"),
+    ("q4_stack.hip", "device"),
+]
+
+
+def _compile(src: str, kind: str) -> str:
+    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    path = os.path.join(CSRC, src)
+    if kind == "host":
+        cmd = [HIPCC, "-x", "c++"] + COMMON + HOST_ONLY + ["-c", path, "-o", out]
+    else:
+        cmd = [HIPCC, "-x", "hip"] + COMMON + DEVICE + ["-c", path, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(*s), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    if not shutil.which(HIPCC) and not os.path.exists(HIPCC):
+        sys.exit("hipcc not found")
+    build(verbose=True)

@@ -1,0 +1,218 @@
+"""GPU parity of the decode products (Q4_0 and Q4_K GEMV) against the oracle.
+
+* Dequantization bit-exact through the public entry point: a one-hot x = e_j
+  returns column j of W_hat exactly (products with one power of two and sums
+  of zeros are exact in every step of the kernel).
+* Outputs within 2e-3, normwise and elementwise (forward-error form), at
+  sizes spanning several tiles with ragged tails, at every workload shape
+  (sampled rows), for token counts 1..8.
+* Layer-stack sequence and graph replay reproduce the single calls bit for bit.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_common import GEMV_TOL, check_tolerance, sample_rows, say, threads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    import oracle
+    import q4_weight_gemv_amd as q4
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    oracle.lib()
+    return torch, q4, oracle
+
+
+def _quantize_both(q4, orc, fmt, w):
+    buf = q4.q4_quantize_ref(fmt, w)
+    ref = orc.quantize(fmt, w)
+    assert np.array_equal(buf, ref), "host quantizer and oracle disagree"
+    return buf
+
+
+def _gemv(env, fmt, buf, x, m, k):
+    torch, q4, _ = env
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    yd = torch.full((x.shape[0], m), float("nan"), dtype=torch.float32, device="cuda")
+    q4.q4_gemv(fmt, wd, xd, yd, m, k)
+    torch.cuda.synchronize()
+    return yd.cpu().numpy()
+
+
+ONEHOT_CASES = [
+    (0, 5, 32), (0, 37, 320), (0, 768, 768), (0, 129, 2560), (0, 300, 4096), (0, 70, 11008),
+    (1, 5, 256), (1, 37, 512), (1, 130, 1024), (1, 300, 4096), (1, 70, 11008),
+]
+
+
+@pytest.mark.parametrize("fmt,m,k", ONEHOT_CASES)
+def test_dequant_bit_exact_onehot(env, fmt, m, k):
+    torch, q4, orc = env
+    w = synth.weights(synth.seed_for(20 + fmt, k % 1000 + m), m, k)
+    buf = _quantize_both(q4, orc, fmt, w)
+    what = orc.dequantize(fmt, buf, m, k)
+    rng = np.random.default_rng(m * 7 + k)
+    cols = sorted(set([0, 1, 15, 16, 17, 31, 32, k - 1, k - 17] + rng.integers(0, k, 23).tolist()))
+    cols = [c for c in cols if 0 <= c < k]
+    for i in range(0, len(cols), 8):
+        group = cols[i:i + 8]
+        x = np.zeros((len(group), k), np.float32)
+        for t, c in enumerate(group):
+            x[t, c] = 1.0
+        say(f"onehot fmt={fmt} m={m} k={k} cols={group}")
+        y = _gemv(env, fmt, buf, x, m, k)
+        for t, c in enumerate(group):
+            got = y[t]
+            exp = what[:, c]
+            assert np.array_equal(got, exp), (c, np.nonzero(got != exp)[0][:5])
+
+
+def _parity(env, fmt, m, k, n, seed, rows=None):
+    torch, q4, orc = env
+    w = synth.weights(synth.seed_for(seed, 1), m, k)
+    x = synth.activations(synth.seed_for(seed, 1, True), n, k)
+    buf = _quantize_both(q4, orc, fmt, w)
+    say(f"parity fmt={fmt} m={m} k={k} n={n}")
+    y = _gemv(env, fmt, buf, x, m, k)
+    if rows is None:
+        yr, ad = orc.matvec(fmt, buf, m, k, x, threads=threads(), absdot=True)
+        idx = None
+    else:
+        ranges, idx = rows
+        yr, ad = orc.matvec(fmt, buf, m, k, x, threads=threads(), absdot=True, rows=ranges)
+    check_tolerance(y, yr, ad, GEMV_TOL, rows=idx, what=f"fmt={fmt} {m}x{k} n={n}")
+    return y
+
+
+SMALL_Q4_0 = [(1, 32), (3, 96), (37, 320), (130, 768), (257, 960), (515, 3072), (300, 4096), (77, 11008),
+              (1000, 2560), (2049, 768)]
+
+
+@pytest.mark.parametrize("m,k", SMALL_Q4_0)
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
+def test_parity_q4_0_small(env, m, k, n):
+    _parity(env, 0, m, k, n, seed=100 + n)
+
+
+SMALL_Q4_K = [(1, 256), (37, 512), (130, 1024), (257, 2560), (300, 4096), (77, 11008), (1025, 768 + 256)]
+
+
+@pytest.mark.parametrize("m,k", SMALL_Q4_K)
+@pytest.mark.parametrize("n", [1, 4, 6, 8])
+def test_parity_q4_k_small(env, m, k, n):
+    _parity(env, 1, m, k, n, seed=200 + n)
+
+
+WORKLOAD_SHAPES = sorted(set(synth.gpt2_124m_step() + synth.smollm2_360m_step() + synth.llama7b_layer()))
+
+
+@pytest.mark.parametrize("k,m", WORKLOAD_SHAPES)
+def test_parity_q4_0_workload_shapes(env, k, m):
+    # N = 1 (decode) at every matrix shape of the GPT-2, SmolLM2 and 7B workloads.
+    _parity(env, 0, m, k, 1, seed=300 + k % 17, rows=sample_rows(m, k))
+
+
+@pytest.mark.parametrize("k,m", synth.llama7b_layer()[:1] + synth.llama7b_layer()[2:])
+@pytest.mark.parametrize("n", [1, 4, 8])
+def test_parity_q4_k_7b(env, k, m, n):
+    _parity(env, 1, m, k, n, seed=400 + n, rows=sample_rows(m, k + n))
+
+
+@pytest.mark.parametrize("k,m", [(4096, 4096), (11008, 4096)])
+@pytest.mark.parametrize("n", [4, 8])
+def test_parity_q4_0_7b_batched(env, k, m, n):
+    _parity(env, 0, m, k, n, seed=500 + n, rows=sample_rows(m, n))
+
+
+def test_zero_rows_and_tokens_are_noops(env):
+    torch, q4, _ = env
+    y = torch.full((2, 8), 7.0, device="cuda")
+    w = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    x = torch.zeros((2, 64), device="cuda")
+    q4.q4_gemv(0, w, x, y, 0, 64)
+    q4.raw().q4_gemv(0, w.data_ptr(), x.data_ptr(), y.data_ptr(), 8, 64, 0, None)
+    torch.cuda.synchronize()
+    assert (y == 7.0).all()
+
+
+def test_misaligned_pointer_rejected(env):
+    torch, q4, _ = env
+    w = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(128, device="cuda")
+    y = torch.full((8,), 3.0, device="cuda")
+    st = q4.raw().q4_gemv(0, w.data_ptr() + 8, x.data_ptr(), y.data_ptr(), 8, 64, 1, None)
+    assert st == q4.Q4_EALIGN
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
+
+
+def test_deterministic(env):
+    torch, q4, orc = env
+    m, k = 2304, 768
+    w = synth.weights(61, m, k)
+    x = synth.activations(62, 3, k)
+    buf = q4.q4_quantize_ref(0, w)
+    a = _gemv(env, 0, buf, x, m, k)
+    b = _gemv(env, 0, buf, x, m, k)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_extreme_activation_scales(env):
+    # Per-unit power-of-two scaling: results track x * 2^s exactly for large
+    # and tiny s (fp16 alone would overflow at 65504 or flush tiny values).
+    torch, q4, orc = env
+    m, k = 96, 1024
+    w = synth.weights(71, m, k)
+    buf = q4.q4_quantize_ref(0, w)
+    x = synth.activations(72, 2, k)
+    y = _gemv(env, 0, buf, x, m, k)
+    for s in (40, -40, 90):
+        ys = _gemv(env, 0, buf, (x * np.float32(2.0 ** s)).astype(np.float32), m, k)
+        assert np.array_equal(ys, (y.astype(np.float64) * 2.0 ** s).astype(np.float32)), s
+    big = x.copy()
+    big[0, 5] = 1e6
+    yb = _gemv(env, 0, buf, big, m, k)
+    yr, ad = orc.matvec(0, buf, m, k, big, absdot=True)
+    check_tolerance(yb, yr, ad, GEMV_TOL, what="large activation")
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_sequence_and_graph_match_single_calls(env, fmt):
+    torch, q4, _ = env
+    shapes = [(768, 2304), (768, 768), (768, 3072), (3072, 768), (960, 320)] if fmt == 0 else \
+             [(1024, 512), (2560, 960), (4096, 257)]
+    n = 2
+    ops, refs = [], []
+    for i, (k, m) in enumerate(shapes):
+        w = synth.weights(800 + i, m, k)
+        x = synth.activations(900 + i, n, k)
+        wd = torch.from_numpy(q4.q4_quantize_ref(fmt, w)).cuda()
+        xd = torch.from_numpy(x).cuda()
+        ref = torch.empty((n, m), device="cuda")
+        q4.q4_gemv(fmt, wd, xd, ref, m, k)
+        refs.append(ref)
+        ops.append((wd, xd, torch.full((n, m), float("nan"), device="cuda"), m, k))
+    say(f"sequence fmt={fmt}")
+    q4.q4_gemv_sequence(fmt, ops, n)
+    torch.cuda.synchronize()
+    for (_, _, y, _, _), ref in zip(ops, refs):
+        assert torch.equal(y, ref)
+    say(f"graph fmt={fmt}")
+    g = q4.Q4Graph(fmt, ops, n)
+    for rep in range(3):
+        for (_, _, y, _, _) in ops:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.launch()
+        torch.cuda.synchronize()
+        _ = torch.randn(1000, device="cuda").sum().item()  # eager work between replays
+        for (_, _, y, _, _), ref in zip(ops, refs):
+            assert torch.equal(y, ref), rep
+    g.close()

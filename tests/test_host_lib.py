@@ -1,0 +1,193 @@
+"""CPU tests of the product library: exports, the host quantizer against the
+oracle (two independent implementations, byte-identical output), and every
+error status of the device entry points (validation precedes any HIP call,
+so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def q4():
+    import q4_weight_gemv_amd as q4
+
+    return q4
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "q4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(q4):
+    declared = _declared_functions()
+    assert set(declared) >= {"q4_weight_bytes", "q4_quantize_ref", "q4_gemv", "q4_gemm", "q4_strerror"}
+    lib = ctypes.CDLL(q4.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(q4.EXPORTS)
+
+
+def test_weight_bytes(q4):
+    assert q4.q4_weight_bytes(0, 768, 768) == 331_776
+    assert q4.q4_weight_bytes(1, 4096, 11008) == 25_362_432
+    assert q4.q4_weight_bytes(0, 4096, 11008) == 25_362_432
+    assert q4.q4_weight_bytes(0, 3, 33) == 0
+    assert q4.q4_weight_bytes(1, 3, 512 + 32) == 0
+    assert q4.q4_weight_bytes(0, -1, 32) == 0
+    assert q4.q4_weight_bytes(7, 1, 32) == 0
+    assert q4.q4_weight_bytes(0, 0, 32) == 0
+    total = sum(q4.q4_weight_bytes(0, m, k) for k, m in synth.gpt2_124m_step())
+    assert total == 69_486_768
+    total = sum(q4.q4_weight_bytes(0, m, k) for k, m in synth.smollm2_360m_step())
+    assert total == 203_489_280
+    total = sum(q4.q4_weight_bytes(1, m, k) for k, m in synth.llama7b_layer())
+    assert total == 85_524_480
+
+
+SHAPES = sorted(set(synth.gpt2_124m_step() + synth.smollm2_360m_step() + synth.llama7b_layer()))
+
+
+@pytest.mark.parametrize("k,m", [s for s in SHAPES if s[1] * s[0] <= 12_000_000])
+def test_quantize_ref_matches_oracle_q4_0(q4, orc, k, m):
+    w = synth.weights(synth.seed_for(9, k % 97 + m % 89), m, k)
+    assert np.array_equal(q4.q4_quantize_ref(0, w), orc.quantize(0, w))
+
+
+@pytest.mark.parametrize("k,m", [(4096, 512), (11008, 128), (768, 64)])
+def test_quantize_ref_matches_oracle_q4_k(q4, orc, k, m):
+    if k % 256:
+        k = 1024
+    w = synth.weights(synth.seed_for(8, k % 97 + m % 89), m, k)
+    assert np.array_equal(q4.q4_quantize_ref(1, w), orc.quantize(1, w))
+
+
+def _edge_matrix(k):
+    """Rows that exercise ties, subnormal scales, clamps, zeros and sign patterns."""
+    rng = np.random.default_rng(17)
+    rows = []
+    d = np.float32(0.0078125)
+    rows.append((rng.integers(-16, 17, size=k) * d / 2).astype(np.float32))   # many exact ties
+    rows.append((rng.standard_normal(k) * 1e-6).astype(np.float32))          # subnormal fp16 scales
+    rows.append(np.zeros(k, np.float32))
+    rows.append(np.full(k, -3.0, np.float32))
+    rows.append(np.full(k, 5.0, np.float32))
+    r = rng.standard_normal(k).astype(np.float32)
+    r[::7] *= 1000
+    rows.append(r)
+    rows.append((rng.standard_normal(k) * 60000).astype(np.float32))
+    rows.append(np.abs(rng.standard_normal(k)).astype(np.float32))              # all positive (Q4_K min 0)
+    rows.append(-np.abs(rng.standard_normal(k)).astype(np.float32) - 0.5)       # all negative
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_quantize_ref_matches_oracle_edges(q4, orc, fmt):
+    w = _edge_matrix(512)
+    assert np.array_equal(q4.q4_quantize_ref(fmt, w), orc.quantize(fmt, w))
+    # Golden blocks (Q4_0) through the product quantizer too.
+    if fmt == 0:
+        from golden import floats, load
+        for name, sec in load("q4_0_blocks.txt").items():
+            buf = q4.q4_quantize_ref(0, floats(sec["w"][0]).reshape(1, 32))
+            assert bytes(buf[:16]).hex() == sec["nibbles"][0], name
+    else:
+        from golden import floats, hexbytes, load
+        sec = load("q4_k_superblocks.txt")["K-B"]
+        assert bytes(q4.q4_quantize_ref(1, floats(sec["w"][0]).reshape(1, 256))) == hexbytes(sec["bytes"][0])
+
+
+def test_quantize_ref_status(q4, orc):
+    w = synth.weights(3, 64, 256)
+    w2 = w.copy()
+    w2[40, 200] = np.nan
+    w2[50, 3] = 1e9  # scale overflow in a later row: the first failing block decides
+    with pytest.raises(q4.Q4Error) as e:
+        q4.q4_quantize_ref(0, w2)
+    assert e.value.status == q4.Q4_ENONFINITE
+    with pytest.raises(orc.OracleError) as eo:
+        orc.quantize(0, w2)
+    assert eo.value.status == e.value.status
+    w3 = w.copy()
+    w3[10, 0] = 1e9
+    w3[11, 0] = np.inf
+    for fmt in (0, 1):
+        with pytest.raises(q4.Q4Error) as e:
+            q4.q4_quantize_ref(fmt, w3)
+        assert e.value.status == q4.Q4_ERANGE
+    lib = q4.raw()
+    out = np.zeros(16, np.uint8)
+    assert lib.q4_quantize_ref(0, w.ctypes.data, 64, 255, out.ctypes.data, 16) == q4.Q4_EINVAL
+    assert lib.q4_quantize_ref(0, w.ctypes.data, 64, 256, out.ctypes.data, 16) == q4.Q4_EINVAL  # short buffer
+    assert lib.q4_quantize_ref(0, None, 64, 256, out.ctypes.data, 1 << 20) == q4.Q4_EINVAL
+    assert lib.q4_quantize_ref(5, w.ctypes.data, 64, 256, out.ctypes.data, 1 << 20) == q4.Q4_EUNSUPPORTED
+    assert lib.q4_quantize_ref(0, w.ctypes.data, 0, 256, out.ctypes.data, 0) == q4.Q4_OK
+
+
+def test_quantize_ref_many_threads_same_bytes(q4, orc):
+    # Large enough that the product quantizer splits rows across threads.
+    w = synth.weights(77, 2048, 1024)
+    assert np.array_equal(q4.q4_quantize_ref(0, w), orc.quantize(0, w))
+    w[1500, 17] = np.nan
+    w[100, 900] = 1e9
+    with pytest.raises(q4.Q4Error) as e:
+        q4.q4_quantize_ref(0, w)
+    assert e.value.status == q4.Q4_ERANGE  # row 100 precedes row 1500
+
+
+A16 = 1 << 20  # fake, 16-byte aligned addresses: validation rejects before any HIP call
+
+
+@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm"])
+def test_product_argument_errors(q4, entry):
+    f = getattr(q4.raw(), entry)
+    ok = (A16, A16 * 2, A16 * 3)
+    assert f(9, *ok, 64, 256, 1, None) == q4.Q4_EUNSUPPORTED          # unknown format
+    assert f(0, *ok, 64, 48, 1, None) == q4.Q4_EINVAL                 # k not a multiple of 32
+    assert f(1, *ok, 64, 288, 1, None) == q4.Q4_EINVAL                # k not a multiple of 256
+    assert f(0, *ok, 64, 0, 1, None) == q4.Q4_EINVAL
+    assert f(0, *ok, -1, 256, 1, None) == q4.Q4_EINVAL
+    assert f(0, *ok, 64, 256, -1, None) == q4.Q4_EINVAL
+    assert f(0, None, A16, A16, 64, 256, 1, None) == q4.Q4_EINVAL     # null pointers
+    assert f(0, A16, None, A16, 64, 256, 1, None) == q4.Q4_EINVAL
+    assert f(0, A16, A16, None, 64, 256, 1, None) == q4.Q4_EINVAL
+    assert f(0, A16 + 2, A16, A16, 64, 256, 1, None) == q4.Q4_EALIGN  # misaligned w
+    assert f(0, A16, A16 + 4, A16, 64, 256, 1, None) == q4.Q4_EALIGN  # misaligned x
+    assert f(0, A16, A16, A16 + 2, 64, 256, 1, None) == q4.Q4_EALIGN  # misaligned y
+    assert f(0, None, None, None, 0, 256, 1, None) == q4.Q4_OK        # m == 0: no-op
+    assert f(0, None, None, None, 64, 256, 0, None) == q4.Q4_OK       # n == 0: no-op
+    assert f(0, *ok, 1 << 30, 1 << 10, 1, None) == q4.Q4_EUNSUPPORTED  # beyond 32-bit offsets
+    if entry == "q4_gemv":
+        assert f(0, *ok, 64, 256, 9, None) == q4.Q4_EUNSUPPORTED       # decode batch is 1..8
+
+
+def test_sequence_and_graph_argument_errors(q4):
+    lib = q4.raw()
+    ops = (q4.q4_gemv_op * 2)()
+    ops[0] = q4.q4_gemv_op(A16, A16, A16, 64, 256)
+    ops[1] = q4.q4_gemv_op(A16, A16 + 4, A16, 64, 256)  # misaligned x in the second op
+    assert lib.q4_gemv_sequence(0, ops, 2, 1, None) == q4.Q4_EALIGN
+    assert lib.q4_gemv_sequence(0, None, 2, 1, None) == q4.Q4_EINVAL
+    assert lib.q4_gemv_sequence(0, ops, -1, 1, None) == q4.Q4_EINVAL
+    assert lib.q4_gemv_sequence(0, ops, 1, 9, None) == q4.Q4_EUNSUPPORTED
+    assert lib.q4_gemv_sequence(0, ops, 0, 1, None) == q4.Q4_OK
+    h = ctypes.c_void_p(None)
+    assert lib.q4_graph_create(0, ops, 2, 1, None, ctypes.byref(h)) == q4.Q4_EALIGN
+    assert h.value is None
+    assert lib.q4_graph_create(0, ops, 1, 1, None, None) == q4.Q4_EINVAL
+    assert lib.q4_graph_launch(None, None) == q4.Q4_EINVAL
+    assert lib.q4_graph_destroy(None) == q4.Q4_OK
+
+
+def test_strerror(q4):
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert q4.q4_strerror(st) and q4.q4_strerror(st) != "unknown status"
+    assert q4.q4_strerror(-99) == "unknown status"
