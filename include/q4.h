@@ -103,6 +103,27 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
 int q4_gemv(int fmt, const void *w, const float *x, float *y,
             int64_t m, int64_t k, int64_t n, void *hip_stream);
 
+/* Tile geometry of the decode product. The library picks it per shape; the
+ * tuned entry point lets a sweep override it (tile and workgroup sizes are
+ * tunable parameters whose defaults come from an empirical sweep: Llamas on
+ * the Web, technical summary, Methodology section 2, "tunable parameters").
+ * A zero field keeps the library's choice. Instantiated geometries
+ * (lanes_per_row, rows_per_lane, waves_per_group): (8,1,1) (8,2,1) (8,4,1)
+ * (16,1,1) (16,2,1) (32,1,1) (32,2,1) (64,1,1) (16,1,4) (32,1,4) (32,2,4)
+ * (64,1,4) (64,2,4) (64,4,4); others return Q4_EUNSUPPORTED. */
+typedef struct {
+    int lanes_per_row;   /* lanes sharing one weight row: 8, 16, 32 or 64 */
+    int rows_per_lane;   /* rows each lane streams at once: 1, 2 or 4 */
+    int waves_per_group; /* waves per workgroup: 1 or 4 */
+    int groups_per_cu;   /* workgroups per compute unit the grid is sized for (0..64) */
+} q4_gemv_tuning;
+
+/* q4_gemv with an explicit tile geometry; same arguments, layouts, results
+ * and errors, plus Q4_EINVAL for a null or negative tuning and
+ * Q4_EUNSUPPORTED for a geometry that is not instantiated. */
+int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y,
+                  int64_t m, int64_t k, int64_t n, const q4_gemv_tuning *tuning, void *hip_stream);
+
 /* Prefill product Y[t][i] = sum_k bf16_rne(w_hat[i][k]) * X[t][k], fp32 out.
  * w: device, quantized as above (Q4_0 or Q4_K), 16-byte aligned; x_bf16: device bf16 bit
  * patterns [n][k], 16-byte aligned; y: device float32 [n][m], 4-byte aligned.

@@ -74,6 +74,7 @@ def lib():
                 "oracle_matvec": (None, [ctypes.c_int, _u8p, _i64, _i64, _f32p, _i64, _f32p, _i64, _i64]),
                 "oracle_matvec_absdot": (None, [ctypes.c_int, _u8p, _i64, _i64, _f32p, _i64, _f32p, _f64p, _i64, _i64]),
                 "oracle_matmul": (None, [ctypes.c_int, _u8p, _i64, _i64, _u16p, _i64, _f32p, ctypes.c_int, _f64p, _i64, _i64]),
+                "oracle_matvec_termscale": (None, [ctypes.c_int, _u8p, _i64, _i64, _f32p, _i64, _f64p, _i64, _i64]),
                 "oracle_matvec_one": (ctypes.c_double, [ctypes.c_int, _u8p, _i64, _i64, _f32p, _i64, _i64, _f64p]),
             }
             for name, (res, args) in sigs.items():
@@ -244,6 +245,23 @@ def matmul(fmt: int, buf: np.ndarray, m: int, k: int, x_bf16: np.ndarray, round_
     ranges = _row_split(m, threads) if rows is None else _split_ranges(rows, threads)
     _parallel(run, ranges)
     return (y, ad) if absdot else y
+
+
+def termscale(fmt: int, buf: np.ndarray, m: int, k: int, x: np.ndarray, threads: int = 1, rows=None):
+    """sum_k (term magnitudes of w_hat[i][k]) * |x[t][k]| per output (see q4_oracle.c)."""
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    n = x.shape[0]
+    out = np.zeros((n, m), dtype=np.float64)
+    L = lib()
+
+    def run(r0, r1):
+        L.oracle_matvec_termscale(fmt, _p(buf, _u8p), m, k, _p(x, _f32p), n, _p(out, _f64p), r0, r1)
+
+    _parallel(run, _row_split(m, threads) if rows is None else _split_ranges(rows, threads))
+    return out
 
 
 def matvec_one(fmt: int, buf: np.ndarray, m: int, k: int, x: np.ndarray, t: int, i: int):

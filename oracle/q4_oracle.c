@@ -435,6 +435,39 @@ void oracle_matmul(int fmt, const uint8_t *w, int64_t m, int64_t k,
     }
 }
 
+/* Magnitude scale of the terms a format's value is built from, summed with
+ * |x|: Q4_0's value is the single term (q - 8)*d, so the scale is
+ * sum_k |w_hat * x|; Q4_K's value is the difference d*sc*q - dmin*m of two
+ * terms, so the scale is sum_k (|d*sc*q| + |dmin*m|) * |x|. An elementwise
+ * forward-error bound for an evaluation that keeps the two Q4_K terms apart
+ * (as the format's structure invites) is stated against this scale. */
+static double term_magnitude(int fmt, const uint8_t *w, int64_t m, int64_t k, int64_t r, int64_t c)
+{
+    if (fmt == 0) return fabs((double)oracle_q4_0_weight(w, m, k, r, c));
+    int64_t ns = k / 256;
+    const uint8_t *sbp = w + (r * ns + c / 256) * 144;
+    int e = (int)(c % 256);
+    int j = e / 32;
+    uint8_t byte = sbp[16 + 32 * (e / 64) + e % 32];
+    int q = ((e % 64) >= 32) ? (byte >> 4) : (byte & 15);
+    uint8_t sc[8], mn[8];
+    oracle_q4_k_unpack_scales(sbp + 4, sc, mn);
+    double d = oracle_fp16_to_fp32((uint16_t)(sbp[0] | (sbp[1] << 8)));
+    double dmin = oracle_fp16_to_fp32((uint16_t)(sbp[2] | (sbp[3] << 8)));
+    return fabs(d * sc[j] * q) + fabs(dmin * mn[j]);
+}
+
+void oracle_matvec_termscale(int fmt, const uint8_t *w, int64_t m, int64_t k, const float *x, int64_t n,
+                             double *scale, int64_t row0, int64_t row1)
+{
+    for (int64_t i = row0; i < row1; i++)
+        for (int64_t t = 0; t < n; t++) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < k; c++) acc += term_magnitude(fmt, w, m, k, i, c) * fabs((double)x[t * k + c]);
+            scale[t * m + i] = acc;
+        }
+}
+
 /* One output of the products, for sampled checks at full size. */
 double oracle_matvec_one(int fmt, const uint8_t *w, int64_t m, int64_t k,
                          const float *x, int64_t t, int64_t i, double *absdot)

@@ -29,9 +29,14 @@ Q4_EHIP = -6
 BLOCK = {Q4_FMT_Q4_0: 32, Q4_FMT_Q4_K: 256}
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m q4_weight_gemv_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python q4_weight_gemv_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+class q4_gemv_tuning(ctypes.Structure):
+    _fields_ = [("lanes_per_row", ctypes.c_int), ("rows_per_lane", ctypes.c_int),
+                ("waves_per_group", ctypes.c_int), ("groups_per_cu", ctypes.c_int)]
 
 
 class q4_gemv_op(ctypes.Structure):
@@ -45,6 +50,8 @@ _SIGS = {
     "q4_weight_bytes": (ctypes.c_size_t, [ctypes.c_int, _i64, _i64]),
     "q4_quantize_ref": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i64, _vp, ctypes.c_size_t]),
     "q4_gemv": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q4_gemv_tuned": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64,
+                                      ctypes.POINTER(q4_gemv_tuning), _vp]),
     "q4_gemm": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q4_gemv_sequence": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_gemv_op), ctypes.c_int, _i64, _vp]),
     "q4_graph_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_gemv_op), ctypes.c_int, _i64, _vp,
@@ -106,6 +113,15 @@ def q4_gemv(fmt: int, w, x, y, m: int, k: int, stream=None) -> None:
     """y[n][m] = W_hat x for n = x.shape[0] tokens (1..8); torch device tensors."""
     n = x.shape[0] if x.dim() == 2 else 1
     _check(_lib.q4_gemv(fmt, w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k, n, _stream_ptr(stream)), "q4_gemv")
+
+
+def q4_gemv_tuned(fmt: int, w, x, y, m: int, k: int, lanes_per_row=0, rows_per_lane=0, waves_per_group=0,
+                  groups_per_cu=0, stream=None) -> None:
+    """q4_gemv with an explicit tile geometry (0 keeps the library's choice)."""
+    n = x.shape[0] if x.dim() == 2 else 1
+    t = q4_gemv_tuning(lanes_per_row, rows_per_lane, waves_per_group, groups_per_cu)
+    _check(_lib.q4_gemv_tuned(fmt, w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k, n, ctypes.byref(t),
+                              _stream_ptr(stream)), "q4_gemv_tuned")
 
 
 def q4_gemm(fmt: int, w, x_bf16, y, m: int, k: int, stream=None) -> None:

@@ -1,8 +1,9 @@
 """Build the in-tree shared library ``libq4gemv.so`` for gfx950 with hipcc.
 
 Every .hip source is compiled for gfx950 only; the host quantizer (.cpp) is
-compiled as plain C++ with floating-point contraction off. Run directly
-(``python -m q4_weight_gemv_amd.build``) or through ``__graft_entry__.build()``.
+compiled as plain C++ with floating-point contraction off. Run as a script
+(``python q4_weight_gemv_amd/build.py``) or through ``__graft_entry__.build()``;
+it does not import the package (which would load the library being rebuilt).
 """
 from __future__ import annotations
 
@@ -32,6 +33,10 @@ HOST_ONLY = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-pthread"]
 SOURCES = [
     ("q4_host.cpp", "host"),
     ("q4_gemv.hip", "device"),
+    ("q4_gemv_q4_0_a.hip", "device"),
+    ("q4_gemv_q4_0_b.hip", "device"),
+    ("q4_gemv_q4_k_a.hip", "device"),
+    ("q4_gemv_q4_k_b.hip", "device"),
     ("q4_gemm.hip", "device"),
     ("q4_stack.hip", "device"),
 ]

@@ -1,0 +1,640 @@
+// Decode product y = W_hat x for 4-bit block-quantized W on gfx950 (MI355X):
+// device code, shared by the per-format instantiation units.
+//
+// Method (Llamas on the Web, technical summary, Methodology section 3,
+// "integrated dequantization"): for the matrix-vector product of decode, the
+// quantized weights are unpacked and scaled in registers and never written
+// anywhere; the format decoder is a compile-time policy (same section,
+// "extensibility"), so Q4_0 and Q4_K share the kernel body.
+//
+// gfx950 design:
+//   * Memory bound: each 32-weight unit is one 16-byte nibble load (plus a
+//     2-byte scale for Q4_0, a 16-byte super-block header for Q4_K). Lanes of
+//     a row read consecutive 16-byte groups, so a wave instruction moves up to
+//     1 KiB of one row (rows are split over LPR lanes; 64/LPR rows per wave).
+//   * No MFMA: the arithmetic intensity is ~3.6 flop/byte.
+//   * VALU budget: a nibble pair is turned into an fp16 pair by one AND:
+//     (w & 0x000F000F) reads as two fp16 subnormals q*2^-24, and
+//     (w & 0x00F000F0) as 16q*2^-24. For Q4_0 one packed fp16 add of
+//     -8*2^-24 (-128*2^-24) makes them (q-8)*2^-24 (16(q-8)*2^-24), still
+//     exact subnormals, so every product (q-8)*x is exact and a zero weight
+//     contributes exactly zero. v_dot2c_f32_f16 multiplies the pairs with fp16
+//     activation pairs and accumulates in fp32. Q4_K keeps unsigned codes and
+//     folds its mins in through precomputed activation sums, one per 16
+//     elements (the format's value is itself that difference of two terms).
+//   * Activations are staged once per workgroup into LDS as fp16 pairs in the
+//     order the unpack produces them, each 32-element unit scaled by a power
+//     of two that puts its largest magnitude in [2^14, 2^15): the scaling is
+//     exact, fp16 cannot overflow, and the unit's result is rescaled by the
+//     same power of two. Each scaled activation is held as an unevaluated sum
+//     hi + lo of two fp16 values (lo = fp16(x - hi)), so it is represented to
+//     about 2^-23 relative and every product term is as accurate as fp32
+//     arithmetic; the two halves cost a second dot2 per pair.
+//   * Workgroups of one wave for short rows need no s_barrier (LDS order
+//     within a wave suffices); longer rows share the staging across 4 waves.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "q4_internal.h"
+
+namespace q4 {
+namespace gemv {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kLo = 0x000F000Fu;  // low nibbles of bytes 0 and 2
+constexpr uint32_t kHi = 0x00F000F0u;  // high nibbles of bytes 0 and 2
+constexpr int kLdsBytesPerUnit = 144;  // 2 x 64 B of fp16 pairs (hi, lo) + 16 B of unit metadata
+constexpr int kMaxLdsBytes = 64 * 1024;
+// Activation items per thread per staging round: one round covers a
+// 11008-long row for one token in a 4-wave group (1376 items / 256 threads).
+template <int WAVES>
+constexpr int kStageRound = WAVES == 1 ? 4 : 6;
+
+// Raw buffer loads: base + voffset + soffset (+ immediate), range-checked by
+// the hardware against num_records (an out-of-range load returns 0 and does
+// not fault), so ragged rows and tiles need no clamps or branches.
+// Descriptor word 3 for the gfx9 family: 32-bit untyped raw buffer.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;  // cache policy bit: streamed data, not kept
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), static_cast<int>(bytes),
+                                             kBufferWord3);
+}
+
+// Descriptor for the bytes [off, bytes) of a buffer: the uniform part of an
+// address goes into the (scalar) base, so the hardware range check, which
+// covers the per-lane offset, still stops at the buffer's end.
+// (Both values are wave-uniform; readfirstlane states that to the compiler,
+// which otherwise may build the descriptor in vector registers and wrap every
+// load in a per-lane loop.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sub_rsrc(const uint8_t *p, uint32_t bytes, uint32_t off)
+{
+    const uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(off < bytes ? off : bytes)));
+    return make_rsrc(p + o, bytes - o);
+}
+
+template <int AUX>
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi)
+{
+    half2_t h = {lo, hi};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// x = hi + lo (+ at most 2^-24 |x|): hi = fp16(x), lo = fp16(x - hi); the
+// difference x - hi is exact in fp32.
+struct Split {
+    _Float16 hi, lo;
+};
+__device__ __forceinline__ Split split(float x)
+{
+    const _Float16 hi = static_cast<_Float16>(x);
+    const _Float16 lo = static_cast<_Float16>(x - static_cast<float>(hi));
+    return Split{hi, lo};
+}
+
+__device__ __forceinline__ float half_lo(uint32_t v)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v & 0xFFFFu)));
+}
+
+__device__ __forceinline__ float half_hi(uint32_t v)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16)));
+}
+
+// Sum of the 16 products of one dword of nibbles with its four fp16 pairs,
+// hi parts (xh) and lo parts (xl).
+// Pair order: (L, L+2), (H, H+2)/16, (L+1, L+3), (H+1, H+3)/16.
+// Packed fp16 add of a constant pair to an fp16 pair given as bits.
+__device__ __forceinline__ uint32_t add_h2(uint32_t a, _Float16 c)
+{
+    const half2_t r = __builtin_bit_cast(half2_t, a) + half2_t{c, c};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Q4_0 codes as signed subnormal pairs: (q-8)*2^-24 for low nibbles,
+// 16(q-8)*2^-24 for high nibbles (exact: integers up to 128 times 2^-24).
+__device__ __forceinline__ float dot_dword(uint32_t q, u32x4 xh, u32x4 xl, float acc)
+{
+    const _Float16 m8 = static_cast<_Float16>(-0x1p-21f);   // -8 * 2^-24
+    const _Float16 m128 = static_cast<_Float16>(-0x1p-17f); // -128 * 2^-24
+    const uint32_t s = q >> 8;
+    const uint32_t p0 = add_h2(q & kLo, m8), p1 = add_h2(q & kHi, m128);
+    const uint32_t p2 = add_h2(s & kLo, m8), p3 = add_h2(s & kHi, m128);
+    acc = dot2(p0, xh.x, acc);
+    acc = dot2(p1, xh.y, acc);
+    acc = dot2(p2, xh.z, acc);
+    acc = dot2(p3, xh.w, acc);
+    acc = dot2(p0, xl.x, acc);
+    acc = dot2(p1, xl.y, acc);
+    acc = dot2(p2, xl.z, acc);
+    acc = dot2(p3, xl.w, acc);
+    return acc;
+}
+
+// ---- format policies --------------------------------------------------------
+// A unit is 32 weights: 16 nibble bytes whose low nibbles are 16 consecutive
+// elements starting at unit_base(u) and whose high nibbles are the 16 elements
+// kHighOffset further on.
+
+struct FmtQ4_0 {
+    static constexpr int kFormat = Q4_FMT_Q4_0;
+    static constexpr int kHighOffset = 16;
+    static constexpr int kBatchUnits = 4;  // units (x rows) per lane per batch: 4 x 20 B in flight
+    __device__ static int unit_base(int u) { return u << 5; }
+
+    struct Regs {
+        u32x4 q;
+        uint32_t d;
+    };
+    // Unit (row, u) with row = trow + rowrel and u = ubase + li + jl: its
+    // 16 nibble bytes at (row*nu + u)*16, its scale at scale_plane +
+    // (row*nu + u)*2. The lane part goes in the VGPR offset, the uniform part
+    // (tile, chunk, batch) in the SGPR offset, jl in the immediate.
+    __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+                                uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl)
+    {
+        const uint32_t uni_u = trow * nu + ubase;
+        const uint32_t lane_u = rowrel * nu + li + jl;
+        g.q = load16<kNonTemporal>(sub_rsrc(w, wbytes, uni_u * 16u), lane_u * 16u, 0);
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(sub_rsrc(w, wbytes, scale_plane + uni_u * 2u), lane_u * 2u, 0, 0);
+    }
+    // Unit metadata: z = 2^(e+24) (unit scale times the fp16-subnormal factor).
+    __device__ static f32x4 meta(float /*gl*/, float /*gh*/, int e)
+    {
+        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + 24), 0.0f};
+    }
+    template <int N, int R>
+    __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
+                                      const f32x4 *__restrict__ meta, int ul, int uc, uint32_t /*u*/,
+                                      float (&acc)[R][N])
+    {
+#pragma unroll
+        for (int t = 0; t < N; t++) {
+            const f32x4 mt = meta[t * uc + ul];
+            u32x4 xh[4], xl[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                xh[i] = xs[(t * 8 + 2 * i) * uc + ul];
+                xl[i] = xs[(t * 8 + 2 * i + 1) * uc + ul];
+            }
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                float a = 0.0f;
+                a = dot_dword(g[r].q.x, xh[0], xl[0], a);
+                a = dot_dword(g[r].q.y, xh[1], xl[1], a);
+                a = dot_dword(g[r].q.z, xh[2], xl[2], a);
+                a = dot_dword(g[r].q.w, xh[3], xl[3], a);
+                acc[r][t] = __builtin_fmaf(half_lo(g[r].d) * mt.z, a, acc[r][t]);
+            }
+        }
+    }
+};
+
+struct FmtQ4_K {
+    static constexpr int kFormat = Q4_FMT_Q4_K;
+    static constexpr int kHighOffset = 32;
+    static constexpr int kBatchUnits = 2;  // each unit is two 16-byte loads
+    // unit u = slice (u & 7) of super-block u >> 3; slice h covers the 16
+    // bytes at 16h of the 128 nibble bytes: chunk c = h >> 1, half h & 1.
+    __device__ static int unit_base(int u) { return ((u >> 3) << 8) + (((u & 7) >> 1) << 6) + ((u & 1) << 4); }
+
+    struct Regs {
+        u32x4 q;
+        u32x4 h;
+    };
+    // Unit u = ubase + li + jl of row trow + rowrel (ubase and jl multiples
+    // of 8): super-block (row*ns + u/8) at 144 bytes each, header at its
+    // start, slice u & 7 = li & 7 at 16 + 16*(li & 7).
+    __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t /*scale_plane*/, uint32_t nu,
+                                uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl)
+    {
+        const uint32_t ns = nu >> 3;
+        const __amdgpu_buffer_rsrc_t r = sub_rsrc(w, wbytes, (trow * ns + (ubase >> 3)) * 144u);
+        const uint32_t lane_b = (rowrel * ns + (li >> 3) + (jl >> 3)) * 144u;
+        g.h = load16<0>(r, lane_b, 0);
+        g.q = load16<kNonTemporal>(r, lane_b + 16u + ((li & 7u) << 4), 0);
+    }
+    // Unit metadata: x = sum of the 16 low-nibble activations, y = 16 x sum of
+    // the 16 pre-divided high-nibble activations (both scaled units),
+    // z = 2^(e+24), w = 2^e.
+    __device__ static f32x4 meta(float gl, float gh, int e)
+    {
+        return f32x4{gl, gh, __builtin_amdgcn_ldexpf(1.0f, e + 24), __builtin_amdgcn_ldexpf(1.0f, e)};
+    }
+    template <int N, int R>
+    __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
+                                      const f32x4 *__restrict__ meta, int ul, int uc, uint32_t u,
+                                      float (&acc)[R][N])
+    {
+        // Sub-blocks a = 2c (low nibbles) and b = 2c+1 (high nibbles), c = (u & 7) >> 1.
+        // Their 6-bit fields sit in bytes 2(c&1) and 2(c&1)+1 of the S words.
+        const uint32_t c = (u & 7u) >> 1;
+        const uint32_t sh = (c & 1u) << 4;
+        const bool upper = c >= 2;
+        float sca[R], scb[R], ma[R], mb[R], fd[R], fm[R];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const uint32_t s0 = g[r].h.y >> sh, s1 = g[r].h.z >> sh, s2 = g[r].h.w >> sh;
+            const uint32_t sca_i = upper ? ((s2 & 15u) | (((s0 >> 6) & 3u) << 4)) : (s0 & 63u);
+            const uint32_t scb_i = upper ? (((s2 >> 8) & 15u) | (((s0 >> 14) & 3u) << 4)) : ((s0 >> 8) & 63u);
+            const uint32_t ma_i = upper ? (((s2 >> 4) & 15u) | (((s1 >> 6) & 3u) << 4)) : (s1 & 63u);
+            const uint32_t mb_i = upper ? (((s2 >> 12) & 15u) | (((s1 >> 14) & 3u) << 4)) : ((s1 >> 8) & 63u);
+            sca[r] = static_cast<float>(sca_i);
+            scb[r] = static_cast<float>(scb_i);
+            ma[r] = static_cast<float>(ma_i);
+            mb[r] = static_cast<float>(mb_i);
+            fd[r] = half_lo(g[r].h.x);
+            fm[r] = half_hi(g[r].h.x);
+        }
+#pragma unroll
+        for (int t = 0; t < N; t++) {
+            const f32x4 mt = meta[t * uc + ul];
+            u32x4 xh[4], xl[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                xh[i] = xs[(t * 8 + 2 * i) * uc + ul];
+                xl[i] = xs[(t * 8 + 2 * i + 1) * uc + ul];
+            }
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                float aa = 0.0f, ab = 0.0f;
+                const u32x4 q = g[r].q;
+                // Each dword: pairs 0 and 2 belong to sub-block a, 1 and 3 to b.
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const uint32_t qi = i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
+                    const uint32_t s = qi >> 8;
+                    const uint32_t p0 = qi & kLo, p1 = qi & kHi, p2 = s & kLo, p3 = s & kHi;
+                    aa = dot2(p0, xh[i].x, aa);
+                    ab = dot2(p1, xh[i].y, ab);
+                    aa = dot2(p2, xh[i].z, aa);
+                    ab = dot2(p3, xh[i].w, ab);
+                    aa = dot2(p0, xl[i].x, aa);
+                    ab = dot2(p1, xl[i].y, ab);
+                    aa = dot2(p2, xl[i].z, aa);
+                    ab = dot2(p3, xl[i].w, ab);
+                }
+                const float t1 = __builtin_fmaf(scb[r], ab, sca[r] * aa);
+                const float t2 = __builtin_fmaf(mb[r], mt.y, ma[r] * mt.x);
+                acc[r][t] = __builtin_fmaf(fd[r] * mt.z, t1, acc[r][t]);
+                acc[r][t] = __builtin_fmaf(-fm[r] * mt.w, t2, acc[r][t]);
+            }
+        }
+    }
+};
+
+// ---- workgroup synchronisation -----------------------------------------------
+
+template <int WAVES>
+__device__ __forceinline__ void wg_sync()
+{
+    if constexpr (WAVES == 1) {
+        // One wave: its LDS operations complete in issue order, so only the
+        // compiler must be kept from moving LDS accesses across this point.
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    } else {
+        __syncthreads();
+    }
+}
+
+// ---- activation staging -------------------------------------------------------
+// Units [c0, c0 + nuc) of every token -> LDS: planes (t, 2i) and (t, 2i+1)
+// hold the hi and lo fp16 pairs for nibble dword i. Item (t, ul, i) handles dword i
+// of unit ul: activations L..L+3 (low nibbles) and H..H+3 (high nibbles),
+// L = unit_base + 4i, H = L + kHighOffset. The four items of a unit are four
+// consecutive lanes, which exchange their maxima and partial sums.
+
+// The four items of a unit are one lane quad (every count and stride here is
+// a multiple of 4), so their exchanges are DPP quad permutations.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Round one of the staging issues P items' activation loads per thread, then
+// calls issue() (the first weight batch), and only then waits for the
+// activations, so the weight loads are in flight during the staging and the
+// staging waits on one L2 round trip per round, not one per item.
+template <class F, int N, int NT, int P, class Issue>
+__device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, int nuc, int uc,
+                                      u32x4 *__restrict__ xs, f32x4 *__restrict__ meta, int tid, Issue issue)
+{
+    const int per_tok = nuc * 4;
+    const int total = N * per_tok;
+    // it / per_tok as a multiply-high by ceil(2^32 / per_tok): exact while
+    // it * per_tok < 2^32 (it < 8 * per_tok and per_tok <= 4 * 65536/144 here).
+    const uint32_t inv = N == 1 ? 0u : 0xFFFFFFFFu / static_cast<uint32_t>(per_tok) + 1u;
+    auto split_item = [&](int it, int &t, int &rem) {
+        if constexpr (N == 1) {
+            t = 0;
+            rem = it;
+        } else {
+            t = static_cast<int>(__umulhi(static_cast<uint32_t>(it), inv));
+            rem = it - t * per_tok;
+        }
+    };
+    bool issued = false;
+    for (int base = tid; base < total || !issued; base += P * NT) {
+        f32x4 a[P], b[P];
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            // Branch-free: an item past the end lands past N*K and reads zeros.
+            int t, rem;
+            split_item(base + p * NT, t, rem);
+            const uint32_t off = static_cast<uint32_t>(t * K + F::unit_base(c0 + (rem >> 2)) + 4 * (rem & 3)) * 4u;
+            a[p] = __builtin_bit_cast(f32x4, load16<0>(xr, off, 0));
+            b[p] = __builtin_bit_cast(f32x4, load16<0>(xr, off + 4u * F::kHighOffset, 0));
+        }
+        if (!issued) {
+            issue();
+            issued = true;
+        }
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            // Items past the end are processed (on zeros) but store nothing:
+            // keeping the arithmetic unconditional keeps the loads above from
+            // being sunk into a branch (which would serialise them behind the
+            // weights).
+            const bool live = base + p * NT < total;
+            int t, rem;
+            split_item(live ? base + p * NT : 0, t, rem);
+            const int ul = rem >> 2;
+            const int i = rem & 3;
+            float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a[p].x), __builtin_fabsf(a[p].y)),
+                                       __builtin_fmaxf(__builtin_fabsf(a[p].z), __builtin_fabsf(a[p].w)));
+            mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(b[p].x), __builtin_fabsf(b[p].y)),
+                                                     __builtin_fmaxf(__builtin_fabsf(b[p].z), __builtin_fabsf(b[p].w))));
+            mx = __builtin_fmaxf(mx, dpp<0xB1>(mx));  // quad_perm [1,0,3,2]
+            mx = __builtin_fmaxf(mx, dpp<0x4E>(mx));  // quad_perm [2,3,0,1]
+            // Largest magnitude -> [2^14, 2^15): x_tilde = x * 2^-e.
+            const int e = __builtin_amdgcn_frexp_expf(mx) - 15;
+            // Scaled activations (exact: power-of-two scaling); the high-nibble
+            // ones pre-divided by 16 to cancel the 16x of their unpacked codes.
+            const float l0 = __builtin_amdgcn_ldexpf(a[p].x, -e), l1 = __builtin_amdgcn_ldexpf(a[p].y, -e);
+            const float l2 = __builtin_amdgcn_ldexpf(a[p].z, -e), l3 = __builtin_amdgcn_ldexpf(a[p].w, -e);
+            const float h0 = __builtin_amdgcn_ldexpf(b[p].x, -e - 4), h1 = __builtin_amdgcn_ldexpf(b[p].y, -e - 4);
+            const float h2 = __builtin_amdgcn_ldexpf(b[p].z, -e - 4), h3 = __builtin_amdgcn_ldexpf(b[p].w, -e - 4);
+            const Split sl0 = split(l0), sl1 = split(l1), sl2 = split(l2), sl3 = split(l3);
+            const Split sh0 = split(h0), sh1 = split(h1), sh2 = split(h2), sh3 = split(h3);
+            const u32x4 vhi = u32x4{pack_h2(sl0.hi, sl2.hi), pack_h2(sh0.hi, sh2.hi), pack_h2(sl1.hi, sl3.hi),
+                                    pack_h2(sh1.hi, sh3.hi)};
+            const u32x4 vlo = u32x4{pack_h2(sl0.lo, sl2.lo), pack_h2(sh0.lo, sh2.lo), pack_h2(sl1.lo, sl3.lo),
+                                    pack_h2(sh1.lo, sh3.lo)};
+            float gl = (l0 + l1) + (l2 + l3);
+            float gh = (h0 + h1) + (h2 + h3);
+            gl += dpp<0xB1>(gl);
+            gh += dpp<0xB1>(gh);
+            gl += dpp<0x4E>(gl);
+            gh += dpp<0x4E>(gh);
+            const f32x4 mv = F::meta(gl, 16.0f * gh, e);
+            if (live) {
+                u32x4 *dst = xs + (t * 8 + 2 * i) * uc + ul;
+                dst[0] = vhi;
+                dst[uc] = vlo;
+                if (i == 0) meta[t * uc + ul] = mv;
+            }
+        }
+    }
+}
+
+// ---- cross-lane row reduction ------------------------------------------------------
+// Sum over the LPR consecutive lanes of a sub-group; the total lands in the
+// sub-group's first lane. Quad and row steps use DPP (quad_perm, row_ror);
+// steps across 16-lane rows use a lane shuffle.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v)
+{
+    return v + dpp<CTRL>(v);
+}
+
+template <int LPR>
+__device__ __forceinline__ float row_reduce(float v)
+{
+    v = dpp_add<0xB1>(v);               // quad_perm [1,0,3,2]: + lane ^ 1
+    v = dpp_add<0x4E>(v);               // quad_perm [2,3,0,1]: + lane ^ 2
+    // row_ror:N moves data N lanes up within a 16-lane row (lane i reads lane
+    // i-N mod 16), so row_ror:12 makes lane i read lane i+4.
+    if constexpr (LPR >= 8) v = dpp_add<0x12C>(v);   // row_ror:12: + lane (i+4) mod 16
+    if constexpr (LPR >= 16) v = dpp_add<0x128>(v);  // row_ror:8: + lane (i+8) mod 16
+    if constexpr (LPR >= 32) v += __shfl_down(v, 16);
+    if constexpr (LPR >= 64) v += __shfl_down(v, 32);
+    return v;
+}
+
+// ---- the kernel -------------------------------------------------------------------
+// Workgroup = WAVES waves; a tile is RPG = WAVES * (64/LPR) * R consecutive
+// rows. In a tile, wave v covers rows v*RPW .. v*RPW + RPW - 1 (RPW =
+// (64/LPR)*R): sub-group s (lanes s*LPR .. s*LPR+LPR-1) handles rows
+// s + r*(64/LPR), r < R. Lane li of a sub-group handles units li, li+LPR, ...
+// of each of its rows, JB unit slots per batch. Workgroups stride over the
+// tiles (grid = min(tiles, resident capacity)), so the activations are staged
+// once per workgroup when they fit in LDS; weight batches are double-buffered
+// across tile boundaries, with the first batch issued before the staging.
+// When the activations do not fit (many tokens x long rows) the row is
+// processed in LDS-sized chunks, restaged per tile.
+
+template <class F, int N, int LPR, int R, int WAVES, int JB>
+__global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restrict__ w, uint32_t wbytes,
+                                                          const float *__restrict__ x,
+                                                          float *__restrict__ y, int M, int K, int uc,
+                                                          int ntiles)
+{
+    constexpr int SUBS = 64 / LPR;
+    constexpr int RPW = SUBS * R;
+    constexpr int RPG = WAVES * RPW;
+    constexpr int NT = 64 * WAVES;
+    extern __shared__ u32x4 lds[];
+    u32x4 *xs = lds;
+    f32x4 *meta = reinterpret_cast<f32x4 *>(lds + N * 8 * uc);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int sub = lane / LPR;
+    const int li = lane % LPR;
+    const int nu = K >> 5;
+    const uint32_t scale_plane = static_cast<uint32_t>(static_cast<uint64_t>(M) * static_cast<uint64_t>(K) / 2u);
+    const int row_in_tile = wave * RPW + sub;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, static_cast<uint32_t>(N) * static_cast<uint32_t>(K) * 4u);
+
+    float acc[R][N];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int r = 0; r < R; r++)
+#pragma unroll
+            for (int t = 0; t < N; t++) acc[r][t] = 0.0f;
+    };
+    zero_acc();
+
+    using Regs = typename F::Regs;
+
+    // Batch of JB unit slots (units c0 + li + (j0+jj)*LPR) of the lane's R rows
+    // in tile `tile`. Branch-free buffer loads that never fault: for a row past
+    // M (also every row of a tile past the last) the Q4_0 scale and every Q4_K
+    // byte lie past the buffer and read as zero, and a Q4_0 nibble read lands
+    // in the scale plane, so the row contributes 0 * (finite) and is never
+    // stored; a slot past the end of a row reads the next row's bytes and is
+    // skipped in compute_batch. With no branch around them the compiler counts
+    // every load as issued, so waiting for one batch never waits for the next.
+    auto load_batch = [&](Regs(&g)[JB][R], int tile, int j0, int c0) {
+        const uint32_t trow = static_cast<uint32_t>(tile) * RPG;
+        const uint32_t ubase = static_cast<uint32_t>(c0 + j0 * LPR);
+#pragma unroll
+        for (int jj = 0; jj < JB; jj++)
+#pragma unroll
+            for (int r = 0; r < R; r++)
+                F::load(g[jj][r], w, wbytes, scale_plane, static_cast<uint32_t>(nu), trow,
+                        static_cast<uint32_t>(row_in_tile + r * SUBS), static_cast<uint32_t>(li), ubase,
+                        static_cast<uint32_t>(jj * LPR));
+    };
+    auto compute_batch = [&](const Regs(&g)[JB][R], int j0, int c0, int nuc) {
+#pragma unroll
+        for (int jj = 0; jj < JB; jj++) {
+            const int ul = li + (j0 + jj) * LPR;
+            if (ul < nuc) F::template accumulate<N, R>(g[jj], xs, meta, ul, uc, static_cast<uint32_t>(c0 + ul), acc);
+        }
+    };
+    auto reduce_store = [&](int tile) {
+        const int row0 = tile * RPG + row_in_tile;
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int row = row0 + r * SUBS;
+#pragma unroll
+            for (int t = 0; t < N; t++) {
+                const float v = row_reduce<LPR>(acc[r][t]);
+                if (li == 0 && row < M) y[static_cast<size_t>(t) * M + row] = v;
+            }
+        }
+    };
+
+    int tile = blockIdx.x;
+    if (tile >= ntiles) return;  // uniform across the workgroup
+    Regs ga[JB][R], gb[JB][R];
+
+    if (uc >= nu) {
+        // Activations staged once; a flat, double-buffered stream of batches
+        // runs through all of this workgroup's tiles.
+        const int nb = ((nu + LPR - 1) / LPR + JB - 1) / JB;  // batches per tile
+        int b = 0;
+        stage<F, N, NT, kStageRound<WAVES>>(xr, K, 0, nu, uc, xs, meta, tid, [&]() { load_batch(ga, tile, 0, 0); });
+        wg_sync<WAVES>();
+        auto step = [&](Regs(&cur)[JB][R], Regs(&nxt)[JB][R]) -> bool {
+            int nt = tile, nbi = b + 1;
+            if (nbi == nb) {
+                nt = tile + static_cast<int>(gridDim.x);
+                nbi = 0;
+            }
+            load_batch(nxt, nt, nbi * JB, 0);  // past the last tile: read, never used
+            compute_batch(cur, b * JB, 0, nu);
+            if (nbi == 0) {
+                reduce_store(tile);
+                zero_acc();
+            }
+            tile = nt;
+            b = nbi;
+            return tile < ntiles;
+        };
+        while (step(ga, gb) && step(gb, ga)) {
+        }
+        return;
+    }
+
+    bool first = true;
+    for (; tile < ntiles; tile += static_cast<int>(gridDim.x)) {
+        for (int c0 = 0; c0 < nu; c0 += uc) {
+            const int nuc = nu - c0 < uc ? nu - c0 : uc;
+            const int jc = (nuc + LPR - 1) / LPR;  // unit slots per lane per row in this chunk
+            if (!first) wg_sync<WAVES>();
+            first = false;
+            stage<F, N, NT, kStageRound<WAVES>>(xr, K, c0, nuc, uc, xs, meta, tid,
+                                                [&]() { load_batch(ga, tile, 0, c0); });
+            wg_sync<WAVES>();
+            // Prefetches are unconditional (a batch past the chunk is read and
+            // dropped) so that no branch makes the compiler wait for them.
+            for (int j0 = 0; j0 < jc; j0 += 2 * JB) {
+                load_batch(gb, tile, j0 + JB, c0);
+                compute_batch(ga, j0, c0, nuc);
+                if (j0 + JB >= jc) break;
+                load_batch(ga, tile, j0 + 2 * JB, c0);
+                compute_batch(gb, j0 + JB, c0, nuc);
+            }
+        }
+        reduce_store(tile);
+        zero_acc();
+    }
+}
+
+// ---- launch -----------------------------------------------------------------------
+
+template <class F, int N, int LPR, int R, int WAVES>
+int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t stream, int cus,
+               int groups_per_cu)
+{
+    constexpr int JB = F::kBatchUnits / R > 0 ? F::kBatchUnits / R : 1;
+    constexpr int rows_per_wg = WAVES * (64 / LPR) * R;
+    const int nu = k / 32;
+    int uc = nu;
+    const int bytes_per_unit = N * kLdsBytesPerUnit;
+    if (uc * bytes_per_unit > kMaxLdsBytes) uc = kMaxLdsBytes / bytes_per_unit / 8 * 8;  // chunks of whole super-blocks
+    if (uc <= 0) return Q4_EUNSUPPORTED;
+    const size_t lds = static_cast<size_t>(uc) * bytes_per_unit;
+    const int ntiles = (m + rows_per_wg - 1) / rows_per_wg;
+    const long long cap = static_cast<long long>(cus) * groups_per_cu;
+    const unsigned grid = static_cast<unsigned>(ntiles < cap ? ntiles : cap);
+    const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(F::kFormat, m, k));
+    hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB>), dim3(grid), dim3(64 * WAVES), lds, stream, w, wbytes,
+                       x, y, m, k, uc, ntiles);
+    return hipGetLastError() == hipSuccess ? Q4_OK : Q4_EHIP;
+}
+
+// The instantiated tile geometries: (lanes per row, rows per lane, waves per group).
+#define Q4_GEMV_CONFIGS(X) \
+    X(8, 1, 1)             \
+    X(8, 2, 1)             \
+    X(8, 4, 1)             \
+    X(16, 1, 1)            \
+    X(16, 2, 1)            \
+    X(32, 1, 1)            \
+    X(32, 2, 1)            \
+    X(64, 1, 1)            \
+    X(16, 1, 4)            \
+    X(32, 1, 4)            \
+    X(32, 2, 4)            \
+    X(64, 1, 4)            \
+    X(64, 2, 4)            \
+    X(64, 4, 4)
+
+template <class F, int N>
+int dispatch_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus)
+{
+#define Q4_CFG_CASE(L, RR, WV) \
+    if (c.lpr == L && c.r == RR && c.waves == WV) return launch_one<F, N, L, RR, WV>(w, x, y, m, k, s, cus, c.groups_per_cu);
+    Q4_GEMV_CONFIGS(Q4_CFG_CASE)
+#undef Q4_CFG_CASE
+    return Q4_EUNSUPPORTED;
+}
+
+}  // namespace gemv
+}  // namespace q4

@@ -17,7 +17,6 @@
 #include <vector>
 
 #include "q4.h"
-#include "q4_internal.h"
 
 namespace {
 

@@ -1,6 +1,8 @@
 // Internal declarations shared by the host launchers of the library.
 #pragma once
 
+#include <hip/hip_runtime_api.h>
+
 #include <cstddef>
 #include <cstdint>
 
@@ -25,4 +27,25 @@ int launch_gemv(int fmt, const void *w, const float *x, float *y,
 int launch_gemm(int fmt, const void *w, const uint16_t *x, float *y,
                 int64_t m, int64_t k, int64_t n, void *stream);
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
+namespace gemv {
+
+// Tile geometry of the decode kernel.
+struct Cfg {
+    int lpr;            // lanes per row: 8, 16, 32 or 64
+    int r;              // rows per lane
+    int waves;          // waves per workgroup: 1 or 4
+    int groups_per_cu;  // resident workgroups per compute unit the grid is sized for
+};
+
+struct FmtQ4_0;
+struct FmtQ4_K;
+
+// Defined in the per-format instantiation units (q4_gemv_q4_*.hip).
+template <class F, int N>
+int dispatch_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus);
+
+}  // namespace gemv
 }  // namespace q4

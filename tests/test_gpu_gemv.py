@@ -183,6 +183,21 @@ def test_extreme_activation_scales(env):
     check_tolerance(yb, yr, ad, GEMV_TOL, what="large activation")
 
 
+def test_extreme_activation_q4_k(env):
+    # Q4_K's value is the difference of two terms (d*sc*q and dmin*m); with an
+    # outlier activation the elementwise error is bounded against the sum of
+    # the term magnitudes (the oracle's termscale), and normwise as usual.
+    torch, q4, orc = env
+    m, k = 96, 1024
+    buf = q4.q4_quantize_ref(1, synth.weights(73, m, k))
+    x = synth.activations(74, 3, k)
+    x[0, 5] = 1e6
+    x[2, 700] = -3e4
+    y = _gemv(env, 1, buf, x, m, k)
+    yr = orc.matvec(1, buf, m, k, x)
+    check_tolerance(y, yr, orc.termscale(1, buf, m, k, x), GEMV_TOL, what="q4_k outlier")
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_sequence_and_graph_match_single_calls(env, fmt):
     torch, q4, _ = env

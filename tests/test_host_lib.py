@@ -169,6 +169,19 @@ def test_product_argument_errors(q4, entry):
         assert f(0, *ok, 64, 256, 9, None) == q4.Q4_EUNSUPPORTED       # decode batch is 1..8
 
 
+def test_tuned_argument_errors(q4):
+    f = q4.raw().q4_gemv_tuned
+    ok = (A16, A16 * 2, A16 * 3)
+    good = q4.q4_gemv_tuning(0, 0, 0, 0)
+    assert f(0, *ok, 64, 256, 1, None, None) == q4.Q4_EINVAL
+    assert f(0, *ok, 64, 256, 1, ctypes.byref(q4.q4_gemv_tuning(-1, 0, 0, 0)), None) == q4.Q4_EINVAL
+    assert f(0, *ok, 64, 256, 1, ctypes.byref(q4.q4_gemv_tuning(0, 0, 0, 65)), None) == q4.Q4_EINVAL
+    assert f(0, *ok, 64, 48, 1, ctypes.byref(good), None) == q4.Q4_EINVAL
+    assert f(0, *ok, 64, 256, 9, ctypes.byref(good), None) == q4.Q4_EUNSUPPORTED
+    assert f(0, A16 + 4, A16, A16, 64, 256, 1, ctypes.byref(good), None) == q4.Q4_EALIGN
+    assert f(0, None, None, None, 0, 256, 1, ctypes.byref(good), None) == q4.Q4_OK
+
+
 def test_sequence_and_graph_argument_errors(q4):
     lib = q4.raw()
     ops = (q4.q4_gemv_op * 2)()

@@ -136,3 +136,34 @@ def test_matmul_bf16(orc):
     assert np.array_equal(yi, wb.T.astype(np.float32))
     yi = orc.matmul(0, buf, m, k, eye)
     assert np.array_equal(yi, what.T)
+
+
+def test_termscale(orc):
+    # Q4_0: the value is one term, so the scale is sum |w_hat x|.
+    m, k = 7, 256
+    w = synth.weights(71, m, k)
+    x = synth.activations(72, 2, k)
+    b0 = orc.quantize(0, w)
+    _, ad0 = orc.matvec(0, b0, m, k, x, absdot=True)
+    assert np.allclose(orc.termscale(0, b0, m, k, x), ad0, rtol=1e-12)
+    # Q4_K: at least sum |w_hat x|, equal when every min is zero, and by hand
+    # on K-A with one activation: |d*sc*q| + |dmin*m| for sub-block 7, q=15:
+    # 945 + 24 = 969.
+    b1 = orc.quantize(1, w)
+    _, ad1 = orc.matvec(1, b1, m, k, x, absdot=True)
+    ts = orc.termscale(1, b1, m, k, x)
+    assert np.all(ts >= ad1 * (1 - 1e-12))
+    z = b1.copy().reshape(-1, 144)
+    z[:, 2:4] = 0  # dmin = 0
+    _, adz = orc.matvec(1, z.reshape(-1), m, k, x, absdot=True)
+    assert np.allclose(orc.termscale(1, z.reshape(-1), m, k, x), adz, rtol=1e-12)
+    S = orc.q4_k_pack_scales([1, 2, 3, 4, 5, 6, 7, 63], [0, 1, 2, 3, 4, 5, 6, 48])
+    sb = np.zeros(144, np.uint8)
+    sb[0:2] = [0x00, 0x3C]
+    sb[2:4] = [0x00, 0x38]
+    sb[4:16] = S
+    sb[16 + 32 * 3 + 32 - 32 + 0] |= 0xF0  # weight 224 = 64*3 + 32 + 0: high nibble of chunk 3 byte 0 -> sub-block 7
+    e = np.zeros((1, 256), np.float32)
+    e[0, 224] = 1.0
+    assert orc.termscale(1, sb, 1, 256, e)[0, 0] == 969.0
+    assert orc.matvec(1, sb, 1, 256, e)[0, 0] == 921.0
