@@ -1,13 +1,289 @@
 // Prefill product Y = bf16(W_hat) X for 4-bit block-quantized W on gfx950.
+//
+// Method (Llamas on the Web, technical summary, Methodology section 3,
+// "integrated dequantization"): for the matrix-matrix product the quantized
+// blocks are loaded, dequantized into shared memory and reused; on gfx950 the
+// reuse is by bf16 matrix-core instructions (v_mfma_f32_16x16x32_bf16, fp32
+// accumulation), since prefill is a dense contraction.
+//
+// Work decomposition: a workgroup of 4 waves computes a TM (weight rows) x TN
+// (tokens) tile of Y over all of K, in stages of 64 along K.
+//   * Weights: each stage's TM x 64 quantized tile is dequantized exactly in
+//     fp32 ((q-8)*d, or d*sc*q - dmin*m for Q4_K), rounded to bf16 (RNE) and
+//     written to LDS once; all four waves read it as MFMA A operands, so each
+//     dequantized weight is reused across the whole token tile.
+//   * Activations: every wave owns TN/4 tokens, so its bf16 X fragments go
+//     straight from memory into registers in the MFMA B layout (no LDS).
+//   * The next stage's loads are issued before the current stage's MFMAs.
+//     (A workgroup barrier waits for all outstanding loads on this target, so
+//     one stage of prefetch is what a barrier-synchronised tile can overlap.)
+//   * Loads are raw buffer loads: rows past M and tokens past N read zeros.
 #include <hip/hip_runtime.h>
+
+#include <cstdint>
 
 #include "q4_internal.h"
 
 namespace q4 {
+namespace gemm {
 
-int launch_gemm(int, const void *, const uint16_t *, float *, int64_t, int64_t, int64_t, void *)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kStageK = 64;              // K per stage
+constexpr int kLdsRow = kStageK + 8;     // bf16 per LDS row (padding staggers banks)
+constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer descriptor, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
-    return Q4_EUNSUPPORTED;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), static_cast<int>(bytes),
+                                             kBufferWord3);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu)));
+}
+
+__device__ __forceinline__ bf16x4 to_bf16(float a, float b, float c, float d)
+{
+    return bf16x4{static_cast<__bf16>(a), static_cast<__bf16>(b), static_cast<__bf16>(c), static_cast<__bf16>(d)};
+}
+
+// ---- format policies ------------------------------------------------------------
+// A stage item is 8 weights of one row: one nibble dword whose 4 low nibbles
+// are stage elements lo..lo+3 and whose 4 high nibbles are hi..hi+3.
+
+struct GemmQ4_0 {
+    static constexpr int kFormat = Q4_FMT_Q4_0;
+    struct Item {
+        uint32_t q;  // 4 nibble bytes
+        uint32_t d;  // fp16 scale bits
+    };
+    // Item it8 (0..7) of stage s: block 2s + it8/4, nibble bytes 4*(it8%4)...
+    __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+                                uint32_t row, int s, int it8)
+    {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
+        const uint32_t blk = row * nu + 2u * static_cast<uint32_t>(s) + static_cast<uint32_t>(it8 >> 2);
+        g.q = __builtin_amdgcn_raw_buffer_load_b32(r, blk * 16u + 4u * static_cast<uint32_t>(it8 & 3), 0, 0);
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(r, scale_plane + blk * 2u, 0, 0);
+    }
+    __device__ static int lo(int it8) { return 32 * (it8 >> 2) + 4 * (it8 & 3); }
+    __device__ static int hi(int it8) { return lo(it8) + 16; }
+    // (q - 8) * d, exact in fp32: q*d is exact and fma rounds the exact result once.
+    __device__ static void dequant(const Item &g, int /*it8*/, bf16x4 &vlo, bf16x4 &vhi)
+    {
+        const float d = half_bits_to_float(g.d);
+        const float m8 = -8.0f * d;
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            v[j] = __builtin_fmaf(static_cast<float>((g.q >> (8 * j)) & 15u), d, m8);
+            v[4 + j] = __builtin_fmaf(static_cast<float>((g.q >> (8 * j + 4)) & 15u), d, m8);
+        }
+        vlo = to_bf16(v[0], v[1], v[2], v[3]);
+        vhi = to_bf16(v[4], v[5], v[6], v[7]);
+    }
+};
+
+struct GemmQ4_K {
+    static constexpr int kFormat = Q4_FMT_Q4_K;
+    struct Item {
+        uint32_t q;  // 4 nibble bytes
+        u32x4 h;     // super-block header: d, dmin, 12 scale bytes
+    };
+    // Stage s is nibble chunk c = s % 4 of super-block s / 4: byte i of the
+    // chunk holds elements i (sub-block 2c) and 32 + i (sub-block 2c+1).
+    __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t /*scale_plane*/, uint32_t nu,
+                                uint32_t row, int s, int it8)
+    {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
+        const uint32_t base = (row * (nu >> 3) + static_cast<uint32_t>(s >> 2)) * 144u;
+        g.h = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, base, 0, 0));
+        g.q = __builtin_amdgcn_raw_buffer_load_b32(r, base + 16u + 32u * static_cast<uint32_t>(s & 3) +
+                                                          4u * static_cast<uint32_t>(it8), 0, 0);
+    }
+    __device__ static int lo(int it8) { return 4 * it8; }
+    __device__ static int hi(int it8) { return 32 + 4 * it8; }
+    // d*sc*q - dmin*m: d*sc*q is exact in fp32 (<= 21 bits), so the fma rounds
+    // the exact difference once, as the format's definition does.
+    __device__ static void dequant(const Item &g, int s, bf16x4 &vlo, bf16x4 &vhi)
+    {
+        // Sub-blocks a = 2c, b = 2c+1 with c = s % 4; their 6-bit fields sit in
+        // bytes 2(c&1), 2(c&1)+1 of the three scale words.
+        const uint32_t c = static_cast<uint32_t>(s & 3);
+        const uint32_t sh = (c & 1u) << 4;
+        const uint32_t s0 = g.h.y >> sh, s1 = g.h.z >> sh, s2 = g.h.w >> sh;
+        const bool upper = c >= 2;
+        const uint32_t sca = upper ? ((s2 & 15u) | (((s0 >> 6) & 3u) << 4)) : (s0 & 63u);
+        const uint32_t scb = upper ? (((s2 >> 8) & 15u) | (((s0 >> 14) & 3u) << 4)) : ((s0 >> 8) & 63u);
+        const uint32_t ma = upper ? (((s2 >> 4) & 15u) | (((s1 >> 6) & 3u) << 4)) : (s1 & 63u);
+        const uint32_t mb = upper ? (((s2 >> 12) & 15u) | (((s1 >> 14) & 3u) << 4)) : ((s1 >> 8) & 63u);
+        const float d = half_bits_to_float(g.h.x), dmin = half_bits_to_float(g.h.x >> 16);
+        const float stepa = d * static_cast<float>(sca), stepb = d * static_cast<float>(scb);
+        const float offa = -(dmin * static_cast<float>(ma)), offb = -(dmin * static_cast<float>(mb));
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            v[j] = __builtin_fmaf(stepa, static_cast<float>((g.q >> (8 * j)) & 15u), offa);
+            v[4 + j] = __builtin_fmaf(stepb, static_cast<float>((g.q >> (8 * j + 4)) & 15u), offb);
+        }
+        vlo = to_bf16(v[0], v[1], v[2], v[3]);
+        vhi = to_bf16(v[4], v[5], v[6], v[7]);
+    }
+};
+
+// ---- the kernel ---------------------------------------------------------------------
+// MFMA 16x16x32 operand layout (wave64): A (16 rows x 32 k): lane l holds row
+// l%16, k = 8(l/16)..8(l/16)+7; B (32 k x 16 cols): lane l holds column
+// l%16, the same k range; D (16 x 16): lane l holds rows 4(l/16)..+3 of
+// column l%16. Rows are weight rows, columns are tokens.
+
+template <class F, int TM, int TN>
+__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w, uint32_t wbytes,
+                                                   const uint16_t *__restrict__ x, float *__restrict__ y, int M,
+                                                   int K, int N)
+{
+    constexpr int FM = TM / 16;        // A fragments (16-row blocks) per wave
+    constexpr int WN = TN / 4;         // tokens per wave
+    constexpr int FN = WN / 16;        // B fragments per wave
+    constexpr int WI = TM * 8 / 256;   // weight items per thread per stage
+    static_assert(WI >= 1 && FN >= 1, "tile too small");
+    __shared__ __attribute__((aligned(16))) __bf16 ws[TM * kLdsRow];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int r0 = blockIdx.x * TM;
+    const int t0 = blockIdx.y * TN;
+    const uint32_t nu = static_cast<uint32_t>(K / 32);
+    const uint32_t scale_plane = static_cast<uint32_t>(static_cast<uint64_t>(M) * static_cast<uint64_t>(K) / 2u);
+    const int S = (K + kStageK - 1) / kStageK;
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(x, static_cast<uint32_t>(static_cast<uint64_t>(N) * static_cast<uint64_t>(K) * 2u));
+    // This lane's token for B fragment fn, and its k offset within a 32-slice.
+    const int ktok = 8 * (lane >> 4);
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    typename F::Item gi[2][WI];
+    bf16x8 xb[2][FN][2];
+
+    auto load_stage = [&](int buf, int s) {
+#pragma unroll
+        for (int i = 0; i < WI; i++) {
+            const int it = tid + 256 * i;
+            F::load(gi[buf][i], w, wbytes, scale_plane, nu, static_cast<uint32_t>(r0 + (it >> 3)), s, it & 7);
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) {
+            const uint32_t tok = static_cast<uint32_t>(t0 + wave * WN + 16 * fn + (lane & 15));
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++) {
+                const uint32_t off = (tok * static_cast<uint32_t>(K) + static_cast<uint32_t>(s * kStageK + 32 * kk + ktok)) * 2u;
+                xb[buf][fn][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+            }
+        }
+    };
+    auto write_stage = [&](int buf, int s) {
+#pragma unroll
+        for (int i = 0; i < WI; i++) {
+            const int it = tid + 256 * i;
+            const int row = it >> 3, it8 = it & 7;
+            bf16x4 vlo, vhi;
+            F::dequant(gi[buf][i], s, vlo, vhi);
+            *reinterpret_cast<bf16x4 *>(&ws[row * kLdsRow + F::lo(it8)]) = vlo;
+            *reinterpret_cast<bf16x4 *>(&ws[row * kLdsRow + F::hi(it8)]) = vhi;
+        }
+    };
+    auto compute_stage = [&](int buf, int s) {
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++) {
+            if (s * kStageK + 32 * kk >= K) break;  // K = 32 mod 64: the last stage is half
+            bf16x8 a[FM];
+#pragma unroll
+            for (int fm = 0; fm < FM; fm++)
+                a[fm] = *reinterpret_cast<const bf16x8 *>(&ws[(16 * fm + (lane & 15)) * kLdsRow + 32 * kk + ktok]);
+#pragma unroll
+            for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+                for (int fn = 0; fn < FN; fn++)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], xb[buf][fn][kk], acc[fm][fn], 0, 0, 0);
+        }
+    };
+
+    load_stage(0, 0);
+    for (int s = 0; s < S; s += 2) {
+        write_stage(0, s);
+        __syncthreads();
+        if (s + 1 < S) load_stage(1, s + 1);
+        compute_stage(0, s);
+        __syncthreads();
+        if (s + 1 >= S) break;
+        write_stage(1, s + 1);
+        __syncthreads();
+        if (s + 2 < S) load_stage(0, s + 2);
+        compute_stage(1, s + 1);
+        __syncthreads();
+    }
+
+    // Store: lane holds rows 4(l/16)..+3 of token column l%16 of each 16x16 tile.
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++) {
+        const int row = r0 + 16 * fm + 4 * (lane >> 4);
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) {
+            const int tok = t0 + wave * WN + 16 * fn + (lane & 15);
+            if (tok >= N) continue;
+            float *dst = y + static_cast<size_t>(tok) * M + row;
+            if (row + 3 < M && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                *reinterpret_cast<f32x4 *>(dst) = acc[fm][fn];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    if (row + r < M) dst[r] = acc[fm][fn][r];
+            }
+        }
+    }
+}
+
+template <class F, int TM, int TN>
+int launch_tile(const void *w, const uint16_t *x, float *y, int64_t m, int64_t k, int64_t n, hipStream_t s)
+{
+    const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(F::kFormat, m, k));
+    const dim3 grid(static_cast<unsigned>((m + TM - 1) / TM), static_cast<unsigned>((n + TN - 1) / TN));
+    hipLaunchKernelGGL((gemm_kernel<F, TM, TN>), grid, dim3(256), 0, s, static_cast<const uint8_t *>(w), wbytes, x,
+                       y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
+    return hipGetLastError() == hipSuccess ? Q4_OK : Q4_EHIP;
+}
+
+template <class F>
+int launch_fmt(const void *w, const uint16_t *x, float *y, int64_t m, int64_t k, int64_t n, hipStream_t s, int cus)
+{
+    // Wider token tiles reuse each dequantized weight more; fall back to
+    // narrower ones while that leaves fewer than two tiles per compute unit.
+    const int64_t tiles128 = ((m + 31) / 32) * ((n + 127) / 128);
+    if (tiles128 >= 2LL * cus || n <= 64) return n <= 64 ? launch_tile<F, 32, 64>(w, x, y, m, k, n, s)
+                                                         : launch_tile<F, 32, 128>(w, x, y, m, k, n, s);
+    return launch_tile<F, 32, 64>(w, x, y, m, k, n, s);
+}
+
+}  // namespace gemm
+
+int launch_gemm(int fmt, const void *w, const uint16_t *x, float *y, int64_t m, int64_t k, int64_t n, void *stream)
+{
+    const int cus = device_cus();
+    if (cus <= 0) return Q4_EHIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fmt == Q4_FMT_Q4_0) return gemm::launch_fmt<gemm::GemmQ4_0>(w, x, y, m, k, n, s, cus);
+    return gemm::launch_fmt<gemm::GemmQ4_K>(w, x, y, m, k, n, s, cus);
 }
 
 }  // namespace q4
@@ -15,8 +291,9 @@ int launch_gemm(int, const void *, const uint16_t *, float *, int64_t, int64_t, 
 extern "C" int q4_gemm(int fmt, const void *w, const uint16_t *x_bf16, float *y, int64_t m, int64_t k, int64_t n,
                        void *hip_stream)
 {
-    int st = q4::check_product_args(fmt, w, x_bf16, y, m, k, n, INT64_MAX);
+    const int st = q4::check_product_args(fmt, w, x_bf16, y, m, k, n, INT64_MAX);
     if (st != Q4_OK) return st;
     if (m == 0 || n == 0) return Q4_OK;
+    if (n >= (1LL << 22)) return Q4_EUNSUPPORTED;
     return q4::launch_gemm(fmt, w, x_bf16, y, m, k, n, hip_stream);
 }

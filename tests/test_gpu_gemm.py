@@ -1,0 +1,100 @@
+"""GPU parity of the prefill product (LDS dequant -> bf16 MFMA) against the oracle.
+
+* Dequantization bit-exact through the public entry point: X = I_K returns
+  bf16(W_hat)^T exactly (one nonzero product per sum, products with 1.0 exact).
+* Outputs within 1e-2 of the oracle with exact fp32 weights (normwise and
+  elementwise), and within 1e-4 of the oracle with bf16-rounded weights (the
+  kernel's own weights: only the fp32 summation order differs).
+* SmolLM2-360M layer shapes at 512 tokens (sampled rows), ragged shapes, Q4_K.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_common import GEMM_TOL, check_tolerance, sample_rows, say, threads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    import oracle
+    import q4_weight_gemv_amd as q4
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    oracle.lib()
+    return torch, q4, oracle
+
+
+def _gemm(env, fmt, buf, xb, m, k):
+    torch, q4, _ = env
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).cuda()
+    yd = torch.full((xb.shape[0], m), float("nan"), dtype=torch.float32, device="cuda")
+    q4.q4_gemm(fmt, wd, xd, yd, m, k)
+    torch.cuda.synchronize()
+    return yd.cpu().numpy()
+
+
+def _quantize_both(q4, orc, fmt, w):
+    buf = q4.q4_quantize_ref(fmt, w)
+    assert np.array_equal(buf, orc.quantize(fmt, w)), "host quantizer and oracle disagree"
+    return buf
+
+
+@pytest.mark.parametrize("fmt,m,k", [(0, 37, 96), (0, 130, 960), (0, 64, 2560), (1, 37, 256), (1, 96, 1024)])
+def test_identity_gives_bf16_weights_exactly(env, fmt, m, k):
+    torch, q4, orc = env
+    buf = _quantize_both(q4, orc, fmt, synth.weights(synth.seed_for(30 + fmt, m), m, k))
+    eye = synth.bf16_bits(np.eye(k, dtype=np.float32))
+    say(f"gemm identity fmt={fmt} m={m} k={k}")
+    y = _gemm(env, fmt, buf, eye, m, k)
+    what = orc.dequantize(fmt, buf, m, k)
+    wb = np.array([[orc.bf16_to_fp32(orc.fp32_to_bf16(float(v))) for v in row] for row in what], np.float32)
+    assert np.array_equal(y, wb.T)
+
+
+def _parity(env, fmt, m, k, n, seed, rows=None):
+    torch, q4, orc = env
+    buf = _quantize_both(q4, orc, fmt, synth.weights(synth.seed_for(seed, 2), m, k))
+    xb = synth.bf16_bits(synth.activations(synth.seed_for(seed, 2, True), n, k))
+    say(f"gemm parity fmt={fmt} m={m} k={k} n={n}")
+    y = _gemm(env, fmt, buf, xb, m, k)
+    ranges, idx = rows if rows is not None else (None, None)
+    yr, ad = orc.matmul(fmt, buf, m, k, xb, threads=threads(), absdot=True, rows=ranges)
+    check_tolerance(y, yr, ad, GEMM_TOL, rows=idx, what=f"gemm fmt={fmt} {m}x{k} n={n}")
+    yb, adb = orc.matmul(fmt, buf, m, k, xb, round_w_bf16=True, threads=threads(), absdot=True, rows=ranges)
+    rel = check_tolerance(y, yb, adb, 1e-4, rows=idx, what=f"gemm(bf16 W) fmt={fmt} {m}x{k} n={n}")
+    return rel
+
+
+@pytest.mark.parametrize("fmt,m,k,n", [
+    (0, 1, 32, 1), (0, 37, 96, 5), (0, 100, 320, 130), (0, 33, 960, 64), (0, 257, 2560, 200),
+    (1, 1, 256, 3), (1, 70, 512, 70), (1, 130, 1024, 257),
+])
+def test_parity_small(env, fmt, m, k, n):
+    _parity(env, fmt, m, k, n, seed=600 + n)
+
+
+@pytest.mark.parametrize("k,m", sorted(set(synth.smollm2_360m_layer())))
+def test_parity_smollm2_layer_512_tokens(env, k, m):
+    _parity(env, 0, m, k, 512, seed=700 + k % 13, rows=sample_rows(m, k, edge=96, rand=64))
+
+
+@pytest.mark.parametrize("k,m", [(1024, 960), (2560, 960)])
+def test_parity_q4_k_512_tokens(env, k, m):
+    _parity(env, 1, m, k, 512, seed=800, rows=sample_rows(m, k, edge=64, rand=48))
+
+
+def test_gemm_misaligned_and_noop(env):
+    torch, q4, _ = env
+    w = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(256, dtype=torch.int16, device="cuda")
+    y = torch.full((8,), 5.0, device="cuda")
+    lib = q4.raw()
+    assert lib.q4_gemm(0, w.data_ptr(), x.data_ptr() + 2, y.data_ptr(), 8, 32, 1, None) == q4.Q4_EALIGN
+    assert lib.q4_gemm(0, w.data_ptr(), x.data_ptr(), y.data_ptr(), 0, 32, 1, None) == q4.Q4_OK
+    torch.cuda.synchronize()
+    assert (y == 5.0).all()
