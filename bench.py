@@ -1,28 +1,36 @@
 #!/usr/bin/env python3
-"""Throughput of the Q4 decode path on one MI355X.
+"""Throughput of the Q4 decode path on one MI355X; prints ONE JSON line.
 
-Default workload: the GPT-2-124M decode step (12 layers x {768->2304,
-768->768, 768->3072, 3072->768} + the 768->50257 LM head = 49 Q4_0 decode
-products, batch 1), captured once into a HIP graph per weight copy and
-replayed, one graph launch per step. Weights rotate over enough copies
-(>= 512 MiB in total) that every step reads them from HBM, not from the
-256 MB Infinity Cache. Inputs are resident in HBM before timing starts.
+Headline workload: the GPT-2-124M decode step at batch 1 -- 12 layers of
+{768->2304 (QKV), 768->768 (attn-out), 768->3072, 3072->768 (MLP)} plus the
+768->50257 LM head = 49 Q4_0 decode products, 69.5 MB of weights. Every
+product's weights, activations and outputs are resident in HBM before the
+timed region. The 49 launches are captured once into a HIP graph per weight
+copy; each step is one graph launch. The weights rotate over enough copies
+(>= 512 MiB) that every step reads them from HBM, not from the 256 MB
+Infinity Cache.
 
-value = algorithmic bytes per step (weights + x + y) x steps
-        / timed seconds, in GB/s; tokens/s = steps / timed seconds.
+  value     = algorithmic bytes per step (quantized W + x + y of the 49
+              products) x steps / timed seconds  [GB/s]
+  tokens/s  = steps / timed seconds
+  roofline  = the decode-product kernel: algorithmic bytes per launch /
+              average launch time (HIP events on the stream the graphs are
+              launched on, timed region / launches), against 8 TB/s HBM.
 
-Also reported: the 7B-class shapes one at a time (Q4_0 at N=1, and Q4_K at
-N=1/4/8), the SmolLM2-360M step, and the prefill GEMM, and the CPU oracle
-timed on a bounded sample of the same step.
-
-Prints ONE JSON line.
+Also reported in "extras": the 7B-class shapes (Q4_0 at N=1 -- the gate
+shapes -- and Q4_K at N=1/4/8), the SmolLM2-360M step, the prefill GEMM over
+a SmolLM2-360M layer at 512 tokens, launches from a plain stream, and the
+per-launch floor. "cpu_baseline" is the CPU oracle timed on the host cores on
+whole repeats of the same step (bounded to about 10 s).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -34,117 +42,214 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 COLD_BYTES = 512 << 20
+METRIC = "Q4 decode GEMV effective HBM GB/s (% of peak) + layer-stack tokens/s at 1 GPU"
+KERNEL_SOURCES = ["q4_gemv_kernel.h", "q4_gemv.hip", "q4_gemv_q4_0_a.hip", "q4_gemv_q4_0_b.hip"]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def gemv_bytes(m, k, n, fmt=0):
-    """Algorithmic bytes of one decode product: quantized W + x + y."""
-    import q4_weight_gemv_amd as q4
-
+def gemv_bytes(q4, fmt, m, k, n):
+    """Algorithmic bytes of one decode product: quantized W + fp32 x + fp32 y."""
     return q4.q4_weight_bytes(fmt, m, k) + 4 * n * k + 4 * n * m
 
 
-class Step:
-    """A decode step: one weight set per copy, shared x/y buffers, one graph per copy."""
+def gemm_bytes(q4, fmt, m, k, n):
+    return q4.q4_weight_bytes(fmt, m, k) + 2 * n * k + 4 * n * m
 
-    def __init__(self, shapes, fmt, n, config_id, copies, torch, q4):
+
+def copies_for(nbytes):
+    return max(2, math.ceil(COLD_BYTES / nbytes) + 1)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "q4_weight_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Timer:
+    """HIP events on torch's current stream, which every launch here uses."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def region(self, fn, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            fn(warmup + i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / 1e3
+
+
+class Step:
+    """A decode step: one set of weights per copy, shared x/y, one graph per copy."""
+
+    def __init__(self, torch, q4, shapes, fmt, n, config_id):
         import synth
 
-        self.shapes = shapes
-        self.fmt = fmt
-        self.n = n
-        self.bytes = sum(gemv_bytes(m, k, n, fmt) for k, m in shapes)
-        host = []
-        for i, (k, m) in enumerate(shapes):
-            w = synth.weights(synth.seed_for(config_id, i), m, k)
-            host.append(q4.q4_quantize_ref(fmt, w))
-        self.host_w = host
-        self.xs = [torch.from_numpy(synth.activations(synth.seed_for(config_id, i, True), n, k)).cuda()
-                   for i, (k, m) in enumerate(shapes)]
+        self.shapes, self.fmt, self.n = shapes, fmt, n
+        self.bytes = sum(gemv_bytes(q4, fmt, m, k, n) for k, m in shapes)
+        self.host_w = [q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(config_id, i), m, k))
+                       for i, (k, m) in enumerate(shapes)]
+        self.host_x = [synth.activations(synth.seed_for(config_id, i, True), n, k) for i, (k, m) in enumerate(shapes)]
+        self.xs = [torch.from_numpy(x).cuda() for x in self.host_x]
         self.ys = [torch.empty((n, m), dtype=torch.float32, device="cuda") for k, m in shapes]
-        self.copies = []
-        for c in range(copies):
-            self.copies.append([torch.from_numpy(h).cuda() for h in host])
-        self.graphs = []
-        for ws in self.copies:
-            ops = [(w, x, y, m, k) for w, x, y, (k, m) in zip(ws, self.xs, self.ys, shapes)]
-            self.graphs.append(q4.Q4Graph(fmt, ops, n))
+        wbytes = sum(h.size for h in self.host_w)
+        self.copies = [[torch.from_numpy(h).cuda() for h in self.host_w] for _ in range(copies_for(wbytes))]
+        self.graphs = [q4.Q4Graph(fmt, self._ops(ws), n) for ws in self.copies]
         torch.cuda.synchronize()
+
+    def _ops(self, ws):
+        return [(w, x, y, m, k) for w, x, y, (k, m) in zip(ws, self.xs, self.ys, self.shapes)]
 
     def run_graph(self, i):
         self.graphs[i % len(self.graphs)].launch()
 
-    def run_plain(self, i, q4):
-        ws = self.copies[i % len(self.copies)]
-        ops = [(w, x, y, m, k) for w, x, y, (k, m) in zip(ws, self.xs, self.ys, self.shapes)]
-        q4.q4_gemv_sequence(self.fmt, ops, self.n)
+    def run_plain(self, q4, i):
+        q4.q4_gemv_sequence(self.fmt, self._ops(self.copies[i % len(self.copies)]), self.n)
 
     def close(self):
         for g in self.graphs:
             g.close()
 
 
-def copies_for(step_bytes):
-    return max(2, math.ceil(COLD_BYTES / step_bytes) + 1)
+def traffic_from_profile(per_launch_bytes):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "pmc_gemv_gpt2_step.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256:\s*(\w+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
 
 
-def time_region(torch, fn, steps, warmup):
-    """HIP events on torch's current stream (the stream every launch uses)."""
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        fn(warmup + i)
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3  # seconds
-
-
-def cpu_baseline(step, budget_s=20.0):
-    """The oracle on the host cores over a bounded sample of the same step."""
+def cpu_baseline(step, budget_s=10.0):
+    """The oracle (as it stands) on whole repeats of the same decode step."""
     import oracle
 
     threads = max(1, min(16, os.cpu_count() or 1))
-    host_x = [x.cpu().numpy() for x in step.xs]
     t0 = time.perf_counter()
-    done_bytes = 0
-    done = 0
-    for i, (k, m) in enumerate(step.shapes):
-        oracle.matvec(step.fmt, step.host_w[i], m, k, host_x[i], threads=threads)
-        done_bytes += gemv_bytes(m, k, step.n, step.fmt)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
+    reps = 0
+    while True:
+        for i, (k, m) in enumerate(step.shapes):
+            oracle.matvec(step.fmt, step.host_w[i], m, k, step.host_x[i], threads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     return {
-        "value": round(done_bytes / dt / 1e9, 4),
+        "value": round(step.bytes * reps / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} of {len(step.shapes)} products of one decode step (rows split over {threads} threads), "
-                  f"{dt:.1f} s",
-        "tokens_per_s": round((done_bytes / step.bytes) / dt, 4),
+        "sample": f"{reps} whole GPT-2-124M decode step(s) (49 products, rows split over {threads} threads), "
+                  f"{dt:.1f} s wall",
+        "tokens_per_s": round(reps / dt, 3),
     }
+
+
+def bench_7b(torch, q4, timer, reps=20):
+    """7B-class shapes one product at a time, cold: a graph of one launch per
+    rotating weight copy, replayed."""
+    import synth
+
+    out = {}
+    for fmt, ns in ((0, (1,)), (1, (1, 4, 8))):
+        layer_t, layer_b = {1: 0.0}, 0
+        for k, m in synth.llama7b_layer()[:2] + synth.llama7b_layer()[3:]:
+            wq = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(4, k + m), m, k))
+            copies = [torch.from_numpy(wq).cuda() for _ in range(copies_for(wq.size))]
+            for n in ns:
+                x = torch.from_numpy(synth.activations(synth.seed_for(4, k, True), n, k)).cuda()
+                y = torch.empty((n, m), device="cuda")
+                g = q4.Q4Graph(fmt, [(c, x, y, m, k) for c in copies], n)
+                t = timer.region(lambda i: g.launch(), reps, 3) / (reps * len(copies))
+                g.close()
+                nb = gemv_bytes(q4, fmt, m, k, n)
+                key = f"{'q4_0' if fmt == 0 else 'q4_k'}_{k}to{m}_n{n}"
+                out[key] = {"us": round(t * 1e6, 3), "GB_s": round(nb / t / 1e9, 1),
+                            "pct_peak": round(100 * nb / t / 1e9 / HBM_PEAK_GBS, 1)}
+                log(f"{key}: {t * 1e6:.2f} us {nb / t / 1e9:.0f} GB/s")
+                if n == 1:
+                    mult = 2 if (k, m) == (4096, 11008) else 1  # gate and up
+                    layer_t[1] += mult * t
+                    layer_b += mult * nb
+            del copies
+        key = f"{'q4_0' if fmt == 0 else 'q4_k'}_7b_layer_as_listed_n1"
+        out[key] = {"us": round(layer_t[1] * 1e6, 2), "GB_s": round(layer_b / layer_t[1] / 1e9, 1),
+                    "pct_peak": round(100 * layer_b / layer_t[1] / 1e9 / HBM_PEAK_GBS, 1)}
+    return out
+
+
+def bench_gemm(torch, q4, timer, n=512, reps=20):
+    """Prefill GEMM over the SmolLM2-360M layer's 7 matrices at 512 tokens:
+    one graph of the 7 launches, replayed (weights 5.5 MB, L2/MALL-resident)."""
+    import synth
+
+    fns, flops, per = [], 0, {}
+    for i, (k, m) in enumerate(synth.smollm2_360m_layer()):
+        wq = torch.from_numpy(q4.q4_quantize_ref(0, synth.weights(synth.seed_for(3, i), m, k))).cuda()
+        xb = torch.from_numpy(synth.bf16_bits(synth.activations(synth.seed_for(3, i, True), n, k)).view(np.int16)).cuda()
+        y = torch.empty((n, m), device="cuda")
+        fns.append((wq, xb, y, m, k))
+        flops += 2 * n * m * k
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        for (w, xb, y, m, k) in fns:
+            q4.q4_gemm(0, w, xb, y, m, k)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for (w, xb, y, m, k) in fns:
+                q4.q4_gemm(0, w, xb, y, m, k)
+    t = timer.region(lambda i: g.replay(), reps, 3) / reps
+    tf = flops / t / 1e12
+    log(f"gemm smollm2 layer x{n}: {t * 1e6:.1f} us {tf:.1f} TFLOP/s")
+    return {"layer_us": round(t * 1e6, 2), "TFLOP_s": round(tf, 1), "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 2),
+            "GFLOP": round(flops / 1e9, 3), "tokens": n}
+
+
+def launch_floor(torch, q4, timer, count=200):
+    """Per-launch time of a tiny decode product (64 x 768) in a graph of 200."""
+    import synth
+
+    w = torch.from_numpy(q4.q4_quantize_ref(0, synth.weights(9, 64, 768))).cuda()
+    x = torch.from_numpy(synth.activations(9, 1, 768)).cuda()
+    y = torch.empty((1, 64), device="cuda")
+    g = q4.Q4Graph(0, [(w, x, y, 64, 768)] * count, 1)
+    t = timer.region(lambda i: g.launch(), 10, 2) / (10 * count)
+    g.close()
+    return round(t * 1e6, 3)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline workload")
-    ap.add_argument("--workload", default="gpt2", choices=["gpt2", "smollm2", "llama7b"])
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 64 MiB device copy (torch) once, as the reference for HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this build measures one GPU: run with --gpus 1 (nothing here uses a second GPU)"}))
         sys.exit(2)
 
     import torch
@@ -154,21 +259,35 @@ def main():
 
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
+    timer = Timer(torch)
     K, W = args.steps, args.warmup
 
-    shapes = {"gpt2": synth.gpt2_124m_step(), "smollm2": synth.smollm2_360m_step(),
-              "llama7b": synth.llama7b_layer()}[args.workload]
-    config_id = {"gpt2": 1, "smollm2": 2, "llama7b": 4}[args.workload]
-    step_bytes = sum(gemv_bytes(m, k, 1) for k, m in shapes)
-    log(f"setup {args.workload}: {len(shapes)} products, {step_bytes / 1e6:.2f} MB/step")
-    step = Step(shapes, 0, 1, config_id, copies_for(step_bytes), torch, q4)
-    t = time_region(torch, step.run_graph, K, W)
-    log(f"graph: {t / K * 1e6:.2f} us/step")
+    if args.calibrate:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters
+        # (64 MiB each way) scale the decode kernel's counters to bytes.
+        src = torch.ones(64 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        flush.fill_(2)  # 1 GiB of writes evicts src from L2 and the Infinity Cache
+        torch.cuda.synchronize()
+        del flush
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    shapes = synth.gpt2_124m_step()
+    log(f"setup GPT-2-124M step: {len(shapes)} products")
+    step = Step(torch, q4, shapes, 0, 1, config_id=1)
+    t = timer.region(step.run_graph, K, W)
     value = step.bytes * K / t / 1e9
+    launches = K * len(shapes)
     per_launch_bytes = step.bytes / len(shapes)
-    per_launch_s = t / (K * len(shapes))
+    achieved = per_launch_bytes / (t / launches) / 1e9
+    log(f"graph: {t / K * 1e6:.2f} us/step, {value:.1f} GB/s, {K / t:.0f} tokens/s")
+    traffic = traffic_from_profile(per_launch_bytes)
+
     result = {
-        "metric": "Q4 decode GEMV effective HBM GB/s (% of peak) + layer-stack tokens/s at 1 GPU",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -178,69 +297,60 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_0 weights, fp16 x products, fp32 accumulate",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; no checkpoints)",
+        "dtype": "f32",
+        "arithmetic": "Q4_0 weights as exact signed fp16 codes; activations as hi+lo fp16 pairs (~2^-23 relative); "
+                      "v_dot2 products, fp32 accumulation",
+        "data": "synthetic: seeded N(0, 0.02) weights, N(0, 1) activations; no checkpoints",
         "config": {
-            "workload": {"gpt2": "GPT-2-124M decode step", "smollm2": "SmolLM2-360M decode step",
-                         "llama7b": "7B-class layer as listed"}[args.workload],
+            "workload": "GPT-2-124M decode step (49 Q4_0 products, batch 1)",
             "format": "Q4_0",
             "tokens": 1,
             "products_per_step": len(shapes),
             "bytes_per_step": step.bytes,
-            "launch": "HIP graph replay, one launch per step",
-            "cache": f"cold: {len(step.copies)} rotating weight copies",
+            "launch": "HIP graph replay, one graph launch per step",
+            "cache": f"cold: {len(step.copies)} rotating weight copies (>= 512 MiB)",
         },
         "tokens_per_s": round(K / t, 1),
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(per_launch_bytes / per_launch_s / 1e9, 2),
+            "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(per_launch_bytes / per_launch_s / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "q4::gemv_kernel (all 49 launches of the step)",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel": "q4::gemv::gemv_kernel (Q4_0, one token)",
             "per_launch_bytes": round(per_launch_bytes),
-            "avg_launch_us": round(per_launch_s * 1e6, 3),
+            "avg_launch_us": round(t / launches * 1e6, 3),
+            "kernel_source_sha256": kernel_source_hash(),
         },
     }
 
     if not args.no_extras:
         extras = {}
-        tp = time_region(torch, lambda i: step.run_plain(i, q4), max(10, K // 4), 3)
-        extras["plain_stream_us_per_step"] = round(tp / max(10, K // 4) * 1e6, 2)
-        extras["plain_stream_tokens_per_s"] = round(max(10, K // 4) / tp, 1)
-        extras.update(bench_shapes(torch, q4, synth))
+        n_plain = max(20, K // 10)
+        tp = timer.region(lambda i: step.run_plain(q4, i), n_plain, 5)
+        extras["gpt2_plain_stream"] = {"us_per_step": round(tp / n_plain * 1e6, 2), "tokens_per_s": round(n_plain / tp, 1)}
+        extras["launch_floor_us"] = launch_floor(torch, q4, timer)
+        extras["gate_7b"] = bench_7b(torch, q4, timer)
+        log("setup SmolLM2-360M step")
+        sm = Step(torch, q4, synth.smollm2_360m_step(), 0, 1, config_id=2)
+        ts = timer.region(sm.run_graph, max(50, K // 10), 5) / max(50, K // 10)
+        extras["smollm2_step"] = {"us_per_step": round(ts * 1e6, 2), "tokens_per_s": round(1 / ts, 1),
+                                  "GB_s": round(sm.bytes / ts / 1e9, 1), "products": len(sm.shapes),
+                                  "cache": f"cold: {len(sm.copies)} copies"}
+        log(f"smollm2 step: {ts * 1e6:.1f} us, {1 / ts:.0f} tokens/s")
+        sm.close()
+        del sm
+        torch.cuda.empty_cache()
+        extras["gemm_smollm2_layer"] = bench_gemm(torch, q4, timer)
         result["extras"] = extras
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(step)
     step.close()
-    print(json.dumps(result))
-
-
-def bench_shapes(torch, q4, synth, reps=20):
-    """Single products at the 7B-class shapes, cold: a graph of one launch per
-    rotating weight copy, replayed; HIP events over the replays."""
-    out = {}
-    for fmt, ns in ((0, (1,)), (1, (1, 4, 8))):
-        for k, m in (synth.llama7b_layer()[:2] + synth.llama7b_layer()[3:]):
-            wq = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(4, k + m), m, k))
-            copies = [torch.from_numpy(wq).cuda() for _ in range(copies_for(wq.size))]
-            for n in ns:
-                x = torch.from_numpy(synth.activations(synth.seed_for(4, k, True), n, k)).cuda()
-                y = torch.empty((n, m), device="cuda")
-                g = q4.Q4Graph(fmt, [(c, x, y, m, k) for c in copies], n)
-                t = time_region(torch, lambda i: g.launch(), reps, 3) / (reps * len(copies))
-                g.close()
-                gbs = gemv_bytes(m, k, n, fmt) / t / 1e9
-                key = f"{'q4_0' if fmt == 0 else 'q4_k'}_{k}x{m}_n{n}"
-                out[key] = {"us": round(t * 1e6, 3), "GB_s": round(gbs, 1),
-                            "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
-                log(f"{key}: {t * 1e6:.2f} us {gbs:.0f} GB/s")
-            del copies
-    return out
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":
