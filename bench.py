@@ -343,6 +343,16 @@ def main():
         sm.close()
         del sm
         torch.cuda.empty_cache()
+        log("setup SmolLM2-360M step, fused shared-input projections")
+        sf = Step(torch, q4, synth.smollm2_360m_step_fused(), 0, 1, config_id=2)
+        tf = timer.region(sf.run_graph, max(50, K // 10), 5) / max(50, K // 10)
+        extras["smollm2_step_fused_qkv_gateup"] = {
+            "us_per_step": round(tf * 1e6, 2), "tokens_per_s": round(1 / tf, 1), "GB_s": round(sf.bytes / tf / 1e9, 1),
+            "products": len(sf.shapes), "cache": f"cold: {len(sf.copies)} copies"}
+        log(f"smollm2 fused step: {tf * 1e6:.1f} us, {1 / tf:.0f} tokens/s")
+        sf.close()
+        del sf
+        torch.cuda.empty_cache()
         extras["gemm_smollm2_layer"] = bench_gemm(torch, q4, timer)
         result["extras"] = extras
 

@@ -134,6 +134,22 @@ int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y,
 int q4_gemm(int fmt, const void *w, const uint16_t *x_bf16, float *y,
             int64_t m, int64_t k, int64_t n, void *hip_stream);
 
+/* Tile geometry of the prefill product: tile_rows x tile_tokens outputs per
+ * workgroup, stage_k weights dequantized per LDS stage (a zero field keeps
+ * the library's choice). Instantiated (rows, tokens, stage_k): (32,64,64)
+ * (32,64,128) (32,64,256) (32,128,64) (32,128,128) (64,64,128) (64,64,256);
+ * Q4_K needs stage_k % 64 == 0. Others return Q4_EUNSUPPORTED. */
+typedef struct {
+    int tile_rows;
+    int tile_tokens;
+    int stage_k;
+} q4_gemm_tuning;
+
+/* q4_gemm with an explicit tile geometry; same arguments, layouts, results
+ * and errors, plus Q4_EINVAL for a null or negative tuning. */
+int q4_gemm_tuned(int fmt, const void *w, const uint16_t *x_bf16, float *y,
+                  int64_t m, int64_t k, int64_t n, const q4_gemm_tuning *tuning, void *hip_stream);
+
 /* One decode product of a layer stack. */
 typedef struct {
     const void *w;   /* device weights */

@@ -39,6 +39,10 @@ class q4_gemv_tuning(ctypes.Structure):
                 ("waves_per_group", ctypes.c_int), ("groups_per_cu", ctypes.c_int)]
 
 
+class q4_gemm_tuning(ctypes.Structure):
+    _fields_ = [("tile_rows", ctypes.c_int), ("tile_tokens", ctypes.c_int), ("stage_k", ctypes.c_int)]
+
+
 class q4_gemv_op(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("m", ctypes.c_int64), ("k", ctypes.c_int64)]
@@ -53,6 +57,8 @@ _SIGS = {
     "q4_gemv_tuned": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64,
                                       ctypes.POINTER(q4_gemv_tuning), _vp]),
     "q4_gemm": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q4_gemm_tuned": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64,
+                                      ctypes.POINTER(q4_gemm_tuning), _vp]),
     "q4_gemv_sequence": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_gemv_op), ctypes.c_int, _i64, _vp]),
     "q4_graph_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_gemv_op), ctypes.c_int, _i64, _vp,
                                         ctypes.POINTER(_vp)]),
@@ -129,6 +135,15 @@ def q4_gemm(fmt: int, w, x_bf16, y, m: int, k: int, stream=None) -> None:
     n = x_bf16.shape[0]
     _check(_lib.q4_gemm(fmt, w.data_ptr(), x_bf16.data_ptr(), y.data_ptr(), m, k, n, _stream_ptr(stream)),
            "q4_gemm")
+
+
+def q4_gemm_tuned(fmt: int, w, x_bf16, y, m: int, k: int, tile_rows=0, tile_tokens=0, stage_k=0,
+                  stream=None) -> None:
+    """q4_gemm with an explicit tile geometry (0 keeps the library's choice)."""
+    n = x_bf16.shape[0]
+    t = q4_gemm_tuning(tile_rows, tile_tokens, stage_k)
+    _check(_lib.q4_gemm_tuned(fmt, w.data_ptr(), x_bf16.data_ptr(), y.data_ptr(), m, k, n, ctypes.byref(t),
+                              _stream_ptr(stream)), "q4_gemm_tuned")
 
 
 def _ops_array(ops):

@@ -32,8 +32,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kStageK = 64;              // K per stage
-constexpr int kLdsRow = kStageK + 8;     // bf16 per LDS row (padding staggers banks)
 constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer descriptor, gfx9 family
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
@@ -62,19 +60,22 @@ struct GemmQ4_0 {
         uint32_t q;  // 4 nibble bytes
         uint32_t d;  // fp16 scale bits
     };
-    // Item it8 (0..7) of stage s: block 2s + it8/4, nibble bytes 4*(it8%4)...
+    // Item it8 (0 .. KC/8-1) of stage s (KC weights per row): block
+    // s*KC/32 + it8/4 of the row, nibble bytes 4*(it8%4) .. +3.
+    template <int KC>
     __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
                                 uint32_t row, int s, int it8)
     {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
-        const uint32_t blk = row * nu + 2u * static_cast<uint32_t>(s) + static_cast<uint32_t>(it8 >> 2);
+        const uint32_t blk = row * nu + static_cast<uint32_t>(s * (KC / 32) + (it8 >> 2));
         g.q = __builtin_amdgcn_raw_buffer_load_b32(r, blk * 16u + 4u * static_cast<uint32_t>(it8 & 3), 0, 0);
         g.d = __builtin_amdgcn_raw_buffer_load_b16(r, scale_plane + blk * 2u, 0, 0);
     }
     __device__ static int lo(int it8) { return 32 * (it8 >> 2) + 4 * (it8 & 3); }
     __device__ static int hi(int it8) { return lo(it8) + 16; }
     // (q - 8) * d, exact in fp32: q*d is exact and fma rounds the exact result once.
-    __device__ static void dequant(const Item &g, int /*it8*/, bf16x4 &vlo, bf16x4 &vhi)
+    template <int KC>
+    __device__ static void dequant(const Item &g, int /*s*/, int /*it8*/, bf16x4 &vlo, bf16x4 &vhi)
     {
         const float d = half_bits_to_float(g.d);
         const float m8 = -8.0f * d;
@@ -95,26 +96,30 @@ struct GemmQ4_K {
         uint32_t q;  // 4 nibble bytes
         u32x4 h;     // super-block header: d, dmin, 12 scale bytes
     };
-    // Stage s is nibble chunk c = s % 4 of super-block s / 4: byte i of the
-    // chunk holds elements i (sub-block 2c) and 32 + i (sub-block 2c+1).
+    // Stage s covers nibble chunks s*KC/64 .. of the row (4 chunks of 32
+    // bytes per super-block); item it8 is bytes 4*(it8%8) .. +3 of chunk
+    // s*KC/64 + it8/8. Byte i of a chunk c holds elements 64c+i (sub-block
+    // 2c) and 64c+32+i (sub-block 2c+1).
+    template <int KC>
     __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t /*scale_plane*/, uint32_t nu,
                                 uint32_t row, int s, int it8)
     {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
-        const uint32_t base = (row * (nu >> 3) + static_cast<uint32_t>(s >> 2)) * 144u;
+        const uint32_t chunk = static_cast<uint32_t>(s * (KC / 64) + (it8 >> 3));
+        const uint32_t base = (row * (nu >> 3) + (chunk >> 2)) * 144u;
         g.h = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, base, 0, 0));
-        g.q = __builtin_amdgcn_raw_buffer_load_b32(r, base + 16u + 32u * static_cast<uint32_t>(s & 3) +
-                                                          4u * static_cast<uint32_t>(it8), 0, 0);
+        g.q = __builtin_amdgcn_raw_buffer_load_b32(r, base + 16u + 32u * (chunk & 3u) + 4u * static_cast<uint32_t>(it8 & 7), 0, 0);
     }
-    __device__ static int lo(int it8) { return 4 * it8; }
-    __device__ static int hi(int it8) { return 32 + 4 * it8; }
+    __device__ static int lo(int it8) { return 64 * (it8 >> 3) + 4 * (it8 & 7); }
+    __device__ static int hi(int it8) { return lo(it8) + 32; }
     // d*sc*q - dmin*m: d*sc*q is exact in fp32 (<= 21 bits), so the fma rounds
     // the exact difference once, as the format's definition does.
-    __device__ static void dequant(const Item &g, int s, bf16x4 &vlo, bf16x4 &vhi)
+    template <int KC>
+    __device__ static void dequant(const Item &g, int s, int it8, bf16x4 &vlo, bf16x4 &vhi)
     {
-        // Sub-blocks a = 2c, b = 2c+1 with c = s % 4; their 6-bit fields sit in
-        // bytes 2(c&1), 2(c&1)+1 of the three scale words.
-        const uint32_t c = static_cast<uint32_t>(s & 3);
+        // Sub-blocks a = 2c, b = 2c+1 of chunk c (within the super-block);
+        // their 6-bit fields sit in bytes 2(c&1), 2(c&1)+1 of the scale words.
+        const uint32_t c = static_cast<uint32_t>(s * (KC / 64) + (it8 >> 3)) & 3u;
         const uint32_t sh = (c & 1u) << 4;
         const uint32_t s0 = g.h.y >> sh, s1 = g.h.z >> sh, s2 = g.h.w >> sh;
         const bool upper = c >= 2;
@@ -142,16 +147,19 @@ struct GemmQ4_K {
 // l%16, the same k range; D (16 x 16): lane l holds rows 4(l/16)..+3 of
 // column l%16. Rows are weight rows, columns are tokens.
 
-template <class F, int TM, int TN>
+template <class F, int TM, int TN, int KC>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w, uint32_t wbytes,
                                                    const uint16_t *__restrict__ x, float *__restrict__ y, int M,
                                                    int K, int N)
 {
-    constexpr int FM = TM / 16;        // A fragments (16-row blocks) per wave
-    constexpr int WN = TN / 4;         // tokens per wave
-    constexpr int FN = WN / 16;        // B fragments per wave
-    constexpr int WI = TM * 8 / 256;   // weight items per thread per stage
-    static_assert(WI >= 1 && FN >= 1, "tile too small");
+    constexpr int FM = TM / 16;              // A fragments (16-row blocks) per wave
+    constexpr int WN = TN / 4;               // tokens per wave
+    constexpr int FN = WN / 16;              // B fragments per wave
+    constexpr int SL = KC / 32;              // 32-wide k slices per stage
+    constexpr int IPR = KC / 8;              // weight items (8 weights) per row per stage
+    constexpr int WI = TM * IPR / 256;       // weight items per thread per stage
+    constexpr int kLdsRow = KC + 8;          // bf16 per LDS row (padding staggers banks)
+    static_assert(WI >= 1 && FN >= 1 && TM * IPR % 256 == 0, "tile too small");
     __shared__ __attribute__((aligned(16))) __bf16 ws[TM * kLdsRow];
 
     const int tid = threadIdx.x;
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
     const int t0 = blockIdx.y * TN;
     const uint32_t nu = static_cast<uint32_t>(K / 32);
     const uint32_t scale_plane = static_cast<uint32_t>(static_cast<uint64_t>(M) * static_cast<uint64_t>(K) / 2u);
-    const int S = (K + kStageK - 1) / kStageK;
+    const int S = (K + KC - 1) / KC;
     const __amdgpu_buffer_rsrc_t xr =
         make_rsrc(x, static_cast<uint32_t>(static_cast<uint64_t>(N) * static_cast<uint64_t>(K) * 2u));
     // This lane's token for B fragment fn, and its k offset within a 32-slice.
@@ -174,20 +182,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
         for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     typename F::Item gi[2][WI];
-    bf16x8 xb[2][FN][2];
+    bf16x8 xb[2][FN][SL];
 
     auto load_stage = [&](int buf, int s) {
 #pragma unroll
         for (int i = 0; i < WI; i++) {
             const int it = tid + 256 * i;
-            F::load(gi[buf][i], w, wbytes, scale_plane, nu, static_cast<uint32_t>(r0 + (it >> 3)), s, it & 7);
+            F::template load<KC>(gi[buf][i], w, wbytes, scale_plane, nu, static_cast<uint32_t>(r0 + it / IPR), s,
+                                 it % IPR);
         }
 #pragma unroll
         for (int fn = 0; fn < FN; fn++) {
             const uint32_t tok = static_cast<uint32_t>(t0 + wave * WN + 16 * fn + (lane & 15));
 #pragma unroll
-            for (int kk = 0; kk < 2; kk++) {
-                const uint32_t off = (tok * static_cast<uint32_t>(K) + static_cast<uint32_t>(s * kStageK + 32 * kk + ktok)) * 2u;
+            for (int kk = 0; kk < SL; kk++) {
+                const uint32_t off = (tok * static_cast<uint32_t>(K) + static_cast<uint32_t>(s * KC + 32 * kk + ktok)) * 2u;
                 xb[buf][fn][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
             }
         }
@@ -196,17 +205,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
 #pragma unroll
         for (int i = 0; i < WI; i++) {
             const int it = tid + 256 * i;
-            const int row = it >> 3, it8 = it & 7;
+            const int row = it / IPR, it8 = it % IPR;
             bf16x4 vlo, vhi;
-            F::dequant(gi[buf][i], s, vlo, vhi);
+            F::template dequant<KC>(gi[buf][i], s, it8, vlo, vhi);
             *reinterpret_cast<bf16x4 *>(&ws[row * kLdsRow + F::lo(it8)]) = vlo;
             *reinterpret_cast<bf16x4 *>(&ws[row * kLdsRow + F::hi(it8)]) = vhi;
         }
     };
     auto compute_stage = [&](int buf, int s) {
 #pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-            if (s * kStageK + 32 * kk >= K) break;  // K = 32 mod 64: the last stage is half
+        for (int kk = 0; kk < SL; kk++) {
+            if (s * KC + 32 * kk >= K) break;  // a last stage shorter than KC
             bf16x8 a[FM];
 #pragma unroll
             for (int fm = 0; fm < FM; fm++)
@@ -254,25 +263,44 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
     }
 }
 
-template <class F, int TM, int TN>
+template <class F, int TM, int TN, int KC>
 int launch_tile(const void *w, const uint16_t *x, float *y, int64_t m, int64_t k, int64_t n, hipStream_t s)
 {
     const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(F::kFormat, m, k));
     const dim3 grid(static_cast<unsigned>((m + TM - 1) / TM), static_cast<unsigned>((n + TN - 1) / TN));
-    hipLaunchKernelGGL((gemm_kernel<F, TM, TN>), grid, dim3(256), 0, s, static_cast<const uint8_t *>(w), wbytes, x,
-                       y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
+    hipLaunchKernelGGL((gemm_kernel<F, TM, TN, KC>), grid, dim3(256), 0, s, static_cast<const uint8_t *>(w), wbytes,
+                       x, y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
     return hipGetLastError() == hipSuccess ? Q4_OK : Q4_EHIP;
+}
+
+// Tile geometries: (rows, tokens, K per stage).
+#define Q4_GEMM_TILES(X) \
+    X(32, 64, 64)        \
+    X(32, 64, 128)       \
+    X(32, 64, 256)       \
+    X(32, 128, 64)       \
+    X(32, 128, 128)      \
+    X(64, 64, 128)       \
+    X(64, 64, 256)
+
+template <class F>
+int launch_geometry(int tm, int tn, int kc, const void *w, const uint16_t *x, float *y, int64_t m, int64_t k,
+                    int64_t n, hipStream_t s)
+{
+#define Q4_TILE_CASE(A, B, C) \
+    if (tm == A && tn == B && kc == C) return launch_tile<F, A, B, C>(w, x, y, m, k, n, s);
+    Q4_GEMM_TILES(Q4_TILE_CASE)
+#undef Q4_TILE_CASE
+    return Q4_EUNSUPPORTED;
 }
 
 template <class F>
 int launch_fmt(const void *w, const uint16_t *x, float *y, int64_t m, int64_t k, int64_t n, hipStream_t s, int cus)
 {
-    // Wider token tiles reuse each dequantized weight more; fall back to
-    // narrower ones while that leaves fewer than two tiles per compute unit.
-    const int64_t tiles128 = ((m + 31) / 32) * ((n + 127) / 128);
-    if (tiles128 >= 2LL * cus || n <= 64) return n <= 64 ? launch_tile<F, 32, 64>(w, x, y, m, k, n, s)
-                                                         : launch_tile<F, 32, 128>(w, x, y, m, k, n, s);
-    return launch_tile<F, 32, 64>(w, x, y, m, k, n, s);
+    (void)cus;
+    // Stages are latency-bound at these sizes, so wide stages win; 32 x 64
+    // tiles keep enough workgroups for the SmolLM2-sized matrices.
+    return launch_geometry<F>(32, 64, 256, w, x, y, m, k, n, s);
 }
 
 }  // namespace gemm
@@ -287,6 +315,23 @@ int launch_gemm(int fmt, const void *w, const uint16_t *x, float *y, int64_t m, 
 }
 
 }  // namespace q4
+
+extern "C" int q4_gemm_tuned(int fmt, const void *w, const uint16_t *x_bf16, float *y, int64_t m, int64_t k,
+                             int64_t n, const q4_gemm_tuning *tuning, void *hip_stream)
+{
+    const int st = q4::check_product_args(fmt, w, x_bf16, y, m, k, n, INT64_MAX);
+    if (st != Q4_OK) return st;
+    if (!tuning || tuning->tile_rows < 0 || tuning->tile_tokens < 0 || tuning->stage_k < 0) return Q4_EINVAL;
+    if (m == 0 || n == 0) return Q4_OK;
+    if (n >= (1LL << 22)) return Q4_EUNSUPPORTED;
+    const int tm = tuning->tile_rows ? tuning->tile_rows : 32;
+    const int tn = tuning->tile_tokens ? tuning->tile_tokens : 64;
+    const int kc = tuning->stage_k ? tuning->stage_k : 256;
+    if (fmt == Q4_FMT_Q4_K && kc % 64) return Q4_EUNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (fmt == Q4_FMT_Q4_0) return q4::gemm::launch_geometry<q4::gemm::GemmQ4_0>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
+    return q4::gemm::launch_geometry<q4::gemm::GemmQ4_K>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
+}
 
 extern "C" int q4_gemm(int fmt, const void *w, const uint16_t *x_bf16, float *y, int64_t m, int64_t k, int64_t n,
                        void *hip_stream)

@@ -113,6 +113,15 @@ def smollm2_360m_step():
     return [s for _ in range(32) for s in layer] + [(h, 49152)]
 
 
+def smollm2_360m_step_fused():
+    """SmolLM2-360M decode step with the shared-input projections stacked by
+    rows: q|k|v 960->1600, o 960->960, gate|up 960->5120, down 2560->960
+    (x 32 layers), then the LM head. Same weight bytes, 129 products."""
+    h = 960
+    layer = [(h, 1600), (h, h), (h, 5120), (2560, h)]
+    return [s for _ in range(32) for s in layer] + [(h, 49152)]
+
+
 def smollm2_360m_layer():
     """The 7 matrices of one SmolLM2-360M layer (prefill GEMM workload)."""
     h = 960

@@ -198,6 +198,24 @@ def test_extreme_activation_q4_k(env):
     check_tolerance(y, yr, orc.termscale(1, buf, m, k, x), GEMV_TOL, what="q4_k outlier")
 
 
+@pytest.mark.parametrize("fmt,k,parts", [(0, 960, (960, 320, 320)), (0, 960, (2560, 2560)), (1, 1024, (512, 256, 256))])
+def test_stacked_projections_equal_separate_products(env, fmt, k, parts):
+    # Shared-input projections (q|k|v, gate|up) row-stacked into one matrix:
+    # blocks never cross rows, so the stacked weights quantize to the
+    # concatenated rows and one launch reproduces the separate products
+    # bit for bit (same tile geometry for every part).
+    torch, q4, orc = env
+    ws = [synth.weights(950 + i, m, k) for i, m in enumerate(parts)]
+    x = synth.activations(960, 2, k)
+    stacked = np.concatenate(ws, axis=0)
+    ys = _gemv(env, fmt, q4.q4_quantize_ref(fmt, stacked), x, stacked.shape[0], k)
+    r = 0
+    for w in ws:
+        y1 = _gemv(env, fmt, q4.q4_quantize_ref(fmt, w), x, w.shape[0], k)
+        assert np.array_equal(ys[:, r:r + w.shape[0]].view(np.uint32), y1.view(np.uint32))
+        r += w.shape[0]
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_sequence_and_graph_match_single_calls(env, fmt):
     torch, q4, _ = env

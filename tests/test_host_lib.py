@@ -182,6 +182,16 @@ def test_tuned_argument_errors(q4):
     assert f(0, None, None, None, 0, 256, 1, ctypes.byref(good), None) == q4.Q4_OK
 
 
+def test_gemm_tuned_argument_errors(q4):
+    f = q4.raw().q4_gemm_tuned
+    ok = (A16, A16 * 2, A16 * 3)
+    assert f(0, *ok, 64, 256, 4, None, None) == q4.Q4_EINVAL
+    assert f(0, *ok, 64, 256, 4, ctypes.byref(q4.q4_gemm_tuning(-1, 0, 0)), None) == q4.Q4_EINVAL
+    assert f(0, *ok, 64, 48, 4, ctypes.byref(q4.q4_gemm_tuning(0, 0, 0)), None) == q4.Q4_EINVAL
+    assert f(0, A16, A16 + 2, A16, 64, 256, 4, ctypes.byref(q4.q4_gemm_tuning(0, 0, 0)), None) == q4.Q4_EALIGN
+    assert f(0, None, None, None, 0, 256, 4, ctypes.byref(q4.q4_gemm_tuning(0, 0, 0)), None) == q4.Q4_OK
+
+
 def test_sequence_and_graph_argument_errors(q4):
     lib = q4.raw()
     ops = (q4.q4_gemv_op * 2)()
