@@ -64,7 +64,7 @@ typedef enum { Q4_FMT_Q4_0 = 0, Q4_FMT_Q4_K = 1 } q4_format;
 enum {
     Q4_OK = 0,
     Q4_EINVAL = -1,       /* bad size, null pointer, k not a whole number of blocks, short buffer */
-    Q4_EUNSUPPORTED = -2, /* n outside 1..8 for gemv; unknown format; size beyond the 32-bit offsets */
+    Q4_EUNSUPPORTED = -2, /* n outside 1..8 for gemv; unknown format; w, x or y of 2 GiB or more */
     Q4_EALIGN = -3,       /* w or x not 16-byte aligned, y not 4-byte aligned */
     Q4_ENONFINITE = -4,   /* NaN or Inf among the weights given to the quantizer */
     Q4_ERANGE = -5,       /* a block scale that rounds to a non-finite fp16 */
@@ -135,10 +135,10 @@ int q4_gemm(int fmt, const void *w, const uint16_t *x_bf16, float *y,
             int64_t m, int64_t k, int64_t n, void *hip_stream);
 
 /* Tile geometry of the prefill product: tile_rows x tile_tokens outputs per
- * workgroup, stage_k weights dequantized per LDS stage (a zero field keeps
- * the library's choice). Instantiated (rows, tokens, stage_k): (32,64,64)
- * (32,64,128) (32,64,256) (32,128,64) (32,128,128) (64,64,128) (64,64,256);
- * Q4_K needs stage_k % 64 == 0. Others return Q4_EUNSUPPORTED. */
+ * workgroup, stage_k weights per row dequantized into LDS per chunk of K (a
+ * zero field keeps the library's choice). Instantiated (rows, tokens,
+ * stage_k): (16,64,512) (16,64,1024) (32,64,256) (32,64,512) (32,64,1024)
+ * (32,128,512) (64,64,512); others return Q4_EUNSUPPORTED. */
 typedef struct {
     int tile_rows;
     int tile_tokens;
@@ -177,6 +177,10 @@ int q4_graph_destroy(q4_graph *graph);
 
 /* Static string for a status code. */
 const char *q4_strerror(int status);
+
+/* Name of the HIP error behind the calling thread's most recent Q4_EHIP
+ * ("hipSuccess" if there was none); a static string. */
+const char *q4_last_hip_error(void);
 
 #ifdef __cplusplus
 }

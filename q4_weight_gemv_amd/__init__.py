@@ -31,6 +31,14 @@ BLOCK = {Q4_FMT_Q4_0: 32, Q4_FMT_Q4_K: 256}
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python q4_weight_gemv_amd/build.py`")
 
+# The library must run on the same HIP runtime as the torch tensors and
+# streams it is handed. torch ships its own libamdhip64 under the same soname
+# as the system one this library links to, and the dynamic linker keeps the
+# first copy loaded; importing torch first makes that copy torch's. (Loaded
+# the other way round, the two end up on different runtimes and the library
+# finds no device.)
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 
@@ -65,6 +73,7 @@ _SIGS = {
     "q4_graph_launch": (ctypes.c_int, [_vp, _vp]),
     "q4_graph_destroy": (ctypes.c_int, [_vp]),
     "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "q4_last_hip_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -76,7 +85,8 @@ EXPORTS = tuple(_SIGS)
 
 class Q4Error(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {q4_strerror(status)} (status {status})")
+        detail = f", {_lib.q4_last_hip_error().decode()}" if status == Q4_EHIP else ""
+        super().__init__(f"{where}: {q4_strerror(status)} (status {status}{detail})")
         self.status = status
 
 
@@ -119,6 +129,15 @@ def q4_gemv(fmt: int, w, x, y, m: int, k: int, stream=None) -> None:
     """y[n][m] = W_hat x for n = x.shape[0] tokens (1..8); torch device tensors."""
     n = x.shape[0] if x.dim() == 2 else 1
     _check(_lib.q4_gemv(fmt, w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k, n, _stream_ptr(stream)), "q4_gemv")
+
+
+# The instantiated tile geometries, as the header lists them.
+# Decode: (lanes_per_row, rows_per_lane, waves_per_group).
+GEMV_GEOMETRIES = ((8, 1, 1), (8, 2, 1), (8, 4, 1), (16, 1, 1), (16, 2, 1), (32, 1, 1), (32, 2, 1), (64, 1, 1),
+                   (16, 1, 4), (32, 1, 4), (32, 2, 4), (64, 1, 4), (64, 2, 4), (64, 4, 4))
+# Prefill: (tile_rows, tile_tokens, stage_k).
+GEMM_TILES = ((16, 64, 512), (16, 64, 1024), (32, 64, 256), (32, 64, 512), (32, 64, 1024), (32, 128, 512),
+              (64, 64, 512))
 
 
 def q4_gemv_tuned(fmt: int, w, x, y, m: int, k: int, lanes_per_row=0, rows_per_lane=0, waves_per_group=0,

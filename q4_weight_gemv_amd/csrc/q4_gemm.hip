@@ -7,19 +7,23 @@
 // accumulation), since prefill is a dense contraction.
 //
 // Work decomposition: a workgroup of 4 waves computes a TM (weight rows) x TN
-// (tokens) tile of Y over all of K, in stages of 64 along K.
-//   * Weights: each stage's TM x 64 quantized tile is dequantized exactly in
+// (tokens) tile of Y over all of K, in chunks of KC along K.
+//   * Weights: each chunk's TM x KC quantized tile is dequantized exactly in
 //     fp32 ((q-8)*d, or d*sc*q - dmin*m for Q4_K), rounded to bf16 (RNE) and
 //     written to LDS once; all four waves read it as MFMA A operands, so each
-//     dequantized weight is reused across the whole token tile.
+//     dequantized weight is reused across the whole token tile. The packed
+//     tile of chunk c+1 is loaded into registers while chunk c is multiplied.
 //   * Activations: every wave owns TN/4 tokens, so its bf16 X fragments go
-//     straight from memory into registers in the MFMA B layout (no LDS).
-//   * The next stage's loads are issued before the current stage's MFMAs.
-//     (A workgroup barrier waits for all outstanding loads on this target, so
-//     one stage of prefetch is what a barrier-synchronised tile can overlap.)
-//   * Loads are raw buffer loads: rows past M and tokens past N read zeros.
+//     straight from memory into registers in the MFMA B layout (no LDS),
+//     through a ring of XD 32-wide k slices that is refilled as it is
+//     consumed, so XD slices of loads are in flight behind the MFMAs.
+//   * Loads are raw buffer loads and are all issued unconditionally: rows past
+//     M, tokens past N and k past K read zeros (out-of-range offsets), so the
+//     last chunk is padded with zero products and no branch sits between
+//     slices, which keeps the compiler's wait counting exact.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "q4_internal.h"
@@ -33,6 +37,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBufferWord3 = 0x00020000; // raw 32-bit buffer descriptor, gfx9 family
+// A lane offset past every descriptor's range (operands are below 2 GiB): the
+// load returns zeros without a memory request.
+constexpr uint32_t kNoFetch = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
@@ -56,20 +63,26 @@ __device__ __forceinline__ bf16x4 to_bf16(float a, float b, float c, float d)
 
 struct GemmQ4_0 {
     static constexpr int kFormat = Q4_FMT_Q4_0;
+    static constexpr int kRingVgprs = 128;  // activation ring budget (Items are 2 VGPRs)
     struct Item {
         uint32_t q;  // 4 nibble bytes
         uint32_t d;  // fp16 scale bits
     };
     // Item it8 (0 .. KC/8-1) of stage s (KC weights per row): block
     // s*KC/32 + it8/4 of the row, nibble bytes 4*(it8%4) .. +3.
+    // Items of a block past the row's end, or of a row past M, read zeros
+    // (d = 0, so they dequantize to zero).
     template <int KC>
     __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
-                                uint32_t row, int s, int it8)
+                                uint32_t row, bool row_ok, int s, int it8)
     {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
-        const uint32_t blk = row * nu + static_cast<uint32_t>(s * (KC / 32) + (it8 >> 2));
-        g.q = __builtin_amdgcn_raw_buffer_load_b32(r, blk * 16u + 4u * static_cast<uint32_t>(it8 & 3), 0, 0);
-        g.d = __builtin_amdgcn_raw_buffer_load_b16(r, scale_plane + blk * 2u, 0, 0);
+        const uint32_t ub = static_cast<uint32_t>(s * (KC / 32) + (it8 >> 2));
+        const uint32_t blk = row * nu + ub;
+        const bool live = row_ok && ub < nu;
+        g.q = __builtin_amdgcn_raw_buffer_load_b32(r, live ? blk * 16u + 4u * static_cast<uint32_t>(it8 & 3) : kNoFetch,
+                                                   0, 0);
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(r, live ? scale_plane + blk * 2u : kNoFetch, 0, 0);
     }
     __device__ static int lo(int it8) { return 32 * (it8 >> 2) + 4 * (it8 & 3); }
     __device__ static int hi(int it8) { return lo(it8) + 16; }
@@ -92,6 +105,7 @@ struct GemmQ4_0 {
 
 struct GemmQ4_K {
     static constexpr int kFormat = Q4_FMT_Q4_K;
+    static constexpr int kRingVgprs = 64;  // activation ring budget (Items are 5 VGPRs)
     struct Item {
         uint32_t q;  // 4 nibble bytes
         u32x4 h;     // super-block header: d, dmin, 12 scale bytes
@@ -100,15 +114,18 @@ struct GemmQ4_K {
     // bytes per super-block); item it8 is bytes 4*(it8%8) .. +3 of chunk
     // s*KC/64 + it8/8. Byte i of a chunk c holds elements 64c+i (sub-block
     // 2c) and 64c+32+i (sub-block 2c+1).
+    // Items past the row's end, or of a row past M, read zeros (d = dmin = 0).
     template <int KC>
     __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t /*scale_plane*/, uint32_t nu,
-                                uint32_t row, int s, int it8)
+                                uint32_t row, bool row_ok, int s, int it8)
     {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
         const uint32_t chunk = static_cast<uint32_t>(s * (KC / 64) + (it8 >> 3));
-        const uint32_t base = (row * (nu >> 3) + (chunk >> 2)) * 144u;
+        const bool live = row_ok && (chunk >> 2) < (nu >> 3);
+        const uint32_t base = live ? (row * (nu >> 3) + (chunk >> 2)) * 144u : kNoFetch;
         g.h = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, base, 0, 0));
-        g.q = __builtin_amdgcn_raw_buffer_load_b32(r, base + 16u + 32u * (chunk & 3u) + 4u * static_cast<uint32_t>(it8 & 7), 0, 0);
+        g.q = __builtin_amdgcn_raw_buffer_load_b32(r, base + 16u + 32u * (chunk & 3u) + 4u * static_cast<uint32_t>(it8 & 7),
+                                                   0, 0);
     }
     __device__ static int lo(int it8) { return 64 * (it8 >> 3) + 4 * (it8 & 7); }
     __device__ static int hi(int it8) { return lo(it8) + 32; }
@@ -155,12 +172,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
     constexpr int FM = TM / 16;              // A fragments (16-row blocks) per wave
     constexpr int WN = TN / 4;               // tokens per wave
     constexpr int FN = WN / 16;              // B fragments per wave
-    constexpr int SL = KC / 32;              // 32-wide k slices per stage
-    constexpr int IPR = KC / 8;              // weight items (8 weights) per row per stage
-    constexpr int WI = TM * IPR / 256;       // weight items per thread per stage
+    constexpr int SPC = KC / 32;             // 32-wide k slices per chunk
+    constexpr int XR = F::kRingVgprs / (4 * FN);
+    constexpr int XD = SPC < XR ? SPC : XR;  // depth of the activation ring, in slices
+    constexpr int IPR = KC / 8;              // weight items (8 weights) per row per chunk
+    constexpr int WI = TM * IPR / 256;       // weight items per thread per chunk
     constexpr int kLdsRow = KC + 8;          // bf16 per LDS row (padding staggers banks)
-    static_assert(WI >= 1 && FN >= 1 && TM * IPR % 256 == 0, "tile too small");
-    __shared__ __attribute__((aligned(16))) __bf16 ws[TM * kLdsRow];
+    static_assert(WI >= 1 && FN >= 1 && TM * IPR % 256 == 0 && XD >= 1 && SPC % XD == 0, "bad tile");
+    extern __shared__ __attribute__((aligned(16))) __bf16 ws[];  // TM x kLdsRow
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -169,11 +188,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
     const int t0 = blockIdx.y * TN;
     const uint32_t nu = static_cast<uint32_t>(K / 32);
     const uint32_t scale_plane = static_cast<uint32_t>(static_cast<uint64_t>(M) * static_cast<uint64_t>(K) / 2u);
-    const int S = (K + KC - 1) / KC;
+    const int C = (K + KC - 1) / KC;
     const __amdgpu_buffer_rsrc_t xr =
         make_rsrc(x, static_cast<uint32_t>(static_cast<uint64_t>(N) * static_cast<uint64_t>(K) * 2u));
-    // This lane's token for B fragment fn, and its k offset within a 32-slice.
+    // This lane's k offset within a 32-slice, and the byte offset of its
+    // token row for each B fragment (a token past N lies past the buffer).
     const int ktok = 8 * (lane >> 4);
+    uint32_t xrow[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+        xrow[fn] = (static_cast<uint32_t>(t0 + wave * WN + 16 * fn + (lane & 15)) * static_cast<uint32_t>(K) +
+                    static_cast<uint32_t>(ktok)) * 2u;
 
     f32x4 acc[FM][FN];
 #pragma unroll
@@ -181,66 +206,67 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
 #pragma unroll
         for (int j = 0; j < FN; j++) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    typename F::Item gi[2][WI];
-    bf16x8 xb[2][FN][SL];
+    typename F::Item gi[WI];
+    bf16x8 xring[XD][FN];
 
-    auto load_stage = [&](int buf, int s) {
+    auto load_w = [&](int c) {
 #pragma unroll
         for (int i = 0; i < WI; i++) {
             const int it = tid + 256 * i;
-            F::template load<KC>(gi[buf][i], w, wbytes, scale_plane, nu, static_cast<uint32_t>(r0 + it / IPR), s,
-                                 it % IPR);
-        }
-#pragma unroll
-        for (int fn = 0; fn < FN; fn++) {
-            const uint32_t tok = static_cast<uint32_t>(t0 + wave * WN + 16 * fn + (lane & 15));
-#pragma unroll
-            for (int kk = 0; kk < SL; kk++) {
-                const uint32_t off = (tok * static_cast<uint32_t>(K) + static_cast<uint32_t>(s * KC + 32 * kk + ktok)) * 2u;
-                xb[buf][fn][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-            }
+            const int row = r0 + it / IPR;
+            F::template load<KC>(gi[i], w, wbytes, scale_plane, nu, static_cast<uint32_t>(row), row < M, c, it % IPR);
         }
     };
-    auto write_stage = [&](int buf, int s) {
+    // Global slice g (k = 32g ..) into ring slot j; past K: zeros, no fetch.
+    auto load_x = [&](int j, int g) {
+        const bool live = 32 * g < K;
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++)
+            xring[j][fn] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, live ? xrow[fn] + 64u * static_cast<uint32_t>(g) : kNoFetch,
+                                                              0, 0));
+    };
+    auto write_w = [&](int c) {
 #pragma unroll
         for (int i = 0; i < WI; i++) {
             const int it = tid + 256 * i;
             const int row = it / IPR, it8 = it % IPR;
             bf16x4 vlo, vhi;
-            F::template dequant<KC>(gi[buf][i], s, it8, vlo, vhi);
+            F::template dequant<KC>(gi[i], c, it8, vlo, vhi);
             *reinterpret_cast<bf16x4 *>(&ws[row * kLdsRow + F::lo(it8)]) = vlo;
             *reinterpret_cast<bf16x4 *>(&ws[row * kLdsRow + F::hi(it8)]) = vhi;
         }
     };
-    auto compute_stage = [&](int buf, int s) {
-#pragma unroll
-        for (int kk = 0; kk < SL; kk++) {
-            if (s * KC + 32 * kk >= K) break;  // a last stage shorter than KC
-            bf16x8 a[FM];
-#pragma unroll
-            for (int fm = 0; fm < FM; fm++)
-                a[fm] = *reinterpret_cast<const bf16x8 *>(&ws[(16 * fm + (lane & 15)) * kLdsRow + 32 * kk + ktok]);
-#pragma unroll
-            for (int fm = 0; fm < FM; fm++)
-#pragma unroll
-                for (int fn = 0; fn < FN; fn++)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], xb[buf][fn][kk], acc[fm][fn], 0, 0, 0);
-        }
-    };
 
-    load_stage(0, 0);
-    for (int s = 0; s < S; s += 2) {
-        write_stage(0, s);
+    // Issue order W(c) then X is the same before the loop and at every chunk
+    // boundary, so each wait below is for exactly the loads it needs.
+    load_w(0);
+    __builtin_amdgcn_sched_barrier(0);  // keep W(0) ahead of the ring in issue order
+#pragma unroll
+    for (int j = 0; j < XD; j++) load_x(j, j);
+    for (int c = 0; c < C; c++) {
+        if (c > 0) __syncthreads();  // every wave is done with chunk c-1 in LDS
+        write_w(c);
         __syncthreads();
-        if (s + 1 < S) load_stage(1, s + 1);
-        compute_stage(0, s);
-        __syncthreads();
-        if (s + 1 >= S) break;
-        write_stage(1, s + 1);
-        __syncthreads();
-        if (s + 2 < S) load_stage(0, s + 2);
-        compute_stage(1, s + 1);
-        __syncthreads();
+        load_w(c + 1);  // past the last chunk: no fetch, never used
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s0 = 0; s0 < SPC; s0 += XD) {
+#pragma unroll
+            for (int j = 0; j < XD; j++) {
+                const int kk = s0 + j;
+                bf16x8 a[FM];
+#pragma unroll
+                for (int fm = 0; fm < FM; fm++)
+                    a[fm] = *reinterpret_cast<const bf16x8 *>(&ws[(16 * fm + (lane & 15)) * kLdsRow + 32 * kk + ktok]);
+#pragma unroll
+                for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+                    for (int fn = 0; fn < FN; fn++)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], xring[j][fn], acc[fm][fn], 0, 0, 0);
+                load_x(j, c * SPC + kk + XD);
+            }
+        }
     }
 
     // Store: lane holds rows 4(l/16)..+3 of token column l%16 of each 16x16 tile.
@@ -266,22 +292,38 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
 template <class F, int TM, int TN, int KC>
 int launch_tile(const void *w, const uint16_t *x, float *y, int64_t m, int64_t k, int64_t n, hipStream_t s)
 {
+    constexpr size_t lds = static_cast<size_t>(TM) * (KC + 8) * 2;
+    if constexpr (lds > 65536) {
+        // Above 64 KB a kernel must opt in to its dynamic LDS size, once per device.
+        static std::atomic<int> opted[64];
+        int dev = 0;
+        if (hip_status(hipGetDevice(&dev)) != Q4_OK) return Q4_EHIP;
+        if (dev < 0 || dev >= 64) return Q4_EUNSUPPORTED;
+        if (!opted[dev].load(std::memory_order_acquire)) {
+            const int st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<F, TM, TN, KC>),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                          static_cast<int>(lds)));
+            if (st != Q4_OK) return st;
+            opted[dev].store(1, std::memory_order_release);
+        }
+    }
     const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(F::kFormat, m, k));
     const dim3 grid(static_cast<unsigned>((m + TM - 1) / TM), static_cast<unsigned>((n + TN - 1) / TN));
-    hipLaunchKernelGGL((gemm_kernel<F, TM, TN, KC>), grid, dim3(256), 0, s, static_cast<const uint8_t *>(w), wbytes,
+    hipLaunchKernelGGL((gemm_kernel<F, TM, TN, KC>), grid, dim3(256), lds, s, static_cast<const uint8_t *>(w), wbytes,
                        x, y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
-    return hipGetLastError() == hipSuccess ? Q4_OK : Q4_EHIP;
+    return hip_status(hipGetLastError());
 }
 
-// Tile geometries: (rows, tokens, K per stage).
+// Tile geometries: (rows, tokens, K per chunk). LDS per workgroup is
+// rows x (chunk + 8) x 2 bytes (16 KB .. 66 KB here).
 #define Q4_GEMM_TILES(X) \
-    X(32, 64, 64)        \
-    X(32, 64, 128)       \
+    X(16, 64, 512)       \
+    X(16, 64, 1024)      \
     X(32, 64, 256)       \
-    X(32, 128, 64)       \
-    X(32, 128, 128)      \
-    X(64, 64, 128)       \
-    X(64, 64, 256)
+    X(32, 64, 512)       \
+    X(32, 64, 1024)      \
+    X(32, 128, 512)      \
+    X(64, 64, 512)
 
 template <class F>
 int launch_geometry(int tm, int tn, int kc, const void *w, const uint16_t *x, float *y, int64_t m, int64_t k,
@@ -298,8 +340,6 @@ template <class F>
 int launch_fmt(const void *w, const uint16_t *x, float *y, int64_t m, int64_t k, int64_t n, hipStream_t s, int cus)
 {
     (void)cus;
-    // Stages are latency-bound at these sizes, so wide stages win; 32 x 64
-    // tiles keep enough workgroups for the SmolLM2-sized matrices.
     return launch_geometry<F>(32, 64, 256, w, x, y, m, k, n, s);
 }
 
@@ -327,7 +367,6 @@ extern "C" int q4_gemm_tuned(int fmt, const void *w, const uint16_t *x_bf16, flo
     const int tm = tuning->tile_rows ? tuning->tile_rows : 32;
     const int tn = tuning->tile_tokens ? tuning->tile_tokens : 64;
     const int kc = tuning->stage_k ? tuning->stage_k : 256;
-    if (fmt == Q4_FMT_Q4_K && kc % 64) return Q4_EUNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     if (fmt == Q4_FMT_Q4_0) return q4::gemm::launch_geometry<q4::gemm::GemmQ4_0>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
     return q4::gemm::launch_geometry<q4::gemm::GemmQ4_K>(tm, tn, kc, w, x_bf16, y, m, k, n, s);

@@ -15,17 +15,29 @@
 
 namespace q4 {
 
+namespace {
+thread_local hipError_t last_hip_error = hipSuccess;
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return Q4_OK;
+    last_hip_error = e;
+    return Q4_EHIP;
+}
+
 int device_cus()
 {
     static std::atomic<int> cache[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hip_status(hipGetDevice(&dev)) != Q4_OK) return -1;
     if (dev >= 0 && dev < 64) {
         int v = cache[dev].load(std::memory_order_relaxed);
         if (v > 0) return v;
     }
     int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return -1;
+    if (hip_status(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != Q4_OK || cus <= 0)
+        return -1;
     if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
@@ -91,9 +103,10 @@ int check_product_args(int fmt, const void *w, const void *x, const float *y, in
     if (n > n_max) return Q4_EUNSUPPORTED;
     if (m == 0 || n == 0) return Q4_OK;
     if (!w || !x || !y) return Q4_EINVAL;
-    // 32-bit byte offsets inside the kernels: weights < 4 GiB, x and y < 2 GiB.
+    // 32-bit byte offsets inside the kernels: weights, x and y each < 2 GiB
+    // (offsets from 2^31 up serve as the kernels' no-fetch lane offset).
     const uint64_t wbytes = static_cast<uint64_t>(q4_weight_bytes(fmt, m, k));
-    if (wbytes >= (1ull << 32) || static_cast<uint64_t>(n) * k * 4 >= (1ull << 31) ||
+    if (wbytes >= (1ull << 31) || static_cast<uint64_t>(n) * k * 4 >= (1ull << 31) ||
         static_cast<uint64_t>(n) * m * 4 >= (1ull << 31) || m >= (1LL << 30))
         return Q4_EUNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(w) & 15) || (reinterpret_cast<uintptr_t>(x) & 15) ||
@@ -103,6 +116,11 @@ int check_product_args(int fmt, const void *w, const void *x, const float *y, in
 }
 
 }  // namespace q4
+
+extern "C" const char *q4_last_hip_error(void)
+{
+    return hipGetErrorName(q4::last_hip_error);
+}
 
 extern "C" int q4_gemv(int fmt, const void *w, const float *x, float *y, int64_t m, int64_t k, int64_t n,
                        void *hip_stream)

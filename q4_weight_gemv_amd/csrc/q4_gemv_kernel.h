@@ -62,6 +62,11 @@ constexpr int kStageRound = WAVES == 1 ? 4 : 6;
 // Descriptor word 3 for the gfx9 family: 32-bit untyped raw buffer.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;  // cache policy bit: streamed data, not kept
+// A per-lane offset past every descriptor's range (weight buffers are below
+// 2 GiB): the load returns zeros and sends no request to memory. Slots past
+// the end of a row and rows past M are pointed here, so every byte fetched
+// from memory is a byte some lane uses.
+constexpr uint32_t kNoFetch = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
@@ -170,12 +175,13 @@ struct FmtQ4_0 {
     // (row*nu + u)*2. The lane part goes in the VGPR offset, the uniform part
     // (tile, chunk, batch) in the SGPR offset, jl in the immediate.
     __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
-                                uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl)
+                                uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl, bool live)
     {
         const uint32_t uni_u = trow * nu + ubase;
         const uint32_t lane_u = rowrel * nu + li + jl;
-        g.q = load16<kNonTemporal>(sub_rsrc(w, wbytes, uni_u * 16u), lane_u * 16u, 0);
-        g.d = __builtin_amdgcn_raw_buffer_load_b16(sub_rsrc(w, wbytes, scale_plane + uni_u * 2u), lane_u * 2u, 0, 0);
+        g.q = load16<kNonTemporal>(sub_rsrc(w, wbytes, uni_u * 16u), live ? lane_u * 16u : kNoFetch, 0);
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(sub_rsrc(w, wbytes, scale_plane + uni_u * 2u),
+                                                   live ? lane_u * 2u : kNoFetch, 0, 0);
     }
     // Unit metadata: z = 2^(e+24) (unit scale times the fp16-subnormal factor).
     __device__ static f32x4 meta(float /*gl*/, float /*gh*/, int e)
@@ -225,11 +231,11 @@ struct FmtQ4_K {
     // of 8): super-block (row*ns + u/8) at 144 bytes each, header at its
     // start, slice u & 7 = li & 7 at 16 + 16*(li & 7).
     __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t /*scale_plane*/, uint32_t nu,
-                                uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl)
+                                uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl, bool live)
     {
         const uint32_t ns = nu >> 3;
         const __amdgpu_buffer_rsrc_t r = sub_rsrc(w, wbytes, (trow * ns + (ubase >> 3)) * 144u);
-        const uint32_t lane_b = (rowrel * ns + (li >> 3) + (jl >> 3)) * 144u;
+        const uint32_t lane_b = live ? (rowrel * ns + (li >> 3) + (jl >> 3)) * 144u : kNoFetch;
         g.h = load16<0>(r, lane_b, 0);
         g.q = load16<kNonTemporal>(r, lane_b + 16u + ((li & 7u) << 4), 0);
     }
@@ -491,23 +497,24 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     using Regs = typename F::Regs;
 
     // Batch of JB unit slots (units c0 + li + (j0+jj)*LPR) of the lane's R rows
-    // in tile `tile`. Branch-free buffer loads that never fault: for a row past
-    // M (also every row of a tile past the last) the Q4_0 scale and every Q4_K
-    // byte lie past the buffer and read as zero, and a Q4_0 nibble read lands
-    // in the scale plane, so the row contributes 0 * (finite) and is never
-    // stored; a slot past the end of a row reads the next row's bytes and is
-    // skipped in compute_batch. With no branch around them the compiler counts
-    // every load as issued, so waiting for one batch never waits for the next.
-    auto load_batch = [&](Regs(&g)[JB][R], int tile, int j0, int c0) {
+    // in tile `tile`. Branch-free buffer loads that never fault: a slot past the
+    // end of the chunk and a row past M (also every row of a tile past the
+    // last) load from kNoFetch and read as zero without touching memory; such
+    // slots are skipped in compute_batch and such rows are never stored. With
+    // no branch around them the compiler counts every load as issued, so
+    // waiting for one batch never waits for the next.
+    auto load_batch = [&](Regs(&g)[JB][R], int tile, int j0, int c0, int nuc) {
         const uint32_t trow = static_cast<uint32_t>(tile) * RPG;
         const uint32_t ubase = static_cast<uint32_t>(c0 + j0 * LPR);
 #pragma unroll
         for (int jj = 0; jj < JB; jj++)
 #pragma unroll
-            for (int r = 0; r < R; r++)
+            for (int r = 0; r < R; r++) {
+                const bool live = li + (j0 + jj) * LPR < nuc && tile * RPG + row_in_tile + r * SUBS < M;
                 F::load(g[jj][r], w, wbytes, scale_plane, static_cast<uint32_t>(nu), trow,
                         static_cast<uint32_t>(row_in_tile + r * SUBS), static_cast<uint32_t>(li), ubase,
-                        static_cast<uint32_t>(jj * LPR));
+                        static_cast<uint32_t>(jj * LPR), live);
+            }
     };
     auto compute_batch = [&](const Regs(&g)[JB][R], int j0, int c0, int nuc) {
 #pragma unroll
@@ -538,7 +545,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
         // runs through all of this workgroup's tiles.
         const int nb = ((nu + LPR - 1) / LPR + JB - 1) / JB;  // batches per tile
         int b = 0;
-        stage<F, N, NT, kStageRound<WAVES>>(xr, K, 0, nu, uc, xs, meta, tid, [&]() { load_batch(ga, tile, 0, 0); });
+        stage<F, N, NT, kStageRound<WAVES>>(xr, K, 0, nu, uc, xs, meta, tid, [&]() { load_batch(ga, tile, 0, 0, nu); });
         wg_sync<WAVES>();
         auto step = [&](Regs(&cur)[JB][R], Regs(&nxt)[JB][R]) -> bool {
             int nt = tile, nbi = b + 1;
@@ -546,7 +553,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
                 nt = tile + static_cast<int>(gridDim.x);
                 nbi = 0;
             }
-            load_batch(nxt, nt, nbi * JB, 0);  // past the last tile: read, never used
+            load_batch(nxt, nt, nbi * JB, 0, nu);  // past the last tile: no fetch, never used
             compute_batch(cur, b * JB, 0, nu);
             if (nbi == 0) {
                 reduce_store(tile);
@@ -569,15 +576,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
             if (!first) wg_sync<WAVES>();
             first = false;
             stage<F, N, NT, kStageRound<WAVES>>(xr, K, c0, nuc, uc, xs, meta, tid,
-                                                [&]() { load_batch(ga, tile, 0, c0); });
+                                                [&]() { load_batch(ga, tile, 0, c0, nuc); });
             wg_sync<WAVES>();
-            // Prefetches are unconditional (a batch past the chunk is read and
-            // dropped) so that no branch makes the compiler wait for them.
+            // Prefetches are unconditional (a batch past the chunk issues
+            // no-fetch loads and is dropped) so that no branch makes the
+            // compiler wait for them.
             for (int j0 = 0; j0 < jc; j0 += 2 * JB) {
-                load_batch(gb, tile, j0 + JB, c0);
+                load_batch(gb, tile, j0 + JB, c0, nuc);
                 compute_batch(ga, j0, c0, nuc);
                 if (j0 + JB >= jc) break;
-                load_batch(ga, tile, j0 + 2 * JB, c0);
+                load_batch(ga, tile, j0 + 2 * JB, c0, nuc);
                 compute_batch(gb, j0 + JB, c0, nuc);
             }
         }
@@ -606,7 +614,7 @@ int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStre
     const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(F::kFormat, m, k));
     hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB>), dim3(grid), dim3(64 * WAVES), lds, stream, w, wbytes,
                        x, y, m, k, uc, ntiles);
-    return hipGetLastError() == hipSuccess ? Q4_OK : Q4_EHIP;
+    return hip_status(hipGetLastError());
 }
 
 // The instantiated tile geometries: (lanes per row, rows per lane, waves per group).

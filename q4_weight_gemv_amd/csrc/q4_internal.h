@@ -30,6 +30,10 @@ int launch_gemm(int fmt, const void *w, const uint16_t *x, float *y,
 // Compute units of the current device (cached per device).
 int device_cus();
 
+// Q4_OK for hipSuccess, else Q4_EHIP, after recording e as the calling
+// thread's last HIP error (reported by q4_last_hip_error).
+int hip_status(hipError_t e);
+
 namespace gemv {
 
 // Tile geometry of the decode kernel.

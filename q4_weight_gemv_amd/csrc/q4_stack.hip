@@ -61,7 +61,8 @@ int q4_graph_create(int fmt, const q4_gemv_op *ops, int count, int64_t n, void *
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipStream_t own = nullptr;
     if (!s) {
-        if (hipStreamCreateWithFlags(&own, hipStreamNonBlocking) != hipSuccess) return Q4_EHIP;
+        const int cst = q4::hip_status(hipStreamCreateWithFlags(&own, hipStreamNonBlocking));
+        if (cst != Q4_OK) return cst;
         s = own;
     }
     q4_graph *g = new (std::nothrow) q4_graph();
@@ -69,15 +70,16 @@ int q4_graph_create(int fmt, const q4_gemv_op *ops, int count, int64_t n, void *
         if (own) (void)hipStreamDestroy(own);
         return Q4_EHIP;
     }
-    st = Q4_EHIP;
-    if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) == hipSuccess) {
+    st = q4::hip_status(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    if (st == Q4_OK) {
         const int est = enqueue_ops(fmt, ops, count, n, s);
-        const hipError_t end = hipStreamEndCapture(s, &g->graph);
-        if (est == Q4_OK && end == hipSuccess &&
-            hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0) == hipSuccess)
-            st = Q4_OK;
-        else if (est != Q4_OK)
+        const int end = q4::hip_status(hipStreamEndCapture(s, &g->graph));
+        if (est != Q4_OK)
             st = est;
+        else if (end != Q4_OK)
+            st = end;
+        else
+            st = q4::hip_status(hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0));
     }
     if (own) (void)hipStreamDestroy(own);
     if (st != Q4_OK) {
@@ -91,15 +93,15 @@ int q4_graph_create(int fmt, const q4_gemv_op *ops, int count, int64_t n, void *
 int q4_graph_launch(q4_graph *graph, void *hip_stream)
 {
     if (!graph || !graph->exec) return Q4_EINVAL;
-    return hipGraphLaunch(graph->exec, static_cast<hipStream_t>(hip_stream)) == hipSuccess ? Q4_OK : Q4_EHIP;
+    return q4::hip_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(hip_stream)));
 }
 
 int q4_graph_destroy(q4_graph *graph)
 {
     if (!graph) return Q4_OK;
     int st = Q4_OK;
-    if (graph->exec && hipGraphExecDestroy(graph->exec) != hipSuccess) st = Q4_EHIP;
-    if (graph->graph && hipGraphDestroy(graph->graph) != hipSuccess) st = Q4_EHIP;
+    if (graph->exec && q4::hip_status(hipGraphExecDestroy(graph->exec)) != Q4_OK) st = Q4_EHIP;
+    if (graph->graph && q4::hip_status(hipGraphDestroy(graph->graph)) != Q4_OK) st = Q4_EHIP;
     delete graph;
     return st;
 }

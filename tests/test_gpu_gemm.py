@@ -88,6 +88,34 @@ def test_parity_q4_k_512_tokens(env, k, m):
     _parity(env, 1, m, k, 512, seed=800, rows=sample_rows(m, k, edge=64, rand=48))
 
 
+def _tiles():
+    import q4_weight_gemv_amd as q4
+
+    return list(q4.GEMM_TILES)
+
+
+@pytest.mark.parametrize("tile", _tiles(), ids=lambda t: f"{t[0]}x{t[1]}x{t[2]}")
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_parity_every_tile(env, fmt, tile):
+    """Every instantiated tile through q4_gemm_tuned: 70 rows and 100 tokens
+    (ragged in both), K = 1280 (a partial last chunk for every chunk size)."""
+    torch, q4, orc = env
+    m, k, n = 70, 1280, 100
+    buf = _quantize_both(q4, orc, fmt, synth.weights(synth.seed_for(950 + fmt, 2), m, k))
+    xb = synth.bf16_bits(synth.activations(synth.seed_for(950 + fmt, 2, True), n, k))
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).cuda()
+    yd = torch.full((n, m), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"gemm tile {tile} fmt={fmt}")
+    q4.q4_gemm_tuned(fmt, wd, xd, yd, m, k, *tile)
+    torch.cuda.synchronize()
+    y = yd.cpu().numpy()
+    yr, ad = orc.matmul(fmt, buf, m, k, xb, threads=threads(), absdot=True)
+    check_tolerance(y, yr, ad, GEMM_TOL, what=f"gemm tile {tile} fmt={fmt}")
+    yb, adb = orc.matmul(fmt, buf, m, k, xb, round_w_bf16=True, threads=threads(), absdot=True)
+    check_tolerance(y, yb, adb, 1e-4, what=f"gemm(bf16 W) tile {tile} fmt={fmt}")
+
+
 def test_gemm_misaligned_and_noop(env):
     torch, q4, _ = env
     w = torch.zeros(4096, dtype=torch.uint8, device="cuda")

@@ -101,6 +101,39 @@ def test_parity_q4_0_small(env, m, k, n):
     _parity(env, 0, m, k, n, seed=100 + n)
 
 
+def _geometry_ids():
+    import q4_weight_gemv_amd as q4
+
+    return [f"L{g[0]}R{g[1]}W{g[2]}" for g in q4.GEMV_GEOMETRIES]
+
+
+def _geometries():
+    import q4_weight_gemv_amd as q4
+
+    return list(q4.GEMV_GEOMETRIES)
+
+
+@pytest.mark.parametrize("geom", _geometries(), ids=_geometry_ids())
+@pytest.mark.parametrize("fmt,n", [(0, 1), (0, 8), (1, 1), (1, 8)])
+def test_parity_every_geometry(env, fmt, n, geom):
+    """Every instantiated tile geometry through q4_gemv_tuned: 600 ragged rows
+    (a grid-stride loop for the short tiles at one group per compute unit) and
+    K = 2304, which at n = 8 exceeds one LDS chunk of activations."""
+    torch, q4, orc = env
+    m, k = 600, 2304
+    w = synth.weights(synth.seed_for(900 + fmt, 1), m, k)
+    x = synth.activations(synth.seed_for(900 + fmt, 1, True), n, k)
+    buf = _quantize_both(q4, orc, fmt, w)
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(x).cuda()
+    yd = torch.full((n, m), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"geometry {geom} fmt={fmt} n={n}")
+    q4.q4_gemv_tuned(fmt, wd, xd, yd, m, k, geom[0], geom[1], geom[2], 1)
+    torch.cuda.synchronize()
+    yr, ad = orc.matvec(fmt, buf, m, k, x, threads=threads(), absdot=True)
+    check_tolerance(yd.cpu().numpy(), yr, ad, GEMV_TOL, what=f"geometry {geom} fmt={fmt} n={n}")
+
+
 SMALL_Q4_K = [(1, 256), (37, 512), (130, 1024), (257, 2560), (300, 4096), (77, 11008), (1025, 768 + 256)]
 
 

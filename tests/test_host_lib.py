@@ -165,6 +165,8 @@ def test_product_argument_errors(q4, entry):
     assert f(0, None, None, None, 0, 256, 1, None) == q4.Q4_OK        # m == 0: no-op
     assert f(0, None, None, None, 64, 256, 0, None) == q4.Q4_OK       # n == 0: no-op
     assert f(0, *ok, 1 << 30, 1 << 10, 1, None) == q4.Q4_EUNSUPPORTED  # beyond 32-bit offsets
+    assert f(0, *ok, 1 << 20, 4096, 1, None) == q4.Q4_EUNSUPPORTED    # weights of 2 GiB or more
+    assert f(1, *ok, 1 << 20, 4096, 1, None) == q4.Q4_EUNSUPPORTED
     if entry == "q4_gemv":
         assert f(0, *ok, 64, 256, 9, None) == q4.Q4_EUNSUPPORTED       # decode batch is 1..8
 
@@ -214,3 +216,30 @@ def test_strerror(q4):
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert q4.q4_strerror(st) and q4.q4_strerror(st) != "unknown status"
     assert q4.q4_strerror(-99) == "unknown status"
+
+
+def test_geometry_lists_match_header(q4):
+    """The binding's geometry lists are the ones the header documents."""
+    import re
+
+    text = open(os.path.join(ROOT, "include", "q4.h")).read()
+    gemv_doc = text[text.index("typedef struct {\n    int lanes_per_row;") - 700:text.index("int lanes_per_row;")]
+    gemm_doc = text[text.index("/* Tile geometry of the prefill product"):text.index("int tile_rows;")]
+    triples = lambda t: tuple(tuple(int(v) for v in m) for m in re.findall(r"\((\d+),(\d+),(\d+)\)", t))
+    assert triples(gemv_doc) == q4.GEMV_GEOMETRIES
+    assert triples(gemm_doc) == q4.GEMM_TILES
+
+
+def test_binding_loads_torch_runtime_first():
+    """The binding imports torch before loading the library, so the library's
+    HIP runtime is torch's (same soname; the first copy loaded wins)."""
+    import subprocess
+    import sys
+
+    code = ("import q4_weight_gemv_amd as q4, sys; "
+            "maps = open('/proc/self/maps').read(); "
+            "hip = sorted({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}); "
+            "print(hip); assert len(hip) == 1 and '/torch/lib/' in hip[0], hip; "
+            "assert q4.raw().q4_last_hip_error() == b'hipSuccess'")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
