@@ -93,9 +93,11 @@ class Timer:
 
 
 class Step:
-    """A decode step: one set of weights per copy, shared x/y, one graph per copy."""
+    """A decode step: one set of weights per copy, shared x/y, one graph per copy.
+    cold: enough weight copies (>= 512 MiB) that every step reads HBM; warm:
+    one copy, replayed (MALL-resident when the step fits in 256 MB)."""
 
-    def __init__(self, torch, q4, shapes, fmt, n, config_id):
+    def __init__(self, torch, q4, shapes, fmt, n, config_id, cold=True):
         import synth
 
         self.shapes, self.fmt, self.n = shapes, fmt, n
@@ -106,7 +108,8 @@ class Step:
         self.xs = [torch.from_numpy(x).cuda() for x in self.host_x]
         self.ys = [torch.empty((n, m), dtype=torch.float32, device="cuda") for k, m in shapes]
         wbytes = sum(h.size for h in self.host_w)
-        self.copies = [[torch.from_numpy(h).cuda() for h in self.host_w] for _ in range(copies_for(wbytes))]
+        ncopies = copies_for(wbytes) if cold else 1
+        self.copies = [[torch.from_numpy(h).cuda() for h in self.host_w] for _ in range(ncopies)]
         self.graphs = [q4.Q4Graph(fmt, self._ops(ws), n) for ws in self.copies]
         torch.cuda.synchronize()
 
@@ -138,20 +141,25 @@ def traffic_from_profile(per_launch_bytes):
     return float(t.group(1))
 
 
-def cpu_baseline(step, budget_s=10.0):
-    """The oracle (as it stands) on whole repeats of the same decode step."""
+def cpu_baseline(step, budget_s=10.0, budget_1core_s=6.0):
+    """The oracle (as it stands) on whole repeats of the same decode step, with
+    its rows split over the host cores, and again on one core."""
     import oracle
 
+    def timed(threads, budget):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            for i, (k, m) in enumerate(step.shapes):
+                oracle.matvec(step.fmt, step.host_w[i], m, k, step.host_x[i], threads=threads)
+            reps += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        return reps, time.perf_counter() - t0
+
     threads = max(1, min(16, os.cpu_count() or 1))
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        for i, (k, m) in enumerate(step.shapes):
-            oracle.matvec(step.fmt, step.host_w[i], m, k, step.host_x[i], threads=threads)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+    reps, dt = timed(threads, budget_s)
+    reps1, dt1 = timed(1, budget_1core_s)
     return {
         "value": round(step.bytes * reps / dt / 1e9, 4),
         "unit": "GB/s",
@@ -160,6 +168,8 @@ def cpu_baseline(step, budget_s=10.0):
         "sample": f"{reps} whole GPT-2-124M decode step(s) (49 products, rows split over {threads} threads), "
                   f"{dt:.1f} s wall",
         "tokens_per_s": round(reps / dt, 3),
+        "one_core": {"GB_s": round(step.bytes * reps1 / dt1 / 1e9, 4), "tokens_per_s": round(reps1 / dt1, 3),
+                     "sample": f"{reps1} whole step(s), {dt1:.1f} s wall"},
     }
 
 
@@ -196,13 +206,14 @@ def bench_7b(torch, q4, timer, reps=20):
     return out
 
 
-def bench_gemm(torch, q4, timer, n=512, reps=20):
-    """Prefill GEMM over the SmolLM2-360M layer's 7 matrices at 512 tokens:
-    one graph of the 7 launches, replayed (weights 5.5 MB, L2/MALL-resident)."""
+def bench_gemm(torch, q4, timer, n=512, reps=20, shapes=None, per_matrix=True):
+    """Prefill GEMM over the SmolLM2-360M layer's matrices at 512 tokens:
+    one graph of the launches, replayed (weights 5.5 MB, L2/MALL-resident);
+    and each matrix alone, as a graph of 20 launches."""
     import synth
 
     fns, flops, per = [], 0, {}
-    for i, (k, m) in enumerate(synth.smollm2_360m_layer()):
+    for i, (k, m) in enumerate(shapes or synth.smollm2_360m_layer()):
         wq = torch.from_numpy(q4.q4_quantize_ref(0, synth.weights(synth.seed_for(3, i), m, k))).cuda()
         xb = torch.from_numpy(synth.bf16_bits(synth.activations(synth.seed_for(3, i, True), n, k)).view(np.int16)).cuda()
         y = torch.empty((n, m), device="cuda")
@@ -220,8 +231,50 @@ def bench_gemm(torch, q4, timer, n=512, reps=20):
     t = timer.region(lambda i: g.replay(), reps, 3) / reps
     tf = flops / t / 1e12
     log(f"gemm smollm2 layer x{n}: {t * 1e6:.1f} us {tf:.1f} TFLOP/s")
-    return {"layer_us": round(t * 1e6, 2), "TFLOP_s": round(tf, 1), "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 2),
-            "GFLOP": round(flops / 1e9, 3), "tokens": n}
+    out = {"layer_us": round(t * 1e6, 2), "TFLOP_s": round(tf, 1), "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 2),
+           "GFLOP": round(flops / 1e9, 3), "tokens": n, "launches": len(fns)}
+    if per_matrix:
+        seen = set()
+        for (w, xb, y, m, k) in fns:
+            if (k, m) in seen:
+                continue
+            seen.add((k, m))
+            gm = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(gm, stream=s):
+                    for _ in range(20):
+                        q4.q4_gemm(0, w, xb, y, m, k)
+            tm = timer.region(lambda i: gm.replay(), reps, 3) / (reps * 20)
+            per[f"{k}to{m}"] = {"us": round(tm * 1e6, 2), "TFLOP_s": round(2 * n * m * k / tm / 1e12, 1)}
+        out["per_matrix"] = per
+    return out
+
+
+def bench_read_ceiling(torch, q4, timer, reps=20):
+    """The measured streaming-read ceiling: 1 GiB read once per launch, and the
+    7B-class weight sizes read cold (rotating copies, one graph of launches)."""
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    out = {}
+    big = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    t = timer.region(lambda i: q4.q4_read_probe(big, sink, groups=4096), 10, 2) / 10
+    out["1GiB"] = {"us": round(t * 1e6, 1), "GB_s": round(big.numel() / t / 1e9, 1)}
+    del big
+    for nbytes in (9_437_184, 25_362_432):
+        copies = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies_for(nbytes))]
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            q4.q4_read_probe(copies[0], sink, groups=2048)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for c in copies:
+                    q4.q4_read_probe(c, sink, groups=2048)
+        t = timer.region(lambda i: g.replay(), reps, 3) / (reps * len(copies))
+        out[f"{nbytes}B_cold"] = {"us": round(t * 1e6, 3), "GB_s": round(nbytes / t / 1e9, 1)}
+        del copies, g
+    torch.cuda.empty_cache()
+    log(f"read ceiling: {out}")
+    return out
 
 
 def launch_floor(torch, q4, timer, count=200):
@@ -244,6 +297,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline workload")
+    ap.add_argument("--extras", default="all",
+                    help="comma list of extras to run (default all): plain, floor, gate_7b, smollm2, smollm2_fused, "
+                         "warm, read_ceiling, gemm")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 64 MiB device copy (torch) once, as the reference for HBM byte counters")
     args = ap.parse_args()
@@ -328,32 +384,51 @@ def main():
 
     if not args.no_extras:
         extras = {}
-        n_plain = max(20, K // 10)
-        tp = timer.region(lambda i: step.run_plain(q4, i), n_plain, 5)
-        extras["gpt2_plain_stream"] = {"us_per_step": round(tp / n_plain * 1e6, 2), "tokens_per_s": round(n_plain / tp, 1)}
-        extras["launch_floor_us"] = launch_floor(torch, q4, timer)
-        extras["gate_7b"] = bench_7b(torch, q4, timer)
-        log("setup SmolLM2-360M step")
-        sm = Step(torch, q4, synth.smollm2_360m_step(), 0, 1, config_id=2)
-        ts = timer.region(sm.run_graph, max(50, K // 10), 5) / max(50, K // 10)
-        extras["smollm2_step"] = {"us_per_step": round(ts * 1e6, 2), "tokens_per_s": round(1 / ts, 1),
-                                  "GB_s": round(sm.bytes / ts / 1e9, 1), "products": len(sm.shapes),
-                                  "cache": f"cold: {len(sm.copies)} copies"}
-        log(f"smollm2 step: {ts * 1e6:.1f} us, {1 / ts:.0f} tokens/s")
-        sm.close()
-        del sm
-        torch.cuda.empty_cache()
-        log("setup SmolLM2-360M step, fused shared-input projections")
-        sf = Step(torch, q4, synth.smollm2_360m_step_fused(), 0, 1, config_id=2)
-        tf = timer.region(sf.run_graph, max(50, K // 10), 5) / max(50, K // 10)
-        extras["smollm2_step_fused_qkv_gateup"] = {
-            "us_per_step": round(tf * 1e6, 2), "tokens_per_s": round(1 / tf, 1), "GB_s": round(sf.bytes / tf / 1e9, 1),
-            "products": len(sf.shapes), "cache": f"cold: {len(sf.copies)} copies"}
-        log(f"smollm2 fused step: {tf * 1e6:.1f} us, {1 / tf:.0f} tokens/s")
-        sf.close()
-        del sf
-        torch.cuda.empty_cache()
-        extras["gemm_smollm2_layer"] = bench_gemm(torch, q4, timer)
+        want = set(args.extras.split(",")) if args.extras != "all" else None
+        on = lambda name: want is None or name in want  # noqa: E731
+        if on("plain"):
+            n_plain = max(20, K // 10)
+            tp = timer.region(lambda i: step.run_plain(q4, i), n_plain, 5)
+            extras["gpt2_plain_stream"] = {"us_per_step": round(tp / n_plain * 1e6, 2),
+                                           "tokens_per_s": round(n_plain / tp, 1)}
+        if on("floor"):
+            extras["launch_floor_us"] = launch_floor(torch, q4, timer)
+        if on("gate_7b"):
+            extras["gate_7b"] = bench_7b(torch, q4, timer, reps=max(2, K // 50))
+        for name, key, shapes_fn in (("smollm2", "smollm2_step", synth.smollm2_360m_step),
+                                     ("smollm2_fused", "smollm2_step_fused_qkv_gateup", synth.smollm2_360m_step_fused)):
+            if not on(name):
+                continue
+            log(f"setup {key}")
+            sm = Step(torch, q4, shapes_fn(), 0, 1, config_id=2)
+            ns = max(50, K // 10)
+            ts = timer.region(sm.run_graph, ns, 5) / ns
+            extras[key] = {"us_per_step": round(ts * 1e6, 2), "tokens_per_s": round(1 / ts, 1),
+                           "GB_s": round(sm.bytes / ts / 1e9, 1), "products": len(sm.shapes),
+                           "cache": f"cold: {len(sm.copies)} copies"}
+            log(f"{key}: {ts * 1e6:.1f} us, {1 / ts:.0f} tokens/s")
+            sm.close()
+            del sm
+            torch.cuda.empty_cache()
+        if on("warm"):
+            for name, shp, cid in (("gpt2_step_warm", synth.gpt2_124m_step(), 1),
+                                   ("smollm2_step_warm", synth.smollm2_360m_step(), 2)):
+                wst = Step(torch, q4, shp, 0, 1, config_id=cid, cold=False)
+                nw = max(50, K // 10)
+                tw = timer.region(wst.run_graph, nw, 5) / nw
+                extras[name] = {"us_per_step": round(tw * 1e6, 2), "tokens_per_s": round(1 / tw, 1),
+                                "GB_s": round(wst.bytes / tw / 1e9, 1), "cache": "warm: one weight copy (MALL-resident)"}
+                log(f"{name}: {tw * 1e6:.1f} us")
+                wst.close()
+                del wst
+            torch.cuda.empty_cache()
+        if on("read_ceiling"):
+            extras["read_ceiling"] = bench_read_ceiling(torch, q4, timer)
+        if on("gemm"):
+            extras["gemm_smollm2_layer"] = bench_gemm(torch, q4, timer, reps=max(2, K // 50))
+            extras["gemm_smollm2_layer_fused_qkv_gateup"] = bench_gemm(
+                torch, q4, timer, reps=max(2, K // 50), shapes=[(960, 1600), (960, 960), (960, 5120), (2560, 960)],
+                per_matrix=False)
         result["extras"] = extras
 
     if not args.no_cpu_baseline:

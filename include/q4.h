@@ -138,7 +138,7 @@ int q4_gemm(int fmt, const void *w, const uint16_t *x_bf16, float *y,
  * workgroup, stage_k weights per row dequantized into LDS per chunk of K (a
  * zero field keeps the library's choice). Instantiated (rows, tokens,
  * stage_k): (16,64,512) (16,64,1024) (32,64,256) (32,64,512) (32,64,1024)
- * (32,128,512) (64,64,512); others return Q4_EUNSUPPORTED. */
+ * (32,128,512) (64,64,256) (64,64,512); others return Q4_EUNSUPPORTED. */
 typedef struct {
     int tile_rows;
     int tile_tokens;

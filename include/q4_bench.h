@@ -1,0 +1,30 @@
+/* Measurement helpers of the Q4 weight-matrix product library.
+ *
+ * Not part of the products: these kernels exist so that a benchmark can put
+ * the products' achieved HBM bandwidth next to what a plain streaming read
+ * reaches on the same device, in the same process. */
+#ifndef Q4_BENCH_H
+#define Q4_BENCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` bytes at device pointer `p` (16-byte aligned, bytes a
+ * multiple of 16) once, with coalesced 16-byte non-temporal loads, using
+ * `groups` workgroups of 256 threads (1 .. 65536) that stride over the
+ * buffer. The data is folded into a value that is written to the 4-byte
+ * device word `sink` only if it equals a fixed constant, so nothing but the
+ * read reaches memory in practice. Enqueued on `hip_stream`; returns a
+ * q4_status value (Q4_EINVAL for bad arguments, Q4_EALIGN for misalignment,
+ * Q4_EHIP if the launch fails). */
+int q4_read_probe(const void *p, size_t bytes, uint32_t *sink, int groups, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_BENCH_H */

@@ -74,6 +74,7 @@ _SIGS = {
     "q4_graph_destroy": (ctypes.c_int, [_vp]),
     "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "q4_last_hip_error": (ctypes.c_char_p, []),
+    "q4_read_probe": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, ctypes.c_int, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -137,7 +138,7 @@ GEMV_GEOMETRIES = ((8, 1, 1), (8, 2, 1), (8, 4, 1), (16, 1, 1), (16, 2, 1), (32,
                    (16, 1, 4), (32, 1, 4), (32, 2, 4), (64, 1, 4), (64, 2, 4), (64, 4, 4))
 # Prefill: (tile_rows, tile_tokens, stage_k).
 GEMM_TILES = ((16, 64, 512), (16, 64, 1024), (32, 64, 256), (32, 64, 512), (32, 64, 1024), (32, 128, 512),
-              (64, 64, 512))
+              (64, 64, 256), (64, 64, 512))
 
 
 def q4_gemv_tuned(fmt: int, w, x, y, m: int, k: int, lanes_per_row=0, rows_per_lane=0, waves_per_group=0,
@@ -163,6 +164,12 @@ def q4_gemm_tuned(fmt: int, w, x_bf16, y, m: int, k: int, tile_rows=0, tile_toke
     t = q4_gemm_tuning(tile_rows, tile_tokens, stage_k)
     _check(_lib.q4_gemm_tuned(fmt, w.data_ptr(), x_bf16.data_ptr(), y.data_ptr(), m, k, n, ctypes.byref(t),
                               _stream_ptr(stream)), "q4_gemm_tuned")
+
+
+def q4_read_probe(buf, sink, groups: int = 2048, stream=None) -> None:
+    """Stream-read a device buffer once (measured HBM ceiling; not a product)."""
+    _check(_lib.q4_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), groups,
+                              _stream_ptr(stream)), "q4_read_probe")
 
 
 def _ops_array(ops):

@@ -39,6 +39,7 @@ SOURCES = [
     ("q4_gemv_q4_k_b.hip", "device"),
     ("q4_gemm.hip", "device"),
     ("q4_stack.hip", "device"),
+    ("q4_bench.hip", "device"),
 ]
 
 

@@ -323,6 +323,7 @@ int launch_tile(const void *w, const uint16_t *x, float *y, int64_t m, int64_t k
     X(32, 64, 512)       \
     X(32, 64, 1024)      \
     X(32, 128, 512)      \
+    X(64, 64, 256)       \
     X(64, 64, 512)
 
 template <class F>
@@ -339,7 +340,13 @@ int launch_geometry(int tm, int tn, int kc, const void *w, const uint16_t *x, fl
 template <class F>
 int launch_fmt(const void *w, const uint16_t *x, float *y, int64_t m, int64_t k, int64_t n, hipStream_t s, int cus)
 {
-    (void)cus;
+    // From a sweep of the instantiated geometries on gfx950 at the SmolLM2-360M
+    // layer shapes x 512 tokens (and 7B-class rows): short matrices want 16-row
+    // tiles to keep workgroups in flight; otherwise 32 x 64 tiles with 256-wide
+    // chunks, and taller tiles once those exceed two workgroups per compute unit.
+    if (m <= 512) return launch_geometry<F>(16, 64, 512, w, x, y, m, k, n, s);
+    const int64_t tiles = ((m + 31) / 32) * ((n + 63) / 64);
+    if (tiles > 2LL * cus) return launch_geometry<F>(64, 64, 256, w, x, y, m, k, n, s);
     return launch_geometry<F>(32, 64, 256, w, x, y, m, k, n, s);
 }
 

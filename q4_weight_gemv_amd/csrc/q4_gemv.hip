@@ -46,20 +46,35 @@ namespace gemv {
 
 // Default geometry, from a sweep of every instantiated geometry on gfx950
 // (cold weights, graph-replayed launches) at the decode shapes of the
-// GPT-2-124M and SmolLM2-360M steps and the 7B-class layer:
-//   rows of <= 32 units (K <= 1024): one-wave groups, 32 lanes per row, two
-//     rows per lane; for very tall matrices (LM heads) 8 lanes x 4 rows;
-//   rows of 33..127 units: 4 waves, 64 lanes per row;
-//   longer rows: 4 waves, 32 lanes x 2 rows, two groups per compute unit
-//     (fewer, longer-lived groups amortise the activation staging).
-Cfg choose(int64_t m, int64_t k, int64_t n, int cus)
+// GPT-2-124M and SmolLM2-360M steps and the 7B-class layer, per format and
+// token count. Rows of nu 32-weight units:
+//   Q4_0, one token: nu <= 32 -> one-wave groups, 32 lanes per row, two rows
+//     per lane (LM heads, m >= 16384: 8 lanes x 4 rows); nu < 128 -> 4 waves,
+//     64 lanes per row; longer rows -> 4 waves, 32 lanes x 2 rows.
+//   Q4_0, several tokens: 4 waves; 64 lanes per row for 33..127 units, else
+//     32 lanes x 2 rows.
+//   Q4_K: 4 waves of 64 lanes per row for 33..127 units; otherwise 16 lanes
+//     per row up to 4 tokens (one-wave groups for short rows and 1..2 tokens;
+//     32 lanes for very long rows at one token), and 32 lanes x 2 rows for
+//     5..8 tokens.
+Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 {
     (void)cus;
-    (void)n;
     const int64_t nu = k / kUnitWeights;
-    if (nu <= 32) return m >= 16384 ? Cfg{8, 4, 1, 8} : Cfg{32, 2, 1, 8};
-    if (nu < 128) return Cfg{64, 1, 4, 4};
-    return Cfg{32, 2, 4, 2};
+    if (fmt == Q4_FMT_Q4_0) {
+        if (n == 1) {
+            if (nu <= 32) return m >= 16384 ? Cfg{8, 4, 1, 8} : Cfg{32, 2, 1, 8};
+            if (nu < 128) return Cfg{64, 1, 4, 4};
+            return Cfg{32, 2, 4, 2};
+        }
+        if (nu > 32 && nu < 128) return Cfg{64, 1, 4, 4};
+        return Cfg{32, 2, 4, 2};
+    }
+    if (nu > 32 && nu < 128) return Cfg{64, 1, 4, 4};
+    if (n >= 5) return Cfg{32, 2, 4, 2};
+    if (nu <= 32) return n <= 2 ? Cfg{16, 1, 1, 8} : Cfg{16, 1, 4, 4};
+    if (n == 1 && nu >= 256) return Cfg{32, 1, 4, 4};
+    return Cfg{16, 1, 4, 4};
 }
 
 int dispatch(int fmt, const Cfg &c, const void *w, const float *x, float *y, int64_t m, int64_t k, int64_t n,
@@ -91,7 +106,7 @@ int launch_gemv(int fmt, const void *w, const float *x, float *y, int64_t m, int
 {
     const int cus = device_cus();
     if (cus <= 0) return Q4_EHIP;
-    return gemv::dispatch(fmt, gemv::choose(m, k, n, cus), w, x, y, m, k, n, stream, cus);
+    return gemv::dispatch(fmt, gemv::choose(fmt, m, k, n, cus), w, x, y, m, k, n, stream, cus);
 }
 
 int check_product_args(int fmt, const void *w, const void *x, const float *y, int64_t m, int64_t k, int64_t n,
@@ -143,7 +158,7 @@ extern "C" int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y, i
     if (m == 0 || n == 0) return Q4_OK;
     const int cus = q4::device_cus();
     if (cus <= 0) return Q4_EHIP;
-    q4::gemv::Cfg c = q4::gemv::choose(m, k, n, cus);
+    q4::gemv::Cfg c = q4::gemv::choose(fmt, m, k, n, cus);
     if (tuning->lanes_per_row) c.lpr = tuning->lanes_per_row;
     if (tuning->rows_per_lane) c.r = tuning->rows_per_lane;
     if (tuning->waves_per_group) c.waves = tuning->waves_per_group;

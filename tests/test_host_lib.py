@@ -22,14 +22,19 @@ def q4():
 
 
 def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "q4.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(q4_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol(q4):
     declared = _declared_functions()
-    assert set(declared) >= {"q4_weight_bytes", "q4_quantize_ref", "q4_gemv", "q4_gemm", "q4_strerror"}
+    assert set(declared) >= {"q4_weight_bytes", "q4_quantize_ref", "q4_gemv", "q4_gemm", "q4_strerror",
+                             "q4_read_probe"}
     lib = ctypes.CDLL(q4.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -243,3 +248,13 @@ def test_binding_loads_torch_runtime_first():
             "assert q4.raw().q4_last_hip_error() == b'hipSuccess'")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_read_probe_argument_errors(q4):
+    f = q4.raw().q4_read_probe
+    assert f(None, 1 << 20, A16, 64, None) == q4.Q4_EINVAL
+    assert f(A16, 0, A16, 64, None) == q4.Q4_EINVAL
+    assert f(A16, 1 << 20, A16, 0, None) == q4.Q4_EINVAL
+    assert f(A16, 1 << 20, A16, 65537, None) == q4.Q4_EINVAL
+    assert f(A16 + 8, 1 << 20, A16, 64, None) == q4.Q4_EALIGN
+    assert f(A16, (1 << 20) + 8, A16, 64, None) == q4.Q4_EALIGN
