@@ -32,7 +32,6 @@ namespace q4 {
 namespace gemm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -52,91 +51,120 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h)
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu)));
 }
 
-__device__ __forceinline__ bf16x4 to_bf16(float a, float b, float c, float d)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 (RNE) in one dword (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 {
-    return bf16x4{static_cast<__bf16>(a), static_cast<__bf16>(b), static_cast<__bf16>(c), static_cast<__bf16>(d)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Nibbles of bytes K and K+1 of `n` (each byte already masked to its nibble q)
+// as the exact fp16 pair (q + 1024 + add): a byte permute places each nibble
+// under the fp16 exponent of 1024 (bits 0x64nn = 1024 + q), then one packed
+// fp16 add. With add = -1032 the pair is q - 8, with add = -1024 it is q.
+template <int K>
+__device__ __forceinline__ half2_t nibble_pair(uint32_t n, half2_t add)
+{
+    constexpr uint32_t sel = K == 0 ? 0x04010400u : 0x04030402u;  // bytes {K, 0x64, K+1, 0x64}
+    return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, n, sel)) + add;
+}
+
+// Eight weights from the masked nibble dwords n0 (elements 0..3) and n1
+// (4..7): value(q) for each, as 8 bf16 in 16 bytes.
+template <class V>
+__device__ __forceinline__ u32x4 eight(uint32_t n0, uint32_t n1, half2_t add, V value)
+{
+    const half2_t p0 = nibble_pair<0>(n0, add), p1 = nibble_pair<2>(n0, add);
+    const half2_t p2 = nibble_pair<0>(n1, add), p3 = nibble_pair<2>(n1, add);
+    return u32x4{pack_bf16(value(p0[0]), value(p0[1])), pack_bf16(value(p1[0]), value(p1[1])),
+                 pack_bf16(value(p2[0]), value(p2[1])), pack_bf16(value(p3[0]), value(p3[1]))};
 }
 
 // ---- format policies ------------------------------------------------------------
-// A stage item is 8 weights of one row: one nibble dword whose 4 low nibbles
-// are stage elements lo..lo+3 and whose 4 high nibbles are hi..hi+3.
+// A chunk item is 16 weights of one row: two nibble dwords whose low nibbles
+// are chunk elements lo..lo+7 and whose high nibbles are hi..hi+7. It is
+// written to LDS as two 16-byte runs of bf16.
 
 struct GemmQ4_0 {
     static constexpr int kFormat = Q4_FMT_Q4_0;
-    static constexpr int kRingVgprs = 128;  // activation ring budget (Items are 2 VGPRs)
+    static constexpr int kRingVgprs = 128;  // activation ring budget (Items are 3 VGPRs)
     struct Item {
-        uint32_t q;  // 4 nibble bytes
+        u32x2 q;     // 8 nibble bytes
         uint32_t d;  // fp16 scale bits
     };
-    // Item it8 (0 .. KC/8-1) of stage s (KC weights per row): block
-    // s*KC/32 + it8/4 of the row, nibble bytes 4*(it8%4) .. +3.
-    // Items of a block past the row's end, or of a row past M, read zeros
-    // (d = 0, so they dequantize to zero).
+    // Item it (0 .. KC/16-1) of chunk s (KC weights per row): block
+    // s*KC/32 + it/2 of the row, nibble bytes 8*(it%2) .. +7. Items of a
+    // block past the row's end, or of a row past M, read zeros (d = 0, so
+    // they dequantize to zero).
     template <int KC>
     __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
-                                uint32_t row, bool row_ok, int s, int it8)
+                                uint32_t row, bool row_ok, int s, int it)
     {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
-        const uint32_t ub = static_cast<uint32_t>(s * (KC / 32) + (it8 >> 2));
+        const uint32_t ub = static_cast<uint32_t>(s * (KC / 32) + (it >> 1));
         const uint32_t blk = row * nu + ub;
         const bool live = row_ok && ub < nu;
-        g.q = __builtin_amdgcn_raw_buffer_load_b32(r, live ? blk * 16u + 4u * static_cast<uint32_t>(it8 & 3) : kNoFetch,
-                                                   0, 0);
+        g.q = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, live ? blk * 16u + 8u * static_cast<uint32_t>(it & 1) : kNoFetch,
+                                                        0, 0));
         g.d = __builtin_amdgcn_raw_buffer_load_b16(r, live ? scale_plane + blk * 2u : kNoFetch, 0, 0);
     }
-    __device__ static int lo(int it8) { return 32 * (it8 >> 2) + 4 * (it8 & 3); }
-    __device__ static int hi(int it8) { return lo(it8) + 16; }
-    // (q - 8) * d, exact in fp32: q*d is exact and fma rounds the exact result once.
+    __device__ static int lo(int it) { return 32 * (it >> 1) + 8 * (it & 1); }
+    __device__ static int hi(int it) { return lo(it) + 16; }
+    // (q - 8) * d: the fp16 code q - 8 times the fp16 scale is exact in fp32,
+    // so the only rounding is the final one to bf16.
     template <int KC>
-    __device__ static void dequant(const Item &g, int /*s*/, int /*it8*/, bf16x4 &vlo, bf16x4 &vhi)
+    __device__ static void dequant(const Item &g, int /*s*/, int /*it*/, u32x4 &vlo, u32x4 &vhi)
     {
         const float d = half_bits_to_float(g.d);
-        const float m8 = -8.0f * d;
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            v[j] = __builtin_fmaf(static_cast<float>((g.q >> (8 * j)) & 15u), d, m8);
-            v[4 + j] = __builtin_fmaf(static_cast<float>((g.q >> (8 * j + 4)) & 15u), d, m8);
-        }
-        vlo = to_bf16(v[0], v[1], v[2], v[3]);
-        vhi = to_bf16(v[4], v[5], v[6], v[7]);
+        const half2_t add = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+        // Written as an fma with a zero addend so the fp16 operand feeds v_fma_mix_f32 directly
+        // (the product is exact, so the fma returns it unchanged; q - 8 is never -0).
+        const auto value = [d](_Float16 c) { return __builtin_fmaf(static_cast<float>(c), d, 0.0f); };
+        vlo = eight(g.q.x & 0x0F0F0F0Fu, g.q.y & 0x0F0F0F0Fu, add, value);
+        vhi = eight((g.q.x >> 4) & 0x0F0F0F0Fu, (g.q.y >> 4) & 0x0F0F0F0Fu, add, value);
     }
 };
 
 struct GemmQ4_K {
     static constexpr int kFormat = Q4_FMT_Q4_K;
-    static constexpr int kRingVgprs = 64;  // activation ring budget (Items are 5 VGPRs)
+    static constexpr int kRingVgprs = 64;  // activation ring budget (Items are 6 VGPRs)
     struct Item {
-        uint32_t q;  // 4 nibble bytes
-        u32x4 h;     // super-block header: d, dmin, 12 scale bytes
+        u32x2 q;  // 8 nibble bytes
+        u32x4 h;  // super-block header: d, dmin, 12 scale bytes
     };
-    // Stage s covers nibble chunks s*KC/64 .. of the row (4 chunks of 32
-    // bytes per super-block); item it8 is bytes 4*(it8%8) .. +3 of chunk
-    // s*KC/64 + it8/8. Byte i of a chunk c holds elements 64c+i (sub-block
-    // 2c) and 64c+32+i (sub-block 2c+1).
-    // Items past the row's end, or of a row past M, read zeros (d = dmin = 0).
+    // Chunk s covers 64-weight nibble groups s*KC/64 .. of the row (4 groups
+    // of 32 bytes per super-block); item it is bytes 8*(it%4) .. +7 of group
+    // s*KC/64 + it/4. Byte i of a group c holds elements 64c+i (sub-block 2c)
+    // and 64c+32+i (sub-block 2c+1). Items past the row's end, or of a row
+    // past M, read zeros (d = dmin = 0).
     template <int KC>
     __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t /*scale_plane*/, uint32_t nu,
-                                uint32_t row, bool row_ok, int s, int it8)
+                                uint32_t row, bool row_ok, int s, int it)
     {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
-        const uint32_t chunk = static_cast<uint32_t>(s * (KC / 64) + (it8 >> 3));
-        const bool live = row_ok && (chunk >> 2) < (nu >> 3);
-        const uint32_t base = live ? (row * (nu >> 3) + (chunk >> 2)) * 144u : kNoFetch;
+        const uint32_t grp = static_cast<uint32_t>(s * (KC / 64) + (it >> 2));
+        const bool live = row_ok && (grp >> 2) < (nu >> 3);
+        const uint32_t base = live ? (row * (nu >> 3) + (grp >> 2)) * 144u : kNoFetch;
         g.h = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, base, 0, 0));
-        g.q = __builtin_amdgcn_raw_buffer_load_b32(r, base + 16u + 32u * (chunk & 3u) + 4u * static_cast<uint32_t>(it8 & 7),
-                                                   0, 0);
+        g.q = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, base + 16u + 32u * (grp & 3u) + 8u * static_cast<uint32_t>(it & 3),
+                                                        0, 0));
     }
-    __device__ static int lo(int it8) { return 64 * (it8 >> 3) + 4 * (it8 & 7); }
-    __device__ static int hi(int it8) { return lo(it8) + 32; }
+    __device__ static int lo(int it) { return 64 * (it >> 2) + 8 * (it & 3); }
+    __device__ static int hi(int it) { return lo(it) + 32; }
     // d*sc*q - dmin*m: d*sc*q is exact in fp32 (<= 21 bits), so the fma rounds
     // the exact difference once, as the format's definition does.
     template <int KC>
-    __device__ static void dequant(const Item &g, int s, int it8, bf16x4 &vlo, bf16x4 &vhi)
+    __device__ static void dequant(const Item &g, int s, int it, u32x4 &vlo, u32x4 &vhi)
     {
-        // Sub-blocks a = 2c, b = 2c+1 of chunk c (within the super-block);
+        // Sub-blocks a = 2c, b = 2c+1 of group c (within the super-block);
         // their 6-bit fields sit in bytes 2(c&1), 2(c&1)+1 of the scale words.
-        const uint32_t c = static_cast<uint32_t>(s * (KC / 64) + (it8 >> 3)) & 3u;
+        const uint32_t c = static_cast<uint32_t>(s * (KC / 64) + (it >> 2)) & 3u;
         const uint32_t sh = (c & 1u) << 4;
         const uint32_t s0 = g.h.y >> sh, s1 = g.h.z >> sh, s2 = g.h.w >> sh;
         const bool upper = c >= 2;
@@ -147,14 +175,11 @@ struct GemmQ4_K {
         const float d = half_bits_to_float(g.h.x), dmin = half_bits_to_float(g.h.x >> 16);
         const float stepa = d * static_cast<float>(sca), stepb = d * static_cast<float>(scb);
         const float offa = -(dmin * static_cast<float>(ma)), offb = -(dmin * static_cast<float>(mb));
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            v[j] = __builtin_fmaf(stepa, static_cast<float>((g.q >> (8 * j)) & 15u), offa);
-            v[4 + j] = __builtin_fmaf(stepb, static_cast<float>((g.q >> (8 * j + 4)) & 15u), offb);
-        }
-        vlo = to_bf16(v[0], v[1], v[2], v[3]);
-        vhi = to_bf16(v[4], v[5], v[6], v[7]);
+        const half2_t add = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-1024.0f)};
+        vlo = eight(g.q.x & 0x0F0F0F0Fu, g.q.y & 0x0F0F0F0Fu, add,
+                    [=](_Float16 q) { return __builtin_fmaf(stepa, static_cast<float>(q), offa); });
+        vhi = eight((g.q.x >> 4) & 0x0F0F0F0Fu, (g.q.y >> 4) & 0x0F0F0F0Fu, add,
+                    [=](_Float16 q) { return __builtin_fmaf(stepb, static_cast<float>(q), offb); });
     }
 };
 
@@ -175,7 +200,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
     constexpr int SPC = KC / 32;             // 32-wide k slices per chunk
     constexpr int XR = F::kRingVgprs / (4 * FN);
     constexpr int XD = SPC < XR ? SPC : XR;  // depth of the activation ring, in slices
-    constexpr int IPR = KC / 8;              // weight items (8 weights) per row per chunk
+    constexpr int IPR = KC / 16;             // weight items (16 weights) per row per chunk
     constexpr int WI = TM * IPR / 256;       // weight items per thread per chunk
     constexpr int kLdsRow = KC + 8;          // bf16 per LDS row (padding staggers banks)
     static_assert(WI >= 1 && FN >= 1 && TM * IPR % 256 == 0 && XD >= 1 && SPC % XD == 0, "bad tile");
@@ -230,11 +255,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
 #pragma unroll
         for (int i = 0; i < WI; i++) {
             const int it = tid + 256 * i;
-            const int row = it / IPR, it8 = it % IPR;
-            bf16x4 vlo, vhi;
-            F::template dequant<KC>(gi[i], c, it8, vlo, vhi);
-            *reinterpret_cast<bf16x4 *>(&ws[row * kLdsRow + F::lo(it8)]) = vlo;
-            *reinterpret_cast<bf16x4 *>(&ws[row * kLdsRow + F::hi(it8)]) = vhi;
+            const int row = it / IPR, iw = it % IPR;
+            u32x4 vlo, vhi;
+            F::template dequant<KC>(gi[i], c, iw, vlo, vhi);
+            *reinterpret_cast<u32x4 *>(&ws[row * kLdsRow + F::lo(iw)]) = vlo;
+            *reinterpret_cast<u32x4 *>(&ws[row * kLdsRow + F::hi(iw)]) = vhi;
         }
     };
 
@@ -341,12 +366,12 @@ template <class F>
 int launch_fmt(const void *w, const uint16_t *x, float *y, int64_t m, int64_t k, int64_t n, hipStream_t s, int cus)
 {
     // From a sweep of the instantiated geometries on gfx950 at the SmolLM2-360M
-    // layer shapes x 512 tokens (and 7B-class rows): short matrices want 16-row
-    // tiles to keep workgroups in flight; otherwise 32 x 64 tiles with 256-wide
-    // chunks, and taller tiles once those exceed two workgroups per compute unit.
-    if (m <= 512) return launch_geometry<F>(16, 64, 512, w, x, y, m, k, n, s);
+    // layer shapes x 512 tokens: 32 x 64 tiles with 256-wide chunks, 16-row
+    // tiles for short Q4_0 matrices (more workgroups in flight), and 64-row
+    // tiles once the 32 x 64 grid exceeds two workgroups per compute unit.
     const int64_t tiles = ((m + 31) / 32) * ((n + 63) / 64);
     if (tiles > 2LL * cus) return launch_geometry<F>(64, 64, 256, w, x, y, m, k, n, s);
+    if (F::kFormat == Q4_FMT_Q4_0 && m <= 512) return launch_geometry<F>(16, 64, 512, w, x, y, m, k, n, s);
     return launch_geometry<F>(32, 64, 256, w, x, y, m, k, n, s);
 }
 
