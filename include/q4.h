@@ -97,9 +97,12 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
  * 16-byte aligned; y: device float32 [n][m], 4-byte aligned, fully written.
  * n must be 1..8 (decode batch); m == 0 is a successful no-op.
  * Weights are dequantized in registers and never written back (Llamas on the
- * Web, technical summary, Methodology section 3). x is rounded to fp16 after
- * an exact power-of-two scaling by its largest magnitude; products and sums
- * are fp32. */
+ * Web, technical summary, Methodology section 3). Each 32-element piece of x
+ * is scaled exactly by a power of two (its largest magnitude into
+ * [2^14, 2^15)), then held as a pair of fp16 values hi + lo (about 2^-23
+ * relative) when m < 256, or as one fp16 value (at most 2^-12 relative, so
+ * every output is within 2^-12 * sum_k |w_hat[i][k] x[t][k]|) when m >= 256;
+ * products and sums are fp32. */
 int q4_gemv(int fmt, const void *w, const float *x, float *y,
             int64_t m, int64_t k, int64_t n, void *hip_stream);
 

@@ -49,7 +49,7 @@ namespace gemv {
 // GPT-2-124M and SmolLM2-360M steps and the 7B-class layer, per format and
 // token count. Rows of nu 32-weight units:
 //   Q4_0, one token: nu <= 32 -> one-wave groups, 32 lanes per row, two rows
-//     per lane (LM heads, m >= 16384: 8 lanes x 4 rows); nu < 128 -> 4 waves,
+//     per lane (LM heads, m >= 16384: 8 lanes x 1 row); nu < 128 -> 4 waves,
 //     64 lanes per row; longer rows -> 4 waves, 32 lanes x 2 rows.
 //   Q4_0, several tokens: 4 waves; 64 lanes per row for 33..127 units, else
 //     32 lanes x 2 rows.
@@ -63,7 +63,7 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
     const int64_t nu = k / kUnitWeights;
     if (fmt == Q4_FMT_Q4_0) {
         if (n == 1) {
-            if (nu <= 32) return m >= 16384 ? Cfg{8, 4, 1, 8} : Cfg{32, 2, 1, 8};
+            if (nu <= 32) return m >= 16384 ? Cfg{8, 1, 1, 8} : Cfg{32, 2, 1, 8};
             if (nu < 128) return Cfg{64, 1, 4, 4};
             return Cfg{32, 2, 4, 2};
         }

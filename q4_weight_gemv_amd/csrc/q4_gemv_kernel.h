@@ -26,10 +26,13 @@
 //     order the unpack produces them, each 32-element unit scaled by a power
 //     of two that puts its largest magnitude in [2^14, 2^15): the scaling is
 //     exact, fp16 cannot overflow, and the unit's result is rescaled by the
-//     same power of two. Each scaled activation is held as an unevaluated sum
-//     hi + lo of two fp16 values (lo = fp16(x - hi)), so it is represented to
-//     about 2^-23 relative and every product term is as accurate as fp32
-//     arithmetic; the two halves cost a second dot2 per pair.
+//     same power of two. For products of fewer than kLoRowLimit rows each
+//     scaled activation is held as an unevaluated sum hi + lo of two fp16
+//     values (lo = fp16(x - hi)), about 2^-23 relative, so every product term
+//     is as accurate as fp32 arithmetic (the second half costs a second dot2
+//     per pair); taller products keep hi only (2^-12 relative per activation,
+//     so each output is within 2^-12 * sum_k |w_ik x_k|), which halves the dot
+//     issues, the activation LDS reads and most of the staging work.
 //   * Workgroups of one wave for short rows need no s_barrier (LDS order
 //     within a wave suffices); longer rows share the staging across 4 waves.
 #pragma once
@@ -51,6 +54,9 @@ constexpr uint32_t kLo = 0x000F000Fu;  // low nibbles of bytes 0 and 2
 constexpr uint32_t kHi = 0x00F000F0u;  // high nibbles of bytes 0 and 2
 constexpr int kLdsBytesPerUnit = 144;  // 2 x 64 B of fp16 pairs (hi, lo) + 16 B of unit metadata
 constexpr int kMaxLdsBytes = 64 * 1024;
+// Products with fewer rows hold activations as hi + lo fp16 pairs; taller
+// ones as a single fp16 each (see launch_one).
+constexpr int kLoRowLimit = 256;
 // Activation items per thread per staging round: one round covers a
 // 11008-long row for one token in a 4-wave group (1376 items / 256 threads).
 template <int WAVES>
@@ -137,6 +143,7 @@ __device__ __forceinline__ uint32_t add_h2(uint32_t a, _Float16 c)
 
 // Q4_0 codes as signed subnormal pairs: (q-8)*2^-24 for low nibbles,
 // 16(q-8)*2^-24 for high nibbles (exact: integers up to 128 times 2^-24).
+template <bool LO>
 __device__ __forceinline__ float dot_dword(uint32_t q, u32x4 xh, u32x4 xl, float acc)
 {
     const _Float16 m8 = static_cast<_Float16>(-0x1p-21f);   // -8 * 2^-24
@@ -148,10 +155,12 @@ __device__ __forceinline__ float dot_dword(uint32_t q, u32x4 xh, u32x4 xl, float
     acc = dot2(p1, xh.y, acc);
     acc = dot2(p2, xh.z, acc);
     acc = dot2(p3, xh.w, acc);
-    acc = dot2(p0, xl.x, acc);
-    acc = dot2(p1, xl.y, acc);
-    acc = dot2(p2, xl.z, acc);
-    acc = dot2(p3, xl.w, acc);
+    if constexpr (LO) {
+        acc = dot2(p0, xl.x, acc);
+        acc = dot2(p1, xl.y, acc);
+        acc = dot2(p2, xl.z, acc);
+        acc = dot2(p3, xl.w, acc);
+    }
     return acc;
 }
 
@@ -188,7 +197,7 @@ struct FmtQ4_0 {
     {
         return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + 24), 0.0f};
     }
-    template <int N, int R>
+    template <int N, int R, bool LO>
     __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
                                       const f32x4 *__restrict__ meta, int ul, int uc, uint32_t /*u*/,
                                       float (&acc)[R][N])
@@ -200,15 +209,15 @@ struct FmtQ4_0 {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 xh[i] = xs[(t * 8 + 2 * i) * uc + ul];
-                xl[i] = xs[(t * 8 + 2 * i + 1) * uc + ul];
+                xl[i] = LO ? xs[(t * 8 + 2 * i + 1) * uc + ul] : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int r = 0; r < R; r++) {
                 float a = 0.0f;
-                a = dot_dword(g[r].q.x, xh[0], xl[0], a);
-                a = dot_dword(g[r].q.y, xh[1], xl[1], a);
-                a = dot_dword(g[r].q.z, xh[2], xl[2], a);
-                a = dot_dword(g[r].q.w, xh[3], xl[3], a);
+                a = dot_dword<LO>(g[r].q.x, xh[0], xl[0], a);
+                a = dot_dword<LO>(g[r].q.y, xh[1], xl[1], a);
+                a = dot_dword<LO>(g[r].q.z, xh[2], xl[2], a);
+                a = dot_dword<LO>(g[r].q.w, xh[3], xl[3], a);
                 acc[r][t] = __builtin_fmaf(half_lo(g[r].d) * mt.z, a, acc[r][t]);
             }
         }
@@ -246,7 +255,7 @@ struct FmtQ4_K {
     {
         return f32x4{gl, gh, __builtin_amdgcn_ldexpf(1.0f, e + 24), __builtin_amdgcn_ldexpf(1.0f, e)};
     }
-    template <int N, int R>
+    template <int N, int R, bool LO>
     __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
                                       const f32x4 *__restrict__ meta, int ul, int uc, uint32_t u,
                                       float (&acc)[R][N])
@@ -278,7 +287,7 @@ struct FmtQ4_K {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 xh[i] = xs[(t * 8 + 2 * i) * uc + ul];
-                xl[i] = xs[(t * 8 + 2 * i + 1) * uc + ul];
+                xl[i] = LO ? xs[(t * 8 + 2 * i + 1) * uc + ul] : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int r = 0; r < R; r++) {
@@ -294,10 +303,12 @@ struct FmtQ4_K {
                     ab = dot2(p1, xh[i].y, ab);
                     aa = dot2(p2, xh[i].z, aa);
                     ab = dot2(p3, xh[i].w, ab);
-                    aa = dot2(p0, xl[i].x, aa);
-                    ab = dot2(p1, xl[i].y, ab);
-                    aa = dot2(p2, xl[i].z, aa);
-                    ab = dot2(p3, xl[i].w, ab);
+                    if constexpr (LO) {
+                        aa = dot2(p0, xl[i].x, aa);
+                        ab = dot2(p1, xl[i].y, ab);
+                        aa = dot2(p2, xl[i].z, aa);
+                        ab = dot2(p3, xl[i].w, ab);
+                    }
                 }
                 const float t1 = __builtin_fmaf(scb[r], ab, sca[r] * aa);
                 const float t2 = __builtin_fmaf(mb[r], mt.y, ma[r] * mt.x);
@@ -342,7 +353,7 @@ __device__ __forceinline__ float dpp(float v)
 // calls issue() (the first weight batch), and only then waits for the
 // activations, so the weight loads are in flight during the staging and the
 // staging waits on one L2 round trip per round, not one per item.
-template <class F, int N, int NT, int P, class Issue>
+template <class F, int N, int NT, int P, bool LO, class Issue>
 __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, int nuc, int uc,
                                       u32x4 *__restrict__ xs, f32x4 *__restrict__ meta, int tid, Issue issue)
 {
@@ -417,7 +428,7 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
             if (live) {
                 u32x4 *dst = xs + (t * 8 + 2 * i) * uc + ul;
                 dst[0] = vhi;
-                dst[uc] = vlo;
+                if constexpr (LO) dst[uc] = vlo;
                 if (i == 0) meta[t * uc + ul] = mv;
             }
         }
@@ -461,7 +472,7 @@ __device__ __forceinline__ float row_reduce(float v)
 // When the activations do not fit (many tokens x long rows) the row is
 // processed in LDS-sized chunks, restaged per tile.
 
-template <class F, int N, int LPR, int R, int WAVES, int JB>
+template <class F, int N, int LPR, int R, int WAVES, int JB, bool LO>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restrict__ w, uint32_t wbytes,
                                                           const float *__restrict__ x,
                                                           float *__restrict__ y, int M, int K, int uc,
@@ -520,7 +531,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
 #pragma unroll
         for (int jj = 0; jj < JB; jj++) {
             const int ul = li + (j0 + jj) * LPR;
-            if (ul < nuc) F::template accumulate<N, R>(g[jj], xs, meta, ul, uc, static_cast<uint32_t>(c0 + ul), acc);
+            if (ul < nuc) F::template accumulate<N, R, LO>(g[jj], xs, meta, ul, uc, static_cast<uint32_t>(c0 + ul), acc);
         }
     };
     auto reduce_store = [&](int tile) {
@@ -535,36 +546,83 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
             }
         }
     };
+    // The same stores issued in every step of the batch stream, writing only
+    // at the end of a tile (elsewhere the offset is out of range and the
+    // store is dropped): stores count in the same wait counter as loads, so
+    // a store on only some paths makes the compiler's wait at the top of the
+    // loop cover every outstanding load. Only the reduction, which touches
+    // no memory, sits behind the (uniform) branch.
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, static_cast<uint32_t>(N) * static_cast<uint32_t>(M) * 4u);
+    auto store_if_end = [&](int tile, bool end) {
+        const int row0 = tile * RPG + row_in_tile;
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int row = row0 + r * SUBS;
+#pragma unroll
+            for (int t = 0; t < N; t++) {
+                float v = 0.0f;
+                if (end) v = row_reduce<LPR>(acc[r][t]);
+                const bool live = end && li == 0 && row < M;
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __builtin_bit_cast(uint32_t, v), yr,
+                    live ? (static_cast<uint32_t>(t) * static_cast<uint32_t>(M) + static_cast<uint32_t>(row)) * 4u
+                         : kNoFetch,
+                    0, 0);
+            }
+        }
+    };
 
     int tile = blockIdx.x;
     if (tile >= ntiles) return;  // uniform across the workgroup
     Regs ga[JB][R], gb[JB][R];
 
     if (uc >= nu) {
-        // Activations staged once; a flat, double-buffered stream of batches
-        // runs through all of this workgroup's tiles.
+        // Activations staged once; a flat stream of batches runs through all
+        // of this workgroup's tiles. Stream position = (tile, batch). Loads
+        // run D batches ahead of the compute (D + 1 register buffers, used in
+        // rotation), the first D issued before the staging waits. Every phase
+        // issues the same loads and stores, so the compiler's wait counts stay
+        // exact; the exit is a uniform branch between phases. (At one token the
+        // batches are VALU-bound once staged: deeper prefetch, tried up to three
+        // batches, only delays the activation loads behind weight traffic.)
+        constexpr int D = 1;
+        constexpr int NBUF = D + 1;
         const int nb = ((nu + LPR - 1) / LPR + JB - 1) / JB;  // batches per tile
-        int b = 0;
-        stage<F, N, NT, kStageRound<WAVES>>(xr, K, 0, nu, uc, xs, meta, tid, [&]() { load_batch(ga, tile, 0, 0, nu); });
-        wg_sync<WAVES>();
-        auto step = [&](Regs(&cur)[JB][R], Regs(&nxt)[JB][R]) -> bool {
-            int nt = tile, nbi = b + 1;
-            if (nbi == nb) {
-                nt = tile + static_cast<int>(gridDim.x);
-                nbi = 0;
+        const int gstride = static_cast<int>(gridDim.x);
+        int lt = tile, lb = 0;  // next position to load (past the last tile: no fetch)
+        int ct = tile, cb = 0;  // next position to compute
+        Regs gbuf[NBUF][JB][R];
+        auto load_next = [&](Regs(&g)[JB][R]) {
+            load_batch(g, lt, lb * JB, 0, nu);
+            if (++lb == nb) {
+                lb = 0;
+                lt += gstride;
             }
-            load_batch(nxt, nt, nbi * JB, 0, nu);  // past the last tile: no fetch, never used
-            compute_batch(cur, b * JB, 0, nu);
-            if (nbi == 0) {
-                reduce_store(tile);
-                zero_acc();
-            }
-            tile = nt;
-            b = nbi;
-            return tile < ntiles;
         };
-        while (step(ga, gb) && step(gb, ga)) {
+        auto compute_next = [&](const Regs(&g)[JB][R]) {
+            compute_batch(g, cb * JB, 0, nu);
+            const bool end = ++cb == nb;
+            store_if_end(ct, end);
+            if (end) {
+                zero_acc();
+                cb = 0;
+                ct += gstride;
+            }
+        };
+        stage<F, N, NT, kStageRound<WAVES>, LO>(xr, K, 0, nu, uc, xs, meta, tid, [&]() {
+#pragma unroll
+            for (int p = 0; p < D; p++) load_next(gbuf[p]);
+        });
+        wg_sync<WAVES>();
+        for (;;) {
+#pragma unroll
+            for (int p = 0; p < NBUF; p++) {
+                load_next(gbuf[(p + D) % NBUF]);
+                compute_next(gbuf[p]);
+                if (ct >= ntiles) goto stream_done;
+            }
         }
+    stream_done:
         return;
     }
 
@@ -575,7 +633,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
             const int jc = (nuc + LPR - 1) / LPR;  // unit slots per lane per row in this chunk
             if (!first) wg_sync<WAVES>();
             first = false;
-            stage<F, N, NT, kStageRound<WAVES>>(xr, K, c0, nuc, uc, xs, meta, tid,
+            stage<F, N, NT, kStageRound<WAVES>, LO>(xr, K, c0, nuc, uc, xs, meta, tid,
                                                 [&]() { load_batch(ga, tile, 0, c0, nuc); });
             wg_sync<WAVES>();
             // Prefetches are unconditional (a batch past the chunk issues
@@ -612,8 +670,15 @@ int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStre
     const long long cap = static_cast<long long>(cus) * groups_per_cu;
     const unsigned grid = static_cast<unsigned>(ntiles < cap ? ntiles : cap);
     const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(F::kFormat, m, k));
-    hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB>), dim3(grid), dim3(64 * WAVES), lds, stream, w, wbytes,
-                       x, y, m, k, uc, ntiles);
+    // Activations as hi + lo fp16 pairs (about 2^-23 relative) for short
+    // matrices, as one fp16 each (2^-12 relative, half the dot issues, LDS
+    // reads and staging work) once there are kLoRowLimit rows or more.
+    if (m < kLoRowLimit)
+        hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB, true>), dim3(grid), dim3(64 * WAVES), lds, stream, w,
+                           wbytes, x, y, m, k, uc, ntiles);
+    else
+        hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB, false>), dim3(grid), dim3(64 * WAVES), lds, stream, w,
+                           wbytes, x, y, m, k, uc, ntiles);
     return hip_status(hipGetLastError());
 }
 
