@@ -372,7 +372,8 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
         }
     };
     bool issued = false;
-    for (int base = tid; base < total || !issued; base += P * NT) {
+    for (int rb = 0; rb < total || !issued; rb += P * NT) {
+        const int base = rb + tid;
         f32x4 a[P], b[P];
 #pragma unroll
         for (int p = 0; p < P; p++) {
@@ -384,15 +385,22 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
             b[p] = __builtin_bit_cast(f32x4, load16<0>(xr, off + 4u * F::kHighOffset, 0));
         }
         if (!issued) {
+            // Keep the scheduler from moving activation loads behind the weights.
+            __builtin_amdgcn_sched_barrier(0);
             issue();
             issued = true;
         }
+        // Every load above is consumed here, so none of them can be sunk into
+        // the branches below (behind the weight loads, whose wait would then
+        // cover them too).
+#pragma unroll
+        for (int p = 0; p < P; p++) asm volatile("" ::"v"(a[p]), "v"(b[p]));
 #pragma unroll
         for (int p = 0; p < P; p++) {
-            // Items past the end are processed (on zeros) but store nothing:
-            // keeping the arithmetic unconditional keeps the loads above from
-            // being sunk into a branch (which would serialise them behind the
-            // weights).
+            // Slots with no live item in the whole workgroup are skipped (a
+            // uniform branch); in the last live slot, lanes past the end
+            // compute on zeros and store nothing.
+            if (rb + p * NT >= total) break;
             const bool live = base + p * NT < total;
             int t, rem;
             split_item(live ? base + p * NT : 0, t, rem);
