@@ -113,11 +113,11 @@ int q4_gemv(int fmt, const void *w, const float *x, float *y,
  * A zero field keeps the library's choice. Instantiated geometries
  * (lanes_per_row, rows_per_lane, waves_per_group): (8,1,1) (8,2,1) (8,4,1)
  * (16,1,1) (16,2,1) (32,1,1) (32,2,1) (64,1,1) (16,1,4) (32,1,4) (32,2,4)
- * (64,1,4) (64,2,4) (64,4,4); others return Q4_EUNSUPPORTED. */
+ * (64,1,4) (64,2,4) (64,4,4) (32,1,8); others return Q4_EUNSUPPORTED. */
 typedef struct {
     int lanes_per_row;   /* lanes sharing one weight row: 8, 16, 32 or 64 */
     int rows_per_lane;   /* rows each lane streams at once: 1, 2 or 4 */
-    int waves_per_group; /* waves per workgroup: 1 or 4 */
+    int waves_per_group; /* waves per workgroup: 1, 4 or 8 */
     int groups_per_cu;   /* workgroups per compute unit the grid is sized for (0..64) */
 } q4_gemv_tuning;
 

@@ -135,7 +135,7 @@ def q4_gemv(fmt: int, w, x, y, m: int, k: int, stream=None) -> None:
 # The instantiated tile geometries, as the header lists them.
 # Decode: (lanes_per_row, rows_per_lane, waves_per_group).
 GEMV_GEOMETRIES = ((8, 1, 1), (8, 2, 1), (8, 4, 1), (16, 1, 1), (16, 2, 1), (32, 1, 1), (32, 2, 1), (64, 1, 1),
-                   (16, 1, 4), (32, 1, 4), (32, 2, 4), (64, 1, 4), (64, 2, 4), (64, 4, 4))
+                   (16, 1, 4), (32, 1, 4), (32, 2, 4), (64, 1, 4), (64, 2, 4), (64, 4, 4), (32, 1, 8))
 # Prefill: (tile_rows, tile_tokens, stage_k).
 GEMM_TILES = ((16, 64, 512), (16, 64, 1024), (32, 64, 256), (32, 64, 512), (32, 64, 1024), (32, 128, 512),
               (64, 64, 256), (64, 64, 512))

@@ -53,10 +53,12 @@ namespace gemv {
 //     64 lanes per row; longer rows -> 4 waves, 32 lanes x 2 rows.
 //   Q4_0, several tokens: 4 waves; 64 lanes per row for 33..127 units, else
 //     32 lanes x 2 rows.
-//   Q4_K: 4 waves of 64 lanes per row for 33..127 units; otherwise 16 lanes
-//     per row up to 4 tokens (one-wave groups for short rows and 1..2 tokens;
-//     32 lanes for very long rows at one token), and 32 lanes x 2 rows for
-//     5..8 tokens.
+//   Q4_K: 4 waves of 64 lanes per row for 33..127 units. Short rows: 16
+//     lanes per row, one-wave groups at 1..2 tokens, 4 waves at 3..4, and 32
+//     lanes x 2 rows from 5 tokens. Rows of 256 units or more: 8-wave groups
+//     of 32 lanes per row. Rows of 128..255 units: the same 8-wave groups for
+//     tall products at one token and at 2..4 tokens, else 4 waves of 16 lanes
+//     per row.
 Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 {
     (void)cus;
@@ -71,9 +73,10 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
         return Cfg{32, 2, 4, 2};
     }
     if (nu > 32 && nu < 128) return Cfg{64, 1, 4, 4};
-    if (n >= 5) return Cfg{32, 2, 4, 2};
-    if (nu <= 32) return n <= 2 ? Cfg{16, 1, 1, 8} : Cfg{16, 1, 4, 4};
-    if (n == 1 && nu >= 256) return Cfg{32, 1, 4, 4};
+    if (nu <= 32) return n <= 2 ? Cfg{16, 1, 1, 8} : n >= 5 ? Cfg{32, 2, 4, 2} : Cfg{16, 1, 4, 4};
+    if (nu >= 256) return Cfg{32, 1, 8, 2};
+    if (n == 1) return m >= 8192 ? Cfg{32, 1, 8, 1} : Cfg{16, 1, 4, 4};
+    if (n <= 4) return Cfg{32, 1, 8, 2};
     return Cfg{16, 1, 4, 4};
 }
 

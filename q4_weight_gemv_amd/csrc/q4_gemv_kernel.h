@@ -705,7 +705,8 @@ int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStre
     X(32, 2, 4)            \
     X(64, 1, 4)            \
     X(64, 2, 4)            \
-    X(64, 4, 4)
+    X(64, 4, 4)            \
+    X(32, 1, 8)
 
 template <class F, int N>
 int dispatch_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus)
