@@ -50,9 +50,10 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def gemv_bytes(q4, fmt, m, k, n):
-    """Algorithmic bytes of one decode product: quantized W + fp32 x + fp32 y."""
-    return q4.q4_weight_bytes(fmt, m, k) + 4 * n * k + 4 * n * m
+def gemv_bytes(q4, fmt, m, k, n, gated=0):
+    """Algorithmic bytes of one decode product: quantized W + fp32 x + fp32 y
+    (a gated product reads 2m weight rows and writes m outputs)."""
+    return q4.q4_weight_bytes(fmt, (2 if gated else 1) * m, k) + 4 * n * k + 4 * n * m
 
 
 def gemm_bytes(q4, fmt, m, k, n):
@@ -100,13 +101,15 @@ class Step:
     def __init__(self, torch, q4, shapes, fmt, n, config_id, cold=True):
         import synth
 
+        # Entries (K, M) or (K, M, gated): a gated product reads 2M weight rows.
+        shapes = [tuple(s) + (0,) * (3 - len(s)) for s in shapes]
         self.shapes, self.fmt, self.n = shapes, fmt, n
-        self.bytes = sum(gemv_bytes(q4, fmt, m, k, n) for k, m in shapes)
-        self.host_w = [q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(config_id, i), m, k))
-                       for i, (k, m) in enumerate(shapes)]
-        self.host_x = [synth.activations(synth.seed_for(config_id, i, True), n, k) for i, (k, m) in enumerate(shapes)]
+        self.bytes = sum(gemv_bytes(q4, fmt, m, k, n, g) for k, m, g in shapes)
+        self.host_w = [q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(config_id, i), (2 if g else 1) * m, k))
+                       for i, (k, m, g) in enumerate(shapes)]
+        self.host_x = [synth.activations(synth.seed_for(config_id, i, True), n, k) for i, (k, m, g) in enumerate(shapes)]
         self.xs = [torch.from_numpy(x).cuda() for x in self.host_x]
-        self.ys = [torch.empty((n, m), dtype=torch.float32, device="cuda") for k, m in shapes]
+        self.ys = [torch.empty((n, m), dtype=torch.float32, device="cuda") for k, m, g in shapes]
         wbytes = sum(h.size for h in self.host_w)
         ncopies = copies_for(wbytes) if cold else 1
         self.copies = [[torch.from_numpy(h).cuda() for h in self.host_w] for _ in range(ncopies)]
@@ -114,7 +117,7 @@ class Step:
         torch.cuda.synchronize()
 
     def _ops(self, ws):
-        return [(w, x, y, m, k) for w, x, y, (k, m) in zip(ws, self.xs, self.ys, self.shapes)]
+        return [(w, x, y, m, k, g) for w, x, y, (k, m, g) in zip(ws, self.xs, self.ys, self.shapes)]
 
     def run_graph(self, i):
         self.graphs[i % len(self.graphs)].launch()
@@ -150,8 +153,11 @@ def cpu_baseline(step, budget_s=10.0, budget_1core_s=6.0):
         t0 = time.perf_counter()
         reps = 0
         while True:
-            for i, (k, m) in enumerate(step.shapes):
-                oracle.matvec(step.fmt, step.host_w[i], m, k, step.host_x[i], threads=threads)
+            for i, (k, m, g) in enumerate(step.shapes):
+                if g:
+                    oracle.matvec_silu_mul(step.fmt, step.host_w[i], m, k, step.host_x[i], threads=threads)
+                else:
+                    oracle.matvec(step.fmt, step.host_w[i], m, k, step.host_x[i], threads=threads)
             reps += 1
             if time.perf_counter() - t0 >= budget:
                 break
@@ -245,7 +251,22 @@ def bench_gemm(torch, q4, timer, n=512, reps=20, shapes=None, per_matrix=True):
                     for _ in range(20):
                         q4.q4_gemm(0, w, xb, y, m, k)
             tm = timer.region(lambda i: gm.replay(), reps, 3) / (reps * 20)
-            per[f"{k}to{m}"] = {"us": round(tm * 1e6, 2), "TFLOP_s": round(2 * n * m * k / tm / 1e12, 1)}
+            # Context only, not the product path: the vendor library's dense
+            # bf16 GEMM (torch.mm -> hipBLASLt) on the same shape with weights
+            # already in bf16 (4x the weight bytes, no dequantization), bf16 out.
+            wt = (torch.randn(k, m, device="cuda") * 0.02).to(torch.bfloat16).contiguous()
+            xd = xb.view(torch.bfloat16)
+            yd = torch.empty((n, m), device="cuda", dtype=torch.bfloat16)
+            gl = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                torch.mm(xd, wt, out=yd)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(gl, stream=s):
+                    for _ in range(20):
+                        torch.mm(xd, wt, out=yd)
+            tl = timer.region(lambda i: gl.replay(), reps, 3) / (reps * 20)
+            per[f"{k}to{m}"] = {"us": round(tm * 1e6, 2), "TFLOP_s": round(2 * n * m * k / tm / 1e12, 1),
+                                "library_dense_bf16_us": round(tl * 1e6, 2)}
         out["per_matrix"] = per
     return out
 
@@ -299,7 +320,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the headline workload")
     ap.add_argument("--extras", default="all",
                     help="comma list of extras to run (default all): plain, floor, gate_7b, smollm2, smollm2_fused, "
-                         "warm, read_ceiling, gemm")
+                         "smollm2_gated, warm, read_ceiling, gemm")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 64 MiB device copy (torch) once, as the reference for HBM byte counters")
     args = ap.parse_args()
@@ -396,7 +417,8 @@ def main():
         if on("gate_7b"):
             extras["gate_7b"] = bench_7b(torch, q4, timer, reps=max(2, K // 50))
         for name, key, shapes_fn in (("smollm2", "smollm2_step", synth.smollm2_360m_step),
-                                     ("smollm2_fused", "smollm2_step_fused_qkv_gateup", synth.smollm2_360m_step_fused)):
+                                     ("smollm2_fused", "smollm2_step_fused_qkv_gateup", synth.smollm2_360m_step_fused),
+                                     ("smollm2_gated", "smollm2_step_qkv_stacked_gated_mlp", synth.smollm2_360m_step_gated)):
             if not on(name):
                 continue
             log(f"setup {key}")

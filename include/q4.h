@@ -106,6 +106,22 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
 int q4_gemv(int fmt, const void *w, const float *x, float *y,
             int64_t m, int64_t k, int64_t n, void *hip_stream);
 
+/* Gated decode product: the gate and up projections of a gated MLP in one
+ * launch, with the activation applied to the gate (kernels fused: WebGPT
+ * README, "Roadmap"; the technical summary of Llamas on the Web credits fused
+ * kernels for prefill throughput, "Experimental results"). w is one quantized
+ * (2m) x k matrix, gate rows 0..m-1 then up rows m..2m-1, in the layout of
+ * q4_quantize_ref for 2m rows (quantize the stacked matrix). For t < n and
+ * i < m:
+ *   y[t][i] = silu(g) * u,  g = sum_k w_hat[i][k] x[t][k],
+ *   u = sum_k w_hat[m+i][k] x[t][k],  silu(g) = g / (1 + exp(-g)).
+ * g and u are summed exactly as q4_gemv sums the rows of the stacked matrix
+ * (same arithmetic, same tolerance); the epilogue is fp32. x [n][k] and
+ * y [n][m] are device arrays, n is 1..8. Errors as q4_gemv, with the size
+ * limits applying to the 2m-row matrix (m below 2^29). */
+int q4_gemv_glu(int fmt, const void *w, const float *x, float *y,
+                int64_t m, int64_t k, int64_t n, void *hip_stream);
+
 /* Tile geometry of the decode product. The library picks it per shape; the
  * tuned entry point lets a sweep override it (tile and workgroup sizes are
  * tunable parameters whose defaults come from an empirical sweep: Llamas on
@@ -153,12 +169,19 @@ typedef struct {
 int q4_gemm_tuned(int fmt, const void *w, const uint16_t *x_bf16, float *y,
                   int64_t m, int64_t k, int64_t n, const q4_gemm_tuning *tuning, void *hip_stream);
 
+/* Epilogue of a layer-stack product. */
+enum {
+    Q4_EPILOGUE_NONE = 0,     /* y = W x (q4_gemv); w has m rows */
+    Q4_EPILOGUE_SILU_MUL = 1  /* y = silu(W_gate x) * (W_up x) (q4_gemv_glu); w has 2m rows */
+};
+
 /* One decode product of a layer stack. */
 typedef struct {
     const void *w;   /* device weights */
     const float *x;  /* device [n][k] */
     float *y;        /* device [n][m] */
-    int64_t m, k;
+    int64_t m, k;    /* output rows, input length */
+    int epilogue;    /* Q4_EPILOGUE_*; any other value is Q4_EINVAL */
 } q4_gemv_op;
 
 /* Enqueue count decode products back-to-back on one stream with no host

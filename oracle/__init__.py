@@ -76,6 +76,8 @@ def lib():
                 "oracle_matmul": (None, [ctypes.c_int, _u8p, _i64, _i64, _u16p, _i64, _f32p, ctypes.c_int, _f64p, _i64, _i64]),
                 "oracle_matvec_termscale": (None, [ctypes.c_int, _u8p, _i64, _i64, _f32p, _i64, _f64p, _i64, _i64]),
                 "oracle_matvec_one": (ctypes.c_double, [ctypes.c_int, _u8p, _i64, _i64, _f32p, _i64, _i64, _f64p]),
+                "oracle_matvec_silu_mul": (None, [ctypes.c_int, _u8p, _i64, _i64, _f32p, _i64, _f32p, _f64p, _f64p,
+                                                  _i64, _i64]),
             }
             for name, (res, args) in sigs.items():
                 fn = getattr(L, name)
@@ -216,6 +218,31 @@ def matvec(fmt: int, buf: np.ndarray, m: int, k: int, x: np.ndarray, threads: in
     ranges = _row_split(m, threads) if rows is None else _split_ranges(rows, threads)
     _parallel(run, ranges)
     return (y, ad) if absdot else y
+
+
+def matvec_silu_mul(fmt: int, buf: np.ndarray, m: int, k: int, x: np.ndarray, threads: int = 1,
+                    parts: bool = False):
+    """Gated product over the stacked (2m) x k matrix: y[n][m] = fp32(silu(g) * u) in float64.
+
+    With ``parts`` also returns the float64 row products g and u.
+    """
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    n = x.shape[0]
+    assert x.shape[1] == k and buf.size == weight_bytes(fmt, 2 * m, k)
+    y = np.zeros((n, m), dtype=np.float32)
+    g = np.zeros((n, m), dtype=np.float64)
+    u = np.zeros((n, m), dtype=np.float64)
+    L = lib()
+
+    def run(r0, r1):
+        L.oracle_matvec_silu_mul(fmt, _p(buf, _u8p), m, k, _p(x, _f32p), n, _p(y, _f32p), _p(g, _f64p),
+                                 _p(u, _f64p), r0, r1)
+
+    _parallel(run, _row_split(m, threads))
+    return (y, g, u) if parts else y
 
 
 def _split_ranges(rows, threads):

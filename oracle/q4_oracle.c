@@ -468,6 +468,32 @@ void oracle_matvec_termscale(int fmt, const uint8_t *w, int64_t m, int64_t k, co
         }
 }
 
+/* Gated decode product (the gate and up projections of a gated MLP fused into
+ * one launch, the activation applied to the gate; kernel fusion: WebGPT
+ * README, "Roadmap"; Llamas on the Web technical summary, "Experimental
+ * results"). The matrix has 2m rows: gate rows 0..m-1, then up rows
+ * m..2m-1. With g and u the fp64 row products (as in oracle_matvec, before
+ * any rounding), y[t][i] = fp32( silu(g) * u ), silu(g) = g / (1 + exp(-g)),
+ * evaluated in fp64. g and u are also returned (fp64) when the pointers are
+ * not null. Rows [row0, row1) of the output. */
+void oracle_matvec_silu_mul(int fmt, const uint8_t *w, int64_t m, int64_t k, const float *x, int64_t n,
+                            float *y, double *g_out, double *u_out, int64_t row0, int64_t row1)
+{
+    for (int64_t i = row0; i < row1; i++) {
+        for (int64_t t = 0; t < n; t++) {
+            double g = 0.0, u = 0.0;
+            for (int64_t c = 0; c < k; c++) {
+                g += (double)weight_at(fmt, w, 2 * m, k, i, c) * (double)x[t * k + c];
+                u += (double)weight_at(fmt, w, 2 * m, k, m + i, c) * (double)x[t * k + c];
+            }
+            double silu = g / (1.0 + exp(-g));
+            y[t * m + i] = (float)(silu * u);
+            if (g_out) g_out[t * m + i] = g;
+            if (u_out) u_out[t * m + i] = u;
+        }
+    }
+}
+
 /* One output of the products, for sampled checks at full size. */
 double oracle_matvec_one(int fmt, const uint8_t *w, int64_t m, int64_t k,
                          const float *x, int64_t t, int64_t i, double *absdot)

@@ -26,6 +26,9 @@ Q4_ENONFINITE = -4
 Q4_ERANGE = -5
 Q4_EHIP = -6
 
+Q4_EPILOGUE_NONE = 0
+Q4_EPILOGUE_SILU_MUL = 1
+
 BLOCK = {Q4_FMT_Q4_0: 32, Q4_FMT_Q4_K: 256}
 
 if not os.path.exists(LIB_PATH):
@@ -53,7 +56,7 @@ class q4_gemm_tuning(ctypes.Structure):
 
 class q4_gemv_op(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
-                ("m", ctypes.c_int64), ("k", ctypes.c_int64)]
+                ("m", ctypes.c_int64), ("k", ctypes.c_int64), ("epilogue", ctypes.c_int)]
 
 
 _i64 = ctypes.c_int64
@@ -62,6 +65,7 @@ _SIGS = {
     "q4_weight_bytes": (ctypes.c_size_t, [ctypes.c_int, _i64, _i64]),
     "q4_quantize_ref": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i64, _vp, ctypes.c_size_t]),
     "q4_gemv": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q4_gemv_glu": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q4_gemv_tuned": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64,
                                       ctypes.POINTER(q4_gemv_tuning), _vp]),
     "q4_gemm": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -132,6 +136,13 @@ def q4_gemv(fmt: int, w, x, y, m: int, k: int, stream=None) -> None:
     _check(_lib.q4_gemv(fmt, w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k, n, _stream_ptr(stream)), "q4_gemv")
 
 
+def q4_gemv_glu(fmt: int, w, x, y, m: int, k: int, stream=None) -> None:
+    """y[n][m] = silu(W_gate x) * (W_up x), w the quantized stacked (2m) x k matrix."""
+    n = x.shape[0] if x.dim() == 2 else 1
+    _check(_lib.q4_gemv_glu(fmt, w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k, n, _stream_ptr(stream)),
+           "q4_gemv_glu")
+
+
 # The instantiated tile geometries, as the header lists them.
 # Decode: (lanes_per_row, rows_per_lane, waves_per_group).
 GEMV_GEOMETRIES = ((8, 1, 1), (8, 2, 1), (8, 4, 1), (16, 1, 1), (16, 2, 1), (32, 1, 1), (32, 2, 1), (64, 1, 1),
@@ -174,13 +185,15 @@ def q4_read_probe(buf, sink, groups: int = 2048, stream=None) -> None:
 
 def _ops_array(ops):
     arr = (q4_gemv_op * len(ops))()
-    for i, (w, x, y, m, k) in enumerate(ops):
-        arr[i] = q4_gemv_op(w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k)
+    for i, op in enumerate(ops):
+        w, x, y, m, k = op[:5]
+        epilogue = op[5] if len(op) > 5 else Q4_EPILOGUE_NONE
+        arr[i] = q4_gemv_op(w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k, epilogue)
     return arr
 
 
 def q4_gemv_sequence(fmt: int, ops, n: int, stream=None) -> None:
-    """Enqueue decode products back-to-back; ops = [(w, x, y, m, k), ...]."""
+    """Enqueue decode products back-to-back; ops = [(w, x, y, m, k[, epilogue]), ...]."""
     arr = _ops_array(ops)
     _check(_lib.q4_gemv_sequence(fmt, arr, len(ops), n, _stream_ptr(stream)), "q4_gemv_sequence")
 

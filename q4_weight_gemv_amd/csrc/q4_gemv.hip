@@ -80,14 +80,31 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
     return Cfg{16, 1, 4, 4};
 }
 
+// The gated product's geometry: the plain product's choice for the stacked
+// 2m-row matrix, moved to a gated geometry (two row slots per lane) with the
+// same lanes per row, so each gate and up row is summed exactly as the plain
+// product sums it, and one-wave groups only where the plain choice has them.
+// (Eight lanes per row, the plain choice for very tall short-row products,
+// becomes sixteen.)
+Cfg choose_glu(int fmt, int64_t m, int64_t k, int64_t n, int cus)
+{
+    const Cfg c = choose(fmt, 2 * m, k, n, cus);
+    const bool one_wave = c.waves == 1;
+    if (c.lpr <= 16) return one_wave ? Cfg{16, 2, 1, 8} : Cfg{16, 2, 4, 4};
+    if (c.lpr == 32) return one_wave ? Cfg{32, 2, 1, 8} : Cfg{32, 2, 4, 2};
+    return Cfg{64, 2, 4, 4};
+}
+
 int dispatch(int fmt, const Cfg &c, const void *w, const float *x, float *y, int64_t m, int64_t k, int64_t n,
-             void *stream, int cus)
+             void *stream, int cus, bool glu = false)
 {
     const auto *wb = static_cast<const uint8_t *>(w);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int mi = static_cast<int>(m), ki = static_cast<int>(k);
-#define Q4_N_CASE(F, NN) \
-    case NN: return dispatch_cfg<F, NN>(c, wb, x, y, mi, ki, s, cus);
+#define Q4_N_CASE(F, NN)                                                            \
+    case NN:                                                                        \
+        return glu ? dispatch_glu_cfg<F, NN>(c, wb, x, y, mi, ki, s, cus)           \
+                   : dispatch_cfg<F, NN>(c, wb, x, y, mi, ki, s, cus);
     if (fmt == Q4_FMT_Q4_0) {
         switch (n) {
             Q4_N_CASE(FmtQ4_0, 1) Q4_N_CASE(FmtQ4_0, 2) Q4_N_CASE(FmtQ4_0, 3) Q4_N_CASE(FmtQ4_0, 4)
@@ -110,6 +127,22 @@ int launch_gemv(int fmt, const void *w, const float *x, float *y, int64_t m, int
     const int cus = device_cus();
     if (cus <= 0) return Q4_EHIP;
     return gemv::dispatch(fmt, gemv::choose(fmt, m, k, n, cus), w, x, y, m, k, n, stream, cus);
+}
+
+int launch_gemv_glu(int fmt, const void *w, const float *x, float *y, int64_t m, int64_t k, int64_t n, void *stream)
+{
+    const int cus = device_cus();
+    if (cus <= 0) return Q4_EHIP;
+    return gemv::dispatch(fmt, gemv::choose_glu(fmt, m, k, n, cus), w, x, y, m, k, n, stream, cus, true);
+}
+
+int check_glu_args(int fmt, const void *w, const void *x, const float *y, int64_t m, int64_t k, int64_t n)
+{
+    if (m < 0) return Q4_EINVAL;
+    if (m >= (1LL << 29)) return Q4_EUNSUPPORTED;
+    // The weights are a (2m) x k matrix; the output is n x m (within the
+    // stacked matrix's own n x 2m bound).
+    return check_product_args(fmt, w, x, y, 2 * m, k, n, 8);
 }
 
 int check_product_args(int fmt, const void *w, const void *x, const float *y, int64_t m, int64_t k, int64_t n,
@@ -147,6 +180,15 @@ extern "C" int q4_gemv(int fmt, const void *w, const float *x, float *y, int64_t
     if (st != Q4_OK) return st;
     if (m == 0 || n == 0) return Q4_OK;
     return q4::launch_gemv(fmt, w, x, y, m, k, n, hip_stream);
+}
+
+extern "C" int q4_gemv_glu(int fmt, const void *w, const float *x, float *y, int64_t m, int64_t k, int64_t n,
+                           void *hip_stream)
+{
+    const int st = q4::check_glu_args(fmt, w, x, y, m, k, n);
+    if (st != Q4_OK) return st;
+    if (m == 0 || n == 0) return Q4_OK;
+    return q4::launch_gemv_glu(fmt, w, x, y, m, k, n, hip_stream);
 }
 
 extern "C" int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y, int64_t m, int64_t k, int64_t n,

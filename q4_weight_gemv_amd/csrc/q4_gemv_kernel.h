@@ -468,6 +468,17 @@ __device__ __forceinline__ float row_reduce(float v)
     return v;
 }
 
+// ---- gated epilogue ------------------------------------------------------------------
+// The gate and up projections of a gated MLP share their input, so one launch
+// computes both and applies the activation to the gate: silu(g) * u, with
+// silu(g) = g / (1 + e^-g) (kernel fusion: WebGPT README, "Roadmap"; the
+// technical summary of Llamas on the Web credits fused kernels for prefill
+// throughput in its experimental results).
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    return g / (1.0f + expf(-g)) * u;
+}
+
 // ---- the kernel -------------------------------------------------------------------
 // Workgroup = WAVES waves; a tile is RPG = WAVES * (64/LPR) * R consecutive
 // rows. In a tile, wave v covers rows v*RPW .. v*RPW + RPW - 1 (RPW =
@@ -479,16 +490,26 @@ __device__ __forceinline__ float row_reduce(float v)
 // across tile boundaries, with the first batch issued before the staging.
 // When the activations do not fit (many tokens x long rows) the row is
 // processed in LDS-sized chunks, restaged per tile.
+//
+// GLU (R even): the weight matrix has 2M rows, gate rows 0..M-1 then up rows
+// M..2M-1, and the output has M rows. A tile is then RPG/2 output rows; the
+// lane's row slots pair up, slot 2p holding gate row o and slot 2p+1 up row
+// M + o of the same output o = tile*RPG/2 + wave*RPW/2 + sub + p*(64/LPR).
+// Each row's sum is formed exactly as in the plain product (same lanes, same
+// order), and the epilogue applies silu_mul to the two reduced sums.
 
-template <class F, int N, int LPR, int R, int WAVES, int JB, bool LO>
+template <class F, int N, int LPR, int R, int WAVES, int JB, bool LO, bool GLU = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restrict__ w, uint32_t wbytes,
                                                           const float *__restrict__ x,
                                                           float *__restrict__ y, int M, int K, int uc,
                                                           int ntiles)
 {
+    static_assert(!GLU || R % 2 == 0, "the gated product pairs row slots");
     constexpr int SUBS = 64 / LPR;
     constexpr int RPW = SUBS * R;
     constexpr int RPG = WAVES * RPW;
+    constexpr int OPG = GLU ? RPG / 2 : RPG;  // output rows per tile
+    constexpr int RO = GLU ? R / 2 : R;       // output rows per lane
     constexpr int NT = 64 * WAVES;
     extern __shared__ u32x4 lds[];
     u32x4 *xs = lds;
@@ -500,8 +521,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     const int sub = lane / LPR;
     const int li = lane % LPR;
     const int nu = K >> 5;
-    const uint32_t scale_plane = static_cast<uint32_t>(static_cast<uint64_t>(M) * static_cast<uint64_t>(K) / 2u);
-    const int row_in_tile = wave * RPW + sub;
+    const uint64_t wrows = GLU ? 2ull * static_cast<uint64_t>(M) : static_cast<uint64_t>(M);
+    const uint32_t scale_plane = static_cast<uint32_t>(wrows * static_cast<uint64_t>(K) / 2u);
+    // Output row of slot r (an output slot for the stores, a weight-row slot
+    // for the loads: for GLU, slots 2p and 2p+1 share output slot p).
+    const int out_in_tile = wave * (RPW / (GLU ? 2 : 1)) + sub;
+    auto out_row = [&](int tile, int ro) { return tile * OPG + out_in_tile + ro * SUBS; };
+    // Weight row of load slot r relative to the tile's first output row.
+    auto wrow_rel = [&](int r) {
+        return GLU ? out_in_tile + (r >> 1) * SUBS + (r & 1) * M : out_in_tile + r * SUBS;
+    };
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, static_cast<uint32_t>(N) * static_cast<uint32_t>(K) * 4u);
 
     float acc[R][N];
@@ -523,15 +552,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     // no branch around them the compiler counts every load as issued, so
     // waiting for one batch never waits for the next.
     auto load_batch = [&](Regs(&g)[JB][R], int tile, int j0, int c0, int nuc) {
-        const uint32_t trow = static_cast<uint32_t>(tile) * RPG;
+        const uint32_t trow = static_cast<uint32_t>(tile) * OPG;
         const uint32_t ubase = static_cast<uint32_t>(c0 + j0 * LPR);
 #pragma unroll
         for (int jj = 0; jj < JB; jj++)
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                const bool live = li + (j0 + jj) * LPR < nuc && tile * RPG + row_in_tile + r * SUBS < M;
+                const bool live = li + (j0 + jj) * LPR < nuc && out_row(tile, GLU ? r >> 1 : r) < M;
                 F::load(g[jj][r], w, wbytes, scale_plane, static_cast<uint32_t>(nu), trow,
-                        static_cast<uint32_t>(row_in_tile + r * SUBS), static_cast<uint32_t>(li), ubase,
+                        static_cast<uint32_t>(wrow_rel(r)), static_cast<uint32_t>(li), ubase,
                         static_cast<uint32_t>(jj * LPR), live);
             }
     };
@@ -542,14 +571,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
             if (ul < nuc) F::template accumulate<N, R, LO>(g[jj], xs, meta, ul, uc, static_cast<uint32_t>(c0 + ul), acc);
         }
     };
+    // Reduced output value of output slot ro, token t.
+    auto finish = [&](int ro, int t) {
+        if constexpr (GLU)
+            return silu_mul(row_reduce<LPR>(acc[2 * ro][t]), row_reduce<LPR>(acc[2 * ro + 1][t]));
+        else
+            return row_reduce<LPR>(acc[ro][t]);
+    };
     auto reduce_store = [&](int tile) {
-        const int row0 = tile * RPG + row_in_tile;
 #pragma unroll
-        for (int r = 0; r < R; r++) {
-            const int row = row0 + r * SUBS;
+        for (int ro = 0; ro < RO; ro++) {
+            const int row = out_row(tile, ro);
 #pragma unroll
             for (int t = 0; t < N; t++) {
-                const float v = row_reduce<LPR>(acc[r][t]);
+                const float v = finish(ro, t);
                 if (li == 0 && row < M) y[static_cast<size_t>(t) * M + row] = v;
             }
         }
@@ -562,14 +597,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     // no memory, sits behind the (uniform) branch.
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, static_cast<uint32_t>(N) * static_cast<uint32_t>(M) * 4u);
     auto store_if_end = [&](int tile, bool end) {
-        const int row0 = tile * RPG + row_in_tile;
 #pragma unroll
-        for (int r = 0; r < R; r++) {
-            const int row = row0 + r * SUBS;
+        for (int ro = 0; ro < RO; ro++) {
+            const int row = out_row(tile, ro);
 #pragma unroll
             for (int t = 0; t < N; t++) {
                 float v = 0.0f;
-                if (end) v = row_reduce<LPR>(acc[r][t]);
+                if (end) v = finish(ro, t);
                 const bool live = end && li == 0 && row < M;
                 __builtin_amdgcn_raw_buffer_store_b32(
                     __builtin_bit_cast(uint32_t, v), yr,
@@ -662,12 +696,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
 
 // ---- launch -----------------------------------------------------------------------
 
-template <class F, int N, int LPR, int R, int WAVES>
+// m is the number of output rows (for GLU the weights have 2m rows).
+template <class F, int N, int LPR, int R, int WAVES, bool GLU = false>
 int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t stream, int cus,
                int groups_per_cu)
 {
     constexpr int JB = F::kBatchUnits / R > 0 ? F::kBatchUnits / R : 1;
-    constexpr int rows_per_wg = WAVES * (64 / LPR) * R;
+    constexpr int rows_per_wg = WAVES * (64 / LPR) * R / (GLU ? 2 : 1);
     const int nu = k / 32;
     int uc = nu;
     const int bytes_per_unit = N * kLdsBytesPerUnit;
@@ -677,16 +712,19 @@ int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStre
     const int ntiles = (m + rows_per_wg - 1) / rows_per_wg;
     const long long cap = static_cast<long long>(cus) * groups_per_cu;
     const unsigned grid = static_cast<unsigned>(ntiles < cap ? ntiles : cap);
-    const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(F::kFormat, m, k));
+    const int64_t wrows = GLU ? 2 * static_cast<int64_t>(m) : m;
+    const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(F::kFormat, wrows, k));
     // Activations as hi + lo fp16 pairs (about 2^-23 relative) for short
     // matrices, as one fp16 each (2^-12 relative, half the dot issues, LDS
-    // reads and staging work) once there are kLoRowLimit rows or more.
-    if (m < kLoRowLimit)
-        hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB, true>), dim3(grid), dim3(64 * WAVES), lds, stream, w,
-                           wbytes, x, y, m, k, uc, ntiles);
+    // reads and staging work) once there are kLoRowLimit rows or more
+    // (weight rows: a gated product rounds like the plain product of its
+    // stacked matrix).
+    if (wrows < kLoRowLimit)
+        hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB, true, GLU>), dim3(grid), dim3(64 * WAVES), lds, stream,
+                           w, wbytes, x, y, m, k, uc, ntiles);
     else
-        hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB, false>), dim3(grid), dim3(64 * WAVES), lds, stream, w,
-                           wbytes, x, y, m, k, uc, ntiles);
+        hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB, false, GLU>), dim3(grid), dim3(64 * WAVES), lds,
+                           stream, w, wbytes, x, y, m, k, uc, ntiles);
     return hip_status(hipGetLastError());
 }
 
@@ -714,6 +752,25 @@ int dispatch_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m
 #define Q4_CFG_CASE(L, RR, WV) \
     if (c.lpr == L && c.r == RR && c.waves == WV) return launch_one<F, N, L, RR, WV>(w, x, y, m, k, s, cus, c.groups_per_cu);
     Q4_GEMV_CONFIGS(Q4_CFG_CASE)
+#undef Q4_CFG_CASE
+    return Q4_EUNSUPPORTED;
+}
+
+// The gated product's geometries (two row slots per lane: a gate and an up row).
+#define Q4_GEMV_GLU_CONFIGS(X) \
+    X(16, 2, 1)                \
+    X(16, 2, 4)                \
+    X(32, 2, 1)                \
+    X(32, 2, 4)                \
+    X(64, 2, 4)
+
+template <class F, int N>
+int dispatch_glu_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus)
+{
+#define Q4_CFG_CASE(L, RR, WV)                                   \
+    if (c.lpr == L && c.r == RR && c.waves == WV)                \
+        return launch_one<F, N, L, RR, WV, true>(w, x, y, m, k, s, cus, c.groups_per_cu);
+    Q4_GEMV_GLU_CONFIGS(Q4_CFG_CASE)
 #undef Q4_CFG_CASE
     return Q4_EUNSUPPORTED;
 }

@@ -7,5 +7,9 @@ template int dispatch_cfg<FmtQ4_0, 1>(const Cfg &, const uint8_t *, const float 
 template int dispatch_cfg<FmtQ4_0, 2>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
 template int dispatch_cfg<FmtQ4_0, 3>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
 template int dispatch_cfg<FmtQ4_0, 4>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
+template int dispatch_glu_cfg<FmtQ4_0, 1>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
+template int dispatch_glu_cfg<FmtQ4_0, 2>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
+template int dispatch_glu_cfg<FmtQ4_0, 3>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
+template int dispatch_glu_cfg<FmtQ4_0, 4>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
 }  // namespace gemv
 }  // namespace q4

@@ -7,5 +7,9 @@ template int dispatch_cfg<FmtQ4_K, 5>(const Cfg &, const uint8_t *, const float 
 template int dispatch_cfg<FmtQ4_K, 6>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
 template int dispatch_cfg<FmtQ4_K, 7>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
 template int dispatch_cfg<FmtQ4_K, 8>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
+template int dispatch_glu_cfg<FmtQ4_K, 5>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
+template int dispatch_glu_cfg<FmtQ4_K, 6>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
+template int dispatch_glu_cfg<FmtQ4_K, 7>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
+template int dispatch_glu_cfg<FmtQ4_K, 8>(const Cfg &, const uint8_t *, const float *, float *, int, int, hipStream_t, int);
 }  // namespace gemv
 }  // namespace q4

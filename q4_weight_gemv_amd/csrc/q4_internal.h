@@ -23,6 +23,13 @@ int check_product_args(int fmt, const void *w, const void *x, const float *y,
 int launch_gemv(int fmt, const void *w, const float *x, float *y,
                 int64_t m, int64_t k, int64_t n, void *stream);
 
+// Validation of a gated decode product (weights of 2m rows, output of m).
+int check_glu_args(int fmt, const void *w, const void *x, const float *y, int64_t m, int64_t k, int64_t n);
+
+// Launch one gated decode product (arguments already validated).
+int launch_gemv_glu(int fmt, const void *w, const float *x, float *y,
+                    int64_t m, int64_t k, int64_t n, void *stream);
+
 // Launch one prefill product (arguments already validated).
 int launch_gemm(int fmt, const void *w, const uint16_t *x, float *y,
                 int64_t m, int64_t k, int64_t n, void *stream);
@@ -40,7 +47,7 @@ namespace gemv {
 struct Cfg {
     int lpr;            // lanes per row: 8, 16, 32 or 64
     int r;              // rows per lane
-    int waves;          // waves per workgroup: 1 or 4
+    int waves;          // waves per workgroup: 1, 4 or 8
     int groups_per_cu;  // resident workgroups per compute unit the grid is sized for
 };
 
@@ -50,6 +57,8 @@ struct FmtQ4_K;
 // Defined in the per-format instantiation units (q4_gemv_q4_*.hip).
 template <class F, int N>
 int dispatch_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus);
+template <class F, int N>
+int dispatch_glu_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus);
 
 }  // namespace gemv
 }  // namespace q4

@@ -24,7 +24,11 @@ int check_ops(int fmt, const q4_gemv_op *ops, int count, int64_t n)
 {
     if (count < 0 || (count > 0 && !ops)) return Q4_EINVAL;
     for (int i = 0; i < count; i++) {
-        const int st = q4::check_product_args(fmt, ops[i].w, ops[i].x, ops[i].y, ops[i].m, ops[i].k, n, 8);
+        int st = Q4_EINVAL;
+        if (ops[i].epilogue == Q4_EPILOGUE_NONE)
+            st = q4::check_product_args(fmt, ops[i].w, ops[i].x, ops[i].y, ops[i].m, ops[i].k, n, 8);
+        else if (ops[i].epilogue == Q4_EPILOGUE_SILU_MUL)
+            st = q4::check_glu_args(fmt, ops[i].w, ops[i].x, ops[i].y, ops[i].m, ops[i].k, n);
         if (st != Q4_OK) return st;
     }
     return Q4_OK;
@@ -34,7 +38,9 @@ int enqueue_ops(int fmt, const q4_gemv_op *ops, int count, int64_t n, hipStream_
 {
     for (int i = 0; i < count; i++) {
         if (ops[i].m == 0 || n == 0) continue;
-        const int st = q4::launch_gemv(fmt, ops[i].w, ops[i].x, ops[i].y, ops[i].m, ops[i].k, n, s);
+        const int st = ops[i].epilogue == Q4_EPILOGUE_SILU_MUL
+                           ? q4::launch_gemv_glu(fmt, ops[i].w, ops[i].x, ops[i].y, ops[i].m, ops[i].k, n, s)
+                           : q4::launch_gemv(fmt, ops[i].w, ops[i].x, ops[i].y, ops[i].m, ops[i].k, n, s);
         if (st != Q4_OK) return st;
     }
     return Q4_OK;

@@ -122,6 +122,15 @@ def smollm2_360m_step_fused():
     return [s for _ in range(32) for s in layer] + [(h, 49152)]
 
 
+def smollm2_360m_step_gated():
+    """SmolLM2-360M decode step with q|k|v stacked and gate|up as one gated
+    product (silu(gate) * up, 2 x 2560 weight rows, 2560 outputs): entries
+    (K, M, gated) with gated = 1 for the gated product. 129 products."""
+    h = 960
+    layer = [(h, 1600, 0), (h, h, 0), (h, 2560, 1), (2560, h, 0)]
+    return [s for _ in range(32) for s in layer] + [(h, 49152, 0)]
+
+
 def smollm2_360m_layer():
     """The 7 matrices of one SmolLM2-360M layer (prefill GEMM workload)."""
     h = 960

@@ -282,3 +282,123 @@ def test_sequence_and_graph_match_single_calls(env, fmt):
         for (_, _, y, _, _), ref in zip(ops, refs):
             assert torch.equal(y, ref), rep
     g.close()
+
+
+# ---- gated product: silu(W_gate x) * (W_up x) from one stacked matrix ------------
+
+def _glu(env, fmt, buf, x, m, k):
+    torch, q4, _ = env
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    yd = torch.full((x.shape[0], m), float("nan"), dtype=torch.float32, device="cuda")
+    q4.q4_gemv_glu(fmt, wd, xd, yd, m, k)
+    torch.cuda.synchronize()
+    return yd.cpu().numpy()
+
+
+def _silu_mul64(g, u):
+    g = np.asarray(g, np.float64)
+    return g / (1.0 + np.exp(-g)) * np.asarray(u, np.float64)
+
+
+GLU_CASES = [
+    (0, 1, 37, 96), (0, 3, 130, 960), (0, 1, 1280, 960), (0, 8, 200, 2560), (0, 1, 300, 4096), (0, 2, 70, 11008),
+    (1, 1, 37, 256), (1, 4, 130, 1024), (1, 1, 300, 4096), (1, 8, 90, 4096), (1, 1, 70, 11008),
+]
+
+
+@pytest.mark.parametrize("fmt,n,m,k", GLU_CASES)
+def test_glu_matches_plain_product_of_stacked_matrix(env, fmt, n, m, k):
+    # The gate and up sums are formed exactly as the plain product forms the
+    # rows of the stacked matrix, so the gated output is silu(g) * u of the
+    # plain product's rows, up to the fp32 epilogue (a few ulp).
+    torch, q4, orc = env
+    buf = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(1100 + fmt, m), 2 * m, k))
+    x = synth.activations(synth.seed_for(1100 + fmt, m, True), n, k)
+    say(f"glu vs plain fmt={fmt} n={n} m={m} k={k}")
+    yp = _gemv(env, fmt, buf, x, 2 * m, k)
+    yg = _glu(env, fmt, buf, x, m, k)
+    ref = _silu_mul64(yp[:, :m], yp[:, m:])
+    scale = np.abs(yp[:, :m].astype(np.float64) * yp[:, m:])
+    assert np.all(np.isfinite(yg))
+    assert np.all(np.abs(yg - ref) <= 4e-6 * scale + 1e-30), np.max(np.abs(yg - ref) / (scale + 1e-30))
+
+
+@pytest.mark.parametrize("fmt,n,m,k", GLU_CASES)
+def test_glu_parity_oracle(env, fmt, n, m, k):
+    # Against the oracle's fp64 silu(g) * u: with |dg| <= tol * sum|w x| over
+    # the gate row and |du| likewise over the up row (the decode product's
+    # elementwise bound), and |silu'| <= 1.1, the gated output is within
+    #   1.1 |u| tol A_g + |silu(g)| tol A_u + 1.1 tol^2 A_g A_u
+    # plus the fp32 epilogue's few ulp.
+    torch, q4, orc = env
+    buf = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(1200 + fmt, m), 2 * m, k))
+    assert np.array_equal(buf, orc.quantize(fmt, synth.weights(synth.seed_for(1200 + fmt, m), 2 * m, k)))
+    x = synth.activations(synth.seed_for(1200 + fmt, m, True), n, k)
+    say(f"glu parity fmt={fmt} n={n} m={m} k={k}")
+    yg = _glu(env, fmt, buf, x, m, k)
+    yr, g, u = orc.matvec_silu_mul(fmt, buf, m, k, x, threads=threads(), parts=True)
+    _, ad = orc.matvec(fmt, buf, 2 * m, k, x, threads=threads(), absdot=True)
+    if fmt == 1:  # Q4_K's elementwise bound is stated against its term scale
+        ad = orc.termscale(fmt, buf, 2 * m, k, x, threads=threads())
+    ag, au = ad[:, :m], ad[:, m:]
+    silu = g / (1.0 + np.exp(-g))
+    bound = (1.1 * np.abs(u) * GEMV_TOL * ag + np.abs(silu) * GEMV_TOL * au + 1.1 * GEMV_TOL ** 2 * ag * au
+             + 4e-6 * np.abs(yr.astype(np.float64)) + 1e-30)
+    err = np.abs(yg.astype(np.float64) - yr)
+    assert np.all(np.isfinite(yg))
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (bad[:5], err[tuple(bad[0])], bound[tuple(bad[0])])
+    # Normwise as the decode product: within 2e-3 of the reference per token.
+    for t in range(n):
+        assert np.linalg.norm(yg[t] - yr[t]) <= GEMV_TOL * np.linalg.norm(yr[t])
+
+
+def test_glu_noop_and_errors(env):
+    torch, q4, _ = env
+    lib = q4.raw()
+    w = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(256, device="cuda")
+    y = torch.full((8,), 5.0, device="cuda")
+    assert lib.q4_gemv_glu(0, w.data_ptr(), x.data_ptr(), y.data_ptr(), 0, 32, 1, None) == q4.Q4_OK
+    assert lib.q4_gemv_glu(0, w.data_ptr(), x.data_ptr(), y.data_ptr(), 4, 32, 0, None) == q4.Q4_OK
+    assert lib.q4_gemv_glu(0, w.data_ptr(), x.data_ptr() + 4, y.data_ptr(), 4, 32, 1, None) == q4.Q4_EALIGN
+    torch.cuda.synchronize()
+    assert (y == 5.0).all()
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_sequence_and_graph_with_gated_ops(env, fmt):
+    # A SmolLM2-like fused layer: q|k|v stacked, o, gate|up gated, down; the
+    # sequence and the replayed graph reproduce the single calls bit for bit.
+    torch, q4, _ = env
+    k0 = 960 if fmt == 0 else 1024
+    k1 = 2560 if fmt == 0 else 2560 + 256 * 2
+    shapes = [(k0, 1600, 0), (k0, k0, 0), (k0, 2560, 1), (k1, k0, 0)]
+    n = 1
+    ops, refs = [], []
+    for i, (k, m, epi) in enumerate(shapes):
+        rows = 2 * m if epi else m
+        wd = torch.from_numpy(q4.q4_quantize_ref(fmt, synth.weights(1300 + i, rows, k))).cuda()
+        xd = torch.from_numpy(synth.activations(1400 + i, n, k)).cuda()
+        ref = torch.empty((n, m), device="cuda")
+        (q4.q4_gemv_glu if epi else q4.q4_gemv)(fmt, wd, xd, ref, m, k)
+        refs.append(ref)
+        ops.append((wd, xd, torch.full((n, m), float("nan"), device="cuda"), m, k, epi))
+    say(f"gated sequence fmt={fmt}")
+    q4.q4_gemv_sequence(fmt, ops, n)
+    torch.cuda.synchronize()
+    for op, ref in zip(ops, refs):
+        assert torch.equal(op[2], ref)
+    say(f"gated graph fmt={fmt}")
+    g = q4.Q4Graph(fmt, ops, n)
+    for rep in range(3):
+        for op in ops:
+            op[2].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.launch()
+        torch.cuda.synchronize()
+        _ = torch.randn(1000, device="cuda").sum().item()
+        for op, ref in zip(ops, refs):
+            assert torch.equal(op[2], ref), rep
+    g.close()

@@ -217,6 +217,36 @@ def test_sequence_and_graph_argument_errors(q4):
     assert lib.q4_graph_destroy(None) == q4.Q4_OK
 
 
+def test_gated_product_argument_errors(q4):
+    f = q4.raw().q4_gemv_glu
+    ok = (A16, A16 * 2, A16 * 3)
+    assert f(0, *ok, -1, 256, 1, None) == q4.Q4_EINVAL
+    assert f(0, *ok, 64, 48, 1, None) == q4.Q4_EINVAL              # k not a multiple of 32
+    assert f(1, *ok, 64, 288, 1, None) == q4.Q4_EINVAL             # Q4_K: k not a multiple of 256
+    assert f(0, *ok, 64, 256, 9, None) == q4.Q4_EUNSUPPORTED       # tokens beyond 8
+    assert f(2, *ok, 64, 256, 1, None) == q4.Q4_EUNSUPPORTED       # unknown format
+    assert f(0, *ok, 1 << 29, 256, 1, None) == q4.Q4_EUNSUPPORTED  # 2m rows beyond the offset range
+    assert f(0, A16 + 8, A16, A16, 64, 256, 1, None) == q4.Q4_EALIGN
+    assert f(0, None, A16, A16, 64, 256, 1, None) == q4.Q4_EINVAL
+    assert f(0, None, None, None, 0, 256, 1, None) == q4.Q4_OK      # m = 0: no-op
+    # The weights of a gated product have 2m rows: a matrix of 2^31 bytes or
+    # more is refused even when m rows alone would fit.
+    m = (1 << 30) // (4096 * 9 // 16) + 1
+    assert q4.q4_weight_bytes(0, m, 4096) < (1 << 31) <= q4.q4_weight_bytes(0, 2 * m, 4096)
+    assert f(0, *ok, m, 4096, 1, None) == q4.Q4_EUNSUPPORTED
+
+
+def test_sequence_epilogue_field(q4):
+    lib = q4.raw()
+    ops = (q4.q4_gemv_op * 1)()
+    ops[0] = q4.q4_gemv_op(A16, A16, A16, 64, 256, 7)  # unknown epilogue
+    assert lib.q4_gemv_sequence(0, ops, 1, 1, None) == q4.Q4_EINVAL
+    ops[0] = q4.q4_gemv_op(A16, A16 + 4, A16, 64, 256, q4.Q4_EPILOGUE_SILU_MUL)
+    assert lib.q4_gemv_sequence(0, ops, 1, 1, None) == q4.Q4_EALIGN
+    ops[0] = q4.q4_gemv_op(A16, A16, A16, 1 << 29, 256, q4.Q4_EPILOGUE_SILU_MUL)
+    assert lib.q4_gemv_sequence(0, ops, 1, 1, None) == q4.Q4_EUNSUPPORTED
+
+
 def test_strerror(q4):
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert q4.q4_strerror(st) and q4.q4_strerror(st) != "unknown status"

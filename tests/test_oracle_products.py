@@ -167,3 +167,67 @@ def test_termscale(orc):
     e[0, 224] = 1.0
     assert orc.termscale(1, sb, 1, 256, e)[0, 0] == 969.0
     assert orc.matvec(1, sb, 1, 256, e)[0, 0] == 921.0
+
+
+# ---- gated product (gate and up rows of one stacked matrix, silu(g) * u) ----
+
+@pytest.mark.parametrize("fmt,m,k,n", [(0, 6, 64, 2), (1, 3, 256, 2)])
+def test_silu_mul_against_library_sigmoid(orc, fmt, m, k, n):
+    # Reduces to the pinned products plus a library sigmoid: y = g * expit(g) * u
+    # with g the gate row (first m rows) and u the up row (rows m..2m-1), each
+    # the exact rational sum rounded once; swapping gate and up, dropping the
+    # factor g, or reading the wrong half of the matrix fails here.
+    from scipy.special import expit
+
+    rng = np.random.default_rng(300 + m + k)
+    w = (rng.standard_normal((2 * m, k)) * 0.05).astype(np.float32)
+    x = rng.standard_normal((n, k)).astype(np.float32)
+    buf = orc.quantize(fmt, w)
+    what = orc.dequantize(fmt, buf, 2 * m, k).astype(np.float64)
+    y, g, u = orc.matvec_silu_mul(fmt, buf, m, k, x, parts=True)
+    for t in range(n):
+        for i in range(m):
+            gf = sum(Fraction(float(what[i, c])) * Fraction(float(x[t, c])) for c in range(k))
+            uf = sum(Fraction(float(what[m + i, c])) * Fraction(float(x[t, c])) for c in range(k))
+            assert abs(g[t, i] - float(gf)) <= 1e-12 * (abs(float(gf)) + 1e-30) + 1e-300
+            assert abs(u[t, i] - float(uf)) <= 1e-12 * (abs(float(uf)) + 1e-30) + 1e-300
+            ref = np.float32(float(gf) * expit(float(gf)) * float(uf))
+            assert _ulp_distance(y[t, i], ref) <= 1, (t, i, y[t, i], ref)
+    # The halves matter: silu(g) * u differs from silu(u) * g here.
+    swapped = np.float32(u * expit(u) * g)
+    assert not np.allclose(y, swapped, rtol=1e-3)
+
+
+def test_silu_mul_closed_forms(orc):
+    # Weights 7 * 2^j quantize exactly (d = 2^j, code 15 or 1), so the row
+    # products below are exact small integers.
+    k = 64
+    x = np.ones((1, k), np.float32)
+    # Gate rows of all-zero weights: g = 0, so y = 0 exactly, whatever u is.
+    w = np.zeros((4, k), np.float32)
+    w[2:] = 0.4375
+    buf = orc.quantize(0, w)
+    y, g, u = orc.matvec_silu_mul(0, buf, 2, k, x, parts=True)
+    assert np.all(g == 0.0) and np.all(u == 28.0) and np.all(y == 0.0)
+    # silu(g) -> g for large g: g = 7 * 64 = 448, exp(-448) is far below fp32
+    # resolution, so y = fp32(448 * u).
+    w = np.zeros((2, k), np.float32)
+    w[0] = 7.0
+    w[1] = 0.875
+    buf = orc.quantize(0, w)
+    y, g, u = orc.matvec_silu_mul(0, buf, 1, k, x, parts=True)
+    assert g[0, 0] == 448.0 and u[0, 0] == 56.0 and y[0, 0] == np.float32(448.0 * 56.0)
+    # silu(g) -> 0 for very negative g: -448 * e^-448 * 56 underflows fp32.
+    w[0] = -7.0
+    buf = orc.quantize(0, w)
+    y = orc.matvec_silu_mul(0, buf, 1, k, x)
+    assert y[0, 0] == 0.0
+    # silu(g) - silu(-g) = g, for the same up row.
+    w = np.zeros((4, k), np.float32)
+    w[0] = 0.21875
+    w[1] = -0.21875
+    w[2:] = 0.875
+    buf = orc.quantize(0, w)
+    y, g, u = orc.matvec_silu_mul(0, buf, 2, k, x, parts=True)
+    assert g[0, 0] == 14.0 and g[0, 1] == -14.0 and np.all(u == 56.0)
+    assert abs((float(y[0, 0]) - float(y[0, 1])) / 56.0 - 14.0) < 1e-5
