@@ -22,6 +22,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 Q4_0 = 0
 Q4_K = 1
+Q8_0 = 2
 
 OK, EINVAL, ENONFINITE, ERANGE = 0, -1, -4, -5
 
@@ -62,6 +63,10 @@ def lib():
                 "oracle_fp32_to_bf16": (ctypes.c_uint16, [ctypes.c_float]),
                 "oracle_q4_0_bytes": (ctypes.c_size_t, [_i64, _i64]),
                 "oracle_q4_k_bytes": (ctypes.c_size_t, [_i64, _i64]),
+                "oracle_q8_0_bytes": (ctypes.c_size_t, [_i64, _i64]),
+                "oracle_q8_0_quantize_block": (ctypes.c_int, [_f32p, ctypes.POINTER(ctypes.c_int8), _u16p]),
+                "oracle_q8_0_quantize": (ctypes.c_int, [_f32p, _i64, _i64, _u8p]),
+                "oracle_q8_0_dequantize": (None, [_u8p, _i64, _i64, _f32p]),
                 "oracle_q4_0_quantize_block": (ctypes.c_int, [_f32p, _u8p, _u16p]),
                 "oracle_q4_0_quantize": (ctypes.c_int, [_f32p, _i64, _i64, _u8p]),
                 "oracle_q4_0_dequantize": (None, [_u8p, _i64, _i64, _f32p]),
@@ -120,15 +125,17 @@ def bf16_to_fp32(b: int) -> float:
 
 
 def weight_bytes(fmt: int, m: int, k: int) -> int:
-    return lib().oracle_q4_0_bytes(m, k) if fmt == Q4_0 else lib().oracle_q4_k_bytes(m, k)
+    L = lib()
+    return {Q4_0: L.oracle_q4_0_bytes, Q4_K: L.oracle_q4_k_bytes, Q8_0: L.oracle_q8_0_bytes}[fmt](m, k)
 
 
 def quantize(fmt: int, w: np.ndarray) -> np.ndarray:
-    """float32 W[m][k] -> packed bytes (plane-split Q4_0, or Q4_K super-blocks)."""
+    """float32 W[m][k] -> packed bytes (plane-split Q4_0 or Q8_0, or Q4_K super-blocks)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     m, k = w.shape
     out = np.zeros(weight_bytes(fmt, m, k), dtype=np.uint8)
-    fn = lib().oracle_q4_0_quantize if fmt == Q4_0 else lib().oracle_q4_k_quantize
+    L = lib()
+    fn = {Q4_0: L.oracle_q4_0_quantize, Q4_K: L.oracle_q4_k_quantize, Q8_0: L.oracle_q8_0_quantize}[fmt]
     st = fn(_p(w, _f32p), m, k, _p(out, _u8p))
     if st != OK:
         raise OracleError(st)
@@ -146,11 +153,24 @@ def quantize_q4_0_block(w32: np.ndarray):
     return nib, d.value
 
 
+def quantize_q8_0_block(w32: np.ndarray):
+    w32 = np.ascontiguousarray(w32, dtype=np.float32)
+    assert w32.shape == (32,)
+    q = np.zeros(32, dtype=np.int8)
+    d = ctypes.c_uint16(0)
+    st = lib().oracle_q8_0_quantize_block(_p(w32, _f32p), q.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)),
+                                          ctypes.byref(d))
+    if st != OK:
+        raise OracleError(st)
+    return q, d.value
+
+
 def dequantize(fmt: int, buf: np.ndarray, m: int, k: int) -> np.ndarray:
     buf = np.ascontiguousarray(buf, dtype=np.uint8)
     assert buf.size == weight_bytes(fmt, m, k)
     out = np.empty((m, k), dtype=np.float32)
-    fn = lib().oracle_q4_0_dequantize if fmt == Q4_0 else lib().oracle_q4_k_dequantize
+    L = lib()
+    fn = {Q4_0: L.oracle_q4_0_dequantize, Q4_K: L.oracle_q4_k_dequantize, Q8_0: L.oracle_q8_0_dequantize}[fmt]
     fn(_p(buf, _u8p), m, k, _p(out, _f32p))
     return out
 

@@ -19,6 +19,11 @@
  *   - Q4_K (the K-quant family named by q4_k_m in the summary's results):
  *     256-weight super-blocks of eight 32-weight sub-blocks, each with a 6-bit
  *     scale and a 6-bit min, plus fp16 d and dmin; value d*sc*q - dmin*m.
+ *   - Q8_0 (the q8_0 the summary's results compare with q4_k_m and q2_k):
+ *     blocks of 32 weights, an fp16 scale d = max|w| / 127, codes q in
+ *     [-127, 127] stored as bytes, value q * d.
+ *   - The gated product silu(g) * u of a stacked gate/up matrix (kernel
+ *     fusion: WebGPT README, "Roadmap"; the summary's experimental results).
  *
  * The pages give no bit layout, tie rule or quantizer search; the readings
  * used here (plane-split Q4_0 buffer, llama.cpp nibble order, half-away-from-
@@ -231,6 +236,82 @@ void oracle_q4_0_aos_to_planes(const uint8_t *aos, int64_t m, int64_t k, uint8_t
 }
 
 /* ------------------------------------------------------------------------
+ * Q8_0 (llama.cpp's legacy 8-bit scheme, the q8_0 that the technical
+ * summary's results compare with q4_k_m and q2_k): blocks of 32 weights, an
+ * fp16 scale d = max|w| / 127, codes q in [-127, 127], value q * d.
+ * Buffer for an m x k matrix, plane-split like Q4_0:
+ *   bytes [0, m*k)            code plane: block (r, b) at (r*k/32 + b)*32,
+ *                             byte j = code of element j (two's complement);
+ *   bytes [m*k, m*k*17/16)    scale plane: fp16 d of block (r, b) at
+ *                             m*k + (r*k/32 + b)*2, little-endian.
+ * ------------------------------------------------------------------------ */
+
+size_t oracle_q8_0_bytes(int64_t m, int64_t k) { return (size_t)(m * k / 32) * 34u; }
+
+/* One block: 32 floats -> 32 codes and the fp16 scale bits. */
+int oracle_q8_0_quantize_block(const float *w, int8_t *q, uint16_t *d_bits)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < 32; i++) {
+        if (!isfinite(w[i])) return ORACLE_ENONFINITE;
+        float a = fabsf(w[i]);
+        if (a > amax) amax = a;
+    }
+    float d32 = amax / 127.0f;                        /* binary32 division */
+    uint16_t dh = oracle_fp32_to_fp16(d32);
+    if ((dh & 0x7C00) == 0x7C00) return ORACLE_ERANGE; /* scale not finite in fp16 */
+    float d = oracle_fp16_to_fp32(dh);
+    for (int i = 0; i < 32; i++) {
+        if (d == 0.0f) {
+            q[i] = 0;
+        } else {
+            /* exact quotient up to double rounding (see the Q4_0 block) */
+            double t = (double)w[i] / (double)d;
+            q[i] = (int8_t)clampi((int)round_half_away(t), -127, 127);
+        }
+    }
+    *d_bits = dh;
+    return ORACLE_OK;
+}
+
+int oracle_q8_0_quantize(const float *w, int64_t m, int64_t k, uint8_t *out)
+{
+    if (m < 0 || k <= 0 || k % 32 != 0) return ORACLE_EINVAL;
+    int64_t nb = k / 32;
+    uint8_t *scales = out + (size_t)(m * k);
+    for (int64_t r = 0; r < m; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            uint16_t dh;
+            int8_t q[32];
+            int st = oracle_q8_0_quantize_block(w + r * k + b * 32, q, &dh);
+            if (st != ORACLE_OK) return st;
+            memcpy(out + (r * nb + b) * 32, q, 32);
+            scales[(r * nb + b) * 2] = (uint8_t)(dh & 0xFF);
+            scales[(r * nb + b) * 2 + 1] = (uint8_t)(dh >> 8);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Dequantized weight (r, c): q * d, exact in binary32 (8 + 11 significant bits). */
+float oracle_q8_0_weight(const uint8_t *buf, int64_t m, int64_t k, int64_t r, int64_t c)
+{
+    int64_t nb = k / 32;
+    int64_t b = c / 32;
+    int q = (int)(int8_t)buf[(r * nb + b) * 32 + c % 32];
+    const uint8_t *s = buf + (size_t)(m * k) + (r * nb + b) * 2;
+    float d = oracle_fp16_to_fp32((uint16_t)(s[0] | (s[1] << 8)));
+    return (float)q * d;
+}
+
+void oracle_q8_0_dequantize(const uint8_t *buf, int64_t m, int64_t k, float *w_hat)
+{
+    for (int64_t r = 0; r < m; r++)
+        for (int64_t c = 0; c < k; c++)
+            w_hat[r * k + c] = oracle_q8_0_weight(buf, m, k, r, c);
+}
+
+/* ------------------------------------------------------------------------
  * Q4_K.  Buffer: m * (k/256) super-blocks of 144 bytes, row-major:
  *   [0,2) fp16 d   [2,4) fp16 dmin   [4,16) twelve bytes S holding eight
  *   6-bit scales and eight 6-bit mins   [16,144) 128 nibble bytes.
@@ -379,7 +460,9 @@ void oracle_q4_k_dequantize(const uint8_t *buf, int64_t m, int64_t k, float *w_h
 
 static float weight_at(int fmt, const uint8_t *w, int64_t m, int64_t k, int64_t r, int64_t c)
 {
-    return fmt == 0 ? oracle_q4_0_weight(w, m, k, r, c) : oracle_q4_k_weight(w, m, k, r, c);
+    if (fmt == 0) return oracle_q4_0_weight(w, m, k, r, c);
+    if (fmt == 2) return oracle_q8_0_weight(w, m, k, r, c);
+    return oracle_q4_k_weight(w, m, k, r, c);
 }
 
 void oracle_matvec(int fmt, const uint8_t *w, int64_t m, int64_t k,
@@ -444,6 +527,7 @@ void oracle_matmul(int fmt, const uint8_t *w, int64_t m, int64_t k,
 static double term_magnitude(int fmt, const uint8_t *w, int64_t m, int64_t k, int64_t r, int64_t c)
 {
     if (fmt == 0) return fabs((double)oracle_q4_0_weight(w, m, k, r, c));
+    if (fmt == 2) return fabs((double)oracle_q8_0_weight(w, m, k, r, c));
     int64_t ns = k / 256;
     const uint8_t *sbp = w + (r * ns + c / 256) * 144;
     int e = (int)(c % 256);

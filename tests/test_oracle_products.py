@@ -34,7 +34,7 @@ def _ulp_distance(a: np.float32, b: np.float32) -> int:
     return abs(ia - ib)
 
 
-@pytest.mark.parametrize("fmt,m,k,n", [(0, 3, 32, 2), (0, 4, 64, 3), (1, 2, 256, 2), (1, 3, 256, 1)])
+@pytest.mark.parametrize("fmt,m,k,n", [(0, 3, 32, 2), (0, 4, 64, 3), (1, 2, 256, 2), (1, 3, 256, 1), (2, 3, 64, 2)])
 def test_brute_force_exact_rationals(orc, fmt, m, k, n):
     rng = np.random.default_rng(100 + m * k + n)
     w = (rng.standard_normal((m, k)) * 0.02).astype(np.float32)
@@ -53,7 +53,7 @@ def test_brute_force_exact_rationals(orc, fmt, m, k, n):
     assert exact_hits >= (m * n + 1) // 2
 
 
-@pytest.mark.parametrize("fmt,m,k", [(0, 37, 320), (1, 19, 512), (0, 5, 2048)])
+@pytest.mark.parametrize("fmt,m,k", [(0, 37, 320), (1, 19, 512), (0, 5, 2048), (2, 29, 416)])
 def test_matches_numpy_float64(orc, fmt, m, k):
     w = synth.weights(21, m, k)
     x = synth.activations(22, 3, k)
@@ -106,6 +106,26 @@ def test_closed_forms_q4_k(orc):
     z[:, 16:] = 0
     z[:, 4:16] = 0
     assert not orc.matvec(1, z.reshape(-1), m, k, synth.activations(42, 2, k)).any()
+
+
+def test_closed_forms_q8_0(orc):
+    m, k = 5, 128
+    buf = orc.quantize(2, synth.weights(45, m, k))
+    what = orc.dequantize(2, buf, m, k)
+    # one-hot x = e_j returns column j exactly
+    for j in (0, 31, 32, 127):
+        e = np.zeros((1, k), np.float32)
+        e[0, j] = 1.0
+        assert np.array_equal(orc.matvec(2, buf, m, k, e)[0], what[:, j])
+    # all codes 0 -> y = 0 exactly, whatever the scales and x
+    z = buf.copy()
+    z[: m * k] = 0
+    assert not orc.matvec(2, z, m, k, synth.activations(46, 2, k)).any()
+    # negating every code (two's complement) negates y exactly
+    neg = buf.copy()
+    neg[: m * k] = (-buf[: m * k].view(np.int8)).view(np.uint8)
+    x = synth.activations(47, 2, k)
+    assert np.array_equal(orc.matvec(2, neg, m, k, x), -orc.matvec(2, buf, m, k, x))
 
 
 def test_threads_do_not_change_result(orc):
