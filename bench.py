@@ -185,7 +185,10 @@ def bench_7b(torch, q4, timer, reps=20):
     import synth
 
     out = {}
-    for fmt, ns in ((0, (1,)), (1, (1, 4, 8))):
+    name = {0: "q4_0", 1: "q4_k", 2: "q8_0"}
+    # Q4_0 at one token (the gate), Q4_K at 1, 4, 8 tokens, and Q8_0 at one
+    # token beside them (the pages compare q8_0 with 4-bit formats).
+    for fmt, ns in ((0, (1,)), (1, (1, 4, 8)), (2, (1,))):
         layer_t, layer_b = {1: 0.0}, 0
         for k, m in synth.llama7b_layer()[:2] + synth.llama7b_layer()[3:]:
             wq = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(4, k + m), m, k))
@@ -197,7 +200,7 @@ def bench_7b(torch, q4, timer, reps=20):
                 t = timer.region(lambda i: g.launch(), reps, 3) / (reps * len(copies))
                 g.close()
                 nb = gemv_bytes(q4, fmt, m, k, n)
-                key = f"{'q4_0' if fmt == 0 else 'q4_k'}_{k}to{m}_n{n}"
+                key = f"{name[fmt]}_{k}to{m}_n{n}"
                 out[key] = {"us": round(t * 1e6, 3), "GB_s": round(nb / t / 1e9, 1),
                             "pct_peak": round(100 * nb / t / 1e9 / HBM_PEAK_GBS, 1)}
                 log(f"{key}: {t * 1e6:.2f} us {nb / t / 1e9:.0f} GB/s")
@@ -206,7 +209,7 @@ def bench_7b(torch, q4, timer, reps=20):
                     layer_t[1] += mult * t
                     layer_b += mult * nb
             del copies
-        key = f"{'q4_0' if fmt == 0 else 'q4_k'}_7b_layer_as_listed_n1"
+        key = f"{name[fmt]}_7b_layer_as_listed_n1"
         out[key] = {"us": round(layer_t[1] * 1e6, 2), "GB_s": round(layer_b / layer_t[1] / 1e9, 1),
                     "pct_peak": round(100 * layer_b / layer_t[1] / 1e9 / HBM_PEAK_GBS, 1)}
     return out

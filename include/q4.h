@@ -45,6 +45,14 @@
  *     (S[j] >> 6) << 4), [16,144) nibbles: four 32-byte chunks; byte i of
  *     chunk c holds weight 64c+i (low nibble) and 64c+32+i (high nibble).
  *     Weight value of sub-block j: d*sc_j*q - dmin*mn_j.
+ *   Q8_0, m x k, k % 32 == 0, m*k*17/16 bytes, plane-split like Q4_0:
+ *     bytes [0, m*k): code plane. Block (r, b) occupies 32 bytes at
+ *       (r*k/32 + b)*32; byte j is the code of weight j, two's complement.
+ *     bytes [m*k, m*k*17/16): scale plane, fp16 d of block (r, b) at
+ *       m*k + (r*k/32 + b)*2, little-endian.
+ *     Weight value: q * d. (The 8-bit format the technical summary's results
+ *     compare with q4_k_m and q2_k: "Experimental results", quantization
+ *     impact.)
  */
 #ifndef Q4_H
 #define Q4_H
@@ -56,9 +64,10 @@
 extern "C" {
 #endif
 
-/* Weight formats: legacy Q4_0 and the K-quant Q4_K (llama.cpp families the
- * technical summary names: problem statement item 3; q4_k_m in its results). */
-typedef enum { Q4_FMT_Q4_0 = 0, Q4_FMT_Q4_K = 1 } q4_format;
+/* Weight formats: legacy Q4_0 and Q8_0 and the K-quant Q4_K (llama.cpp
+ * families the technical summary names: problem statement item 3; q8_0 and
+ * q4_k_m in its results). */
+typedef enum { Q4_FMT_Q4_0 = 0, Q4_FMT_Q4_K = 1, Q4_FMT_Q8_0 = 2 } q4_format;
 
 /* Status codes. */
 enum {
@@ -72,8 +81,8 @@ enum {
 };
 
 /* Bytes of the quantized buffer for an m x k matrix; 0 if k is not a
- * positive multiple of the block (32 for Q4_0, 256 for Q4_K), m < 0, or the
- * format is unknown. Host only; no device work. */
+ * positive multiple of the block (32 for Q4_0 and Q8_0, 256 for Q4_K),
+ * m < 0, or the format is unknown. Host only; no device work. */
 size_t q4_weight_bytes(int fmt, int64_t m, int64_t k);
 
 /* Host quantizer: float32 W[m][k] (host memory) -> packed buffer `out`
@@ -85,6 +94,8 @@ size_t q4_weight_bytes(int fmt, int64_t m, int64_t k);
  *   d = fp16_rne(max s / 63), dmin = fp16_rne(max mu / 63);
  *   sc = clamp(round_half_away(s/d), 0, 63), mn = clamp(round_half_away(mu/dmin), 0, 63);
  *   q = clamp(round_half_away((w + dmin*mn)/(d*sc)), 0, 15) (0 where a divisor is 0).
+ * Q8_0 block: d = fp16_rne(max|w| / 127) (binary32 division); codes
+ *   q = clamp(round_half_away(w / d), -127, 127), all 0 when d == 0.
  * Blocks are quantized row by row; the status is that of the first failing
  * block in row-major order (Q4_ENONFINITE for NaN/Inf, Q4_ERANGE for a scale
  * that overflows fp16), and `out` is then unspecified.

@@ -92,6 +92,7 @@ __device__ __forceinline__ u32x4 eight(uint32_t n0, uint32_t n1, half2_t add, V 
 struct GemmQ4_0 {
     static constexpr int kFormat = Q4_FMT_Q4_0;
     static constexpr int kRingVgprs = 128;  // activation ring budget (Items are 3 VGPRs)
+    __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k / 2u); }
     struct Item {
         u32x2 q;     // 8 nibble bytes
         uint32_t d;  // fp16 scale bits
@@ -130,9 +131,49 @@ struct GemmQ4_0 {
     }
 };
 
+// Q8_0: an item is 16 consecutive weights of one block, half h = it & 1 of
+// block it / 2: code bytes 16h .. 16h+15 (elements lo .. lo+7 and hi .. hi+7,
+// hi = lo + 8). Codes become exact fp16 values by the byte-permute trick
+// (offset by 128 under the exponent of 1024, then -1152).
+struct GemmQ8_0 {
+    static constexpr int kFormat = Q4_FMT_Q8_0;
+    static constexpr int kRingVgprs = 64;  // activation ring budget (Items are 5 VGPRs)
+    __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k); }
+    struct Item {
+        u32x4 q;     // 16 code bytes
+        uint32_t d;  // fp16 scale bits
+    };
+    template <int KC>
+    __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+                                uint32_t row, bool row_ok, int s, int it)
+    {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
+        const uint32_t ub = static_cast<uint32_t>(s * (KC / 32) + (it >> 1));
+        const uint32_t blk = row * nu + ub;
+        const bool live = row_ok && ub < nu;
+        g.q = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, live ? blk * 32u + 16u * static_cast<uint32_t>(it & 1) : kNoFetch,
+                                                         0, 0));
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(r, live ? scale_plane + blk * 2u : kNoFetch, 0, 0);
+    }
+    __device__ static int lo(int it) { return 32 * (it >> 1) + 16 * (it & 1); }
+    __device__ static int hi(int it) { return lo(it) + 8; }
+    // q * d: exact in fp32 (8 + 11 significant bits); the only rounding is to bf16.
+    template <int KC>
+    __device__ static void dequant(const Item &g, int /*s*/, int /*it*/, u32x4 &vlo, u32x4 &vhi)
+    {
+        const float d = half_bits_to_float(g.d);
+        const half2_t add = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
+        const auto value = [d](_Float16 c) { return __builtin_fmaf(static_cast<float>(c), d, 0.0f); };
+        vlo = eight(g.q.x ^ 0x80808080u, g.q.y ^ 0x80808080u, add, value);
+        vhi = eight(g.q.z ^ 0x80808080u, g.q.w ^ 0x80808080u, add, value);
+    }
+};
+
 struct GemmQ4_K {
     static constexpr int kFormat = Q4_FMT_Q4_K;
     static constexpr int kRingVgprs = 64;  // activation ring budget (Items are 6 VGPRs)
+    __device__ static uint32_t scale_plane(uint64_t, uint64_t) { return 0; }  // headers are in the super-blocks
     struct Item {
         u32x2 q;  // 8 nibble bytes
         u32x4 h;  // super-block header: d, dmin, 12 scale bytes
@@ -212,7 +253,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ w
     const int r0 = blockIdx.x * TM;
     const int t0 = blockIdx.y * TN;
     const uint32_t nu = static_cast<uint32_t>(K / 32);
-    const uint32_t scale_plane = static_cast<uint32_t>(static_cast<uint64_t>(M) * static_cast<uint64_t>(K) / 2u);
+    const uint32_t scale_plane = F::scale_plane(static_cast<uint64_t>(M), static_cast<uint64_t>(K));
     const int C = (K + KC - 1) / KC;
     const __amdgpu_buffer_rsrc_t xr =
         make_rsrc(x, static_cast<uint32_t>(static_cast<uint64_t>(N) * static_cast<uint64_t>(K) * 2u));
@@ -383,6 +424,7 @@ int launch_gemm(int fmt, const void *w, const uint16_t *x, float *y, int64_t m, 
     if (cus <= 0) return Q4_EHIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (fmt == Q4_FMT_Q4_0) return gemm::launch_fmt<gemm::GemmQ4_0>(w, x, y, m, k, n, s, cus);
+    if (fmt == Q4_FMT_Q8_0) return gemm::launch_fmt<gemm::GemmQ8_0>(w, x, y, m, k, n, s, cus);
     return gemm::launch_fmt<gemm::GemmQ4_K>(w, x, y, m, k, n, s, cus);
 }
 
@@ -401,6 +443,7 @@ extern "C" int q4_gemm_tuned(int fmt, const void *w, const uint16_t *x_bf16, flo
     const int kc = tuning->stage_k ? tuning->stage_k : 256;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     if (fmt == Q4_FMT_Q4_0) return q4::gemm::launch_geometry<q4::gemm::GemmQ4_0>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
+    if (fmt == Q4_FMT_Q8_0) return q4::gemm::launch_geometry<q4::gemm::GemmQ8_0>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
     return q4::gemm::launch_geometry<q4::gemm::GemmQ4_K>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
 }
 

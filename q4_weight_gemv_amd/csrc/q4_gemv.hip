@@ -53,6 +53,7 @@ namespace gemv {
 //     64 lanes per row; longer rows -> 4 waves, 32 lanes x 2 rows.
 //   Q4_0, several tokens: 4 waves; 64 lanes per row for 33..127 units, else
 //     32 lanes x 2 rows.
+//   Q8_0: the Q4_0 choices (same unit of 32 weights, twice the bytes).
 //   Q4_K: 4 waves of 64 lanes per row for 33..127 units. Short rows: 16
 //     lanes per row, one-wave groups at 1..2 tokens, 4 waves at 3..4, and 32
 //     lanes x 2 rows from 5 tokens. Rows of 256 units or more: 8-wave groups
@@ -63,7 +64,7 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 {
     (void)cus;
     const int64_t nu = k / kUnitWeights;
-    if (fmt == Q4_FMT_Q4_0) {
+    if (fmt == Q4_FMT_Q4_0 || fmt == Q4_FMT_Q8_0) {
         if (n == 1) {
             if (nu <= 32) return m >= 16384 ? Cfg{8, 1, 1, 8} : Cfg{32, 2, 1, 8};
             if (nu < 128) return Cfg{64, 1, 4, 4};
@@ -112,6 +113,13 @@ int dispatch(int fmt, const Cfg &c, const void *w, const float *x, float *y, int
         default: return Q4_EUNSUPPORTED;
         }
     }
+    if (fmt == Q4_FMT_Q8_0) {
+        switch (n) {
+            Q4_N_CASE(FmtQ8_0, 1) Q4_N_CASE(FmtQ8_0, 2) Q4_N_CASE(FmtQ8_0, 3) Q4_N_CASE(FmtQ8_0, 4)
+            Q4_N_CASE(FmtQ8_0, 5) Q4_N_CASE(FmtQ8_0, 6) Q4_N_CASE(FmtQ8_0, 7) Q4_N_CASE(FmtQ8_0, 8)
+        default: return Q4_EUNSUPPORTED;
+        }
+    }
     switch (n) {
         Q4_N_CASE(FmtQ4_K, 1) Q4_N_CASE(FmtQ4_K, 2) Q4_N_CASE(FmtQ4_K, 3) Q4_N_CASE(FmtQ4_K, 4)
         Q4_N_CASE(FmtQ4_K, 5) Q4_N_CASE(FmtQ4_K, 6) Q4_N_CASE(FmtQ4_K, 7) Q4_N_CASE(FmtQ4_K, 8)
@@ -148,8 +156,8 @@ int check_glu_args(int fmt, const void *w, const void *x, const float *y, int64_
 int check_product_args(int fmt, const void *w, const void *x, const float *y, int64_t m, int64_t k, int64_t n,
                        int64_t n_max)
 {
-    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K) return Q4_EUNSUPPORTED;
-    const int64_t blk = fmt == Q4_FMT_Q4_0 ? 32 : 256;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0) return Q4_EUNSUPPORTED;
+    const int64_t blk = fmt == Q4_FMT_Q4_K ? 256 : 32;
     if (m < 0 || k <= 0 || k % blk != 0 || n < 0) return Q4_EINVAL;
     if (n > n_max) return Q4_EUNSUPPORTED;
     if (m == 0 || n == 0) return Q4_OK;

@@ -174,6 +174,7 @@ struct FmtQ4_0 {
     static constexpr int kHighOffset = 16;
     static constexpr int kBatchUnits = 4;  // units (x rows) per lane per batch: 4 x 20 B in flight
     __device__ static int unit_base(int u) { return u << 5; }
+    __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k / 2u); }
 
     struct Regs {
         u32x4 q;
@@ -224,10 +225,101 @@ struct FmtQ4_0 {
     }
 };
 
+// Q8_0 codes as exact fp16 pairs: a byte permute places two code bytes
+// (offset by 128, so 0..255) under the exponent byte E, and one packed add
+// removes the offset. E = 0x64 gives 1024 + u (spacing 1), so adding -1152
+// leaves the code q; E = 0x74 gives 16384 + 16u (spacing 16), so adding
+// -18432 leaves 16q. Both exact.
+template <uint32_t E, int S>
+__device__ __forceinline__ uint32_t q8_pair(uint32_t u)
+{
+    // Bytes {S, E, S+2, E}: the codes of elements S and S+2 of the dword.
+    constexpr uint32_t sel = S == 0 ? 0x04020400u : 0x04030401u;
+    const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(E * 0x01010101u, u, sel));
+    constexpr float off = E == 0x64u ? -1152.0f : -18432.0f;
+    return __builtin_bit_cast(uint32_t, h + half2_t{static_cast<_Float16>(off), static_cast<_Float16>(off)});
+}
+
+// Q8_0: a unit is one block, 32 code bytes (elements in order) and an fp16
+// scale in the scale plane. The activations are staged as for Q4_0 (pairs
+// (L, L+2), (H, H+2)/16, (L+1, L+3), (H+1, H+3)/16, H = L + 16), so the codes
+// of the block's second half enter as 16q.
+struct FmtQ8_0 {
+    static constexpr int kFormat = Q4_FMT_Q8_0;
+    static constexpr int kHighOffset = 16;
+    static constexpr int kBatchUnits = 2;  // each unit is two 16-byte loads and a scale
+    __device__ static int unit_base(int u) { return u << 5; }
+    __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k); }
+
+    struct Regs {
+        u32x4 q0, q1;  // code bytes 0..15 and 16..31
+        uint32_t d;
+    };
+    // Unit (row, u), row = trow + rowrel, u = ubase + li + jl: its 32 code
+    // bytes at (row*nu + u)*32, its scale at scale_plane + (row*nu + u)*2.
+    __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+                                uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl, bool live)
+    {
+        const uint32_t uni_u = trow * nu + ubase;
+        const uint32_t lane_u = rowrel * nu + li + jl;
+        const __amdgpu_buffer_rsrc_t r = sub_rsrc(w, wbytes, uni_u * 32u);
+        const uint32_t off = live ? lane_u * 32u : kNoFetch;
+        g.q0 = load16<kNonTemporal>(r, off, 0);
+        g.q1 = load16<kNonTemporal>(r, off + 16u, 0);
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(sub_rsrc(w, wbytes, scale_plane + uni_u * 2u),
+                                                   live ? lane_u * 2u : kNoFetch, 0, 0);
+    }
+    // Unit metadata: z = 2^e (the unit's activation scale; the codes are
+    // integers).
+    __device__ static f32x4 meta(float /*gl*/, float /*gh*/, int e)
+    {
+        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e), 0.0f};
+    }
+    template <int N, int R, bool LO>
+    __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
+                                      const f32x4 *__restrict__ meta, int ul, int uc, uint32_t /*u*/,
+                                      float (&acc)[R][N])
+    {
+#pragma unroll
+        for (int t = 0; t < N; t++) {
+            const f32x4 mt = meta[t * uc + ul];
+            u32x4 xh[4], xl[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                xh[i] = xs[(t * 8 + 2 * i) * uc + ul];
+                xl[i] = LO ? xs[(t * 8 + 2 * i + 1) * uc + ul] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const uint32_t lo = (i == 0 ? g[r].q0.x : i == 1 ? g[r].q0.y : i == 2 ? g[r].q0.z : g[r].q0.w) ^ 0x80808080u;
+                    const uint32_t hi = (i == 0 ? g[r].q1.x : i == 1 ? g[r].q1.y : i == 2 ? g[r].q1.z : g[r].q1.w) ^ 0x80808080u;
+                    const uint32_t p0 = q8_pair<0x64u, 0>(lo), p2 = q8_pair<0x64u, 1>(lo);
+                    const uint32_t p1 = q8_pair<0x74u, 0>(hi), p3 = q8_pair<0x74u, 1>(hi);
+                    a = dot2(p0, xh[i].x, a);
+                    a = dot2(p1, xh[i].y, a);
+                    a = dot2(p2, xh[i].z, a);
+                    a = dot2(p3, xh[i].w, a);
+                    if constexpr (LO) {
+                        a = dot2(p0, xl[i].x, a);
+                        a = dot2(p1, xl[i].y, a);
+                        a = dot2(p2, xl[i].z, a);
+                        a = dot2(p3, xl[i].w, a);
+                    }
+                }
+                acc[r][t] = __builtin_fmaf(half_lo(g[r].d) * mt.z, a, acc[r][t]);
+            }
+        }
+    }
+};
+
 struct FmtQ4_K {
     static constexpr int kFormat = Q4_FMT_Q4_K;
     static constexpr int kHighOffset = 32;
     static constexpr int kBatchUnits = 2;  // each unit is two 16-byte loads
+    __device__ static uint32_t scale_plane(uint64_t, uint64_t) { return 0; }  // headers are in the super-blocks
     // unit u = slice (u & 7) of super-block u >> 3; slice h covers the 16
     // bytes at 16h of the 128 nibble bytes: chunk c = h >> 1, half h & 1.
     __device__ static int unit_base(int u) { return ((u >> 3) << 8) + (((u & 7) >> 1) << 6) + ((u & 1) << 4); }
@@ -522,7 +614,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     const int li = lane % LPR;
     const int nu = K >> 5;
     const uint64_t wrows = GLU ? 2ull * static_cast<uint64_t>(M) : static_cast<uint64_t>(M);
-    const uint32_t scale_plane = static_cast<uint32_t>(wrows * static_cast<uint64_t>(K) / 2u);
+    const uint32_t scale_plane = F::scale_plane(wrows, static_cast<uint64_t>(K));
     // Output row of slot r (an output slot for the stores, a weight-row slot
     // for the loads: for GLU, slots 2p and 2p+1 share output slot p).
     const int out_in_tile = wave * (RPW / (GLU ? 2 : 1)) + sub;

@@ -67,6 +67,35 @@ int q4_0_row(const float *wr, int64_t nb, uint8_t *nib_row, uint8_t *scale_row, 
     return Q4_OK;
 }
 
+// ---- Q8_0 -----------------------------------------------------------------
+
+// Quantize row r of a Q8_0 matrix into the code and scale planes.
+int q8_0_row(const float *wr, int64_t nb, uint8_t *code_row, uint8_t *scale_row, int64_t *bad)
+{
+    for (int64_t b = 0; b < nb; b++) {
+        const float *v = wr + 32 * b;
+        float amax = 0.0f;
+        bool finite = true;
+        for (int i = 0; i < 32; i++) {
+            finite = finite && std::isfinite(v[i]);
+            amax = std::max(amax, std::fabs(v[i]));
+        }
+        if (!finite) { *bad = b; return Q4_ENONFINITE; }
+        _Float16 dh = static_cast<_Float16>(amax / 127.0f);
+        if (!half_is_finite(dh)) { *bad = b; return Q4_ERANGE; }
+        const double d = static_cast<double>(static_cast<float>(dh));
+        for (int i = 0; i < 32; i++) {
+            // code_of clamps to [0, 254] around the bias 127: codes -127..127.
+            const int q = d == 0.0 ? 0 : code_of(v[i] / d, 127, 254) - 127;
+            code_row[32 * b + i] = static_cast<uint8_t>(static_cast<int8_t>(q));
+        }
+        const uint16_t bits = half_bits(dh);
+        scale_row[2 * b] = static_cast<uint8_t>(bits);
+        scale_row[2 * b + 1] = static_cast<uint8_t>(bits >> 8);
+    }
+    return Q4_OK;
+}
+
 // ---- Q4_K -----------------------------------------------------------------
 
 inline void pack_6bit(const uint8_t sc[8], const uint8_t mn[8], uint8_t S[12])
@@ -174,14 +203,15 @@ size_t q4_weight_bytes(int fmt, int64_t m, int64_t k)
     if (m < 0 || k <= 0) return 0;
     if (fmt == Q4_FMT_Q4_0) return k % 32 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 32) * 18u;
     if (fmt == Q4_FMT_Q4_K) return k % 256 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 256) * 144u;
+    if (fmt == Q4_FMT_Q8_0) return k % 32 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 32) * 34u;
     return 0;
 }
 
 int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, size_t out_bytes)
 {
-    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K) return Q4_EUNSUPPORTED;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0) return Q4_EUNSUPPORTED;
     const size_t need = q4_weight_bytes(fmt, m, k);
-    if (need == 0 && !(m == 0 && k > 0 && k % (fmt == Q4_FMT_Q4_0 ? 32 : 256) == 0)) return Q4_EINVAL;
+    if (need == 0 && !(m == 0 && k > 0 && k % (fmt == Q4_FMT_Q4_K ? 256 : 32) == 0)) return Q4_EINVAL;
     if (m == 0) return Q4_OK;
     if (!w || !out || out_bytes < need) return Q4_EINVAL;
     uint8_t *o = static_cast<uint8_t *>(out);
@@ -191,6 +221,14 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
         uint8_t *scl = o + static_cast<size_t>(m) * static_cast<size_t>(k) / 2;
         return for_rows(m, nb, [&](int64_t r, int64_t *bad) {
             return q4_0_row(w + r * k, nb, nib + r * nb * 16, scl + r * nb * 2, bad);
+        });
+    }
+    if (fmt == Q4_FMT_Q8_0) {
+        const int64_t nb = k / 32;
+        uint8_t *codes = o;
+        uint8_t *scl = o + static_cast<size_t>(m) * static_cast<size_t>(k);
+        return for_rows(m, nb, [&](int64_t r, int64_t *bad) {
+            return q8_0_row(w + r * k, nb, codes + r * nb * 32, scl + r * nb * 2, bad);
         });
     }
     const int64_t ns = k / 256;

@@ -44,7 +44,8 @@ def _quantize_both(q4, orc, fmt, w):
     return buf
 
 
-@pytest.mark.parametrize("fmt,m,k", [(0, 37, 96), (0, 130, 960), (0, 64, 2560), (1, 37, 256), (1, 96, 1024)])
+@pytest.mark.parametrize("fmt,m,k", [(0, 37, 96), (0, 130, 960), (0, 64, 2560), (1, 37, 256), (1, 96, 1024),
+                                     (2, 37, 96), (2, 130, 960)])
 def test_identity_gives_bf16_weights_exactly(env, fmt, m, k):
     torch, q4, orc = env
     buf = _quantize_both(q4, orc, fmt, synth.weights(synth.seed_for(30 + fmt, m), m, k))
@@ -73,6 +74,7 @@ def _parity(env, fmt, m, k, n, seed, rows=None):
 @pytest.mark.parametrize("fmt,m,k,n", [
     (0, 1, 32, 1), (0, 37, 96, 5), (0, 100, 320, 130), (0, 33, 960, 64), (0, 257, 2560, 200),
     (1, 1, 256, 3), (1, 70, 512, 70), (1, 130, 1024, 257),
+    (2, 1, 32, 1), (2, 100, 320, 130), (2, 257, 2560, 200),
 ])
 def test_parity_small(env, fmt, m, k, n):
     _parity(env, fmt, m, k, n, seed=600 + n)
@@ -88,6 +90,11 @@ def test_parity_q4_k_512_tokens(env, k, m):
     _parity(env, 1, m, k, 512, seed=800, rows=sample_rows(m, k, edge=64, rand=48))
 
 
+@pytest.mark.parametrize("k,m", [(960, 960), (2560, 960)])
+def test_parity_q8_0_512_tokens(env, k, m):
+    _parity(env, 2, m, k, 512, seed=850, rows=sample_rows(m, k, edge=64, rand=48))
+
+
 def _tiles():
     import q4_weight_gemv_amd as q4
 
@@ -95,7 +102,7 @@ def _tiles():
 
 
 @pytest.mark.parametrize("tile", _tiles(), ids=lambda t: f"{t[0]}x{t[1]}x{t[2]}")
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 2])
 def test_parity_every_tile(env, fmt, tile):
     """Every instantiated tile through q4_gemm_tuned: 70 rows and 100 tokens
     (ragged in both), K = 1280 (a partial last chunk for every chunk size)."""

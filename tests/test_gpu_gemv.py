@@ -49,6 +49,7 @@ def _gemv(env, fmt, buf, x, m, k):
 ONEHOT_CASES = [
     (0, 5, 32), (0, 37, 320), (0, 768, 768), (0, 129, 2560), (0, 300, 4096), (0, 70, 11008),
     (1, 5, 256), (1, 37, 512), (1, 130, 1024), (1, 300, 4096), (1, 70, 11008),
+    (2, 5, 32), (2, 37, 320), (2, 768, 768), (2, 300, 4096), (2, 70, 11008),
 ]
 
 
@@ -114,7 +115,7 @@ def _geometries():
 
 
 @pytest.mark.parametrize("geom", _geometries(), ids=_geometry_ids())
-@pytest.mark.parametrize("fmt,n", [(0, 1), (0, 8), (1, 1), (1, 8)])
+@pytest.mark.parametrize("fmt,n", [(0, 1), (0, 8), (1, 1), (1, 8), (2, 1), (2, 8)])
 def test_parity_every_geometry(env, fmt, n, geom):
     """Every instantiated tile geometry through q4_gemv_tuned: 600 ragged rows
     (a grid-stride loop for the short tiles at one group per compute unit) and
@@ -162,6 +163,40 @@ def test_parity_q4_k_7b(env, k, m, n):
 @pytest.mark.parametrize("n", [4, 8])
 def test_parity_q4_0_7b_batched(env, k, m, n):
     _parity(env, 0, m, k, n, seed=500 + n, rows=sample_rows(m, n))
+
+
+SMALL_Q8_0 = [(1, 32), (37, 320), (130, 768), (257, 960), (300, 4096), (77, 11008), (2049, 768)]
+
+
+@pytest.mark.parametrize("m,k", SMALL_Q8_0)
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_parity_q8_0_small(env, m, k, n):
+    _parity(env, 2, m, k, n, seed=150 + n)
+
+
+@pytest.mark.parametrize("k,m", synth.llama7b_layer()[:2] + synth.llama7b_layer()[3:])
+@pytest.mark.parametrize("n", [1, 8])
+def test_parity_q8_0_7b(env, k, m, n):
+    _parity(env, 2, m, k, n, seed=450 + n, rows=sample_rows(m, k + n))
+
+
+def test_q8_0_extreme_codes(env):
+    # Hand-built Q8_0 blocks with every code -128..127 (a code of -128 is legal
+    # input though the quantizer never writes it) and mixed scales: one-hot x
+    # returns each dequantized weight exactly.
+    torch, q4, orc = env
+    m, k = 8, 256
+    codes = (np.arange(m * k) % 256).astype(np.uint8).reshape(m * k)
+    d = np.array([0.5, 0.0078125, 3.0, 1.5e-5] * (m * k // 32 // 4), np.float16)
+    buf = np.concatenate([codes, d.view(np.uint8)])
+    assert buf.size == q4.q4_weight_bytes(2, m, k)
+    what = orc.dequantize(2, buf, m, k)
+    for c0 in range(0, k, 8):
+        x = np.zeros((8, k), np.float32)
+        for t in range(8):
+            x[t, c0 + t] = 1.0
+        y = _gemv(env, 2, buf, x, m, k)
+        assert np.array_equal(y, what[:, c0:c0 + 8].T), c0
 
 
 def test_zero_rows_and_tokens_are_noops(env):
@@ -304,6 +339,7 @@ def _silu_mul64(g, u):
 GLU_CASES = [
     (0, 1, 37, 96), (0, 3, 130, 960), (0, 1, 1280, 960), (0, 8, 200, 2560), (0, 1, 300, 4096), (0, 2, 70, 11008),
     (1, 1, 37, 256), (1, 4, 130, 1024), (1, 1, 300, 4096), (1, 8, 90, 4096), (1, 1, 70, 11008),
+    (2, 1, 130, 960), (2, 4, 300, 4096),
 ]
 
 

@@ -56,6 +56,10 @@ def test_weight_bytes(q4):
     assert total == 203_489_280
     total = sum(q4.q4_weight_bytes(1, m, k) for k, m in synth.llama7b_layer())
     assert total == 85_524_480
+    # Q8_0: 34 bytes per 32 weights, k a multiple of 32.
+    assert q4.q4_weight_bytes(2, 4096, 4096) == 4096 * 4096 * 34 // 32
+    assert q4.q4_weight_bytes(2, 3, 33) == 0
+    assert q4.q4_weight_bytes(2, 5, 96) == 5 * 3 * 34
 
 
 SHAPES = sorted(set(synth.gpt2_124m_step() + synth.smollm2_360m_step() + synth.llama7b_layer()))
@@ -73,6 +77,12 @@ def test_quantize_ref_matches_oracle_q4_k(q4, orc, k, m):
         k = 1024
     w = synth.weights(synth.seed_for(8, k % 97 + m % 89), m, k)
     assert np.array_equal(q4.q4_quantize_ref(1, w), orc.quantize(1, w))
+
+
+@pytest.mark.parametrize("k,m", [(768, 768), (960, 320), (4096, 512), (11008, 96)])
+def test_quantize_ref_matches_oracle_q8_0(q4, orc, k, m):
+    w = synth.weights(synth.seed_for(7, k % 97 + m % 89), m, k)
+    assert np.array_equal(q4.q4_quantize_ref(2, w), orc.quantize(2, w))
 
 
 def _edge_matrix(k):
@@ -94,12 +104,18 @@ def _edge_matrix(k):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1, 2])
 def test_quantize_ref_matches_oracle_edges(q4, orc, fmt):
     w = _edge_matrix(512)
     assert np.array_equal(q4.q4_quantize_ref(fmt, w), orc.quantize(fmt, w))
-    # Golden blocks (Q4_0) through the product quantizer too.
-    if fmt == 0:
+    # Golden blocks through the product quantizer too.
+    if fmt == 2:
+        from golden import floats, hexbytes, load
+        for name, sec in load("q8_0_blocks.txt").items():
+            buf = q4.q4_quantize_ref(2, floats(sec["w"][0]).reshape(1, 32))
+            assert bytes(buf[:32]) == hexbytes(sec["codes"][0]), name
+            assert int(buf[32]) | (int(buf[33]) << 8) == int(sec["d_bits"][0], 16), name
+    elif fmt == 0:
         from golden import floats, load
         for name, sec in load("q4_0_blocks.txt").items():
             buf = q4.q4_quantize_ref(0, floats(sec["w"][0]).reshape(1, 32))
@@ -124,7 +140,7 @@ def test_quantize_ref_status(q4, orc):
     w3 = w.copy()
     w3[10, 0] = 1e9
     w3[11, 0] = np.inf
-    for fmt in (0, 1):
+    for fmt in (0, 1, 2):
         with pytest.raises(q4.Q4Error) as e:
             q4.q4_quantize_ref(fmt, w3)
         assert e.value.status == q4.Q4_ERANGE
@@ -172,6 +188,8 @@ def test_product_argument_errors(q4, entry):
     assert f(0, *ok, 1 << 30, 1 << 10, 1, None) == q4.Q4_EUNSUPPORTED  # beyond 32-bit offsets
     assert f(0, *ok, 1 << 20, 4096, 1, None) == q4.Q4_EUNSUPPORTED    # weights of 2 GiB or more
     assert f(1, *ok, 1 << 20, 4096, 1, None) == q4.Q4_EUNSUPPORTED
+    assert f(2, *ok, 64, 48, 1, None) == q4.Q4_EINVAL                 # Q8_0: k a multiple of 32
+    assert f(2, *ok, 1 << 19, 4096, 1, None) == q4.Q4_EUNSUPPORTED    # Q8_0 weights of 2 GiB or more
     if entry == "q4_gemv":
         assert f(0, *ok, 64, 256, 9, None) == q4.Q4_EUNSUPPORTED       # decode batch is 1..8
 
@@ -224,7 +242,7 @@ def test_gated_product_argument_errors(q4):
     assert f(0, *ok, 64, 48, 1, None) == q4.Q4_EINVAL              # k not a multiple of 32
     assert f(1, *ok, 64, 288, 1, None) == q4.Q4_EINVAL             # Q4_K: k not a multiple of 256
     assert f(0, *ok, 64, 256, 9, None) == q4.Q4_EUNSUPPORTED       # tokens beyond 8
-    assert f(2, *ok, 64, 256, 1, None) == q4.Q4_EUNSUPPORTED       # unknown format
+    assert f(9, *ok, 64, 256, 1, None) == q4.Q4_EUNSUPPORTED       # unknown format
     assert f(0, *ok, 1 << 29, 256, 1, None) == q4.Q4_EUNSUPPORTED  # 2m rows beyond the offset range
     assert f(0, A16 + 8, A16, A16, 64, 256, 1, None) == q4.Q4_EALIGN
     assert f(0, None, A16, A16, 64, 256, 1, None) == q4.Q4_EINVAL
