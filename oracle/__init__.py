@@ -23,6 +23,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 Q4_0 = 0
 Q4_K = 1
 Q8_0 = 2
+Q2_K = 3
 
 OK, EINVAL, ENONFINITE, ERANGE = 0, -1, -4, -5
 
@@ -64,6 +65,9 @@ def lib():
                 "oracle_q4_0_bytes": (ctypes.c_size_t, [_i64, _i64]),
                 "oracle_q4_k_bytes": (ctypes.c_size_t, [_i64, _i64]),
                 "oracle_q8_0_bytes": (ctypes.c_size_t, [_i64, _i64]),
+                "oracle_q2_k_bytes": (ctypes.c_size_t, [_i64, _i64]),
+                "oracle_q2_k_quantize": (ctypes.c_int, [_f32p, _i64, _i64, _u8p]),
+                "oracle_q2_k_dequantize": (None, [_u8p, _i64, _i64, _f32p]),
                 "oracle_q8_0_quantize_block": (ctypes.c_int, [_f32p, ctypes.POINTER(ctypes.c_int8), _u16p]),
                 "oracle_q8_0_quantize": (ctypes.c_int, [_f32p, _i64, _i64, _u8p]),
                 "oracle_q8_0_dequantize": (None, [_u8p, _i64, _i64, _f32p]),
@@ -126,7 +130,8 @@ def bf16_to_fp32(b: int) -> float:
 
 def weight_bytes(fmt: int, m: int, k: int) -> int:
     L = lib()
-    return {Q4_0: L.oracle_q4_0_bytes, Q4_K: L.oracle_q4_k_bytes, Q8_0: L.oracle_q8_0_bytes}[fmt](m, k)
+    return {Q4_0: L.oracle_q4_0_bytes, Q4_K: L.oracle_q4_k_bytes, Q8_0: L.oracle_q8_0_bytes,
+            Q2_K: L.oracle_q2_k_bytes}[fmt](m, k)
 
 
 def quantize(fmt: int, w: np.ndarray) -> np.ndarray:
@@ -135,7 +140,8 @@ def quantize(fmt: int, w: np.ndarray) -> np.ndarray:
     m, k = w.shape
     out = np.zeros(weight_bytes(fmt, m, k), dtype=np.uint8)
     L = lib()
-    fn = {Q4_0: L.oracle_q4_0_quantize, Q4_K: L.oracle_q4_k_quantize, Q8_0: L.oracle_q8_0_quantize}[fmt]
+    fn = {Q4_0: L.oracle_q4_0_quantize, Q4_K: L.oracle_q4_k_quantize, Q8_0: L.oracle_q8_0_quantize,
+          Q2_K: L.oracle_q2_k_quantize}[fmt]
     st = fn(_p(w, _f32p), m, k, _p(out, _u8p))
     if st != OK:
         raise OracleError(st)
@@ -170,7 +176,8 @@ def dequantize(fmt: int, buf: np.ndarray, m: int, k: int) -> np.ndarray:
     assert buf.size == weight_bytes(fmt, m, k)
     out = np.empty((m, k), dtype=np.float32)
     L = lib()
-    fn = {Q4_0: L.oracle_q4_0_dequantize, Q4_K: L.oracle_q4_k_dequantize, Q8_0: L.oracle_q8_0_dequantize}[fmt]
+    fn = {Q4_0: L.oracle_q4_0_dequantize, Q4_K: L.oracle_q4_k_dequantize, Q8_0: L.oracle_q8_0_dequantize,
+          Q2_K: L.oracle_q2_k_dequantize}[fmt]
     fn(_p(buf, _u8p), m, k, _p(out, _f32p))
     return out
 

@@ -19,6 +19,9 @@
  *   - Q4_K (the K-quant family named by q4_k_m in the summary's results):
  *     256-weight super-blocks of eight 32-weight sub-blocks, each with a 6-bit
  *     scale and a 6-bit min, plus fp16 d and dmin; value d*sc*q - dmin*m.
+ *   - Q2_K (the summary's q2_k): 256-weight super-blocks of sixteen 16-weight
+ *     sub-blocks with 4-bit scales and mins, fp16 d and dmin, 2-bit codes;
+ *     value d*sc*q - dmin*m.
  *   - Q8_0 (the q8_0 the summary's results compare with q4_k_m and q2_k):
  *     blocks of 32 weights, an fp16 scale d = max|w| / 127, codes q in
  *     [-127, 127] stored as bytes, value q * d.
@@ -312,6 +315,115 @@ void oracle_q8_0_dequantize(const uint8_t *buf, int64_t m, int64_t k, float *w_h
 }
 
 /* ------------------------------------------------------------------------
+ * Q2_K (llama.cpp's 2-bit K-quant, the q2_k of the technical summary's
+ * results): 256-weight super-blocks of sixteen 16-weight sub-blocks; per
+ * sub-block a 4-bit scale sc and a 4-bit min m (one byte: sc low nibble,
+ * m high nibble); per super-block fp16 d and dmin; 2-bit codes q; value
+ * d*sc*q - dmin*m. The same fields as llama.cpp's 84-byte block, stored in
+ * three planes so that every field is naturally aligned:
+ *   bytes [0, m*k/4)                code plane: super-block (r, s) at
+ *       (r*ns + s)*64; the code of its element e is bits 2j, 2j+1 of byte
+ *       32*(e/128) + e%32, j = (e%128)/32 (llama.cpp's order);
+ *   bytes [m*k/4, m*k*5/16)         scale plane: byte e/16 of super-block
+ *       (r, s) at m*k/4 + (r*ns + s)*16;
+ *   bytes [m*k*5/16, m*k*21/64)     fp16 d then fp16 dmin of super-block
+ *       (r, s) at m*k*5/16 + (r*ns + s)*4, little-endian.
+ * ------------------------------------------------------------------------ */
+
+size_t oracle_q2_k_bytes(int64_t m, int64_t k) { return (size_t)(m * (k / 256)) * 84u; }
+
+/* Min/max quantizer for one super-block, in float64 (the Q4_K reading with
+ * 2-bit codes and 4-bit scales):
+ *   per 16-weight sub-block: lo = min(0, min w), hi = max w, s = (hi - lo)/3, mu = -lo
+ *   d = fp16(max s / 15), dmin = fp16(max mu / 15)
+ *   sc = clamp(round(s/d), 0, 15), m = clamp(round(mu/dmin), 0, 15)
+ *   q = clamp(round((w + dmin*m) / (d*sc)), 0, 3)   (0 where a divisor is 0)
+ * Writes the 64 code bytes, 16 scale bytes and 4 bytes of d, dmin. */
+int oracle_q2_k_quantize_superblock(const float *w, uint8_t *codes, uint8_t *scales, uint8_t *dd)
+{
+    double s[16], mu[16];
+    double smax = 0.0, mumax = 0.0;
+    for (int i = 0; i < 256; i++)
+        if (!isfinite(w[i])) return ORACLE_ENONFINITE;
+    for (int j = 0; j < 16; j++) {
+        double lo = 0.0, hi = (double)w[16 * j];
+        for (int i = 0; i < 16; i++) {
+            double v = (double)w[16 * j + i];
+            if (v < lo) lo = v;
+            if (v > hi) hi = v;
+        }
+        s[j] = (hi - lo) / 3.0;
+        mu[j] = -lo;
+        if (s[j] > smax) smax = s[j];
+        if (mu[j] > mumax) mumax = mu[j];
+    }
+    uint16_t dh = oracle_f64_to_fp16(smax / 15.0);
+    uint16_t mh = oracle_f64_to_fp16(mumax / 15.0);
+    if ((dh & 0x7C00) == 0x7C00 || (mh & 0x7C00) == 0x7C00) return ORACLE_ERANGE;
+    double d = (double)oracle_fp16_to_fp32(dh);
+    double dmin = (double)oracle_fp16_to_fp32(mh);
+    int sc[16], mn[16];
+    for (int j = 0; j < 16; j++) {
+        sc[j] = d == 0.0 ? 0 : clampi((int)round_half_away(s[j] / d), 0, 15);
+        mn[j] = dmin == 0.0 ? 0 : clampi((int)round_half_away(mu[j] / dmin), 0, 15);
+        scales[j] = (uint8_t)(sc[j] | (mn[j] << 4));
+    }
+    for (int b = 0; b < 64; b++) codes[b] = 0;
+    for (int e = 0; e < 256; e++) {
+        int j = e / 16;
+        double step = d * (double)sc[j];
+        double off = dmin * (double)mn[j];
+        int q = step == 0.0 ? 0 : clampi((int)round_half_away(((double)w[e] + off) / step), 0, 3);
+        codes[32 * (e / 128) + e % 32] |= (uint8_t)(q << (2 * ((e % 128) / 32)));
+    }
+    dd[0] = (uint8_t)(dh & 0xFF);
+    dd[1] = (uint8_t)(dh >> 8);
+    dd[2] = (uint8_t)(mh & 0xFF);
+    dd[3] = (uint8_t)(mh >> 8);
+    return ORACLE_OK;
+}
+
+int oracle_q2_k_quantize(const float *w, int64_t m, int64_t k, uint8_t *out)
+{
+    if (m < 0 || k <= 0 || k % 256 != 0) return ORACLE_EINVAL;
+    int64_t ns = k / 256;
+    uint8_t *scales = out + (size_t)(m * k / 4);
+    uint8_t *dd = out + (size_t)(m * k / 4 + m * k / 16);
+    for (int64_t r = 0; r < m; r++)
+        for (int64_t sb = 0; sb < ns; sb++) {
+            int64_t i = r * ns + sb;
+            int st = oracle_q2_k_quantize_superblock(w + r * k + sb * 256, out + i * 64, scales + i * 16, dd + i * 4);
+            if (st != ORACLE_OK) return st;
+        }
+    return ORACLE_OK;
+}
+
+/* Dequantized weight (r, c): (d*sc)*q - dmin*m in binary32; both products are
+ * exact (at most 17 and 15 significant bits), the subtraction rounds once. */
+float oracle_q2_k_weight(const uint8_t *buf, int64_t m, int64_t k, int64_t r, int64_t c)
+{
+    int64_t ns = k / 256;
+    int64_t i = r * ns + c / 256;
+    int e = (int)(c % 256);
+    uint8_t byte = buf[i * 64 + 32 * (e / 128) + e % 32];
+    int q = (byte >> (2 * ((e % 128) / 32))) & 3;
+    uint8_t scm = buf[(size_t)(m * k / 4) + i * 16 + e / 16];
+    const uint8_t *dd = buf + (size_t)(m * k / 4 + m * k / 16) + i * 4;
+    float d = oracle_fp16_to_fp32((uint16_t)(dd[0] | (dd[1] << 8)));
+    float dmin = oracle_fp16_to_fp32((uint16_t)(dd[2] | (dd[3] << 8)));
+    float a = (d * (float)(scm & 15)) * (float)q;
+    float b = dmin * (float)(scm >> 4);
+    return a - b;
+}
+
+void oracle_q2_k_dequantize(const uint8_t *buf, int64_t m, int64_t k, float *w_hat)
+{
+    for (int64_t r = 0; r < m; r++)
+        for (int64_t c = 0; c < k; c++)
+            w_hat[r * k + c] = oracle_q2_k_weight(buf, m, k, r, c);
+}
+
+/* ------------------------------------------------------------------------
  * Q4_K.  Buffer: m * (k/256) super-blocks of 144 bytes, row-major:
  *   [0,2) fp16 d   [2,4) fp16 dmin   [4,16) twelve bytes S holding eight
  *   6-bit scales and eight 6-bit mins   [16,144) 128 nibble bytes.
@@ -462,6 +574,7 @@ static float weight_at(int fmt, const uint8_t *w, int64_t m, int64_t k, int64_t 
 {
     if (fmt == 0) return oracle_q4_0_weight(w, m, k, r, c);
     if (fmt == 2) return oracle_q8_0_weight(w, m, k, r, c);
+    if (fmt == 3) return oracle_q2_k_weight(w, m, k, r, c);
     return oracle_q4_k_weight(w, m, k, r, c);
 }
 
@@ -528,6 +641,16 @@ static double term_magnitude(int fmt, const uint8_t *w, int64_t m, int64_t k, in
 {
     if (fmt == 0) return fabs((double)oracle_q4_0_weight(w, m, k, r, c));
     if (fmt == 2) return fabs((double)oracle_q8_0_weight(w, m, k, r, c));
+    if (fmt == 3) {
+        int64_t i = r * (k / 256) + c / 256;
+        int e = (int)(c % 256);
+        int q = (w[i * 64 + 32 * (e / 128) + e % 32] >> (2 * ((e % 128) / 32))) & 3;
+        uint8_t scm = w[(size_t)(m * k / 4) + i * 16 + e / 16];
+        const uint8_t *dd = w + (size_t)(m * k / 4 + m * k / 16) + i * 4;
+        double d = oracle_fp16_to_fp32((uint16_t)(dd[0] | (dd[1] << 8)));
+        double dmin = oracle_fp16_to_fp32((uint16_t)(dd[2] | (dd[3] << 8)));
+        return fabs(d * (scm & 15) * q) + fabs(dmin * (scm >> 4));
+    }
     int64_t ns = k / 256;
     const uint8_t *sbp = w + (r * ns + c / 256) * 144;
     int e = (int)(c % 256);

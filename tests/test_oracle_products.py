@@ -34,7 +34,8 @@ def _ulp_distance(a: np.float32, b: np.float32) -> int:
     return abs(ia - ib)
 
 
-@pytest.mark.parametrize("fmt,m,k,n", [(0, 3, 32, 2), (0, 4, 64, 3), (1, 2, 256, 2), (1, 3, 256, 1), (2, 3, 64, 2)])
+@pytest.mark.parametrize("fmt,m,k,n", [(0, 3, 32, 2), (0, 4, 64, 3), (1, 2, 256, 2), (1, 3, 256, 1), (2, 3, 64, 2),
+                                       (3, 2, 256, 2)])
 def test_brute_force_exact_rationals(orc, fmt, m, k, n):
     rng = np.random.default_rng(100 + m * k + n)
     w = (rng.standard_normal((m, k)) * 0.02).astype(np.float32)
@@ -53,7 +54,7 @@ def test_brute_force_exact_rationals(orc, fmt, m, k, n):
     assert exact_hits >= (m * n + 1) // 2
 
 
-@pytest.mark.parametrize("fmt,m,k", [(0, 37, 320), (1, 19, 512), (0, 5, 2048), (2, 29, 416)])
+@pytest.mark.parametrize("fmt,m,k", [(0, 37, 320), (1, 19, 512), (0, 5, 2048), (2, 29, 416), (3, 13, 768)])
 def test_matches_numpy_float64(orc, fmt, m, k):
     w = synth.weights(21, m, k)
     x = synth.activations(22, 3, k)
@@ -187,6 +188,20 @@ def test_termscale(orc):
     e[0, 224] = 1.0
     assert orc.termscale(1, sb, 1, 256, e)[0, 0] == 969.0
     assert orc.matvec(1, sb, 1, 256, e)[0, 0] == 921.0
+    # Q2_K: likewise at least sum |w_hat x|; by hand on a one-code super-block
+    # (d = 1, dmin = 0.5, sub-block 12 with sc 12, m 3, element 200 with q 3):
+    # |12*3| + |0.5*3| = 37.5 against the value 34.5.
+    b3 = orc.quantize(3, w)
+    _, ad3 = orc.matvec(3, b3, m, k, x, absdot=True)
+    assert np.all(orc.termscale(3, b3, m, k, x) >= ad3 * (1 - 1e-12))
+    hb = np.zeros(84, np.uint8)
+    hb[40] = 0x30
+    hb[64 + 12] = 12 | (3 << 4)
+    hb[80:84] = [0x00, 0x3C, 0x00, 0x38]
+    e = np.zeros((1, 256), np.float32)
+    e[0, 200] = 1.0
+    assert orc.termscale(3, hb, 1, 256, e)[0, 0] == 37.5
+    assert orc.matvec(3, hb, 1, 256, e)[0, 0] == 34.5
 
 
 # ---- gated product (gate and up rows of one stacked matrix, silu(g) * u) ----
