@@ -185,10 +185,10 @@ def bench_7b(torch, q4, timer, reps=20):
     import synth
 
     out = {}
-    name = {0: "q4_0", 1: "q4_k", 2: "q8_0"}
-    # Q4_0 at one token (the gate), Q4_K at 1, 4, 8 tokens, and Q8_0 at one
-    # token beside them (the pages compare q8_0 with 4-bit formats).
-    for fmt, ns in ((0, (1,)), (1, (1, 4, 8)), (2, (1,))):
+    name = {0: "q4_0", 1: "q4_k", 2: "q8_0", 3: "q2_k"}
+    # Q4_0 at one token (the gate), Q4_K at 1, 4, 8 tokens, and Q8_0 and Q2_K
+    # at one token beside them (the pages compare q8_0, q4_k_m and q2_k).
+    for fmt, ns in ((0, (1,)), (1, (1, 4, 8)), (2, (1,)), (3, (1,))):
         layer_t, layer_b = {1: 0.0}, 0
         for k, m in synth.llama7b_layer()[:2] + synth.llama7b_layer()[3:]:
             wq = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(4, k + m), m, k))

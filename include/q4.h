@@ -53,6 +53,17 @@
  *     Weight value: q * d. (The 8-bit format the technical summary's results
  *     compare with q4_k_m and q2_k: "Experimental results", quantization
  *     impact.)
+ *   Q2_K, m x k, k % 256 == 0, m*(k/256)*84 bytes: the fields of llama.cpp's
+ *     84-byte 2-bit K-quant block in three planes (ns = k/256 super-blocks
+ *     per row, super-block (r, s) has index i = r*ns + s):
+ *     bytes [0, m*k/4): code plane, 64 bytes per super-block at i*64; the
+ *       2-bit code of its element e is bits 2j, 2j+1 of byte
+ *       32*(e/128) + e%32, j = (e%128)/32.
+ *     bytes [m*k/4, m*k*5/16): scale plane, 16 bytes per super-block at
+ *       m*k/4 + i*16; byte e/16 holds the 4-bit scale sc (low nibble) and
+ *       4-bit min mn (high nibble) of element e's 16-weight sub-block.
+ *     bytes [m*k*5/16, m*k*21/64): fp16 d then fp16 dmin at m*k*5/16 + i*4.
+ *     Weight value: d*sc*q - dmin*mn.
  */
 #ifndef Q4_H
 #define Q4_H
@@ -64,10 +75,10 @@
 extern "C" {
 #endif
 
-/* Weight formats: legacy Q4_0 and Q8_0 and the K-quant Q4_K (llama.cpp
- * families the technical summary names: problem statement item 3; q8_0 and
- * q4_k_m in its results). */
-typedef enum { Q4_FMT_Q4_0 = 0, Q4_FMT_Q4_K = 1, Q4_FMT_Q8_0 = 2 } q4_format;
+/* Weight formats: legacy Q4_0 and Q8_0 and the K-quants Q4_K and Q2_K
+ * (llama.cpp families the technical summary names: problem statement item 3;
+ * q8_0, q4_k_m and q2_k in its results). */
+typedef enum { Q4_FMT_Q4_0 = 0, Q4_FMT_Q4_K = 1, Q4_FMT_Q8_0 = 2, Q4_FMT_Q2_K = 3 } q4_format;
 
 /* Status codes. */
 enum {
@@ -81,7 +92,7 @@ enum {
 };
 
 /* Bytes of the quantized buffer for an m x k matrix; 0 if k is not a
- * positive multiple of the block (32 for Q4_0 and Q8_0, 256 for Q4_K),
+ * positive multiple of the block (32 for Q4_0 and Q8_0, 256 for the K-quants),
  * m < 0, or the format is unknown. Host only; no device work. */
 size_t q4_weight_bytes(int fmt, int64_t m, int64_t k);
 
@@ -96,6 +107,9 @@ size_t q4_weight_bytes(int fmt, int64_t m, int64_t k);
  *   q = clamp(round_half_away((w + dmin*mn)/(d*sc)), 0, 15) (0 where a divisor is 0).
  * Q8_0 block: d = fp16_rne(max|w| / 127) (binary32 division); codes
  *   q = clamp(round_half_away(w / d), -127, 127), all 0 when d == 0.
+ * Q2_K super-block: the Q4_K reading with 16-weight sub-blocks, s = (hi - lo)/3,
+ *   d = fp16_rne(max s / 15), dmin = fp16_rne(max mu / 15), 4-bit sc and mn
+ *   (clamp 0..15) and 2-bit codes (clamp 0..3).
  * Blocks are quantized row by row; the status is that of the first failing
  * block in row-major order (Q4_ENONFINITE for NaN/Inf, Q4_ERANGE for a scale
  * that overflows fp16), and `out` is then unspecified.

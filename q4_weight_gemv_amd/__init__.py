@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libq4gemv.so")
 Q4_FMT_Q4_0 = 0
 Q4_FMT_Q4_K = 1
 Q4_FMT_Q8_0 = 2
+Q4_FMT_Q2_K = 3
 
 Q4_OK = 0
 Q4_EINVAL = -1

@@ -39,6 +39,8 @@ SOURCES = [
     ("q4_gemv_q4_k_b.hip", "device"),
     ("q4_gemv_q8_0_a.hip", "device"),
     ("q4_gemv_q8_0_b.hip", "device"),
+    ("q4_gemv_q2_k_a.hip", "device"),
+    ("q4_gemv_q2_k_b.hip", "device"),
     ("q4_gemm.hip", "device"),
     ("q4_stack.hip", "device"),
     ("q4_bench.hip", "device"),

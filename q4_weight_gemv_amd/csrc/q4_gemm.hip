@@ -170,6 +170,67 @@ struct GemmQ8_0 {
     }
 };
 
+// Q2_K: an item is two 8-element runs of one super-block that share 8 code
+// bytes: w16 = it % 16 of super-block s*KC/256 + it/16 gives half h = w16/8,
+// run pair p = (w16/4) % 2 and byte group i = w16 % 4: code bytes 32h + 8i ..
+// +7, whose bit pairs 4p and 4p+2 hold runs j = 2p and 2p+1 (elements
+// 128h + 32j + 8i .. +7). Run j lies in sub-block 8h + 2j + (i >= 2).
+struct GemmQ2_K {
+    static constexpr int kFormat = Q4_FMT_Q2_K;
+    static constexpr int kRingVgprs = 64;  // activation ring budget (Items are 7 VGPRs)
+    __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k / 4u); }
+    struct Item {
+        u32x2 q;      // 8 code bytes
+        u32x4 sc;     // the super-block's 16 scale bytes
+        uint32_t dd;  // fp16 d | fp16 dmin << 16
+    };
+    template <int KC>
+    __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+                                uint32_t row, bool row_ok, int s, int it)
+    {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
+        const uint32_t ns = nu >> 3;
+        const uint32_t sbr = static_cast<uint32_t>(s * (KC / 256) + (it >> 4));
+        const bool live = row_ok && sbr < ns;
+        const uint32_t sb = row * ns + sbr;
+        const uint32_t w16 = static_cast<uint32_t>(it & 15);
+        const uint32_t byte = 32u * (w16 >> 3) + 8u * (w16 & 3u);
+        g.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, live ? sb * 64u + byte : kNoFetch, 0, 0));
+        g.sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, live ? scale_plane + sb * 16u : kNoFetch,
+                                                                                0, 0));
+        g.dd = __builtin_amdgcn_raw_buffer_load_b32(r, live ? scale_plane + scale_plane / 4u + sb * 4u : kNoFetch, 0, 0);
+    }
+    __device__ static int lo(int it)
+    {
+        const int w16 = it & 15;
+        return 256 * (it >> 4) + 128 * (w16 >> 3) + 64 * ((w16 >> 2) & 1) + 8 * (w16 & 3);
+    }
+    __device__ static int hi(int it) { return lo(it) + 32; }
+    // (d*sc)*q - dmin*m: (d*sc)*q is exact in fp32, so the fma rounds the exact
+    // difference once, as the format's definition does.
+    template <int KC>
+    __device__ static void dequant(const Item &g, int /*s*/, int it, u32x4 &vlo, u32x4 &vhi)
+    {
+        const int w16 = it & 15;
+        const int h = w16 >> 3, p = (w16 >> 2) & 1, c = (w16 & 3) >> 1;
+        const float d = half_bits_to_float(g.dd), dmin = half_bits_to_float(g.dd >> 16);
+        const auto scale_byte = [&](int j) {
+            const int b = 8 * h + 2 * j + c;
+            const uint32_t word = b < 4 ? g.sc.x : b < 8 ? g.sc.y : b < 12 ? g.sc.z : g.sc.w;
+            return (word >> (8 * (b & 3))) & 0xFFu;
+        };
+        const half2_t add = {static_cast<_Float16>(-1024.0f), static_cast<_Float16>(-1024.0f)};
+        const int ja = 2 * p, jb = 2 * p + 1;
+        const uint32_t sa = scale_byte(ja), sbb = scale_byte(jb);
+        const float stepa = d * static_cast<float>(sa & 15u), offa = -(dmin * static_cast<float>(sa >> 4));
+        const float stepb = d * static_cast<float>(sbb & 15u), offb = -(dmin * static_cast<float>(sbb >> 4));
+        vlo = eight((g.q.x >> (2 * ja)) & 0x03030303u, (g.q.y >> (2 * ja)) & 0x03030303u, add,
+                    [=](_Float16 q) { return __builtin_fmaf(stepa, static_cast<float>(q), offa); });
+        vhi = eight((g.q.x >> (2 * jb)) & 0x03030303u, (g.q.y >> (2 * jb)) & 0x03030303u, add,
+                    [=](_Float16 q) { return __builtin_fmaf(stepb, static_cast<float>(q), offb); });
+    }
+};
+
 struct GemmQ4_K {
     static constexpr int kFormat = Q4_FMT_Q4_K;
     static constexpr int kRingVgprs = 64;  // activation ring budget (Items are 6 VGPRs)
@@ -425,6 +486,7 @@ int launch_gemm(int fmt, const void *w, const uint16_t *x, float *y, int64_t m, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (fmt == Q4_FMT_Q4_0) return gemm::launch_fmt<gemm::GemmQ4_0>(w, x, y, m, k, n, s, cus);
     if (fmt == Q4_FMT_Q8_0) return gemm::launch_fmt<gemm::GemmQ8_0>(w, x, y, m, k, n, s, cus);
+    if (fmt == Q4_FMT_Q2_K) return gemm::launch_fmt<gemm::GemmQ2_K>(w, x, y, m, k, n, s, cus);
     return gemm::launch_fmt<gemm::GemmQ4_K>(w, x, y, m, k, n, s, cus);
 }
 
@@ -444,6 +506,7 @@ extern "C" int q4_gemm_tuned(int fmt, const void *w, const uint16_t *x_bf16, flo
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     if (fmt == Q4_FMT_Q4_0) return q4::gemm::launch_geometry<q4::gemm::GemmQ4_0>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
     if (fmt == Q4_FMT_Q8_0) return q4::gemm::launch_geometry<q4::gemm::GemmQ8_0>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
+    if (fmt == Q4_FMT_Q2_K) return q4::gemm::launch_geometry<q4::gemm::GemmQ2_K>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
     return q4::gemm::launch_geometry<q4::gemm::GemmQ4_K>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
 }
 

@@ -123,6 +123,13 @@ int dispatch(int fmt, const Cfg &c, const void *w, const float *x, float *y, int
         default: return Q4_EUNSUPPORTED;
         }
     }
+    if (fmt == Q4_FMT_Q2_K) {
+        switch (n) {
+            Q4_N_CASE(FmtQ2_K, 1) Q4_N_CASE(FmtQ2_K, 2) Q4_N_CASE(FmtQ2_K, 3) Q4_N_CASE(FmtQ2_K, 4)
+            Q4_N_CASE(FmtQ2_K, 5) Q4_N_CASE(FmtQ2_K, 6) Q4_N_CASE(FmtQ2_K, 7) Q4_N_CASE(FmtQ2_K, 8)
+        default: return Q4_EUNSUPPORTED;
+        }
+    }
     switch (n) {
         Q4_N_CASE(FmtQ4_K, 1) Q4_N_CASE(FmtQ4_K, 2) Q4_N_CASE(FmtQ4_K, 3) Q4_N_CASE(FmtQ4_K, 4)
         Q4_N_CASE(FmtQ4_K, 5) Q4_N_CASE(FmtQ4_K, 6) Q4_N_CASE(FmtQ4_K, 7) Q4_N_CASE(FmtQ4_K, 8)
@@ -159,8 +166,8 @@ int check_glu_args(int fmt, const void *w, const void *x, const float *y, int64_
 int check_product_args(int fmt, const void *w, const void *x, const float *y, int64_t m, int64_t k, int64_t n,
                        int64_t n_max)
 {
-    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0) return Q4_EUNSUPPORTED;
-    const int64_t blk = fmt == Q4_FMT_Q4_K ? 256 : 32;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0 && fmt != Q4_FMT_Q2_K) return Q4_EUNSUPPORTED;
+    const int64_t blk = fmt == Q4_FMT_Q4_K || fmt == Q4_FMT_Q2_K ? 256 : 32;
     if (m < 0 || k <= 0 || k % blk != 0 || n < 0) return Q4_EINVAL;
     if (n > n_max) return Q4_EUNSUPPORTED;
     if (m == 0 || n == 0) return Q4_OK;

@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "q4_internal.h"
 
@@ -48,6 +49,7 @@ namespace gemv {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kLo = 0x000F000Fu;  // low nibbles of bytes 0 and 2
@@ -174,6 +176,7 @@ struct FmtQ4_0 {
     static constexpr int kHighOffset = 16;
     static constexpr int kBatchUnits = 4;  // units (x rows) per lane per batch: 4 x 20 B in flight
     __device__ static int unit_base(int u) { return u << 5; }
+    __device__ static int item_base(int u, int i) { return unit_base(u) + 4 * i; }
     __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k / 2u); }
 
     struct Regs {
@@ -249,6 +252,7 @@ struct FmtQ8_0 {
     static constexpr int kHighOffset = 16;
     static constexpr int kBatchUnits = 2;  // each unit is two 16-byte loads and a scale
     __device__ static int unit_base(int u) { return u << 5; }
+    __device__ static int item_base(int u, int i) { return unit_base(u) + 4 * i; }
     __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k); }
 
     struct Regs {
@@ -315,6 +319,133 @@ struct FmtQ8_0 {
     }
 };
 
+// Q2_K: unit u = 8 code bytes of super-block u >> 3: bytes 32h + 8i .. +7
+// of its 64 code bytes, h = (u & 7) >> 2, i = u & 3. Those bytes hold, in
+// bit pairs 2j, 2j+1, the codes of the four runs j = 0..3 of 8 elements
+// 128h + 32j + 8i .. +7; run j lies in sub-block 8h + 2j + (i >= 2). Item j
+// of the unit is run j: L = its first four elements, H = its last four
+// (kHighOffset 4, staged divided by 16). A code pair is the masked bits
+// themselves as fp16 subnormals: q*2^-24 (L) or 16q*2^-24 (H).
+template <int J>
+__device__ __forceinline__ uint32_t q2_hi_pair(uint32_t b)
+{
+    // Bits 2J, 2J+1 of bytes 0 and 2 moved to bits 4, 5 of each half.
+    if constexpr (J < 2) return (b << (4 - 2 * J)) & 0x00300030u;
+    else return (b >> (2 * J - 4)) & 0x00300030u;
+}
+
+struct FmtQ2_K {
+    static constexpr int kFormat = Q4_FMT_Q2_K;
+    static constexpr int kHighOffset = 4;
+    static constexpr int kBatchUnits = 4;  // 8 code bytes, 8 scale bytes and d, dmin per unit
+    __device__ static int item_base(int u, int i) { return ((u >> 3) << 8) + (((u & 7) >> 2) << 7) + 32 * i + 8 * (u & 3); }
+    // Offset of the scale plane; the d, dmin plane follows it at a quarter of its offset.
+    __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k / 4u); }
+
+    struct Regs {
+        u32x2 q;   // 8 code bytes
+        u32x2 sc;  // scale bytes 8h .. 8h+7 of the super-block
+        uint32_t dd;  // fp16 d | fp16 dmin << 16
+    };
+    // Unit u = ubase + li + jl of row trow + rowrel (ubase and jl multiples of
+    // 8): super-block (row*ns + u/8); code bytes at 64 per super-block + 8*(u & 7),
+    // scale bytes at scale_plane + 16 per super-block + 8h, d and dmin at
+    // scale_plane*5/4 + 4 per super-block.
+    __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+                                uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl, bool live)
+    {
+        const uint32_t ns = nu >> 3;
+        const uint32_t uni_sb = trow * ns + (ubase >> 3);
+        const uint32_t lane_sb = rowrel * ns + (li >> 3) + (jl >> 3);
+        const uint32_t dd_plane = scale_plane + scale_plane / 4u;
+        g.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                            sub_rsrc(w, wbytes, uni_sb * 64u),
+                                            live ? lane_sb * 64u + 8u * (li & 7u) : kNoFetch, 0, kNonTemporal));
+        g.sc = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             sub_rsrc(w, wbytes, scale_plane + uni_sb * 16u),
+                                             live ? lane_sb * 16u + 8u * ((li & 7u) >> 2) : kNoFetch, 0, 0));
+        g.dd = __builtin_amdgcn_raw_buffer_load_b32(sub_rsrc(w, wbytes, dd_plane + uni_sb * 4u),
+                                                    live ? lane_sb * 4u : kNoFetch, 0, 0);
+    }
+    // Unit metadata: z = 2^(e+24), w = 2^e.
+    __device__ static f32x4 meta(float /*gl*/, float /*gh*/, int e)
+    {
+        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + 24), __builtin_amdgcn_ldexpf(1.0f, e)};
+    }
+    template <int N, int R, bool LO>
+    __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
+                                      const f32x4 *__restrict__ meta, int ul, int uc, uint32_t u,
+                                      float (&acc)[R][N])
+    {
+        constexpr uint32_t one = 0x3C003C00u, sixteen = 0x4C004C00u;  // fp16 pairs (1, 1) and (16, 16)
+        const uint32_t c = (u & 3u) >> 1;  // runs of units i >= 2 lie in the odd sub-blocks
+        float dsc[R][4], dmn[R][4];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const float d = half_lo(g[r].dd), dmin = half_hi(g[r].dd);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                // Scale byte 2j + c of the 8 loaded: dword j >> 1, byte 2(j & 1) + c.
+                const uint32_t word = (j >> 1) ? g[r].sc.y : g[r].sc.x;
+                const uint32_t byte = (word >> (8u * (2u * (j & 1) + c))) & 0xFFu;
+                dsc[r][j] = d * static_cast<float>(byte & 15u);
+                dmn[r][j] = dmin * static_cast<float>(byte >> 4);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < N; t++) {
+            const f32x4 mt = meta[t * uc + ul];
+            u32x4 xh[4], xl[4];
+            float sx[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                xh[j] = xs[(t * 8 + 2 * j) * uc + ul];
+                xl[j] = LO ? xs[(t * 8 + 2 * j + 1) * uc + ul] : u32x4{0u, 0u, 0u, 0u};
+                // Sum of the run's staged activations (the H ones counted 16 times).
+                float s = dot2(xh[j].x, one, 0.0f);
+                s = dot2(xh[j].y, sixteen, s);
+                s = dot2(xh[j].z, one, s);
+                s = dot2(xh[j].w, sixteen, s);
+                if constexpr (LO) {
+                    s = dot2(xl[j].x, one, s);
+                    s = dot2(xl[j].y, sixteen, s);
+                    s = dot2(xl[j].z, one, s);
+                    s = dot2(xl[j].w, sixteen, s);
+                }
+                sx[j] = s;
+            }
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const uint32_t a = g[r].q.x, b = g[r].q.y;
+                float ts = 0.0f, tm = 0.0f;
+                auto run = [&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const uint32_t p0 = (a >> (2 * j)) & 0x00030003u, p2 = (a >> (2 * j + 8)) & 0x00030003u;
+                    const uint32_t p1 = q2_hi_pair<j>(b), p3 = (b >> (2 * j + 4)) & 0x00300030u;
+                    float aj = dot2(p0, xh[j].x, 0.0f);
+                    aj = dot2(p1, xh[j].y, aj);
+                    aj = dot2(p2, xh[j].z, aj);
+                    aj = dot2(p3, xh[j].w, aj);
+                    if constexpr (LO) {
+                        aj = dot2(p0, xl[j].x, aj);
+                        aj = dot2(p1, xl[j].y, aj);
+                        aj = dot2(p2, xl[j].z, aj);
+                        aj = dot2(p3, xl[j].w, aj);
+                    }
+                    ts = __builtin_fmaf(dsc[r][j], aj, ts);
+                    tm = __builtin_fmaf(dmn[r][j], sx[j], tm);
+                };
+                run(std::integral_constant<int, 0>{});
+                run(std::integral_constant<int, 1>{});
+                run(std::integral_constant<int, 2>{});
+                run(std::integral_constant<int, 3>{});
+                acc[r][t] = __builtin_fmaf(mt.z, ts, acc[r][t]);
+                acc[r][t] = __builtin_fmaf(-mt.w, tm, acc[r][t]);
+            }
+        }
+    }
+};
+
 struct FmtQ4_K {
     static constexpr int kFormat = Q4_FMT_Q4_K;
     static constexpr int kHighOffset = 32;
@@ -323,6 +454,7 @@ struct FmtQ4_K {
     // unit u = slice (u & 7) of super-block u >> 3; slice h covers the 16
     // bytes at 16h of the 128 nibble bytes: chunk c = h >> 1, half h & 1.
     __device__ static int unit_base(int u) { return ((u >> 3) << 8) + (((u & 7) >> 1) << 6) + ((u & 1) << 4); }
+    __device__ static int item_base(int u, int i) { return unit_base(u) + 4 * i; }
 
     struct Regs {
         u32x4 q;
@@ -430,7 +562,8 @@ __device__ __forceinline__ void wg_sync()
 // Units [c0, c0 + nuc) of every token -> LDS: planes (t, 2i) and (t, 2i+1)
 // hold the hi and lo fp16 pairs for nibble dword i. Item (t, ul, i) handles dword i
 // of unit ul: activations L..L+3 (low nibbles) and H..H+3 (high nibbles),
-// L = unit_base + 4i, H = L + kHighOffset. The four items of a unit are four
+// L = item_base(unit, i) (unit_base + 4i for the nibble formats), H = L +
+// kHighOffset. The four items of a unit are four
 // consecutive lanes, which exchange their maxima and partial sums.
 
 // The four items of a unit are one lane quad (every count and stride here is
@@ -472,7 +605,7 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
             // Branch-free: an item past the end lands past N*K and reads zeros.
             int t, rem;
             split_item(base + p * NT, t, rem);
-            const uint32_t off = static_cast<uint32_t>(t * K + F::unit_base(c0 + (rem >> 2)) + 4 * (rem & 3)) * 4u;
+            const uint32_t off = static_cast<uint32_t>(t * K + F::item_base(c0 + (rem >> 2), rem & 3)) * 4u;
             a[p] = __builtin_bit_cast(f32x4, load16<0>(xr, off, 0));
             b[p] = __builtin_bit_cast(f32x4, load16<0>(xr, off + 4u * F::kHighOffset, 0));
         }

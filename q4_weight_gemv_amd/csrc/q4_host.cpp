@@ -153,6 +153,54 @@ int q4_k_superblock(const float *v, uint8_t *out)
     return Q4_OK;
 }
 
+// ---- Q2_K -----------------------------------------------------------------
+
+// One 256-weight super-block into its three fields: 64 code bytes, 16 scale
+// bytes (sc | mn << 4 per 16-weight sub-block) and fp16 d, dmin.
+int q2_k_superblock(const float *v, uint8_t *codes, uint8_t *scales, uint8_t *dd)
+{
+    double step[16], off[16];
+    double smax = 0.0, mumax = 0.0;
+    for (int i = 0; i < 256; i++)
+        if (!std::isfinite(v[i])) return Q4_ENONFINITE;
+    for (int j = 0; j < 16; j++) {
+        const float *s = v + 16 * j;
+        double mn = std::min(0.0, static_cast<double>(*std::min_element(s, s + 16)));
+        double mx = static_cast<double>(*std::max_element(s, s + 16));
+        step[j] = (mx - mn) / 3.0;
+        off[j] = -mn;
+        smax = std::max(smax, step[j]);
+        mumax = std::max(mumax, off[j]);
+    }
+    _Float16 dh = static_cast<_Float16>(smax / 15.0);
+    _Float16 mh = static_cast<_Float16>(mumax / 15.0);
+    if (!half_is_finite(dh) || !half_is_finite(mh)) return Q4_ERANGE;
+    const double d = static_cast<float>(dh);
+    const double dmin = static_cast<float>(mh);
+    int sc[16], mn[16];
+    for (int j = 0; j < 16; j++) {
+        sc[j] = d == 0.0 ? 0 : code_of(step[j] / d, 0, 15);
+        mn[j] = dmin == 0.0 ? 0 : code_of(off[j] / dmin, 0, 15);
+        scales[j] = static_cast<uint8_t>(sc[j] | (mn[j] << 4));
+    }
+    std::memset(codes, 0, 64);
+    for (int h = 0; h < 2; h++)
+        for (int j = 0; j < 4; j++)
+            for (int r = 0; r < 32; r++) {
+                const int e = 128 * h + 32 * j + r;
+                const double st = d * sc[e / 16];
+                const double o = dmin * mn[e / 16];
+                const int q = st == 0.0 ? 0 : code_of((v[e] + o) / st, 0, 3);
+                codes[32 * h + r] = static_cast<uint8_t>(codes[32 * h + r] | (q << (2 * j)));
+            }
+    const uint16_t db = half_bits(dh), mb = half_bits(mh);
+    dd[0] = static_cast<uint8_t>(db);
+    dd[1] = static_cast<uint8_t>(db >> 8);
+    dd[2] = static_cast<uint8_t>(mb);
+    dd[3] = static_cast<uint8_t>(mb >> 8);
+    return Q4_OK;
+}
+
 // Run fn(row, &bad_col_block) over rows on a few threads; return the status
 // of the first failing block in row-major order.
 template <class F>
@@ -204,14 +252,16 @@ size_t q4_weight_bytes(int fmt, int64_t m, int64_t k)
     if (fmt == Q4_FMT_Q4_0) return k % 32 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 32) * 18u;
     if (fmt == Q4_FMT_Q4_K) return k % 256 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 256) * 144u;
     if (fmt == Q4_FMT_Q8_0) return k % 32 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 32) * 34u;
+    if (fmt == Q4_FMT_Q2_K) return k % 256 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 256) * 84u;
     return 0;
 }
 
 int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, size_t out_bytes)
 {
-    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0) return Q4_EUNSUPPORTED;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0 && fmt != Q4_FMT_Q2_K) return Q4_EUNSUPPORTED;
     const size_t need = q4_weight_bytes(fmt, m, k);
-    if (need == 0 && !(m == 0 && k > 0 && k % (fmt == Q4_FMT_Q4_K ? 256 : 32) == 0)) return Q4_EINVAL;
+    const int64_t blk = fmt == Q4_FMT_Q4_K || fmt == Q4_FMT_Q2_K ? 256 : 32;
+    if (need == 0 && !(m == 0 && k > 0 && k % blk == 0)) return Q4_EINVAL;
     if (m == 0) return Q4_OK;
     if (!w || !out || out_bytes < need) return Q4_EINVAL;
     uint8_t *o = static_cast<uint8_t *>(out);
@@ -232,6 +282,18 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
         });
     }
     const int64_t ns = k / 256;
+    if (fmt == Q4_FMT_Q2_K) {
+        uint8_t *scl = o + static_cast<size_t>(m) * static_cast<size_t>(k) / 4;
+        uint8_t *dd = scl + static_cast<size_t>(m) * static_cast<size_t>(k) / 16;
+        return for_rows(m, ns, [&](int64_t r, int64_t *bad) {
+            for (int64_t s = 0; s < ns; s++) {
+                const int64_t i = r * ns + s;
+                int st = q2_k_superblock(w + r * k + s * 256, o + i * 64, scl + i * 16, dd + i * 4);
+                if (st != Q4_OK) { *bad = s; return st; }
+            }
+            return static_cast<int>(Q4_OK);
+        });
+    }
     return for_rows(m, ns, [&](int64_t r, int64_t *bad) {
         for (int64_t s = 0; s < ns; s++) {
             int st = q4_k_superblock(w + r * k + s * 256, o + (r * ns + s) * 144);

@@ -54,6 +54,7 @@ struct Cfg {
 struct FmtQ4_0;
 struct FmtQ4_K;
 struct FmtQ8_0;
+struct FmtQ2_K;
 
 // Defined in the per-format instantiation units (q4_gemv_q4_*.hip).
 template <class F, int N>

@@ -45,7 +45,7 @@ def _quantize_both(q4, orc, fmt, w):
 
 
 @pytest.mark.parametrize("fmt,m,k", [(0, 37, 96), (0, 130, 960), (0, 64, 2560), (1, 37, 256), (1, 96, 1024),
-                                     (2, 37, 96), (2, 130, 960)])
+                                     (2, 37, 96), (2, 130, 960), (3, 37, 256), (3, 96, 1024)])
 def test_identity_gives_bf16_weights_exactly(env, fmt, m, k):
     torch, q4, orc = env
     buf = _quantize_both(q4, orc, fmt, synth.weights(synth.seed_for(30 + fmt, m), m, k))
@@ -75,6 +75,7 @@ def _parity(env, fmt, m, k, n, seed, rows=None):
     (0, 1, 32, 1), (0, 37, 96, 5), (0, 100, 320, 130), (0, 33, 960, 64), (0, 257, 2560, 200),
     (1, 1, 256, 3), (1, 70, 512, 70), (1, 130, 1024, 257),
     (2, 1, 32, 1), (2, 100, 320, 130), (2, 257, 2560, 200),
+    (3, 1, 256, 3), (3, 70, 512, 70), (3, 130, 1024, 257),
 ])
 def test_parity_small(env, fmt, m, k, n):
     _parity(env, fmt, m, k, n, seed=600 + n)
@@ -102,7 +103,7 @@ def _tiles():
 
 
 @pytest.mark.parametrize("tile", _tiles(), ids=lambda t: f"{t[0]}x{t[1]}x{t[2]}")
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_parity_every_tile(env, fmt, tile):
     """Every instantiated tile through q4_gemm_tuned: 70 rows and 100 tokens
     (ragged in both), K = 1280 (a partial last chunk for every chunk size)."""

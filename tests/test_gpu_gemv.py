@@ -50,6 +50,7 @@ ONEHOT_CASES = [
     (0, 5, 32), (0, 37, 320), (0, 768, 768), (0, 129, 2560), (0, 300, 4096), (0, 70, 11008),
     (1, 5, 256), (1, 37, 512), (1, 130, 1024), (1, 300, 4096), (1, 70, 11008),
     (2, 5, 32), (2, 37, 320), (2, 768, 768), (2, 300, 4096), (2, 70, 11008),
+    (3, 5, 256), (3, 37, 512), (3, 130, 1024), (3, 300, 4096), (3, 70, 11008),
 ]
 
 
@@ -115,7 +116,7 @@ def _geometries():
 
 
 @pytest.mark.parametrize("geom", _geometries(), ids=_geometry_ids())
-@pytest.mark.parametrize("fmt,n", [(0, 1), (0, 8), (1, 1), (1, 8), (2, 1), (2, 8)])
+@pytest.mark.parametrize("fmt,n", [(0, 1), (0, 8), (1, 1), (1, 8), (2, 1), (2, 8), (3, 1), (3, 8)])
 def test_parity_every_geometry(env, fmt, n, geom):
     """Every instantiated tile geometry through q4_gemv_tuned: 600 ragged rows
     (a grid-stride loop for the short tiles at one group per compute unit) and
@@ -178,6 +179,21 @@ def test_parity_q8_0_small(env, m, k, n):
 @pytest.mark.parametrize("n", [1, 8])
 def test_parity_q8_0_7b(env, k, m, n):
     _parity(env, 2, m, k, n, seed=450 + n, rows=sample_rows(m, k + n))
+
+
+SMALL_Q2_K = [(1, 256), (37, 512), (130, 1024), (257, 2560), (300, 4096), (77, 11008), (1025, 768 + 256)]
+
+
+@pytest.mark.parametrize("m,k", SMALL_Q2_K)
+@pytest.mark.parametrize("n", [1, 4, 8])
+def test_parity_q2_k_small(env, m, k, n):
+    _parity(env, 3, m, k, n, seed=250 + n)
+
+
+@pytest.mark.parametrize("k,m", synth.llama7b_layer()[:2] + synth.llama7b_layer()[3:])
+@pytest.mark.parametrize("n", [1, 8])
+def test_parity_q2_k_7b(env, k, m, n):
+    _parity(env, 3, m, k, n, seed=470 + n, rows=sample_rows(m, k + n))
 
 
 def test_q8_0_extreme_codes(env):
@@ -340,6 +356,7 @@ GLU_CASES = [
     (0, 1, 37, 96), (0, 3, 130, 960), (0, 1, 1280, 960), (0, 8, 200, 2560), (0, 1, 300, 4096), (0, 2, 70, 11008),
     (1, 1, 37, 256), (1, 4, 130, 1024), (1, 1, 300, 4096), (1, 8, 90, 4096), (1, 1, 70, 11008),
     (2, 1, 130, 960), (2, 4, 300, 4096),
+    (3, 1, 130, 1024), (3, 4, 300, 4096),
 ]
 
 
@@ -375,7 +392,7 @@ def test_glu_parity_oracle(env, fmt, n, m, k):
     yg = _glu(env, fmt, buf, x, m, k)
     yr, g, u = orc.matvec_silu_mul(fmt, buf, m, k, x, threads=threads(), parts=True)
     _, ad = orc.matvec(fmt, buf, 2 * m, k, x, threads=threads(), absdot=True)
-    if fmt == 1:  # Q4_K's elementwise bound is stated against its term scale
+    if fmt in (1, 3):  # the K-quants' elementwise bound is stated against their term scale
         ad = orc.termscale(fmt, buf, 2 * m, k, x, threads=threads())
     ag, au = ad[:, :m], ad[:, m:]
     silu = g / (1.0 + np.exp(-g))

@@ -60,6 +60,9 @@ def test_weight_bytes(q4):
     assert q4.q4_weight_bytes(2, 4096, 4096) == 4096 * 4096 * 34 // 32
     assert q4.q4_weight_bytes(2, 3, 33) == 0
     assert q4.q4_weight_bytes(2, 5, 96) == 5 * 3 * 34
+    # Q2_K: 84 bytes per 256 weights, k a multiple of 256.
+    assert q4.q4_weight_bytes(3, 4096, 11008) == 4096 * 43 * 84
+    assert q4.q4_weight_bytes(3, 3, 288) == 0
 
 
 SHAPES = sorted(set(synth.gpt2_124m_step() + synth.smollm2_360m_step() + synth.llama7b_layer()))
@@ -85,6 +88,12 @@ def test_quantize_ref_matches_oracle_q8_0(q4, orc, k, m):
     assert np.array_equal(q4.q4_quantize_ref(2, w), orc.quantize(2, w))
 
 
+@pytest.mark.parametrize("k,m", [(768, 768), (1024, 320), (4096, 512), (11008, 96)])
+def test_quantize_ref_matches_oracle_q2_k(q4, orc, k, m):
+    w = synth.weights(synth.seed_for(6, k % 97 + m % 89), m, k)
+    assert np.array_equal(q4.q4_quantize_ref(3, w), orc.quantize(3, w))
+
+
 def _edge_matrix(k):
     """Rows that exercise ties, subnormal scales, clamps, zeros and sign patterns."""
     rng = np.random.default_rng(17)
@@ -104,12 +113,17 @@ def _edge_matrix(k):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 def test_quantize_ref_matches_oracle_edges(q4, orc, fmt):
     w = _edge_matrix(512)
     assert np.array_equal(q4.q4_quantize_ref(fmt, w), orc.quantize(fmt, w))
     # Golden blocks through the product quantizer too.
-    if fmt == 2:
+    if fmt == 3:
+        from golden import floats, hexbytes, load
+        sec = load("q2_k_superblocks.txt")["K2-B"]
+        buf = q4.q4_quantize_ref(3, floats(sec["w"][0]).reshape(1, 256))
+        assert bytes(buf) == hexbytes(sec["codes"][0]) + hexbytes(sec["scales"][0]) + hexbytes(sec["dd"][0])
+    elif fmt == 2:
         from golden import floats, hexbytes, load
         for name, sec in load("q8_0_blocks.txt").items():
             buf = q4.q4_quantize_ref(2, floats(sec["w"][0]).reshape(1, 32))
@@ -140,7 +154,7 @@ def test_quantize_ref_status(q4, orc):
     w3 = w.copy()
     w3[10, 0] = 1e9
     w3[11, 0] = np.inf
-    for fmt in (0, 1, 2):
+    for fmt in (0, 1, 2, 3):
         with pytest.raises(q4.Q4Error) as e:
             q4.q4_quantize_ref(fmt, w3)
         assert e.value.status == q4.Q4_ERANGE
@@ -190,6 +204,7 @@ def test_product_argument_errors(q4, entry):
     assert f(1, *ok, 1 << 20, 4096, 1, None) == q4.Q4_EUNSUPPORTED
     assert f(2, *ok, 64, 48, 1, None) == q4.Q4_EINVAL                 # Q8_0: k a multiple of 32
     assert f(2, *ok, 1 << 19, 4096, 1, None) == q4.Q4_EUNSUPPORTED    # Q8_0 weights of 2 GiB or more
+    assert f(3, *ok, 64, 288, 1, None) == q4.Q4_EINVAL                # Q2_K: k a multiple of 256
     if entry == "q4_gemv":
         assert f(0, *ok, 64, 256, 9, None) == q4.Q4_EUNSUPPORTED       # decode batch is 1..8
 
