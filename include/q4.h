@@ -226,6 +226,66 @@ int q4_graph_create(int fmt, const q4_gemv_op *ops, int count, int64_t n, void *
 int q4_graph_launch(q4_graph *graph, void *hip_stream);
 int q4_graph_destroy(q4_graph *graph);
 
+/* ---- A whole synthetic decode step (Llama family) ----------------------------
+ * The decode step of a Llama-family model (the SmolLM2 models the MicroLLM Lab
+ * post runs) around the quantized products: the token's embedding (a row of the
+ * tied LM-head matrix, dequantized), then per layer
+ *   x += delta (from the second layer on); h = rmsnorm(x) * norm_attn;
+ *   qkv = W_qkv h (q|k|v stacked); rotary embedding of q and k (rotate-half,
+ *   angle pos * theta^(-2i/head_dim)); k and v appended to the caches at pos;
+ *   att = grouped-query attention over positions 0..pos (query head h reads
+ *   key/value head h / (heads / kv_heads), softmax of q.k / sqrt(head_dim));
+ *   delta = W_o att; x += delta; h = rmsnorm(x) * norm_mlp;
+ *   act = silu(W_gate h) * (W_up h) (the gated product); delta = W_down act;
+ * then x += delta, h = rmsnorm(x) * norm_final, logits = W_emb h, and the next
+ * token = argmax(logits) (lowest index among equals), with pos advanced by one.
+ * rmsnorm(x) = x / sqrt(mean(x^2) + norm_eps). Keys and values stay cached and
+ * the selection runs on the device (WebGPT README, "Roadmap"); all buffers are
+ * the caller's (Llamas on the Web, technical summary, Methodology section 1).
+ * The token and its position are device int32 values read by the step's
+ * kernels, so a captured step replays as a generation loop. A position outside
+ * [0, max_pos) makes the attention outputs NaN and writes no cache entry. */
+typedef struct {
+    int layers, hidden, heads, kv_heads, head_dim, ffn, vocab, max_pos;
+    float rope_theta, norm_eps;
+} q4_llama_config;
+
+typedef struct {
+    const void *qkv;        /* (heads + 2 kv_heads) * head_dim rows x hidden */
+    const void *o;          /* hidden rows x heads * head_dim */
+    const void *gate_up;    /* 2 ffn rows (gate, then up) x hidden, as for q4_gemv_glu */
+    const void *down;       /* hidden rows x ffn */
+    const float *norm_attn, *norm_mlp;  /* hidden each */
+} q4_llama_layer;
+
+typedef struct {            /* device buffers, all caller-owned (16-byte aligned) */
+    float *x, *h;           /* hidden each: the residual stream and the normed input */
+    float *qkv;             /* (heads + 2 kv_heads) * head_dim */
+    float *att;             /* heads * head_dim */
+    float *delta;           /* hidden */
+    float *act;             /* ffn */
+    float *logits;          /* vocab */
+    float *k_cache, *v_cache;  /* layers x kv_heads x max_pos x head_dim each */
+    int32_t *token;         /* [1]: the current token in, the next token out */
+    int32_t *pos;           /* [1]: the current token's position, advanced by one */
+} q4_llama_state;
+
+/* Enqueue one decode step (fmt for every matrix; emb: vocab x hidden, also the
+ * LM head). Limits: head_dim even, at most 128 and dividing 256; max_pos at
+ * most 8192; hidden at most 16384; hidden, heads * head_dim and ffn whole
+ * numbers of blocks. Errors as q4_gemv for each product, Q4_EINVAL for a null
+ * pointer or an inconsistent configuration, Q4_EUNSUPPORTED beyond the limits. */
+int q4_llama_step(int fmt, const q4_llama_config *cfg, const void *emb, const float *norm_final,
+                  const q4_llama_layer *layers, const q4_llama_state *state, void *hip_stream);
+
+/* The same step captured once into a HIP graph; each launch runs one step. */
+typedef struct q4_llama_graph q4_llama_graph;
+int q4_llama_graph_create(int fmt, const q4_llama_config *cfg, const void *emb, const float *norm_final,
+                          const q4_llama_layer *layers, const q4_llama_state *state, void *hip_stream,
+                          q4_llama_graph **graph_out);
+int q4_llama_graph_launch(q4_llama_graph *graph, void *hip_stream);
+int q4_llama_graph_destroy(q4_llama_graph *graph);
+
 /* Static string for a status code. */
 const char *q4_strerror(int status);
 

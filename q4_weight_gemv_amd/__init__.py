@@ -61,6 +61,22 @@ class q4_gemv_op(ctypes.Structure):
                 ("m", ctypes.c_int64), ("k", ctypes.c_int64), ("epilogue", ctypes.c_int)]
 
 
+class q4_llama_config(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int), ("hidden", ctypes.c_int), ("heads", ctypes.c_int), ("kv_heads", ctypes.c_int),
+                ("head_dim", ctypes.c_int), ("ffn", ctypes.c_int), ("vocab", ctypes.c_int), ("max_pos", ctypes.c_int),
+                ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+
+
+class q4_llama_layer(ctypes.Structure):
+    _fields_ = [("qkv", ctypes.c_void_p), ("o", ctypes.c_void_p), ("gate_up", ctypes.c_void_p),
+                ("down", ctypes.c_void_p), ("norm_attn", ctypes.c_void_p), ("norm_mlp", ctypes.c_void_p)]
+
+
+class q4_llama_state(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("x", "h", "qkv", "att", "delta", "act", "logits", "k_cache", "v_cache",
+                                               "token", "pos")]
+
+
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
 _SIGS = {
@@ -78,6 +94,13 @@ _SIGS = {
                                         ctypes.POINTER(_vp)]),
     "q4_graph_launch": (ctypes.c_int, [_vp, _vp]),
     "q4_graph_destroy": (ctypes.c_int, [_vp]),
+    "q4_llama_step": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_llama_config), _vp, _vp,
+                                      ctypes.POINTER(q4_llama_layer), ctypes.POINTER(q4_llama_state), _vp]),
+    "q4_llama_graph_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_llama_config), _vp, _vp,
+                                              ctypes.POINTER(q4_llama_layer), ctypes.POINTER(q4_llama_state), _vp,
+                                              ctypes.POINTER(_vp)]),
+    "q4_llama_graph_launch": (ctypes.c_int, [_vp, _vp]),
+    "q4_llama_graph_destroy": (ctypes.c_int, [_vp]),
     "q4_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "q4_last_hip_error": (ctypes.c_char_p, []),
     "q4_read_probe": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, ctypes.c_int, _vp]),
@@ -229,3 +252,65 @@ class Q4Graph:
 def raw():
     """The ctypes library handle (tests call entry points with raw pointers)."""
     return _lib
+
+
+class LlamaStep:
+    """A Llama-family decode step over caller-owned device tensors
+    (q4_llama_step, and q4_llama_graph_* for the captured form).
+
+    cfg: dict with layers, hidden, heads, kv_heads, head_dim, ffn, vocab,
+    max_pos, theta, eps. w: dict of device tensors: emb, norm_final, and per
+    layer i qkv{i}, o{i}, gu{i}, down{i} (quantized, fmt), norm_attn{i},
+    norm_mlp{i} (float32). The state buffers are allocated here once.
+    """
+
+    def __init__(self, fmt: int, cfg: dict, w: dict):
+        import torch as _t
+
+        self.fmt, self.cfg, self.w = fmt, cfg, w
+        c = cfg
+        qkv_n = (c["heads"] + 2 * c["kv_heads"]) * c["head_dim"]
+        f32 = dict(dtype=_t.float32, device="cuda")
+        self.buf = {
+            "x": _t.zeros(c["hidden"], **f32), "h": _t.zeros(c["hidden"], **f32), "qkv": _t.zeros(qkv_n, **f32),
+            "att": _t.zeros(c["heads"] * c["head_dim"], **f32), "delta": _t.zeros(c["hidden"], **f32),
+            "act": _t.zeros(c["ffn"], **f32), "logits": _t.zeros(c["vocab"], **f32),
+            "k_cache": _t.zeros(c["layers"] * c["kv_heads"] * c["max_pos"] * c["head_dim"], **f32),
+            "v_cache": _t.zeros(c["layers"] * c["kv_heads"] * c["max_pos"] * c["head_dim"], **f32),
+            "token": _t.zeros(1, dtype=_t.int32, device="cuda"), "pos": _t.zeros(1, dtype=_t.int32, device="cuda"),
+        }
+        self._cfg = q4_llama_config(c["layers"], c["hidden"], c["heads"], c["kv_heads"], c["head_dim"], c["ffn"],
+                                    c["vocab"], c["max_pos"], c["theta"], c["eps"])
+        self._layers = (q4_llama_layer * c["layers"])()
+        for i in range(c["layers"]):
+            self._layers[i] = q4_llama_layer(w[f"qkv{i}"].data_ptr(), w[f"o{i}"].data_ptr(), w[f"gu{i}"].data_ptr(),
+                                             w[f"down{i}"].data_ptr(), w[f"norm_attn{i}"].data_ptr(),
+                                             w[f"norm_mlp{i}"].data_ptr())
+        self._state = q4_llama_state(*[self.buf[n].data_ptr() for n in
+                                       ("x", "h", "qkv", "att", "delta", "act", "logits", "k_cache", "v_cache",
+                                        "token", "pos")])
+        self._graph = None
+
+    def set(self, token: int, pos: int) -> None:
+        self.buf["token"].fill_(token)
+        self.buf["pos"].fill_(pos)
+
+    def step(self, stream=None) -> None:
+        _check(_lib.q4_llama_step(self.fmt, ctypes.byref(self._cfg), self.w["emb"].data_ptr(),
+                                  self.w["norm_final"].data_ptr(), self._layers, ctypes.byref(self._state),
+                                  _stream_ptr(stream)), "q4_llama_step")
+
+    def capture(self, stream=None) -> None:
+        h = ctypes.c_void_p(None)
+        _check(_lib.q4_llama_graph_create(self.fmt, ctypes.byref(self._cfg), self.w["emb"].data_ptr(),
+                                          self.w["norm_final"].data_ptr(), self._layers, ctypes.byref(self._state),
+                                          _stream_ptr(stream), ctypes.byref(h)), "q4_llama_graph_create")
+        self._graph = h
+
+    def replay(self, stream=None) -> None:
+        _check(_lib.q4_llama_graph_launch(self._graph, _stream_ptr(stream)), "q4_llama_graph_launch")
+
+    def close(self) -> None:
+        if self._graph is not None:
+            _lib.q4_llama_graph_destroy(self._graph)
+            self._graph = None

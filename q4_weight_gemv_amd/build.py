@@ -43,6 +43,7 @@ SOURCES = [
     ("q4_gemv_q2_k_b.hip", "device"),
     ("q4_gemm.hip", "device"),
     ("q4_stack.hip", "device"),
+    ("q4_step.hip", "device"),
     ("q4_bench.hip", "device"),
 ]
 

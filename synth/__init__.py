@@ -140,3 +140,32 @@ def smollm2_360m_layer():
 def llama7b_layer():
     """7B-class layer as listed: 4096->4096, 4096->11008 (gate, up) and 11008->4096."""
     return [(4096, 4096), (4096, 11008), (4096, 11008), (11008, 4096)]
+
+
+# ---------------------------------------------------------------------------
+# A whole Llama-family model (float weights only; quantization happens elsewhere).
+# ---------------------------------------------------------------------------
+
+SMOLLM2_360M = dict(layers=32, hidden=960, heads=15, kv_heads=5, head_dim=64, ffn=2560, vocab=49152, max_pos=1024,
+                    theta=100000.0, eps=1e-5)
+
+
+def llama_float_weights(cfg: dict, seed: int = 5000):
+    """Seeded float32 weights for every matrix of a Llama-family model (keys as
+    the decode-step runners use them: emb, qkv{i}, o{i}, gu{i} (gate rows then
+    up rows), down{i}) and its norm gains (norm_attn{i}, norm_mlp{i},
+    norm_final: 1 + N(0, 0.1)). Matrices ~ N(0, 0.02), the embedding N(0, 0.5)
+    so that a token's row is of order one."""
+    c = cfg
+    qn, kvn = c["heads"] * c["head_dim"], c["kv_heads"] * c["head_dim"]
+    out = {"emb": weights(seed, c["vocab"], c["hidden"], 0.5)}
+    for i in range(c["layers"]):
+        s = seed + 10 * (i + 1)
+        out[f"qkv{i}"] = weights(s + 1, qn + 2 * kvn, c["hidden"])
+        out[f"o{i}"] = weights(s + 2, c["hidden"], qn)
+        out[f"gu{i}"] = weights(s + 3, 2 * c["ffn"], c["hidden"])
+        out[f"down{i}"] = weights(s + 4, c["hidden"], c["ffn"])
+        out[f"norm_attn{i}"] = (1.0 + activations(s + 5, 1, c["hidden"], 0.1)[0]).astype(np.float32)
+        out[f"norm_mlp{i}"] = (1.0 + activations(s + 6, 1, c["hidden"], 0.1)[0]).astype(np.float32)
+    out["norm_final"] = (1.0 + activations(seed + 7, 1, c["hidden"], 0.1)[0]).astype(np.float32)
+    return out

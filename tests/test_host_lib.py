@@ -280,6 +280,39 @@ def test_sequence_epilogue_field(q4):
     assert lib.q4_gemv_sequence(0, ops, 1, 1, None) == q4.Q4_EUNSUPPORTED
 
 
+def test_llama_step_argument_errors(q4):
+    lib = q4.raw()
+    cfg = q4.q4_llama_config(2, 128, 4, 2, 32, 256, 384, 16, 1e4, 1e-5)
+    layers = (q4.q4_llama_layer * 2)()
+    for i in range(2):
+        layers[i] = q4.q4_llama_layer(A16, A16, A16, A16, A16, A16)
+    st = q4.q4_llama_state(*([A16] * 11))
+    f = lib.q4_llama_step
+    ok = lambda c=cfg, s=st: f(0, ctypes.byref(c), A16, A16, layers, ctypes.byref(s), None)  # noqa: E731
+    assert f(0, None, A16, A16, layers, ctypes.byref(st), None) == q4.Q4_EINVAL
+    assert f(0, ctypes.byref(cfg), None, A16, layers, ctypes.byref(st), None) == q4.Q4_EINVAL
+    assert f(9, ctypes.byref(cfg), A16, A16, layers, ctypes.byref(st), None) == q4.Q4_EUNSUPPORTED
+    bad = q4.q4_llama_config(2, 128, 4, 3, 32, 256, 384, 16, 1e4, 1e-5)       # heads % kv_heads
+    assert ok(bad) == q4.Q4_EINVAL
+    bad = q4.q4_llama_config(2, 128, 4, 2, 33, 256, 384, 16, 1e4, 1e-5)       # odd head_dim
+    assert ok(bad) == q4.Q4_EUNSUPPORTED
+    bad = q4.q4_llama_config(2, 128, 4, 2, 32, 256, 384, 9000, 1e4, 1e-5)     # cache beyond the LDS scores
+    assert ok(bad) == q4.Q4_EUNSUPPORTED
+    bad = q4.q4_llama_config(2, 100, 4, 2, 32, 256, 384, 16, 1e4, 1e-5)       # hidden not whole blocks
+    assert ok(bad) == q4.Q4_EINVAL
+    bad = q4.q4_llama_config(2, 128, 4, 2, 32, 256, 384, 16, -1.0, 1e-5)      # theta
+    assert ok(bad) == q4.Q4_EINVAL
+    st2 = q4.q4_llama_state(*([A16] * 10 + [None]))                            # no position buffer
+    assert ok(cfg, st2) == q4.Q4_EINVAL
+    st3 = q4.q4_llama_state(*([A16] + [A16 + 4] + [A16] * 9))                  # misaligned h (a product input)
+    assert ok(cfg, st3) == q4.Q4_EALIGN
+    h = ctypes.c_void_p(None)
+    assert lib.q4_llama_graph_create(0, None, A16, A16, layers, ctypes.byref(st), None, ctypes.byref(h)) == q4.Q4_EINVAL
+    assert h.value is None
+    assert lib.q4_llama_graph_launch(None, None) == q4.Q4_EINVAL
+    assert lib.q4_llama_graph_destroy(None) == q4.Q4_OK
+
+
 def test_strerror(q4):
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert q4.q4_strerror(st) and q4.q4_strerror(st) != "unknown status"
