@@ -274,6 +274,43 @@ def bench_gemm(torch, q4, timer, n=512, reps=20, shapes=None, per_matrix=True):
     return out
 
 
+def bench_full_step(torch, q4, timer, fmt=0, steps=256, warmup=8):
+    """The whole SmolLM2-360M decode step (embedding, 32 layers of norm, products,
+    attention with its KV cache, the gated MLP, LM head, greedy token) as one
+    captured graph, replayed as a generation loop: tokens chain on the device.
+    One copy of the weights (a generation loop rereads the same model each step;
+    203 MB of Q4_0 weights fit the 256 MB memory-side cache)."""
+    import synth
+
+    cfg = dict(synth.SMOLLM2_360M)
+    fw = synth.llama_float_weights(cfg)
+    dev = {}
+    wbytes = 0
+    for k, v in fw.items():
+        if k.startswith("norm"):
+            dev[k] = torch.from_numpy(v).cuda()
+        else:
+            buf = q4.q4_quantize_ref(fmt, v)
+            wbytes += buf.size
+            dev[k] = torch.from_numpy(buf).cuda()
+    del fw
+    st = q4.LlamaStep(fmt, cfg, dev)
+    st.set(token=1, pos=0)
+    st.capture()
+    for _ in range(warmup):
+        st.replay()
+    torch.cuda.synchronize()
+    t = timer.region(lambda i: st.replay(), steps, 0) / steps
+    pos = int(st.buf["pos"].item())
+    st.close()
+    launches = 4 + 7 * cfg["layers"]
+    log(f"full step smollm2-360m: {t * 1e6:.1f} us/token, {1 / t:.0f} tokens/s")
+    return {"us_per_token": round(t * 1e6, 2), "tokens_per_s": round(1 / t, 1), "launches_per_step": launches,
+            "weight_bytes": wbytes, "GB_s_weights": round(wbytes / t / 1e9, 1),
+            "positions": f"{warmup}..{pos - 1}", "format": {0: "Q4_0", 1: "Q4_K", 2: "Q8_0", 3: "Q2_K"}[fmt],
+            "cache": "one weight copy (a generation loop)"}
+
+
 def bench_read_ceiling(torch, q4, timer, reps=20):
     """The measured streaming-read ceiling: 1 GiB read once per launch, and the
     7B-class weight sizes read cold (rotating copies, one graph of launches)."""
@@ -323,7 +360,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the headline workload")
     ap.add_argument("--extras", default="all",
                     help="comma list of extras to run (default all): plain, floor, gate_7b, smollm2, smollm2_fused, "
-                         "smollm2_gated, warm, read_ceiling, gemm")
+                         "smollm2_gated, warm, read_ceiling, full_step, gemm")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 64 MiB device copy (torch) once, as the reference for HBM byte counters")
     args = ap.parse_args()
@@ -449,6 +486,8 @@ def main():
             torch.cuda.empty_cache()
         if on("read_ceiling"):
             extras["read_ceiling"] = bench_read_ceiling(torch, q4, timer)
+        if on("full_step"):
+            extras["smollm2_full_decode_step"] = bench_full_step(torch, q4, timer)
         if on("gemm"):
             extras["gemm_smollm2_layer"] = bench_gemm(torch, q4, timer, reps=max(2, K // 50))
             extras["gemm_smollm2_layer_fused_qkv_gateup"] = bench_gemm(

@@ -271,9 +271,8 @@ typedef struct {            /* device buffers, all caller-owned (16-byte aligned
 } q4_llama_state;
 
 /* Enqueue one decode step (fmt for every matrix; emb: vocab x hidden, also the
- * LM head). Limits: head_dim even, at most 128 and dividing 256; max_pos at
- * most 8192; hidden at most 16384; hidden, heads * head_dim and ffn whole
- * numbers of blocks. Errors as q4_gemv for each product, Q4_EINVAL for a null
+ * LM head). Limits: head_dim 32, 64 or 128; max_pos at most 8192; hidden,
+ * heads * head_dim and ffn whole numbers of blocks. Errors as q4_gemv for each product, Q4_EINVAL for a null
  * pointer or an inconsistent configuration, Q4_EUNSUPPORTED beyond the limits. */
 int q4_llama_step(int fmt, const q4_llama_config *cfg, const void *emb, const float *norm_final,
                   const q4_llama_layer *layers, const q4_llama_state *state, void *hip_stream);

@@ -24,9 +24,8 @@ namespace q4 {
 namespace step {
 
 constexpr int kThreads = 256;
-constexpr int kMaxHeadDim = 128;
 constexpr int kMaxPos = 8192;       // scores of one head live in LDS
-constexpr int kMaxHidden = 16384;   // per-thread registers of the norm kernel: 64 values
+constexpr int kMaxHidden = 1 << 20;
 
 __device__ __forceinline__ float block_sum(float v, float *red)
 {
@@ -52,35 +51,33 @@ __device__ __forceinline__ float block_max(float v, float *red)
     return s;
 }
 
-// x += delta (when given), then h = x / sqrt(mean(x^2) + eps) * g. One group.
+// x += delta (when given), then h = x / sqrt(mean(x^2) + eps) * g. One group;
+// each thread reads its elements in one batch of loads per pass (the loops run
+// over ceil(n / 256) elements; the second pass rereads x, this thread's own
+// writes of the first).
 __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(float *__restrict__ x, const float *__restrict__ delta,
                                                                const float *__restrict__ g, float *__restrict__ h,
                                                                int n, float eps)
 {
     __shared__ float red[kThreads / 64];
-    constexpr int kPer = kMaxHidden / kThreads;
-    float v[kPer];
     float ss = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kPer; j++) {
-        const int i = threadIdx.x + j * kThreads;
-        v[j] = 0.0f;
-        if (i < n) {
-            float a = x[i];
-            if (delta) {
-                a += delta[i];
-                x[i] = a;
-            }
-            v[j] = a;
+    if (delta) {
+#pragma unroll 4
+        for (int i = threadIdx.x; i < n; i += kThreads) {
+            const float a = x[i] + delta[i];
+            x[i] = a;
+            ss = fmaf(a, a, ss);
+        }
+    } else {
+#pragma unroll 4
+        for (int i = threadIdx.x; i < n; i += kThreads) {
+            const float a = x[i];
             ss = fmaf(a, a, ss);
         }
     }
     const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(n) + eps);
-#pragma unroll
-    for (int j = 0; j < kPer; j++) {
-        const int i = threadIdx.x + j * kThreads;
-        if (i < n) h[i] = v[j] * inv * g[i];
-    }
+#pragma unroll 4
+    for (int i = threadIdx.x; i < n; i += kThreads) h[i] = x[i] * inv * g[i];
 }
 
 // Dequantized weight (r, c) of a quantized m x k matrix, any format (one value;
@@ -136,55 +133,69 @@ __device__ __forceinline__ void rope_cs(int i, int d, int pos, float log2_theta,
 // Grouped-query attention for one query head per workgroup, at the position
 // held in pos[0]: rotates the head's query and its key/value head's new key,
 // appends key and value to the caches (the group's first head writes them),
-// then softmax(q . k_t / sqrt(d)) over t <= pos and the weighted sum of values.
-// Caches: [kv_heads][max_pos][d]. A position outside [0, max_pos) writes NaN
-// outputs and touches no cache.
+// then softmax(q . k_t / sqrt(D)) over t <= pos and the weighted sum of values.
+// Caches: [kv_heads][max_pos][D]. A position outside [0, max_pos) writes NaN
+// outputs and touches no cache. Scores: one position per thread, its key row
+// read as D/4 16-byte loads issued together; values: thread (i, p) sums
+// dimension i over positions p, p + 256/D, ... four at a time.
+template <int D>
 __global__ __launch_bounds__(kThreads) void attention_kernel(const float *__restrict__ qkv, float *__restrict__ kcache,
                                                              float *__restrict__ vcache, const int32_t *__restrict__ posp,
-                                                             int heads, int kv_heads, int d, int max_pos,
-                                                             float log2_theta, float *__restrict__ out)
+                                                             int heads, int kv_heads, int max_pos, float log2_theta,
+                                                             float *__restrict__ out)
 {
-    __shared__ float qs[kMaxHeadDim], ks[kMaxHeadDim], vs[kMaxHeadDim];
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) float qs[D];
+    __shared__ __attribute__((aligned(16))) float ks[D];
+    __shared__ float vs[D];
     __shared__ float scores[kMaxPos];
     __shared__ float part[kThreads];
     __shared__ float red[kThreads / 64];
+    constexpr int half = D / 2;
     const int h = blockIdx.x;
     const int g = h / (heads / kv_heads);
     const int tid = threadIdx.x;
     const int pos = posp[0];
     if (pos < 0 || pos >= max_pos) {
-        for (int i = tid; i < d; i += kThreads) out[h * d + i] = __builtin_nanf("");
+        for (int i = tid; i < D; i += kThreads) out[h * D + i] = __builtin_nanf("");
         return;
     }
-    const int half = d / 2;
-    const float *q = qkv + h * d;
-    const float *k = qkv + heads * d + g * d;
-    const float *v = qkv + (heads + kv_heads) * d + g * d;
-    for (int i = tid; i < half; i += kThreads) {
+    const float *q = qkv + h * D;
+    const float *k = qkv + heads * D + g * D;
+    const float *v = qkv + (heads + kv_heads) * D + g * D;
+    if (tid < half) {
         float c, s;
-        rope_cs(i, d, pos, log2_theta, c, s);
-        qs[i] = q[i] * c - q[i + half] * s;
-        qs[i + half] = q[i + half] * c + q[i] * s;
-        ks[i] = k[i] * c - k[i + half] * s;
-        ks[i + half] = k[i + half] * c + k[i] * s;
+        rope_cs(tid, D, pos, log2_theta, c, s);
+        qs[tid] = q[tid] * c - q[tid + half] * s;
+        qs[tid + half] = q[tid + half] * c + q[tid] * s;
+        ks[tid] = k[tid] * c - k[tid + half] * s;
+        ks[tid + half] = k[tid + half] * c + k[tid] * s;
     }
-    for (int i = tid; i < d; i += kThreads) vs[i] = v[i];
+    if (tid < D) vs[tid] = v[tid];
     __syncthreads();
-    float *kc = kcache + static_cast<size_t>(g) * max_pos * d;
-    float *vc = vcache + static_cast<size_t>(g) * max_pos * d;
-    if (h % (heads / kv_heads) == 0)
-        for (int i = tid; i < d; i += kThreads) {
-            kc[static_cast<size_t>(pos) * d + i] = ks[i];
-            vc[static_cast<size_t>(pos) * d + i] = vs[i];
-        }
-    // Scores: one position per thread (positions before pos from the cache,
-    // pos itself from the rotated key just computed).
-    const float scale = 1.0f / sqrtf(static_cast<float>(d));
+    float *kc = kcache + static_cast<size_t>(g) * max_pos * D;
+    float *vc = vcache + static_cast<size_t>(g) * max_pos * D;
+    if (h % (heads / kv_heads) == 0 && tid < D) {
+        kc[static_cast<size_t>(pos) * D + tid] = ks[tid];
+        vc[static_cast<size_t>(pos) * D + tid] = vs[tid];
+    }
+    const float scale = 1.0f / sqrtf(static_cast<float>(D));
     float mx = -INFINITY;
     for (int t = tid; t <= pos; t += kThreads) {
-        const float *kt = t == pos ? ks : kc + static_cast<size_t>(t) * d;
+        const f4 *kt = reinterpret_cast<const f4 *>(t == pos ? ks : kc + static_cast<size_t>(t) * D);
+        const f4 *qv = reinterpret_cast<const f4 *>(qs);
+        f4 r[D / 4];
+#pragma unroll
+        for (int j = 0; j < D / 4; j++) r[j] = kt[j];
         float s = 0.0f;
-        for (int i = 0; i < d; i++) s = fmaf(qs[i], kt[i], s);
+#pragma unroll
+        for (int j = 0; j < D / 4; j++) {
+            const f4 qq = qv[j];
+            s = fmaf(qq.x, r[j].x, s);
+            s = fmaf(qq.y, r[j].y, s);
+            s = fmaf(qq.z, r[j].z, s);
+            s = fmaf(qq.w, r[j].w, s);
+        }
         s *= scale;
         scores[t] = s;
         mx = fmaxf(mx, s);
@@ -197,20 +208,26 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const float *__rest
         sum += e;
     }
     sum = block_sum(sum, red);  // its barriers also publish scores[]
-    // Output: thread (i, p) sums dimension i over positions p, p + P, ...
-    const int P = kThreads / d;  // d divides kThreads (checked by the host)
-    const int i = tid % d, p0 = tid / d;
-    float acc = 0.0f;
-    for (int t = p0; t <= pos; t += P) {
-        const float vt = t == pos ? vs[i] : vc[static_cast<size_t>(t) * d + i];
-        acc = fmaf(scores[t], vt, acc);
+    constexpr int P = kThreads / D;
+    const int i = tid % D, p0 = tid / D;
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    int t = p0;
+    for (; t + 3 * P < pos; t += 4 * P) {  // four positions before pos at a time
+        const float v0 = vc[static_cast<size_t>(t) * D + i], v1 = vc[static_cast<size_t>(t + P) * D + i];
+        const float v2 = vc[static_cast<size_t>(t + 2 * P) * D + i], v3 = vc[static_cast<size_t>(t + 3 * P) * D + i];
+        a0 = fmaf(scores[t], v0, a0);
+        a1 = fmaf(scores[t + P], v1, a1);
+        a2 = fmaf(scores[t + 2 * P], v2, a2);
+        a3 = fmaf(scores[t + 3 * P], v3, a3);
     }
-    part[tid] = acc;
+    for (; t <= pos; t += P) a0 = fmaf(scores[t], t == pos ? vs[i] : vc[static_cast<size_t>(t) * D + i], a0);
+    part[tid] = (a0 + a1) + (a2 + a3);
     __syncthreads();
-    if (tid < d) {
+    if (tid < D) {
         float o = 0.0f;
-        for (int p = 0; p < P; p++) o += part[p * d + tid];
-        out[h * d + tid] = o / sum;
+#pragma unroll
+        for (int p = 0; p < P; p++) o += part[p * D + tid];
+        out[h * D + tid] = o / sum;
     }
 }
 
@@ -223,9 +240,10 @@ __global__ __launch_bounds__(1024) void argmax_advance_kernel(const float *__res
     __shared__ int bi[16];
     float best = -INFINITY;
     int idx = 0x7FFFFFFF;
-    for (int i = threadIdx.x; i < n; i += 1024) {
+#pragma unroll 8
+    for (int i = threadIdx.x; i < n; i += 1024) {  // indices ascend, so a strict > keeps the lowest
         const float v = logits[i];
-        if (v > best || (v == best && i < idx)) {
+        if (v > best) {
             best = v;
             idx = i;
         }
@@ -272,7 +290,7 @@ int check_step(int fmt, const q4_llama_config *c, const void *emb, const float *
     if (c->layers <= 0 || c->heads <= 0 || c->kv_heads <= 0 || c->heads % c->kv_heads || c->vocab <= 0 ||
         c->max_pos <= 0 || !(c->norm_eps >= 0.0f) || !(c->rope_theta > 0.0f))
         return Q4_EINVAL;
-    if (c->head_dim < 2 || c->head_dim % 2 || c->head_dim > kMaxHeadDim || kThreads % c->head_dim) return Q4_EUNSUPPORTED;
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return Q4_EUNSUPPORTED;
     if (c->max_pos > kMaxPos || c->hidden > kMaxHidden) return Q4_EUNSUPPORTED;
     // Every product's input length is a whole number of blocks.
     if (!multiple(c->hidden, blk) || !multiple(static_cast<int64_t>(c->heads) * c->head_dim, blk) || !multiple(c->ffn, blk))
@@ -280,6 +298,9 @@ int check_step(int fmt, const q4_llama_config *c, const void *emb, const float *
     if (!st->x || !st->h || !st->qkv || !st->att || !st->delta || !st->act || !st->logits || !st->k_cache ||
         !st->v_cache || !st->token || !st->pos)
         return Q4_EINVAL;
+    // The attention reads cache rows as 16-byte vectors.
+    if ((reinterpret_cast<uintptr_t>(st->k_cache) & 15) || (reinterpret_cast<uintptr_t>(st->v_cache) & 15))
+        return Q4_EALIGN;
     const int64_t qkv_n = static_cast<int64_t>(c->heads + 2 * c->kv_heads) * c->head_dim;
     const int64_t hd = c->hidden, qn = static_cast<int64_t>(c->heads) * c->head_dim;
     for (int i = 0; i < c->layers; i++) {
@@ -311,9 +332,16 @@ int enqueue_step(int fmt, const q4_llama_config *c, const void *emb, const float
         r = ok(hipGetLastError());
         if (r == Q4_OK) r = q4::launch_gemv(fmt, L[i].qkv, st->h, st->qkv, qkv_n, hd, 1, s);
         if (r == Q4_OK) {
-            hipLaunchKernelGGL(attention_kernel, dim3(c->heads), dim3(kThreads), 0, s, st->qkv, st->k_cache + i * cache_layer,
-                               st->v_cache + i * cache_layer, st->pos, c->heads, c->kv_heads, c->head_dim, c->max_pos,
-                               log2_theta, st->att);
+            float *kc = st->k_cache + i * cache_layer, *vc = st->v_cache + i * cache_layer;
+            if (c->head_dim == 32)
+                hipLaunchKernelGGL(attention_kernel<32>, dim3(c->heads), dim3(kThreads), 0, s, st->qkv, kc, vc, st->pos,
+                                   c->heads, c->kv_heads, c->max_pos, log2_theta, st->att);
+            else if (c->head_dim == 64)
+                hipLaunchKernelGGL(attention_kernel<64>, dim3(c->heads), dim3(kThreads), 0, s, st->qkv, kc, vc, st->pos,
+                                   c->heads, c->kv_heads, c->max_pos, log2_theta, st->att);
+            else
+                hipLaunchKernelGGL(attention_kernel<128>, dim3(c->heads), dim3(kThreads), 0, s, st->qkv, kc, vc, st->pos,
+                                   c->heads, c->kv_heads, c->max_pos, log2_theta, st->att);
             r = ok(hipGetLastError());
         }
         if (r == Q4_OK) r = q4::launch_gemv(fmt, L[i].o, st->att, st->delta, hd, qn, 1, s);

@@ -294,7 +294,7 @@ def test_llama_step_argument_errors(q4):
     assert f(9, ctypes.byref(cfg), A16, A16, layers, ctypes.byref(st), None) == q4.Q4_EUNSUPPORTED
     bad = q4.q4_llama_config(2, 128, 4, 3, 32, 256, 384, 16, 1e4, 1e-5)       # heads % kv_heads
     assert ok(bad) == q4.Q4_EINVAL
-    bad = q4.q4_llama_config(2, 128, 4, 2, 33, 256, 384, 16, 1e4, 1e-5)       # odd head_dim
+    bad = q4.q4_llama_config(2, 128, 4, 2, 48, 256, 384, 16, 1e4, 1e-5)       # head_dim not 32, 64, 128
     assert ok(bad) == q4.Q4_EUNSUPPORTED
     bad = q4.q4_llama_config(2, 128, 4, 2, 32, 256, 384, 9000, 1e4, 1e-5)     # cache beyond the LDS scores
     assert ok(bad) == q4.Q4_EUNSUPPORTED
@@ -306,6 +306,8 @@ def test_llama_step_argument_errors(q4):
     assert ok(cfg, st2) == q4.Q4_EINVAL
     st3 = q4.q4_llama_state(*([A16] + [A16 + 4] + [A16] * 9))                  # misaligned h (a product input)
     assert ok(cfg, st3) == q4.Q4_EALIGN
+    st4 = q4.q4_llama_state(*([A16] * 7 + [A16 + 8] + [A16] * 3))              # misaligned key cache
+    assert ok(cfg, st4) == q4.Q4_EALIGN
     h = ctypes.c_void_p(None)
     assert lib.q4_llama_graph_create(0, None, A16, A16, layers, ctypes.byref(st), None, ctypes.byref(h)) == q4.Q4_EINVAL
     assert h.value is None
