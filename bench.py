@@ -275,8 +275,9 @@ def bench_gemm(torch, q4, timer, n=512, reps=20, shapes=None, per_matrix=True):
 
 
 def bench_full_step(torch, q4, timer, fmt=0, steps=256, warmup=8):
-    """The whole SmolLM2-360M decode step (embedding, 32 layers of norm, products,
-    attention with its KV cache, the gated MLP, LM head, greedy token) as one
+    """The whole SmolLM2-360M decode step (embedding, 32 layers of products with
+    the residual add + RMSNorm fused in, attention with its KV cache, the gated
+    MLP, LM head, greedy token) as one
     captured graph, replayed as a generation loop: tokens chain on the device.
     One copy of the weights (a generation loop rereads the same model each step;
     203 MB of Q4_0 weights fit the 256 MB memory-side cache)."""
@@ -303,7 +304,7 @@ def bench_full_step(torch, q4, timer, fmt=0, steps=256, warmup=8):
     t = timer.region(lambda i: st.replay(), steps, 0) / steps
     pos = int(st.buf["pos"].item())
     st.close()
-    launches = 4 + 7 * cfg["layers"]
+    launches = 3 + 5 * cfg["layers"]  # embedding; per layer 5; LM head, selection
     log(f"full step smollm2-360m: {t * 1e6:.1f} us/token, {1 / t:.0f} tokens/s")
     return {"us_per_token": round(t * 1e6, 2), "tokens_per_s": round(1 / t, 1), "launches_per_step": launches,
             "weight_bytes": wbytes, "GB_s_weights": round(wbytes / t / 1e9, 1),

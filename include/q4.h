@@ -147,6 +147,28 @@ int q4_gemv(int fmt, const void *w, const float *x, float *y,
 int q4_gemv_glu(int fmt, const void *w, const float *x, float *y,
                 int64_t m, int64_t k, int64_t n, void *hip_stream);
 
+/* One-token decode product with the residual add and RMSNorm of its input
+ * fused into the launch (the normalisation ahead of each projection block of
+ * a Llama-family model, the family of the SmolLM2 models the MicroLLM Lab post
+ * runs; fused kernels: WebGPT README, "Roadmap"). With v = x + delta (v = x if
+ * delta is NULL) and h = v / sqrt(mean(v^2) + eps) * gain:
+ *   epilogue Q4_EPILOGUE_NONE:     y = W h, W of m rows (as q4_gemv, n = 1);
+ *   epilogue Q4_EPILOGUE_SILU_MUL: y = silu(W_gate h) * (W_up h), W of 2m
+ *     rows (as q4_gemv_glu, n = 1);
+ * and, if x_out is not NULL, x_out = v (the updated residual stream).
+ * The kernel stages v * gain and scales each reduced row sum by the fp32
+ * factor 1/sqrt(mean(v^2) + eps) (the same value for every row), so the
+ * product's tolerance is q4_gemv's, relative to the normalised input.
+ * x, delta, gain, x_out: device float32 [k], 16-byte aligned; x_out must not
+ * overlap x, delta or y (it is written while they are read). y: device
+ * float32 [m]. k at most 14560 (the whole row is staged in one workgroup's
+ * LDS). Errors as q4_gemv / q4_gemv_glu, plus Q4_EINVAL for a NULL gain, an
+ * eps that is negative, infinite or NaN, an overlapping x_out or an unknown
+ * epilogue, Q4_EALIGN for a misaligned delta, gain or x_out and
+ * Q4_EUNSUPPORTED for a longer row. */
+int q4_gemv_addnorm(int fmt, const void *w, const float *x, const float *delta, const float *gain, float eps,
+                    float *x_out, float *y, int64_t m, int64_t k, int epilogue, void *hip_stream);
+
 /* Tile geometry of the decode product. The library picks it per shape; the
  * tuned entry point lets a sweep override it (tile and workgroup sizes are
  * tunable parameters whose defaults come from an empirical sweep: Llamas on
@@ -167,6 +189,16 @@ typedef struct {
  * Q4_EUNSUPPORTED for a geometry that is not instantiated. */
 int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y,
                   int64_t m, int64_t k, int64_t n, const q4_gemv_tuning *tuning, void *hip_stream);
+
+/* q4_gemv_addnorm with an explicit tile geometry; same arguments, results and
+ * errors, plus Q4_EINVAL for a null or negative tuning and Q4_EUNSUPPORTED for
+ * a geometry that is not instantiated for the fused product. Instantiated:
+ * (8,1,1) (16,1,1) (16,1,4) (32,1,4) (32,1,8) (32,2,1) (32,2,4) (64,1,4) with
+ * Q4_EPILOGUE_NONE; (16,2,1) (16,2,4) (32,2,1) (32,2,4) (64,2,4) with
+ * Q4_EPILOGUE_SILU_MUL. */
+int q4_gemv_addnorm_tuned(int fmt, const void *w, const float *x, const float *delta, const float *gain, float eps,
+                          float *x_out, float *y, int64_t m, int64_t k, int epilogue,
+                          const q4_gemv_tuning *tuning, void *hip_stream);
 
 /* Prefill product Y[t][i] = sum_k bf16_rne(w_hat[i][k]) * X[t][k], fp32 out.
  * w: device, quantized as above (Q4_0 or Q4_K), 16-byte aligned; x_bf16: device bf16 bit
@@ -244,7 +276,11 @@ int q4_graph_destroy(q4_graph *graph);
  * the caller's (Llamas on the Web, technical summary, Methodology section 1).
  * The token and its position are device int32 values read by the step's
  * kernels, so a captured step replays as a generation loop. A position outside
- * [0, max_pos) makes the attention outputs NaN and writes no cache entry. */
+ * [0, max_pos) makes the attention outputs NaN and writes no cache entry.
+ * Each residual add and RMSNorm runs inside the product that consumes it
+ * (q4_gemv_addnorm): the residual stream alternates between the buffers x and
+ * h (a product reads one and writes x + delta to the other), and after the
+ * step h holds the final residual stream x + delta. */
 typedef struct {
     int layers, hidden, heads, kv_heads, head_dim, ffn, vocab, max_pos;
     float rope_theta, norm_eps;
@@ -255,11 +291,11 @@ typedef struct {
     const void *o;          /* hidden rows x heads * head_dim */
     const void *gate_up;    /* 2 ffn rows (gate, then up) x hidden, as for q4_gemv_glu */
     const void *down;       /* hidden rows x ffn */
-    const float *norm_attn, *norm_mlp;  /* hidden each */
+    const float *norm_attn, *norm_mlp;  /* hidden each, device, 16-byte aligned */
 } q4_llama_layer;
 
 typedef struct {            /* device buffers, all caller-owned (16-byte aligned) */
-    float *x, *h;           /* hidden each: the residual stream and the normed input */
+    float *x, *h;           /* hidden each: the residual stream, alternating between the two */
     float *qkv;             /* (heads + 2 kv_heads) * head_dim */
     float *att;             /* heads * head_dim */
     float *delta;           /* hidden */
@@ -271,7 +307,8 @@ typedef struct {            /* device buffers, all caller-owned (16-byte aligned
 } q4_llama_state;
 
 /* Enqueue one decode step (fmt for every matrix; emb: vocab x hidden, also the
- * LM head). Limits: head_dim 32, 64 or 128; max_pos at most 8192; hidden,
+ * LM head; norm_final: hidden, device, 16-byte aligned). Limits: head_dim 32,
+ * 64 or 128; max_pos at most 8192; hidden at most 14560; hidden,
  * heads * head_dim and ffn whole numbers of blocks. Errors as q4_gemv for each product, Q4_EINVAL for a null
  * pointer or an inconsistent configuration, Q4_EUNSUPPORTED beyond the limits. */
 int q4_llama_step(int fmt, const q4_llama_config *cfg, const void *emb, const float *norm_final,

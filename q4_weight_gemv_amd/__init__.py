@@ -84,6 +84,10 @@ _SIGS = {
     "q4_quantize_ref": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i64, _vp, ctypes.c_size_t]),
     "q4_gemv": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "q4_gemv_glu": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "q4_gemv_addnorm": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _i64, _i64,
+                                        ctypes.c_int, _vp]),
+    "q4_gemv_addnorm_tuned": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _i64, _i64,
+                                              ctypes.c_int, ctypes.POINTER(q4_gemv_tuning), _vp]),
     "q4_gemv_tuned": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64,
                                       ctypes.POINTER(q4_gemv_tuning), _vp]),
     "q4_gemm": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -166,6 +170,25 @@ def q4_gemv_glu(fmt: int, w, x, y, m: int, k: int, stream=None) -> None:
     n = x.shape[0] if x.dim() == 2 else 1
     _check(_lib.q4_gemv_glu(fmt, w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k, n, _stream_ptr(stream)),
            "q4_gemv_glu")
+
+
+def q4_gemv_addnorm(fmt: int, w, x, delta, gain, eps: float, x_out, y, m: int, k: int,
+                    epilogue: int = 0, stream=None) -> None:
+    """One token: v = x + delta (delta may be None), x_out = v (if given), and
+    y = W rmsnorm(v) * gain, or silu(W_gate .) * (W_up .) with Q4_EPILOGUE_SILU_MUL."""
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    _check(_lib.q4_gemv_addnorm(fmt, w.data_ptr(), x.data_ptr(), ptr(delta), ptr(gain), eps, ptr(x_out),
+                                y.data_ptr(), m, k, epilogue, _stream_ptr(stream)), "q4_gemv_addnorm")
+
+
+def q4_gemv_addnorm_tuned(fmt: int, w, x, delta, gain, eps: float, x_out, y, m: int, k: int, epilogue: int,
+                          lanes_per_row=0, rows_per_lane=0, waves_per_group=0, groups_per_cu=0, stream=None) -> None:
+    """q4_gemv_addnorm with an explicit tile geometry (0 keeps the library's choice)."""
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    t = q4_gemv_tuning(lanes_per_row, rows_per_lane, waves_per_group, groups_per_cu)
+    _check(_lib.q4_gemv_addnorm_tuned(fmt, w.data_ptr(), x.data_ptr(), ptr(delta), ptr(gain), eps, ptr(x_out),
+                                      y.data_ptr(), m, k, epilogue, ctypes.byref(t), _stream_ptr(stream)),
+           "q4_gemv_addnorm_tuned")
 
 
 # The instantiated tile geometries, as the header lists them.

@@ -574,14 +574,25 @@ __device__ __forceinline__ float dpp(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
+// Buffers of the fused residual add + RMSNorm (one token): the staged
+// activation is (x + delta) * gain; `out` receives x + delta (its range is
+// empty except in the one workgroup that writes it); ssq accumulates this
+// thread's squares of x + delta.
+struct NormIo {
+    __amdgpu_buffer_rsrc_t delta, gain, out;
+    float ssq;
+};
+
 // Round one of the staging issues P items' activation loads per thread, then
 // calls issue() (the first weight batch), and only then waits for the
 // activations, so the weight loads are in flight during the staging and the
 // staging waits on one L2 round trip per round, not one per item.
-template <class F, int N, int NT, int P, bool LO, class Issue>
+template <class F, int N, int NT, int P, bool LO, bool NORM, class Issue>
 __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, int nuc, int uc,
-                                      u32x4 *__restrict__ xs, f32x4 *__restrict__ meta, int tid, Issue issue)
+                                      u32x4 *__restrict__ xs, f32x4 *__restrict__ meta, int tid, NormIo &nio,
+                                      Issue issue)
 {
+    static_assert(!NORM || N == 1, "the fused norm is a one-token prologue");
     const int per_tok = nuc * 4;
     const int total = N * per_tok;
     // it / per_tok as a multiply-high by ceil(2^32 / per_tok): exact while
@@ -599,15 +610,23 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
     bool issued = false;
     for (int rb = 0; rb < total || !issued; rb += P * NT) {
         const int base = rb + tid;
-        f32x4 a[P], b[P];
+        f32x4 a[P], b[P], da[P], db[P], ga[P], gb[P];
+        uint32_t offs[P];
 #pragma unroll
         for (int p = 0; p < P; p++) {
             // Branch-free: an item past the end lands past N*K and reads zeros.
             int t, rem;
             split_item(base + p * NT, t, rem);
             const uint32_t off = static_cast<uint32_t>(t * K + F::item_base(c0 + (rem >> 2), rem & 3)) * 4u;
+            offs[p] = off;
             a[p] = __builtin_bit_cast(f32x4, load16<0>(xr, off, 0));
             b[p] = __builtin_bit_cast(f32x4, load16<0>(xr, off + 4u * F::kHighOffset, 0));
+            if constexpr (NORM) {
+                da[p] = __builtin_bit_cast(f32x4, load16<0>(nio.delta, off, 0));
+                db[p] = __builtin_bit_cast(f32x4, load16<0>(nio.delta, off + 4u * F::kHighOffset, 0));
+                ga[p] = __builtin_bit_cast(f32x4, load16<0>(nio.gain, off, 0));
+                gb[p] = __builtin_bit_cast(f32x4, load16<0>(nio.gain, off + 4u * F::kHighOffset, 0));
+            }
         }
         if (!issued) {
             // Keep the scheduler from moving activation loads behind the weights.
@@ -620,6 +639,10 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
         // cover them too).
 #pragma unroll
         for (int p = 0; p < P; p++) asm volatile("" ::"v"(a[p]), "v"(b[p]));
+        if constexpr (NORM) {
+#pragma unroll
+            for (int p = 0; p < P; p++) asm volatile("" ::"v"(da[p]), "v"(db[p]), "v"(ga[p]), "v"(gb[p]));
+        }
 #pragma unroll
         for (int p = 0; p < P; p++) {
             // Slots with no live item in the whole workgroup are skipped (a
@@ -627,6 +650,27 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
             // compute on zeros and store nothing.
             if (rb + p * NT >= total) break;
             const bool live = base + p * NT < total;
+            if constexpr (NORM) {
+                // Residual add, its squares, its write-back (dead lanes hold
+                // zeros at offsets past the end: nothing added or stored),
+                // then the gain; the row's 1/rms scales the reduced sums.
+                a[p] += da[p];
+                b[p] += db[p];
+                float q = a[p].x * a[p].x;
+                q = __builtin_fmaf(a[p].y, a[p].y, q);
+                q = __builtin_fmaf(a[p].z, a[p].z, q);
+                q = __builtin_fmaf(a[p].w, a[p].w, q);
+                q = __builtin_fmaf(b[p].x, b[p].x, q);
+                q = __builtin_fmaf(b[p].y, b[p].y, q);
+                q = __builtin_fmaf(b[p].z, b[p].z, q);
+                q = __builtin_fmaf(b[p].w, b[p].w, q);
+                nio.ssq += q;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a[p]), nio.out, offs[p], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b[p]), nio.out,
+                                                       offs[p] + 4u * F::kHighOffset, 0, 0);
+                a[p] *= ga[p];
+                b[p] *= gb[p];
+            }
             int t, rem;
             split_item(live ? base + p * NT : 0, t, rem);
             const int ul = rem >> 2;
@@ -722,14 +766,22 @@ __device__ __forceinline__ float silu_mul(float g, float u)
 // M + o of the same output o = tile*RPG/2 + wave*RPW/2 + sub + p*(64/LPR).
 // Each row's sum is formed exactly as in the plain product (same lanes, same
 // order), and the epilogue applies silu_mul to the two reduced sums.
+//
+// NORM (one token, whole row staged): the input is rmsnorm(x + delta) *
+// gain. Staging forms v = x + delta, stages v * gain and sums v^2; workgroup
+// 0 also writes v to pro.x_out. As W (r v * gain) = r W (v * gain), the
+// factor r = 1/sqrt(mean(v^2) + eps) multiplies each reduced row sum (before
+// the gated epilogue). Every workgroup forms the same sum of squares (the
+// same items, lanes and order), so every row sees the same r.
 
-template <class F, int N, int LPR, int R, int WAVES, int JB, bool LO, bool GLU = false>
+template <class F, int N, int LPR, int R, int WAVES, int JB, bool LO, bool GLU = false, bool NORM = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restrict__ w, uint32_t wbytes,
                                                           const float *__restrict__ x,
                                                           float *__restrict__ y, int M, int K, int uc,
-                                                          int ntiles)
+                                                          int ntiles, Prologue pro)
 {
     static_assert(!GLU || R % 2 == 0, "the gated product pairs row slots");
+    static_assert(!NORM || N == 1, "the fused norm is a one-token prologue");
     constexpr int SUBS = 64 / LPR;
     constexpr int RPW = SUBS * R;
     constexpr int RPG = WAVES * RPW;
@@ -739,6 +791,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     extern __shared__ u32x4 lds[];
     u32x4 *xs = lds;
     f32x4 *meta = reinterpret_cast<f32x4 *>(lds + N * 8 * uc);
+    float *wave_ssq = reinterpret_cast<float *>(meta + N * uc);  // NORM: one sum per wave
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -796,12 +849,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
             if (ul < nuc) F::template accumulate<N, R, LO>(g[jj], xs, meta, ul, uc, static_cast<uint32_t>(c0 + ul), acc);
         }
     };
+    // 1/rms of the fused norm (set once the staging is complete).
+    float rn = 1.0f;
+    auto scaled = [&](float v) {
+        if constexpr (NORM)
+            return v * rn;
+        else
+            return v;
+    };
     // Reduced output value of output slot ro, token t.
     auto finish = [&](int ro, int t) {
         if constexpr (GLU)
-            return silu_mul(row_reduce<LPR>(acc[2 * ro][t]), row_reduce<LPR>(acc[2 * ro + 1][t]));
+            return silu_mul(scaled(row_reduce<LPR>(acc[2 * ro][t])), scaled(row_reduce<LPR>(acc[2 * ro + 1][t])));
         else
-            return row_reduce<LPR>(acc[ro][t]);
+            return scaled(row_reduce<LPR>(acc[ro][t]));
     };
     auto reduce_store = [&](int tile) {
 #pragma unroll
@@ -842,6 +903,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     int tile = blockIdx.x;
     if (tile >= ntiles) return;  // uniform across the workgroup
     Regs ga[JB][R], gb[JB][R];
+    NormIo nio{xr, xr, xr, 0.0f};
+    if constexpr (NORM) {
+        const uint32_t kb = static_cast<uint32_t>(K) * 4u;
+        nio.delta = make_rsrc(pro.delta, pro.delta ? kb : 0u);
+        nio.gain = make_rsrc(pro.gain, kb);
+        nio.out = make_rsrc(pro.x_out, pro.x_out && blockIdx.x == 0 ? kb : 0u);
+    }
 
     if (uc >= nu) {
         // Activations staged once; a flat stream of batches runs through all
@@ -876,11 +944,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
                 ct += gstride;
             }
         };
-        stage<F, N, NT, kStageRound<WAVES>, LO>(xr, K, 0, nu, uc, xs, meta, tid, [&]() {
+        stage<F, N, NT, kStageRound<WAVES>, LO, NORM>(xr, K, 0, nu, uc, xs, meta, tid, nio, [&]() {
 #pragma unroll
             for (int p = 0; p < D; p++) load_next(gbuf[p]);
         });
+        if constexpr (NORM) {
+            const float s = row_reduce<64>(nio.ssq);
+            if (lane == 0) wave_ssq[wave] = s;
+        }
         wg_sync<WAVES>();
+        if constexpr (NORM) {
+            float s = 0.0f;
+#pragma unroll
+            for (int v = 0; v < WAVES; v++) s += wave_ssq[v];
+            rn = 1.0f / __builtin_sqrtf(s / static_cast<float>(K) + pro.eps);
+        }
         for (;;) {
 #pragma unroll
             for (int p = 0; p < NBUF; p++) {
@@ -893,6 +971,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
         return;
     }
 
+    if constexpr (NORM) return;  // the host stages the whole row for the fused norm
     bool first = true;
     for (; tile < ntiles; tile += static_cast<int>(gridDim.x)) {
         for (int c0 = 0; c0 < nu; c0 += uc) {
@@ -900,8 +979,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
             const int jc = (nuc + LPR - 1) / LPR;  // unit slots per lane per row in this chunk
             if (!first) wg_sync<WAVES>();
             first = false;
-            stage<F, N, NT, kStageRound<WAVES>, LO>(xr, K, c0, nuc, uc, xs, meta, tid,
-                                                [&]() { load_batch(ga, tile, 0, c0, nuc); });
+            stage<F, N, NT, kStageRound<WAVES>, LO, false>(xr, K, c0, nuc, uc, xs, meta, tid, nio,
+                                                       [&]() { load_batch(ga, tile, 0, c0, nuc); });
             wg_sync<WAVES>();
             // Prefetches are unconditional (a batch past the chunk issues
             // no-fetch loads and is dropped) so that no branch makes the
@@ -922,9 +1001,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
 // ---- launch -----------------------------------------------------------------------
 
 // m is the number of output rows (for GLU the weights have 2m rows).
-template <class F, int N, int LPR, int R, int WAVES, bool GLU = false>
+template <class F, int N, int LPR, int R, int WAVES, bool GLU = false, bool NORM = false>
 int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t stream, int cus,
-               int groups_per_cu)
+               int groups_per_cu, const Prologue &pro = Prologue{})
 {
     constexpr int JB = F::kBatchUnits / R > 0 ? F::kBatchUnits / R : 1;
     constexpr int rows_per_wg = WAVES * (64 / LPR) * R / (GLU ? 2 : 1);
@@ -933,7 +1012,8 @@ int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStre
     const int bytes_per_unit = N * kLdsBytesPerUnit;
     if (uc * bytes_per_unit > kMaxLdsBytes) uc = kMaxLdsBytes / bytes_per_unit / 8 * 8;  // chunks of whole super-blocks
     if (uc <= 0) return Q4_EUNSUPPORTED;
-    const size_t lds = static_cast<size_t>(uc) * bytes_per_unit;
+    if (NORM && uc < nu) return Q4_EUNSUPPORTED;  // the fused norm needs the whole row staged
+    const size_t lds = static_cast<size_t>(uc) * bytes_per_unit + (NORM ? 4 * WAVES : 0);
     const int ntiles = (m + rows_per_wg - 1) / rows_per_wg;
     const long long cap = static_cast<long long>(cus) * groups_per_cu;
     const unsigned grid = static_cast<unsigned>(ntiles < cap ? ntiles : cap);
@@ -945,11 +1025,11 @@ int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStre
     // (weight rows: a gated product rounds like the plain product of its
     // stacked matrix).
     if (wrows < kLoRowLimit)
-        hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB, true, GLU>), dim3(grid), dim3(64 * WAVES), lds, stream,
-                           w, wbytes, x, y, m, k, uc, ntiles);
+        hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB, true, GLU, NORM>), dim3(grid), dim3(64 * WAVES), lds,
+                           stream, w, wbytes, x, y, m, k, uc, ntiles, pro);
     else
-        hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB, false, GLU>), dim3(grid), dim3(64 * WAVES), lds,
-                           stream, w, wbytes, x, y, m, k, uc, ntiles);
+        hipLaunchKernelGGL((gemv_kernel<F, N, LPR, R, WAVES, JB, false, GLU, NORM>), dim3(grid), dim3(64 * WAVES), lds,
+                           stream, w, wbytes, x, y, m, k, uc, ntiles, pro);
     return hip_status(hipGetLastError());
 }
 
@@ -995,6 +1075,36 @@ int dispatch_glu_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, i
 #define Q4_CFG_CASE(L, RR, WV)                                   \
     if (c.lpr == L && c.r == RR && c.waves == WV)                \
         return launch_one<F, N, L, RR, WV, true>(w, x, y, m, k, s, cus, c.groups_per_cu);
+    Q4_GEMV_GLU_CONFIGS(Q4_CFG_CASE)
+#undef Q4_CFG_CASE
+    return Q4_EUNSUPPORTED;
+}
+
+// The fused-norm product's geometries: every one-token choice of choose()
+// and choose_glu().
+#define Q4_GEMV_NORM_CONFIGS(X) \
+    X(8, 1, 1)                  \
+    X(16, 1, 1)                 \
+    X(16, 1, 4)                 \
+    X(32, 1, 4)                 \
+    X(32, 1, 8)                 \
+    X(32, 2, 1)                 \
+    X(32, 2, 4)                 \
+    X(64, 1, 4)
+
+template <class F>
+int dispatch_norm_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus,
+                      bool glu, const Prologue &pro)
+{
+    static_assert(kMaxLdsBytes / kLdsBytesPerUnit == kNormMaxUnits, "fused-norm row limit");
+#define Q4_CFG_CASE(L, RR, WV) \
+    if (!glu && c.lpr == L && c.r == RR && c.waves == WV) \
+        return launch_one<F, 1, L, RR, WV, false, true>(w, x, y, m, k, s, cus, c.groups_per_cu, pro);
+    Q4_GEMV_NORM_CONFIGS(Q4_CFG_CASE)
+#undef Q4_CFG_CASE
+#define Q4_CFG_CASE(L, RR, WV) \
+    if (glu && c.lpr == L && c.r == RR && c.waves == WV) \
+        return launch_one<F, 1, L, RR, WV, true, true>(w, x, y, m, k, s, cus, c.groups_per_cu, pro);
     Q4_GEMV_GLU_CONFIGS(Q4_CFG_CASE)
 #undef Q4_CFG_CASE
     return Q4_EUNSUPPORTED;

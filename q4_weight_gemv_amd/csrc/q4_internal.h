@@ -41,6 +41,27 @@ int device_cus();
 // thread's last HIP error (reported by q4_last_hip_error).
 int hip_status(hipError_t e);
 
+// The fused residual add + RMSNorm ahead of a one-token decode product:
+// the input is rmsnorm(x + delta) * gain, and x + delta goes to x_out.
+struct Prologue {
+    const float *delta = nullptr;  // null: no residual add
+    const float *gain = nullptr;
+    float *x_out = nullptr;        // null: not written
+    float eps = 0.0f;
+};
+
+// Longest row (in 32-weight units) the fused norm takes: the whole row is
+// staged in one workgroup's LDS (144 bytes per unit, 64 KiB).
+constexpr int64_t kNormMaxUnits = 455;
+
+// Validation of a fused-norm product (one token; glu: weights of 2m rows).
+int check_addnorm_args(int fmt, const void *w, const float *x, const Prologue &pro, const float *y, int64_t m,
+                       int64_t k, bool glu);
+
+// Launch one fused-norm product (arguments already validated).
+int launch_gemv_addnorm(int fmt, const void *w, const float *x, const Prologue &pro, float *y, int64_t m, int64_t k,
+                        bool glu, void *stream, const q4_gemv_tuning *tuning = nullptr);
+
 namespace gemv {
 
 // Tile geometry of the decode kernel.
@@ -61,6 +82,9 @@ template <class F, int N>
 int dispatch_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus);
 template <class F, int N>
 int dispatch_glu_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus);
+template <class F>
+int dispatch_norm_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus,
+                      bool glu, const Prologue &pro);
 
 }  // namespace gemv
 }  // namespace q4

@@ -8,8 +8,10 @@
 // (WebGPT README, "Roadmap"); every buffer is the caller's, allocated up front
 // (Llamas on the Web, technical summary, Methodology section 1).
 //
-// The products are the library's decode kernels (q4_gemv, the gated product);
-// the kernels here are the small operators between them. The token and its
+// The products are the library's decode kernels (q4_gemv, and for the
+// products that follow a norm the fused residual add + RMSNorm variant,
+// q4_gemv_addnorm); the kernels here are the small operators between them:
+// the embedding gather, attention and the token selection. The token and its
 // position live in device memory, read by the kernels and advanced by the last
 // one, so a captured step replays as a generation loop with no host work.
 #include <hip/hip_runtime.h>
@@ -25,7 +27,6 @@ namespace step {
 
 constexpr int kThreads = 256;
 constexpr int kMaxPos = 8192;       // scores of one head live in LDS
-constexpr int kMaxHidden = 1 << 20;
 
 __device__ __forceinline__ float block_sum(float v, float *red)
 {
@@ -49,35 +50,6 @@ __device__ __forceinline__ float block_max(float v, float *red)
     float s = red[0];
     for (int i = 1; i < kThreads / 64; i++) s = fmaxf(s, red[i]);
     return s;
-}
-
-// x += delta (when given), then h = x / sqrt(mean(x^2) + eps) * g. One group;
-// each thread reads its elements in one batch of loads per pass (the loops run
-// over ceil(n / 256) elements; the second pass rereads x, this thread's own
-// writes of the first).
-__global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(float *__restrict__ x, const float *__restrict__ delta,
-                                                               const float *__restrict__ g, float *__restrict__ h,
-                                                               int n, float eps)
-{
-    __shared__ float red[kThreads / 64];
-    float ss = 0.0f;
-    if (delta) {
-#pragma unroll 4
-        for (int i = threadIdx.x; i < n; i += kThreads) {
-            const float a = x[i] + delta[i];
-            x[i] = a;
-            ss = fmaf(a, a, ss);
-        }
-    } else {
-#pragma unroll 4
-        for (int i = threadIdx.x; i < n; i += kThreads) {
-            const float a = x[i];
-            ss = fmaf(a, a, ss);
-        }
-    }
-    const float inv = 1.0f / sqrtf(block_sum(ss, red) / static_cast<float>(n) + eps);
-#pragma unroll 4
-    for (int i = threadIdx.x; i < n; i += kThreads) h[i] = x[i] * inv * g[i];
 }
 
 // Dequantized weight (r, c) of a quantized m x k matrix, any format (one value;
@@ -135,9 +107,15 @@ __device__ __forceinline__ void rope_cs(int i, int d, int pos, float log2_theta,
 // appends key and value to the caches (the group's first head writes them),
 // then softmax(q . k_t / sqrt(D)) over t <= pos and the weighted sum of values.
 // Caches: [kv_heads][max_pos][D]. A position outside [0, max_pos) writes NaN
-// outputs and touches no cache. Scores: one position per thread, its key row
-// read as D/4 16-byte loads issued together; values: thread (i, p) sums
-// dimension i over positions p, p + 256/D, ... four at a time.
+// outputs and touches no cache.
+// The step's q, k and v are loaded alongside the position. Scores: one
+// position per thread, its key row read as D/4 16-byte loads issued together
+// (rows past pos read row pos and are dropped; the current position's key
+// comes from LDS, since another workgroup may be writing it to the cache).
+// Values: thread (c, r) holds dimensions 4c..4c+3 of positions r, r + RR, ...
+// (RR = 256 / (D/4)); VJ rows per thread are loaded at once, the first VJ
+// right behind the first key rows so that their latency overlaps the scores
+// and the softmax; the per-thread sums meet in LDS at the end.
 template <int D>
 __global__ __launch_bounds__(kThreads) void attention_kernel(const float *__restrict__ qkv, float *__restrict__ kcache,
                                                              float *__restrict__ vcache, const int32_t *__restrict__ posp,
@@ -145,33 +123,45 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const float *__rest
                                                              float *__restrict__ out)
 {
     typedef float f4 __attribute__((ext_vector_type(4)));
+    constexpr int VQ = D / 4;          // 16-byte pieces per row
+    constexpr int RR = kThreads / VQ;  // value rows per round of the workgroup
+    constexpr int VJ = 16;             // value rows per thread per chunk
+    constexpr int CH = RR * VJ;        // positions per value chunk
     __shared__ __attribute__((aligned(16))) float qs[D];
     __shared__ __attribute__((aligned(16))) float ks[D];
-    __shared__ float vs[D];
+    __shared__ __attribute__((aligned(16))) float vs[D];
     __shared__ float scores[kMaxPos];
-    __shared__ float part[kThreads];
+    __shared__ __attribute__((aligned(16))) float part[RR * D];
     __shared__ float red[kThreads / 64];
     constexpr int half = D / 2;
     const int h = blockIdx.x;
     const int g = h / (heads / kv_heads);
     const int tid = threadIdx.x;
+    const float *q = qkv + h * D;
+    const float *k = qkv + heads * D + g * D;
+    const float *v = qkv + (heads + kv_heads) * D + g * D;
+    float q0 = 0.0f, q1 = 0.0f, k0 = 0.0f, k1 = 0.0f, v0 = 0.0f;
+    if (tid < half) {
+        q0 = q[tid];
+        q1 = q[tid + half];
+        k0 = k[tid];
+        k1 = k[tid + half];
+    }
+    if (tid < D) v0 = v[tid];
     const int pos = posp[0];
     if (pos < 0 || pos >= max_pos) {
         for (int i = tid; i < D; i += kThreads) out[h * D + i] = __builtin_nanf("");
         return;
     }
-    const float *q = qkv + h * D;
-    const float *k = qkv + heads * D + g * D;
-    const float *v = qkv + (heads + kv_heads) * D + g * D;
     if (tid < half) {
         float c, s;
         rope_cs(tid, D, pos, log2_theta, c, s);
-        qs[tid] = q[tid] * c - q[tid + half] * s;
-        qs[tid + half] = q[tid + half] * c + q[tid] * s;
-        ks[tid] = k[tid] * c - k[tid + half] * s;
-        ks[tid + half] = k[tid + half] * c + k[tid] * s;
+        qs[tid] = q0 * c - q1 * s;
+        qs[tid + half] = q1 * c + q0 * s;
+        ks[tid] = k0 * c - k1 * s;
+        ks[tid + half] = k1 * c + k0 * s;
     }
-    if (tid < D) vs[tid] = v[tid];
+    if (tid < D) vs[tid] = v0;
     __syncthreads();
     float *kc = kcache + static_cast<size_t>(g) * max_pos * D;
     float *vc = vcache + static_cast<size_t>(g) * max_pos * D;
@@ -180,25 +170,50 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const float *__rest
         vc[static_cast<size_t>(pos) * D + tid] = vs[tid];
     }
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
-    float mx = -INFINITY;
-    for (int t = tid; t <= pos; t += kThreads) {
-        const f4 *kt = reinterpret_cast<const f4 *>(t == pos ? ks : kc + static_cast<size_t>(t) * D);
-        const f4 *qv = reinterpret_cast<const f4 *>(qs);
-        f4 r[D / 4];
+    const f4 *qv = reinterpret_cast<const f4 *>(qs);
+    const f4 *kl = reinterpret_cast<const f4 *>(ks);
+    auto key_row = [&](int t, f4(&r)[VQ]) {
+        const f4 *row = reinterpret_cast<const f4 *>(kc + static_cast<size_t>(t < pos ? t : pos) * D);
 #pragma unroll
-        for (int j = 0; j < D / 4; j++) r[j] = kt[j];
+        for (int j = 0; j < VQ; j++) r[j] = row[j];
+    };
+    float mx = -INFINITY;
+    auto score = [&](int t, const f4(&r)[VQ]) {
         float s = 0.0f;
 #pragma unroll
-        for (int j = 0; j < D / 4; j++) {
+        for (int j = 0; j < VQ; j++) {
             const f4 qq = qv[j];
-            s = fmaf(qq.x, r[j].x, s);
-            s = fmaf(qq.y, r[j].y, s);
-            s = fmaf(qq.z, r[j].z, s);
-            s = fmaf(qq.w, r[j].w, s);
+            const f4 kk = t == pos ? kl[j] : r[j];
+            s = fmaf(qq.x, kk.x, s);
+            s = fmaf(qq.y, kk.y, s);
+            s = fmaf(qq.z, kk.z, s);
+            s = fmaf(qq.w, kk.w, s);
         }
-        s *= scale;
-        scores[t] = s;
-        mx = fmaxf(mx, s);
+        if (t <= pos) {
+            s *= scale;
+            scores[t] = s;
+            mx = fmaxf(mx, s);
+        }
+    };
+    const int vcol = tid % VQ, vrow0 = tid / VQ;
+    f4 vrows[VJ];
+    auto value_rows = [&](int t0) {
+#pragma unroll
+        for (int j = 0; j < VJ; j++) {
+            const int t = t0 + vrow0 + j * RR;
+            vrows[j] = reinterpret_cast<const f4 *>(vc + static_cast<size_t>(t < pos ? t : pos) * D)[vcol];
+        }
+    };
+    {
+        f4 r[VQ];
+        key_row(tid, r);
+        value_rows(0);
+        score(tid, r);
+    }
+    for (int t0 = kThreads; t0 <= pos; t0 += kThreads) {
+        f4 r[VQ];
+        key_row(t0 + tid, r);
+        score(t0 + tid, r);
     }
     mx = block_max(mx, red);
     float sum = 0.0f;
@@ -208,25 +223,29 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const float *__rest
         sum += e;
     }
     sum = block_sum(sum, red);  // its barriers also publish scores[]
-    constexpr int P = kThreads / D;
-    const int i = tid % D, p0 = tid / D;
-    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-    int t = p0;
-    for (; t + 3 * P < pos; t += 4 * P) {  // four positions before pos at a time
-        const float v0 = vc[static_cast<size_t>(t) * D + i], v1 = vc[static_cast<size_t>(t + P) * D + i];
-        const float v2 = vc[static_cast<size_t>(t + 2 * P) * D + i], v3 = vc[static_cast<size_t>(t + 3 * P) * D + i];
-        a0 = fmaf(scores[t], v0, a0);
-        a1 = fmaf(scores[t + P], v1, a1);
-        a2 = fmaf(scores[t + 2 * P], v2, a2);
-        a3 = fmaf(scores[t + 3 * P], v3, a3);
+    const f4 vcur = reinterpret_cast<const f4 *>(vs)[vcol];
+    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto accumulate = [&](int t0) {
+#pragma unroll
+        for (int j = 0; j < VJ; j++) {
+            const int t = t0 + vrow0 + j * RR;
+            const float w = scores[t < pos ? t : pos];
+            const f4 vv = t == pos ? vcur : vrows[j];
+            const f4 a = acc + w * vv;
+            acc = t <= pos ? a : acc;
+        }
+    };
+    accumulate(0);
+    for (int t0 = CH; t0 <= pos; t0 += CH) {
+        value_rows(t0);
+        accumulate(t0);
     }
-    for (; t <= pos; t += P) a0 = fmaf(scores[t], t == pos ? vs[i] : vc[static_cast<size_t>(t) * D + i], a0);
-    part[tid] = (a0 + a1) + (a2 + a3);
+    reinterpret_cast<f4 *>(part)[vrow0 * VQ + vcol] = acc;
     __syncthreads();
     if (tid < D) {
         float o = 0.0f;
 #pragma unroll
-        for (int p = 0; p < P; p++) o += part[p * D + tid];
+        for (int r = 0; r < RR; r++) o += part[r * D + tid];
         out[h * D + tid] = o / sum;
     }
 }
@@ -291,7 +310,7 @@ int check_step(int fmt, const q4_llama_config *c, const void *emb, const float *
         c->max_pos <= 0 || !(c->norm_eps >= 0.0f) || !(c->rope_theta > 0.0f))
         return Q4_EINVAL;
     if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return Q4_EUNSUPPORTED;
-    if (c->max_pos > kMaxPos || c->hidden > kMaxHidden) return Q4_EUNSUPPORTED;
+    if (c->max_pos > kMaxPos || c->hidden > q4::kNormMaxUnits * q4::kUnitWeights) return Q4_EUNSUPPORTED;
     // Every product's input length is a whole number of blocks.
     if (!multiple(c->hidden, blk) || !multiple(static_cast<int64_t>(c->heads) * c->head_dim, blk) || !multiple(c->ffn, blk))
         return Q4_EINVAL;
@@ -303,15 +322,26 @@ int check_step(int fmt, const q4_llama_config *c, const void *emb, const float *
         return Q4_EALIGN;
     const int64_t qkv_n = static_cast<int64_t>(c->heads + 2 * c->kv_heads) * c->head_dim;
     const int64_t hd = c->hidden, qn = static_cast<int64_t>(c->heads) * c->head_dim;
+    // The residual stream alternates between x and h; each fused-norm product
+    // reads one and the delta and writes the other.
+    auto norm_io = [&](const float *gain, float *out) {
+        q4::Prologue p;
+        p.delta = st->delta;
+        p.gain = gain;
+        p.x_out = out;
+        p.eps = c->norm_eps;
+        return p;
+    };
     for (int i = 0; i < c->layers; i++) {
         if (!L[i].norm_attn || !L[i].norm_mlp) return Q4_EINVAL;
-        int s = q4::check_product_args(fmt, L[i].qkv, st->h, st->qkv, qkv_n, hd, 1, 8);
+        int s = q4::check_addnorm_args(fmt, L[i].qkv, st->x, norm_io(L[i].norm_attn, st->h), st->qkv, qkv_n, hd, false);
         if (s == Q4_OK) s = q4::check_product_args(fmt, L[i].o, st->att, st->delta, hd, qn, 1, 8);
-        if (s == Q4_OK) s = q4::check_glu_args(fmt, L[i].gate_up, st->h, st->act, c->ffn, hd, 1);
+        if (s == Q4_OK)
+            s = q4::check_addnorm_args(fmt, L[i].gate_up, st->h, norm_io(L[i].norm_mlp, st->x), st->act, c->ffn, hd, true);
         if (s == Q4_OK) s = q4::check_product_args(fmt, L[i].down, st->act, st->delta, hd, c->ffn, 1, 8);
         if (s != Q4_OK) return s;
     }
-    return q4::check_product_args(fmt, emb, st->h, st->logits, c->vocab, hd, 1, 8);
+    return q4::check_addnorm_args(fmt, emb, st->x, norm_io(norm_final, st->h), st->logits, c->vocab, hd, false);
 }
 
 int enqueue_step(int fmt, const q4_llama_config *c, const void *emb, const float *norm_final, const q4_llama_layer *L,
@@ -323,14 +353,23 @@ int enqueue_step(int fmt, const q4_llama_config *c, const void *emb, const float
     const size_t cache_layer = static_cast<size_t>(c->kv_heads) * c->max_pos * c->head_dim;
     const float log2_theta = std::log2(c->rope_theta);
     auto ok = [](hipError_t e) { return q4::hip_status(e); };
+    // Residual add + RMSNorm fused into the next product: it reads the stream
+    // from `in` (plus delta) and writes the updated stream to `out`.
+    auto addnorm = [&](const void *w, const float *in, bool add, const float *gain, float *out, float *y, int64_t m,
+                       bool glu) {
+        q4::Prologue p;
+        p.delta = add ? st->delta : nullptr;
+        p.gain = gain;
+        p.x_out = out;
+        p.eps = c->norm_eps;
+        return q4::launch_gemv_addnorm(fmt, w, in, p, y, m, hd, glu, s);
+    };
     hipLaunchKernelGGL(embed_kernel, dim3(1), dim3(kThreads), 0, s, fmt, static_cast<const uint8_t *>(emb), c->vocab,
                        c->hidden, st->token, st->x);
     int r = ok(hipGetLastError());
     for (int i = 0; i < c->layers && r == Q4_OK; i++) {
-        hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(1), dim3(kThreads), 0, s, st->x, i == 0 ? nullptr : st->delta,
-                           L[i].norm_attn, st->h, c->hidden, c->norm_eps);
-        r = ok(hipGetLastError());
-        if (r == Q4_OK) r = q4::launch_gemv(fmt, L[i].qkv, st->h, st->qkv, qkv_n, hd, 1, s);
+        // x (+ the previous layer's delta) -> h.
+        r = addnorm(L[i].qkv, st->x, i > 0, L[i].norm_attn, st->h, st->qkv, qkv_n, false);
         if (r == Q4_OK) {
             float *kc = st->k_cache + i * cache_layer, *vc = st->v_cache + i * cache_layer;
             if (c->head_dim == 32)
@@ -345,19 +384,13 @@ int enqueue_step(int fmt, const q4_llama_config *c, const void *emb, const float
             r = ok(hipGetLastError());
         }
         if (r == Q4_OK) r = q4::launch_gemv(fmt, L[i].o, st->att, st->delta, hd, qn, 1, s);
-        if (r == Q4_OK) {
-            hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(1), dim3(kThreads), 0, s, st->x, st->delta, L[i].norm_mlp, st->h,
-                               c->hidden, c->norm_eps);
-            r = ok(hipGetLastError());
-        }
-        if (r == Q4_OK) r = q4::launch_gemv_glu(fmt, L[i].gate_up, st->h, st->act, c->ffn, hd, 1, s);
+        // h + delta -> x.
+        if (r == Q4_OK) r = addnorm(L[i].gate_up, st->h, true, L[i].norm_mlp, st->x, st->act, c->ffn, true);
         if (r == Q4_OK) r = q4::launch_gemv(fmt, L[i].down, st->act, st->delta, hd, c->ffn, 1, s);
     }
     if (r != Q4_OK) return r;
-    hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(1), dim3(kThreads), 0, s, st->x, st->delta, norm_final, st->h, c->hidden,
-                       c->norm_eps);
-    r = ok(hipGetLastError());
-    if (r == Q4_OK) r = q4::launch_gemv(fmt, emb, st->h, st->logits, c->vocab, hd, 1, s);
+    // x + delta -> h: the final stream.
+    r = addnorm(emb, st->x, true, norm_final, st->h, st->logits, c->vocab, false);
     if (r == Q4_OK) {
         hipLaunchKernelGGL(argmax_advance_kernel, dim3(1), dim3(1024), 0, s, st->logits, c->vocab, st->token, st->pos);
         r = ok(hipGetLastError());

@@ -98,7 +98,7 @@ def test_graph_replays_match_eager_steps(env):
         graph.replay()
         torch.cuda.synchronize()
         _ = torch.randn(1000, device="cuda").sum().item()  # eager work between replays
-        for name in ("logits", "token", "pos", "x"):
+        for name in ("logits", "token", "pos", "x", "h"):
             assert torch.equal(eager.buf[name], graph.buf[name]), (pos, name)
     assert torch.equal(eager.buf["k_cache"], graph.buf["k_cache"])
     graph.close()

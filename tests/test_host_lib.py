@@ -269,6 +269,30 @@ def test_gated_product_argument_errors(q4):
     assert f(0, *ok, m, 4096, 1, None) == q4.Q4_EUNSUPPORTED
 
 
+def test_addnorm_argument_errors(q4):
+    f = q4.raw().q4_gemv_addnorm
+    W, X, D, G, XO, Y = (A16 * i for i in range(1, 7))  # disjoint fake buffers
+    assert f(0, W, X, D, None, 1e-5, XO, Y, 64, 256, 0, None) == q4.Q4_EINVAL       # no gain
+    assert f(0, W, X, D, G + 4, 1e-5, XO, Y, 64, 256, 0, None) == q4.Q4_EALIGN     # misaligned gain
+    assert f(0, W, X, D + 8, G, 1e-5, XO, Y, 64, 256, 0, None) == q4.Q4_EALIGN     # misaligned delta
+    assert f(0, W, X, D, G, 1e-5, XO + 4, Y, 64, 256, 0, None) == q4.Q4_EALIGN     # misaligned x_out
+    assert f(0, W, X + 4, D, G, 1e-5, XO, Y, 64, 256, 0, None) == q4.Q4_EALIGN     # misaligned x
+    assert f(0, W, X, D, G, 1e-5, X, Y, 64, 256, 0, None) == q4.Q4_EINVAL          # x_out is x
+    assert f(0, W, X, D, G, 1e-5, X + 512, Y, 64, 256, 0, None) == q4.Q4_EINVAL    # x_out overlaps x
+    assert f(0, W, X, D, G, 1e-5, D - 16, Y, 64, 256, 0, None) == q4.Q4_EINVAL     # x_out overlaps delta
+    assert f(0, W, X, D, G, 1e-5, Y + 64, Y, 64, 256, 0, None) == q4.Q4_EINVAL     # x_out overlaps y
+    for eps in (-1e-6, float("inf"), float("nan")):
+        assert f(0, W, X, D, G, eps, XO, Y, 64, 256, 0, None) == q4.Q4_EINVAL
+    assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 256, 7, None) == q4.Q4_EINVAL          # unknown epilogue
+    assert f(9, W, X, D, G, 1e-5, XO, Y, 64, 256, 0, None) == q4.Q4_EUNSUPPORTED    # unknown format
+    assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 48, 0, None) == q4.Q4_EINVAL           # k not whole blocks
+    assert f(1, W, X, D, G, 1e-5, XO, Y, 64, 288, 0, None) == q4.Q4_EINVAL          # Q4_K: k % 256
+    assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 14592, 0, None) == q4.Q4_EUNSUPPORTED  # row beyond LDS
+    assert f(0, W, X, D, G, 1e-5, XO, Y, 1 << 29, 256, 1, None) == q4.Q4_EUNSUPPORTED  # 2m rows
+    assert f(0, None, X, D, G, 1e-5, XO, Y, 64, 256, 0, None) == q4.Q4_EINVAL
+    assert f(0, None, None, None, None, 1e-5, None, None, 0, 256, 0, None) == q4.Q4_OK  # m = 0: no-op
+
+
 def test_sequence_epilogue_field(q4):
     lib = q4.raw()
     ops = (q4.q4_gemv_op * 1)()
