@@ -24,6 +24,7 @@ Q4_0 = 0
 Q4_K = 1
 Q8_0 = 2
 Q2_K = 3
+Q1_0 = 4
 
 OK, EINVAL, ENONFINITE, ERANGE = 0, -1, -4, -5
 
@@ -66,6 +67,10 @@ def lib():
                 "oracle_q4_k_bytes": (ctypes.c_size_t, [_i64, _i64]),
                 "oracle_q8_0_bytes": (ctypes.c_size_t, [_i64, _i64]),
                 "oracle_q2_k_bytes": (ctypes.c_size_t, [_i64, _i64]),
+                "oracle_q1_0_bytes": (ctypes.c_size_t, [_i64, _i64]),
+                "oracle_q1_0_quantize_block": (ctypes.c_int, [_f32p, ctypes.POINTER(ctypes.c_uint32), _u16p]),
+                "oracle_q1_0_quantize": (ctypes.c_int, [_f32p, _i64, _i64, _u8p]),
+                "oracle_q1_0_dequantize": (None, [_u8p, _i64, _i64, _f32p]),
                 "oracle_q2_k_quantize": (ctypes.c_int, [_f32p, _i64, _i64, _u8p]),
                 "oracle_q2_k_dequantize": (None, [_u8p, _i64, _i64, _f32p]),
                 "oracle_q8_0_quantize_block": (ctypes.c_int, [_f32p, ctypes.POINTER(ctypes.c_int8), _u16p]),
@@ -131,7 +136,7 @@ def bf16_to_fp32(b: int) -> float:
 def weight_bytes(fmt: int, m: int, k: int) -> int:
     L = lib()
     return {Q4_0: L.oracle_q4_0_bytes, Q4_K: L.oracle_q4_k_bytes, Q8_0: L.oracle_q8_0_bytes,
-            Q2_K: L.oracle_q2_k_bytes}[fmt](m, k)
+            Q2_K: L.oracle_q2_k_bytes, Q1_0: L.oracle_q1_0_bytes}[fmt](m, k)
 
 
 def quantize(fmt: int, w: np.ndarray) -> np.ndarray:
@@ -141,7 +146,7 @@ def quantize(fmt: int, w: np.ndarray) -> np.ndarray:
     out = np.zeros(weight_bytes(fmt, m, k), dtype=np.uint8)
     L = lib()
     fn = {Q4_0: L.oracle_q4_0_quantize, Q4_K: L.oracle_q4_k_quantize, Q8_0: L.oracle_q8_0_quantize,
-          Q2_K: L.oracle_q2_k_quantize}[fmt]
+          Q2_K: L.oracle_q2_k_quantize, Q1_0: L.oracle_q1_0_quantize}[fmt]
     st = fn(_p(w, _f32p), m, k, _p(out, _u8p))
     if st != OK:
         raise OracleError(st)
@@ -171,13 +176,24 @@ def quantize_q8_0_block(w32: np.ndarray):
     return q, d.value
 
 
+def quantize_q1_0_block(w32: np.ndarray):
+    w32 = np.ascontiguousarray(w32, dtype=np.float32)
+    assert w32.shape == (32,)
+    bits = ctypes.c_uint32(0)
+    d = ctypes.c_uint16(0)
+    st = lib().oracle_q1_0_quantize_block(_p(w32, _f32p), ctypes.byref(bits), ctypes.byref(d))
+    if st != OK:
+        raise OracleError(st)
+    return bits.value, d.value
+
+
 def dequantize(fmt: int, buf: np.ndarray, m: int, k: int) -> np.ndarray:
     buf = np.ascontiguousarray(buf, dtype=np.uint8)
     assert buf.size == weight_bytes(fmt, m, k)
     out = np.empty((m, k), dtype=np.float32)
     L = lib()
     fn = {Q4_0: L.oracle_q4_0_dequantize, Q4_K: L.oracle_q4_k_dequantize, Q8_0: L.oracle_q8_0_dequantize,
-          Q2_K: L.oracle_q2_k_dequantize}[fmt]
+          Q2_K: L.oracle_q2_k_dequantize, Q1_0: L.oracle_q1_0_dequantize}[fmt]
     fn(_p(buf, _u8p), m, k, _p(out, _f32p))
     return out
 

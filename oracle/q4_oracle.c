@@ -25,6 +25,10 @@
  *   - Q8_0 (the q8_0 the summary's results compare with q4_k_m and q2_k):
  *     blocks of 32 weights, an fp16 scale d = max|w| / 127, codes q in
  *     [-127, 127] stored as bytes, value q * d.
+ *   - Q1_0 (the 1-bit format the technical summary names as an example of a
+ *     format added by writing one dequantization routine): blocks of 32
+ *     weights, an fp16 scale d = mean |w|, one sign bit per weight, value
+ *     +d or -d.
  *   - The gated product silu(g) * u of a stacked gate/up matrix (kernel
  *     fusion: WebGPT README, "Roadmap"; the summary's experimental results).
  *
@@ -315,6 +319,81 @@ void oracle_q8_0_dequantize(const uint8_t *buf, int64_t m, int64_t k, float *w_h
 }
 
 /* ------------------------------------------------------------------------
+ * Q1_0 (the 1-bit format the technical summary's extensibility point names;
+ * the pages define no more than that it holds 1-bit models). Reading: the
+ * Q4_0 block structure with a one-bit code. Blocks of 32 weights; code
+ * b = 1 for w >= 0 (either zero included), 0 for w < 0; one fp16 scale
+ * d = RNE(sum |w| / 32) (float64 sum and quotient), the least-squares scale
+ * for codes of fixed sign: sum (w - d s)^2 with s = +-1 is smallest at
+ * d = mean |w|. Value (2b - 1) * d, exact in binary32.
+ * Buffer for an m x k matrix, plane-split like Q4_0:
+ *   bytes [0, m*k/8)          bit plane: block (r, b) at (r*k/32 + b)*4, a
+ *                             little-endian 32-bit word whose bit e is the
+ *                             code of element e;
+ *   bytes [m*k/8, m*k*3/16)   scale plane: fp16 d of block (r, b) at
+ *                             m*k/8 + (r*k/32 + b)*2, little-endian.
+ * ------------------------------------------------------------------------ */
+
+size_t oracle_q1_0_bytes(int64_t m, int64_t k) { return (size_t)(m * k / 32) * 6u; }
+
+/* One block: 32 floats -> the 32-bit code word and the fp16 scale bits. */
+int oracle_q1_0_quantize_block(const float *w, uint32_t *bits, uint16_t *d_bits)
+{
+    double sum = 0.0;
+    for (int i = 0; i < 32; i++) {
+        if (!isfinite(w[i])) return ORACLE_ENONFINITE;
+        sum += fabs((double)w[i]);
+    }
+    uint16_t dh = oracle_f64_to_fp16(sum / 32.0);
+    if ((dh & 0x7C00) == 0x7C00) return ORACLE_ERANGE; /* scale not finite in fp16 */
+    uint32_t word = 0;
+    for (int i = 0; i < 32; i++)
+        if (w[i] >= 0.0f) word |= (uint32_t)1 << i;
+    *bits = word;
+    *d_bits = dh;
+    return ORACLE_OK;
+}
+
+int oracle_q1_0_quantize(const float *w, int64_t m, int64_t k, uint8_t *out)
+{
+    if (m < 0 || k <= 0 || k % 32 != 0) return ORACLE_EINVAL;
+    int64_t nb = k / 32;
+    uint8_t *scales = out + (size_t)(m * k / 8);
+    for (int64_t r = 0; r < m; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            uint32_t word;
+            uint16_t dh;
+            int st = oracle_q1_0_quantize_block(w + r * k + b * 32, &word, &dh);
+            if (st != ORACLE_OK) return st;
+            uint8_t *o = out + (r * nb + b) * 4;
+            for (int j = 0; j < 4; j++) o[j] = (uint8_t)(word >> (8 * j));
+            scales[(r * nb + b) * 2] = (uint8_t)(dh & 0xFF);
+            scales[(r * nb + b) * 2 + 1] = (uint8_t)(dh >> 8);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Dequantized weight (r, c): +d or -d, exact in binary32. */
+float oracle_q1_0_weight(const uint8_t *buf, int64_t m, int64_t k, int64_t r, int64_t c)
+{
+    int64_t nb = k / 32;
+    int64_t b = c / 32;
+    int e = (int)(c % 32);
+    int bit = (buf[(r * nb + b) * 4 + e / 8] >> (e % 8)) & 1;
+    const uint8_t *s = buf + (size_t)(m * k / 8) + (r * nb + b) * 2;
+    float d = oracle_fp16_to_fp32((uint16_t)(s[0] | (s[1] << 8)));
+    return bit ? d : -d;
+}
+
+void oracle_q1_0_dequantize(const uint8_t *buf, int64_t m, int64_t k, float *w_hat)
+{
+    for (int64_t r = 0; r < m; r++)
+        for (int64_t c = 0; c < k; c++)
+            w_hat[r * k + c] = oracle_q1_0_weight(buf, m, k, r, c);
+}
+
+/* ------------------------------------------------------------------------
  * Q2_K (llama.cpp's 2-bit K-quant, the q2_k of the technical summary's
  * results): 256-weight super-blocks of sixteen 16-weight sub-blocks; per
  * sub-block a 4-bit scale sc and a 4-bit min m (one byte: sc low nibble,
@@ -575,6 +654,7 @@ static float weight_at(int fmt, const uint8_t *w, int64_t m, int64_t k, int64_t 
     if (fmt == 0) return oracle_q4_0_weight(w, m, k, r, c);
     if (fmt == 2) return oracle_q8_0_weight(w, m, k, r, c);
     if (fmt == 3) return oracle_q2_k_weight(w, m, k, r, c);
+    if (fmt == 4) return oracle_q1_0_weight(w, m, k, r, c);
     return oracle_q4_k_weight(w, m, k, r, c);
 }
 
@@ -641,6 +721,7 @@ static double term_magnitude(int fmt, const uint8_t *w, int64_t m, int64_t k, in
 {
     if (fmt == 0) return fabs((double)oracle_q4_0_weight(w, m, k, r, c));
     if (fmt == 2) return fabs((double)oracle_q8_0_weight(w, m, k, r, c));
+    if (fmt == 4) return fabs((double)oracle_q1_0_weight(w, m, k, r, c));
     if (fmt == 3) {
         int64_t i = r * (k / 256) + c / 256;
         int e = (int)(c % 256);

@@ -35,7 +35,7 @@ def _ulp_distance(a: np.float32, b: np.float32) -> int:
 
 
 @pytest.mark.parametrize("fmt,m,k,n", [(0, 3, 32, 2), (0, 4, 64, 3), (1, 2, 256, 2), (1, 3, 256, 1), (2, 3, 64, 2),
-                                       (3, 2, 256, 2)])
+                                       (3, 2, 256, 2), (4, 3, 64, 2)])
 def test_brute_force_exact_rationals(orc, fmt, m, k, n):
     rng = np.random.default_rng(100 + m * k + n)
     w = (rng.standard_normal((m, k)) * 0.02).astype(np.float32)
@@ -54,7 +54,8 @@ def test_brute_force_exact_rationals(orc, fmt, m, k, n):
     assert exact_hits >= (m * n + 1) // 2
 
 
-@pytest.mark.parametrize("fmt,m,k", [(0, 37, 320), (1, 19, 512), (0, 5, 2048), (2, 29, 416), (3, 13, 768)])
+@pytest.mark.parametrize("fmt,m,k", [(0, 37, 320), (1, 19, 512), (0, 5, 2048), (2, 29, 416), (3, 13, 768),
+                                     (4, 23, 320)])
 def test_matches_numpy_float64(orc, fmt, m, k):
     w = synth.weights(21, m, k)
     x = synth.activations(22, 3, k)
@@ -127,6 +128,30 @@ def test_closed_forms_q8_0(orc):
     neg[: m * k] = (-buf[: m * k].view(np.int8)).view(np.uint8)
     x = synth.activations(47, 2, k)
     assert np.array_equal(orc.matvec(2, neg, m, k, x), -orc.matvec(2, buf, m, k, x))
+
+
+def test_closed_forms_q1_0(orc):
+    m, k = 5, 128
+    buf = orc.quantize(4, synth.weights(48, m, k))
+    what = orc.dequantize(4, buf, m, k)
+    nb = m * k // 32
+    d = buf[m * k // 8:].view(np.float16).astype(np.float64).reshape(m, k // 32)
+    # one-hot x = e_j returns column j exactly
+    for j in (0, 31, 32, 127):
+        e = np.zeros((1, k), np.float32)
+        e[0, j] = 1.0
+        assert np.array_equal(orc.matvec(4, buf, m, k, e)[0], what[:, j])
+    # every bit set: y_i = sum over blocks of d_ib * (sum of the block's x)
+    ones = buf.copy()
+    ones[: nb * 4] = 0xFF
+    x = synth.activations(49, 2, k)
+    bsum = x.astype(np.float64).reshape(2, k // 32, 32).sum(axis=2)
+    ref = (bsum[:, None, :] * d[None, :, :]).sum(axis=2)
+    assert np.allclose(orc.matvec(4, ones, m, k, x), ref.astype(np.float32), rtol=1e-6, atol=1e-12)
+    # flipping every bit negates y exactly
+    flip = buf.copy()
+    flip[: nb * 4] = ~buf[: nb * 4]
+    assert np.array_equal(orc.matvec(4, flip, m, k, x), -orc.matvec(4, buf, m, k, x))
 
 
 def test_threads_do_not_change_result(orc):
