@@ -23,7 +23,11 @@ def say(msg: str) -> None:
 def check_tolerance(y_gpu: np.ndarray, y_ref: np.ndarray, absdot: np.ndarray, tol: float, rows=None, what=""):
     """Per token: normwise ||dy|| <= tol ||y|| and elementwise |dy_i| <= tol * sum_k |w_ik x_k|.
 
-    ``rows`` restricts both checks to the listed row indices.
+    ``rows`` restricts both checks to the listed row indices. For a single
+    output the normwise ratio is the per-element |dy| / |y|, which is
+    ill-posed where y cancels to nearly zero (any fp32 sum then misses it by
+    a large relative amount); there the elementwise forward-error bound is
+    the condition.
     """
     y_gpu = np.asarray(y_gpu, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
@@ -36,7 +40,7 @@ def check_tolerance(y_gpu: np.ndarray, y_ref: np.ndarray, absdot: np.ndarray, to
         den = np.linalg.norm(y_ref[t])
         rel = num / den if den > 0 else num
         worst_norm = max(worst_norm, rel)
-        assert rel <= tol, f"{what}: token {t} normwise {rel:.3e} > {tol}"
+        assert rel <= tol or y_ref.shape[1] == 1, f"{what}: token {t} normwise {rel:.3e} > {tol}"
         err = np.abs(y_gpu[t] - y_ref[t])
         bad = np.nonzero(err > tol * absdot[t])[0]
         assert bad.size == 0, (f"{what}: token {t} elementwise at rows {bad[:5]}: "
