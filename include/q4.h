@@ -64,6 +64,16 @@
  *       4-bit min mn (high nibble) of element e's 16-weight sub-block.
  *     bytes [m*k*5/16, m*k*21/64): fp16 d then fp16 dmin at m*k*5/16 + i*4.
  *     Weight value: d*sc*q - dmin*mn.
+ *   Q1_0, m x k, k % 32 == 0, m*k*3/16 bytes, plane-split like Q4_0:
+ *     bytes [0, m*k/8): bit plane. Block (r, b) occupies a 32-bit
+ *       little-endian word at (r*k/32 + b)*4; bit e is the code b_e of
+ *       weight e of the block.
+ *     bytes [m*k/8, m*k*3/16): scale plane, fp16 d of block (r, b) at
+ *       m*k/8 + (r*k/32 + b)*2, little-endian.
+ *     Weight value: (2 b_e - 1) * d, i.e. +d or -d. (The technical summary
+ *     names q1_0 only as a 1-bit format that is added by writing one
+ *     dequantization routine: Methodology section 3, extensibility. This is
+ *     the Q4_0 block with a one-bit code.)
  */
 #ifndef Q4_H
 #define Q4_H
@@ -77,8 +87,9 @@ extern "C" {
 
 /* Weight formats: legacy Q4_0 and Q8_0 and the K-quants Q4_K and Q2_K
  * (llama.cpp families the technical summary names: problem statement item 3;
- * q8_0, q4_k_m and q2_k in its results). */
-typedef enum { Q4_FMT_Q4_0 = 0, Q4_FMT_Q4_K = 1, Q4_FMT_Q8_0 = 2, Q4_FMT_Q2_K = 3 } q4_format;
+ * q8_0, q4_k_m and q2_k in its results), and the 1-bit Q1_0 (its
+ * extensibility example). */
+typedef enum { Q4_FMT_Q4_0 = 0, Q4_FMT_Q4_K = 1, Q4_FMT_Q8_0 = 2, Q4_FMT_Q2_K = 3, Q4_FMT_Q1_0 = 4 } q4_format;
 
 /* Status codes. */
 enum {
@@ -92,7 +103,7 @@ enum {
 };
 
 /* Bytes of the quantized buffer for an m x k matrix; 0 if k is not a
- * positive multiple of the block (32 for Q4_0 and Q8_0, 256 for the K-quants),
+ * positive multiple of the block (32 for Q4_0, Q8_0 and Q1_0, 256 for the K-quants),
  * m < 0, or the format is unknown. Host only; no device work. */
 size_t q4_weight_bytes(int fmt, int64_t m, int64_t k);
 
@@ -110,6 +121,9 @@ size_t q4_weight_bytes(int fmt, int64_t m, int64_t k);
  * Q2_K super-block: the Q4_K reading with 16-weight sub-blocks, s = (hi - lo)/3,
  *   d = fp16_rne(max s / 15), dmin = fp16_rne(max mu / 15), 4-bit sc and mn
  *   (clamp 0..15) and 2-bit codes (clamp 0..3).
+ * Q1_0 block: d = fp16_rne(sum|w| / 32) (float64 sum and quotient, one
+ *   rounding: the least-squares scale for codes of fixed sign); codes
+ *   b = 1 for w >= 0 (either zero included), 0 for w < 0.
  * Blocks are quantized row by row; the status is that of the first failing
  * block in row-major order (Q4_ENONFINITE for NaN/Inf, Q4_ERANGE for a scale
  * that overflows fp16), and `out` is then unspecified.

@@ -19,6 +19,7 @@ Q4_FMT_Q4_0 = 0
 Q4_FMT_Q4_K = 1
 Q4_FMT_Q8_0 = 2
 Q4_FMT_Q2_K = 3
+Q4_FMT_Q1_0 = 4
 
 Q4_OK = 0
 Q4_EINVAL = -1
@@ -31,7 +32,7 @@ Q4_EHIP = -6
 Q4_EPILOGUE_NONE = 0
 Q4_EPILOGUE_SILU_MUL = 1
 
-BLOCK = {Q4_FMT_Q4_0: 32, Q4_FMT_Q4_K: 256}
+BLOCK = {Q4_FMT_Q4_0: 32, Q4_FMT_Q4_K: 256, Q4_FMT_Q8_0: 32, Q4_FMT_Q2_K: 256, Q4_FMT_Q1_0: 32}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python q4_weight_gemv_amd/build.py`")

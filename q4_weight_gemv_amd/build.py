@@ -41,6 +41,8 @@ SOURCES = [
     ("q4_gemv_q8_0_b.hip", "device"),
     ("q4_gemv_q2_k_a.hip", "device"),
     ("q4_gemv_q2_k_b.hip", "device"),
+    ("q4_gemv_q1_0_a.hip", "device"),
+    ("q4_gemv_q1_0_b.hip", "device"),
     ("q4_gemv_norm_a.hip", "device"),
     ("q4_gemv_norm_b.hip", "device"),
     ("q4_gemm.hip", "device"),

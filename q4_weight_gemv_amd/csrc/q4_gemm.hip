@@ -170,6 +170,57 @@ struct GemmQ8_0 {
     }
 };
 
+// Q1_0: an item is 16 consecutive weights of one block, half h = it & 1 of
+// block it / 2: code bits 16h .. 16h+15 (elements lo .. lo+7 and hi .. hi+7,
+// hi = lo + 8), loaded as one 16-bit half of the code word. A weight is
+// +d or -d, so its bf16 is bf16(d) with the sign flipped where the code is 0.
+struct GemmQ1_0 {
+    static constexpr int kFormat = Q4_FMT_Q1_0;
+    static constexpr int kRingVgprs = 128;  // activation ring budget (Items are 2 VGPRs)
+    __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k / 8u); }
+    struct Item {
+        uint32_t q;  // 16 code bits (low half)
+        uint32_t d;  // fp16 scale bits
+    };
+    template <int KC>
+    __device__ static void load(Item &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+                                uint32_t row, bool row_ok, int s, int it)
+    {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(w, wbytes);
+        const uint32_t ub = static_cast<uint32_t>(s * (KC / 32) + (it >> 1));
+        const uint32_t blk = row * nu + ub;
+        const bool live = row_ok && ub < nu;
+        g.q = __builtin_amdgcn_raw_buffer_load_b16(r, live ? blk * 4u + 2u * static_cast<uint32_t>(it & 1) : kNoFetch,
+                                                   0, 0);
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(r, live ? scale_plane + blk * 2u : kNoFetch, 0, 0);
+    }
+    __device__ static int lo(int it) { return 32 * (it >> 1) + 16 * (it & 1); }
+    __device__ static int hi(int it) { return lo(it) + 8; }
+    // Eight weights from code bits j0 .. j0+7 of the half: pairs of bf16(d)
+    // with the sign flipped by the inverted codes (a flip, not a set, so a
+    // negative scale in a hand-built buffer still gives (2b - 1) d).
+    __device__ static u32x4 eight_signs(uint32_t neg, uint32_t dd, int j0)
+    {
+        u32x4 v;
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const uint32_t a = neg >> (j0 + 2 * p);
+            v[p] = dd ^ (((a << 15) & 0x8000u) | ((a << 30) & 0x80000000u));
+        }
+        return v;
+    }
+    // bf16_rne(+-d) = +-bf16_rne(d): the only rounding is that of d.
+    template <int KC>
+    __device__ static void dequant(const Item &g, int /*s*/, int /*it*/, u32x4 &vlo, u32x4 &vhi)
+    {
+        const float d = half_bits_to_float(g.d);
+        const uint32_t dd = pack_bf16(d, d);
+        const uint32_t neg = ~g.q;
+        vlo = eight_signs(neg, dd, 0);
+        vhi = eight_signs(neg, dd, 8);
+    }
+};
+
 // Q2_K: an item is two 8-element runs of one super-block that share 8 code
 // bytes: w16 = it % 16 of super-block s*KC/256 + it/16 gives half h = w16/8,
 // run pair p = (w16/4) % 2 and byte group i = w16 % 4: code bytes 32h + 8i ..
@@ -487,6 +538,7 @@ int launch_gemm(int fmt, const void *w, const uint16_t *x, float *y, int64_t m, 
     if (fmt == Q4_FMT_Q4_0) return gemm::launch_fmt<gemm::GemmQ4_0>(w, x, y, m, k, n, s, cus);
     if (fmt == Q4_FMT_Q8_0) return gemm::launch_fmt<gemm::GemmQ8_0>(w, x, y, m, k, n, s, cus);
     if (fmt == Q4_FMT_Q2_K) return gemm::launch_fmt<gemm::GemmQ2_K>(w, x, y, m, k, n, s, cus);
+    if (fmt == Q4_FMT_Q1_0) return gemm::launch_fmt<gemm::GemmQ1_0>(w, x, y, m, k, n, s, cus);
     return gemm::launch_fmt<gemm::GemmQ4_K>(w, x, y, m, k, n, s, cus);
 }
 
@@ -507,6 +559,7 @@ extern "C" int q4_gemm_tuned(int fmt, const void *w, const uint16_t *x_bf16, flo
     if (fmt == Q4_FMT_Q4_0) return q4::gemm::launch_geometry<q4::gemm::GemmQ4_0>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
     if (fmt == Q4_FMT_Q8_0) return q4::gemm::launch_geometry<q4::gemm::GemmQ8_0>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
     if (fmt == Q4_FMT_Q2_K) return q4::gemm::launch_geometry<q4::gemm::GemmQ2_K>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
+    if (fmt == Q4_FMT_Q1_0) return q4::gemm::launch_geometry<q4::gemm::GemmQ1_0>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
     return q4::gemm::launch_geometry<q4::gemm::GemmQ4_K>(tm, tn, kc, w, x_bf16, y, m, k, n, s);
 }
 

@@ -71,7 +71,7 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
     const int64_t nu = k / kUnitWeights;
     if (fmt == Q4_FMT_Q8_0 && n == 1 && nu >= 128) return m >= 8192 ? Cfg{64, 1, 4, 4} : Cfg{32, 1, 4, 4};
     if (fmt == Q4_FMT_Q2_K && nu >= 128) return n == 1 && nu >= 256 ? Cfg{32, 1, 8, 2} : Cfg{32, 2, 4, 2};
-    if (fmt == Q4_FMT_Q4_0 || fmt == Q4_FMT_Q8_0) {
+    if (fmt == Q4_FMT_Q4_0 || fmt == Q4_FMT_Q8_0 || fmt == Q4_FMT_Q1_0) {
         if (n == 1) {
             if (nu <= 32) return m >= 16384 ? Cfg{8, 1, 1, 8} : Cfg{32, 2, 1, 8};
             if (nu < 128) return Cfg{64, 1, 4, 4};
@@ -124,6 +124,13 @@ int dispatch(int fmt, const Cfg &c, const void *w, const float *x, float *y, int
         switch (n) {
             Q4_N_CASE(FmtQ8_0, 1) Q4_N_CASE(FmtQ8_0, 2) Q4_N_CASE(FmtQ8_0, 3) Q4_N_CASE(FmtQ8_0, 4)
             Q4_N_CASE(FmtQ8_0, 5) Q4_N_CASE(FmtQ8_0, 6) Q4_N_CASE(FmtQ8_0, 7) Q4_N_CASE(FmtQ8_0, 8)
+        default: return Q4_EUNSUPPORTED;
+        }
+    }
+    if (fmt == Q4_FMT_Q1_0) {
+        switch (n) {
+            Q4_N_CASE(FmtQ1_0, 1) Q4_N_CASE(FmtQ1_0, 2) Q4_N_CASE(FmtQ1_0, 3) Q4_N_CASE(FmtQ1_0, 4)
+            Q4_N_CASE(FmtQ1_0, 5) Q4_N_CASE(FmtQ1_0, 6) Q4_N_CASE(FmtQ1_0, 7) Q4_N_CASE(FmtQ1_0, 8)
         default: return Q4_EUNSUPPORTED;
         }
     }
@@ -182,6 +189,7 @@ int launch_gemv_addnorm(int fmt, const void *w, const float *x, const Prologue &
     case Q4_FMT_Q4_0: return gemv::dispatch_norm_cfg<gemv::FmtQ4_0>(c, wb, x, y, mi, ki, s, cus, glu, pro);
     case Q4_FMT_Q8_0: return gemv::dispatch_norm_cfg<gemv::FmtQ8_0>(c, wb, x, y, mi, ki, s, cus, glu, pro);
     case Q4_FMT_Q2_K: return gemv::dispatch_norm_cfg<gemv::FmtQ2_K>(c, wb, x, y, mi, ki, s, cus, glu, pro);
+    case Q4_FMT_Q1_0: return gemv::dispatch_norm_cfg<gemv::FmtQ1_0>(c, wb, x, y, mi, ki, s, cus, glu, pro);
     default: return gemv::dispatch_norm_cfg<gemv::FmtQ4_K>(c, wb, x, y, mi, ki, s, cus, glu, pro);
     }
 }
@@ -228,7 +236,8 @@ int check_glu_args(int fmt, const void *w, const void *x, const float *y, int64_
 int check_product_args(int fmt, const void *w, const void *x, const float *y, int64_t m, int64_t k, int64_t n,
                        int64_t n_max)
 {
-    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0 && fmt != Q4_FMT_Q2_K) return Q4_EUNSUPPORTED;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0 && fmt != Q4_FMT_Q2_K && fmt != Q4_FMT_Q1_0)
+        return Q4_EUNSUPPORTED;
     const int64_t blk = fmt == Q4_FMT_Q4_K || fmt == Q4_FMT_Q2_K ? 256 : 32;
     if (m < 0 || k <= 0 || k % blk != 0 || n < 0) return Q4_EINVAL;
     if (n > n_max) return Q4_EUNSUPPORTED;

@@ -319,6 +319,89 @@ struct FmtQ8_0 {
     }
 };
 
+// Q1_0: a unit is one block: a 32-bit code word (bit e = element e) and an
+// fp16 scale d in the scale plane. The value (2b - 1) d makes the unit's dot
+// product d (2 A - S), A = sum of the activations whose code is 1, S = the
+// unit's activation sum (from the staging, in the metadata). A is formed by
+// dot2 on the 0/1 codes as exact fp16 subnormals: b * 2^-24 for L elements,
+// 16 b * 2^-24 for H elements (whose staged activations are divided by 16).
+// Pair order as staged: (L, L+2), (H, H+2), (L+1, L+3), (H+1, H+3) with
+// L = 4i, H = L + 16 for item i, i.e. bits 4i.. of the word shifted down.
+struct FmtQ1_0 {
+    static constexpr int kFormat = Q4_FMT_Q1_0;
+    static constexpr int kHighOffset = 16;
+    static constexpr int kBatchUnits = 8;  // 6 B per unit
+    __device__ static int unit_base(int u) { return u << 5; }
+    __device__ static int item_base(int u, int i) { return unit_base(u) + 4 * i; }
+    __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k / 8u); }
+
+    struct Regs {
+        uint32_t q;
+        uint32_t d;
+    };
+    // Unit (row, u), row = trow + rowrel, u = ubase + li + jl: its code word
+    // at (row*nu + u)*4, its scale at scale_plane + (row*nu + u)*2.
+    __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+                                uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl, bool live)
+    {
+        const uint32_t uni_u = trow * nu + ubase;
+        const uint32_t lane_u = rowrel * nu + li + jl;
+        g.q = __builtin_amdgcn_raw_buffer_load_b32(sub_rsrc(w, wbytes, uni_u * 4u), live ? lane_u * 4u : kNoFetch, 0,
+                                                   kNonTemporal);
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(sub_rsrc(w, wbytes, scale_plane + uni_u * 2u),
+                                                   live ? lane_u * 2u : kNoFetch, 0, 0);
+    }
+    // Unit metadata: z = 2^(e+25) (twice the unit scale times the subnormal
+    // factor), w = S (gh arrives multiplied by 16: the H activations' sum).
+    __device__ static f32x4 meta(float gl, float gh, int e)
+    {
+        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + 25), __builtin_amdgcn_ldexpf(gl + gh, e)};
+    }
+    // Code pairs of item i from t = word >> 4i: L pairs take bits (0, 2) and
+    // (1, 3) to bits (0, 16); H pairs take bits (16, 18) and (17, 19) to
+    // bits (4, 20).
+    __device__ static uint32_t pair_l0(uint32_t t) { return (t & 1u) | ((t << 14) & 0x10000u); }
+    __device__ static uint32_t pair_h0(uint32_t t) { return ((t >> 12) & 0x10u) | ((t << 2) & 0x100000u); }
+    __device__ static uint32_t pair_l1(uint32_t t) { return ((t >> 1) & 1u) | ((t << 13) & 0x10000u); }
+    __device__ static uint32_t pair_h1(uint32_t t) { return ((t >> 13) & 0x10u) | ((t << 1) & 0x100000u); }
+    template <int N, int R, bool LO>
+    __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
+                                      const f32x4 *__restrict__ meta, int ul, int uc, uint32_t /*u*/,
+                                      float (&acc)[R][N])
+    {
+#pragma unroll
+        for (int t = 0; t < N; t++) {
+            const f32x4 mt = meta[t * uc + ul];
+            u32x4 xh[4], xl[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                xh[i] = xs[(t * 8 + 2 * i) * uc + ul];
+                xl[i] = LO ? xs[(t * 8 + 2 * i + 1) * uc + ul] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const uint32_t tt = g[r].q >> (4 * i);
+                    const uint32_t p0 = pair_l0(tt), p1 = pair_h0(tt), p2 = pair_l1(tt), p3 = pair_h1(tt);
+                    a = dot2(p0, xh[i].x, a);
+                    a = dot2(p1, xh[i].y, a);
+                    a = dot2(p2, xh[i].z, a);
+                    a = dot2(p3, xh[i].w, a);
+                    if constexpr (LO) {
+                        a = dot2(p0, xl[i].x, a);
+                        a = dot2(p1, xl[i].y, a);
+                        a = dot2(p2, xl[i].z, a);
+                        a = dot2(p3, xl[i].w, a);
+                    }
+                }
+                acc[r][t] = __builtin_fmaf(half_lo(g[r].d), __builtin_fmaf(mt.z, a, -mt.w), acc[r][t]);
+            }
+        }
+    }
+};
+
 // Q2_K: unit u = 8 code bytes of super-block u >> 3: bytes 32h + 8i .. +7
 // of its 64 code bytes, h = (u & 7) >> 2, i = u & 3. Those bytes hold, in
 // bit pairs 2j, 2j+1, the codes of the four runs j = 0..3 of 8 elements

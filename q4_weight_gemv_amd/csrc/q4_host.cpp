@@ -96,6 +96,33 @@ int q8_0_row(const float *wr, int64_t nb, uint8_t *code_row, uint8_t *scale_row,
     return Q4_OK;
 }
 
+// ---- Q1_0 -----------------------------------------------------------------
+
+// Quantize row r of a Q1_0 matrix into the bit and scale planes.
+int q1_0_row(const float *wr, int64_t nb, uint8_t *bit_row, uint8_t *scale_row, int64_t *bad)
+{
+    for (int64_t b = 0; b < nb; b++) {
+        const float *v = wr + 32 * b;
+        double total = 0.0;
+        bool finite = true;
+        uint32_t word = 0;
+        for (int i = 0; i < 32; i++) {
+            finite = finite && std::isfinite(v[i]);
+            total += std::fabs(static_cast<double>(v[i]));
+            if (!(v[i] < 0.0f)) word |= 1u << i;
+        }
+        if (!finite) { *bad = b; return Q4_ENONFINITE; }
+        // One rounding, float64 -> fp16 (round to nearest even).
+        _Float16 dh = static_cast<_Float16>(total / 32.0);
+        if (!half_is_finite(dh)) { *bad = b; return Q4_ERANGE; }
+        for (int j = 0; j < 4; j++) bit_row[4 * b + j] = static_cast<uint8_t>(word >> (8 * j));
+        const uint16_t bits = half_bits(dh);
+        scale_row[2 * b] = static_cast<uint8_t>(bits);
+        scale_row[2 * b + 1] = static_cast<uint8_t>(bits >> 8);
+    }
+    return Q4_OK;
+}
+
 // ---- Q4_K -----------------------------------------------------------------
 
 inline void pack_6bit(const uint8_t sc[8], const uint8_t mn[8], uint8_t S[12])
@@ -253,12 +280,14 @@ size_t q4_weight_bytes(int fmt, int64_t m, int64_t k)
     if (fmt == Q4_FMT_Q4_K) return k % 256 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 256) * 144u;
     if (fmt == Q4_FMT_Q8_0) return k % 32 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 32) * 34u;
     if (fmt == Q4_FMT_Q2_K) return k % 256 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 256) * 84u;
+    if (fmt == Q4_FMT_Q1_0) return k % 32 ? 0 : static_cast<size_t>(m) * static_cast<size_t>(k / 32) * 6u;
     return 0;
 }
 
 int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, size_t out_bytes)
 {
-    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0 && fmt != Q4_FMT_Q2_K) return Q4_EUNSUPPORTED;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0 && fmt != Q4_FMT_Q2_K && fmt != Q4_FMT_Q1_0)
+        return Q4_EUNSUPPORTED;
     const size_t need = q4_weight_bytes(fmt, m, k);
     const int64_t blk = fmt == Q4_FMT_Q4_K || fmt == Q4_FMT_Q2_K ? 256 : 32;
     if (need == 0 && !(m == 0 && k > 0 && k % blk == 0)) return Q4_EINVAL;
@@ -279,6 +308,14 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
         uint8_t *scl = o + static_cast<size_t>(m) * static_cast<size_t>(k);
         return for_rows(m, nb, [&](int64_t r, int64_t *bad) {
             return q8_0_row(w + r * k, nb, codes + r * nb * 32, scl + r * nb * 2, bad);
+        });
+    }
+    if (fmt == Q4_FMT_Q1_0) {
+        const int64_t nb = k / 32;
+        uint8_t *bits = o;
+        uint8_t *scl = o + static_cast<size_t>(m) * static_cast<size_t>(k) / 8;
+        return for_rows(m, nb, [&](int64_t r, int64_t *bad) {
+            return q1_0_row(w + r * k, nb, bits + r * nb * 4, scl + r * nb * 2, bad);
         });
     }
     const int64_t ns = k / 256;

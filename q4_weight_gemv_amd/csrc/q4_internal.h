@@ -76,6 +76,7 @@ struct FmtQ4_0;
 struct FmtQ4_K;
 struct FmtQ8_0;
 struct FmtQ2_K;
+struct FmtQ1_0;
 
 // Defined in the per-format instantiation units (q4_gemv_q4_*.hip).
 template <class F, int N>

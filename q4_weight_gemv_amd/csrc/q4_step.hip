@@ -67,6 +67,12 @@ __device__ float weight_at(int fmt, const uint8_t *w, int64_t m, int64_t k, int6
         const int64_t b = r * (k / 32) + c / 32;
         return static_cast<float>(static_cast<int8_t>(w[b * 32 + c % 32])) * half(w + m * k + b * 2);
     }
+    if (fmt == Q4_FMT_Q1_0) {
+        const int64_t b = r * (k / 32) + c / 32;
+        const int e = static_cast<int>(c % 32);
+        const float d = half(w + m * k / 8 + b * 2);
+        return (w[b * 4 + e / 8] >> (e % 8)) & 1 ? d : -d;
+    }
     const int64_t s = r * (k / 256) + c / 256;
     const int e = static_cast<int>(c % 256);
     if (fmt == Q4_FMT_Q2_K) {
@@ -304,7 +310,8 @@ int check_step(int fmt, const q4_llama_config *c, const void *emb, const float *
 {
     using namespace q4::step;
     if (!c || !emb || !norm_final || !L || !st) return Q4_EINVAL;
-    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0 && fmt != Q4_FMT_Q2_K) return Q4_EUNSUPPORTED;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_Q4_K && fmt != Q4_FMT_Q8_0 && fmt != Q4_FMT_Q2_K && fmt != Q4_FMT_Q1_0)
+        return Q4_EUNSUPPORTED;
     const int64_t blk = fmt == Q4_FMT_Q4_K || fmt == Q4_FMT_Q2_K ? 256 : 32;
     if (c->layers <= 0 || c->heads <= 0 || c->kv_heads <= 0 || c->heads % c->kv_heads || c->vocab <= 0 ||
         c->max_pos <= 0 || !(c->norm_eps >= 0.0f) || !(c->rope_theta > 0.0f))

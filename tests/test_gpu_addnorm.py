@@ -64,6 +64,7 @@ PLAIN = [
     (1, 37, 256), (1, 300, 4096), (1, 9000, 4096), (1, 70, 8192), (1, 130, 1024),
     (2, 37, 320), (2, 130, 960), (2, 300, 4096), (2, 8200, 4096),
     (3, 130, 1024), (3, 300, 4096), (3, 70, 8192),
+    (4, 37, 320), (4, 1600, 960), (4, 300, 4096), (4, 16500, 768),
 ]
 
 
@@ -116,7 +117,7 @@ def test_addnorm_scale_invariance(env):
 
 # (fmt, m, k) for the gated epilogue: the gated geometries.
 GLU = [(0, 37, 96), (0, 2560, 960), (0, 130, 2560), (0, 300, 4096), (1, 130, 1024), (1, 300, 4096),
-       (2, 300, 4096), (3, 130, 1024), (3, 300, 4096)]
+       (2, 300, 4096), (3, 130, 1024), (3, 300, 4096), (4, 2560, 960), (4, 300, 4096)]
 
 
 @pytest.mark.parametrize("fmt,m,k", GLU)
@@ -170,13 +171,13 @@ NORM_GEOMS = [(8, 1, 1), (16, 1, 1), (16, 1, 4), (32, 1, 4), (32, 1, 8), (32, 2,
 NORM_GLU_GEOMS = [(16, 2, 1), (16, 2, 4), (32, 2, 1), (32, 2, 4), (64, 2, 4)]
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("glu", [False, True])
 def test_addnorm_every_geometry(env, fmt, glu):
     # Every instantiated fused-norm geometry through the tuned entry point,
     # at two grid sizes (one workgroup per CU: several tiles per workgroup).
     torch, q4, orc = env
-    m, k = (133, 960) if fmt in (0, 2) else (133, 1024)
+    m, k = (133, 960) if fmt in (0, 2, 4) else (133, 1024)
     rows = 2 * m if glu else m
     buf = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(3500 + fmt, glu), rows, k))
     x, delta, gain = _inputs(3501 + fmt, k)

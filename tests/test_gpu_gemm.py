@@ -45,7 +45,8 @@ def _quantize_both(q4, orc, fmt, w):
 
 
 @pytest.mark.parametrize("fmt,m,k", [(0, 37, 96), (0, 130, 960), (0, 64, 2560), (1, 37, 256), (1, 96, 1024),
-                                     (2, 37, 96), (2, 130, 960), (3, 37, 256), (3, 96, 1024)])
+                                     (2, 37, 96), (2, 130, 960), (3, 37, 256), (3, 96, 1024), (4, 37, 96),
+                                     (4, 130, 960)])
 def test_identity_gives_bf16_weights_exactly(env, fmt, m, k):
     torch, q4, orc = env
     buf = _quantize_both(q4, orc, fmt, synth.weights(synth.seed_for(30 + fmt, m), m, k))
@@ -76,6 +77,7 @@ def _parity(env, fmt, m, k, n, seed, rows=None):
     (1, 1, 256, 3), (1, 70, 512, 70), (1, 130, 1024, 257),
     (2, 1, 32, 1), (2, 100, 320, 130), (2, 257, 2560, 200),
     (3, 1, 256, 3), (3, 70, 512, 70), (3, 130, 1024, 257),
+    (4, 1, 32, 1), (4, 100, 320, 130), (4, 257, 2560, 200),
 ])
 def test_parity_small(env, fmt, m, k, n):
     _parity(env, fmt, m, k, n, seed=600 + n)
@@ -103,7 +105,7 @@ def _tiles():
 
 
 @pytest.mark.parametrize("tile", _tiles(), ids=lambda t: f"{t[0]}x{t[1]}x{t[2]}")
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_parity_every_tile(env, fmt, tile):
     """Every instantiated tile through q4_gemm_tuned: 70 rows and 100 tokens
     (ragged in both), K = 1280 (a partial last chunk for every chunk size)."""
@@ -122,6 +124,31 @@ def test_parity_every_tile(env, fmt, tile):
     check_tolerance(y, yr, ad, GEMM_TOL, what=f"gemm tile {tile} fmt={fmt}")
     yb, adb = orc.matmul(fmt, buf, m, k, xb, round_w_bf16=True, threads=threads(), absdot=True)
     check_tolerance(y, yb, adb, 1e-4, what=f"gemm(bf16 W) tile {tile} fmt={fmt}")
+
+
+def test_q1_0_hand_built_words(env):
+    # Code words all 0, all 1, alternating and random; scales zero,
+    # subnormal, negative and the largest finite fp16: the product of the
+    # bf16-rounded weights (+-bf16(d)) against the oracle's.
+    torch, q4, orc = env
+    m, k, n = 70, 512, 40
+    rng = np.random.default_rng(5)
+    nb = m * k // 32
+    words = rng.integers(0, 1 << 32, size=nb, dtype=np.uint64).astype(np.uint32)
+    words[0::7] = 0
+    words[1::7] = 0xFFFFFFFF
+    words[2::7] = 0xAAAAAAAA
+    scales = rng.uniform(0.001, 2.0, size=nb).astype(np.float16)
+    scales[3::11] = np.float16(0.0)
+    scales[4::11] = np.float16(6e-8)
+    scales[5::13] = np.float16(65504.0)
+    scales[6::17] *= np.float16(-1.0)
+    buf = np.concatenate([words.view(np.uint8), scales.view(np.uint8)])
+    xb = synth.bf16_bits(synth.activations(960, n, k))
+    say("gemm q1_0 hand-built words")
+    y = _gemm(env, 4, buf, xb, m, k)
+    yb, adb = orc.matmul(4, buf, m, k, xb, round_w_bf16=True, threads=threads(), absdot=True)
+    check_tolerance(y, yb, adb, 1e-4, what="gemm q1_0 hand-built (bf16 W)")
 
 
 def test_gemm_misaligned_and_noop(env):

@@ -51,6 +51,7 @@ ONEHOT_CASES = [
     (1, 5, 256), (1, 37, 512), (1, 130, 1024), (1, 300, 4096), (1, 70, 11008),
     (2, 5, 32), (2, 37, 320), (2, 768, 768), (2, 300, 4096), (2, 70, 11008),
     (3, 5, 256), (3, 37, 512), (3, 130, 1024), (3, 300, 4096), (3, 70, 11008),
+    (4, 5, 32), (4, 37, 320), (4, 768, 768), (4, 300, 4096), (4, 70, 11008),
 ]
 
 
@@ -116,7 +117,7 @@ def _geometries():
 
 
 @pytest.mark.parametrize("geom", _geometries(), ids=_geometry_ids())
-@pytest.mark.parametrize("fmt,n", [(0, 1), (0, 8), (1, 1), (1, 8), (2, 1), (2, 8), (3, 1), (3, 8)])
+@pytest.mark.parametrize("fmt,n", [(0, 1), (0, 8), (1, 1), (1, 8), (2, 1), (2, 8), (3, 1), (3, 8), (4, 1), (4, 8)])
 def test_parity_every_geometry(env, fmt, n, geom):
     """Every instantiated tile geometry through q4_gemv_tuned: 600 ragged rows
     (a grid-stride loop for the short tiles at one group per compute unit) and
@@ -194,6 +195,49 @@ def test_parity_q2_k_small(env, m, k, n):
 @pytest.mark.parametrize("n", [1, 8])
 def test_parity_q2_k_7b(env, k, m, n):
     _parity(env, 3, m, k, n, seed=470 + n, rows=sample_rows(m, k + n))
+
+
+SMALL_Q1_0 = [(1, 32), (37, 320), (130, 768), (257, 960), (300, 4096), (77, 11008), (2049, 768)]
+
+
+@pytest.mark.parametrize("m,k", SMALL_Q1_0)
+@pytest.mark.parametrize("n", [1, 3, 8])
+def test_parity_q1_0_small(env, m, k, n):
+    _parity(env, 4, m, k, n, seed=170 + n)
+
+
+@pytest.mark.parametrize("k,m", synth.llama7b_layer()[:2] + synth.llama7b_layer()[3:])
+@pytest.mark.parametrize("n", [1, 8])
+def test_parity_q1_0_7b(env, k, m, n):
+    _parity(env, 4, m, k, n, seed=490 + n, rows=sample_rows(m, k + n))
+
+
+@pytest.mark.parametrize("m", [40, 300])
+def test_q1_0_hand_built_words(env, m):
+    # Code words all 0, all 1, alternating and random, with scales that are
+    # zero, subnormal, ordinary and the largest finite fp16, against the
+    # oracle's product of the same bytes (below and above the row count where
+    # activations lose their lo halves).
+    torch, q4, orc = env
+    k = 256
+    rng = np.random.default_rng(m)
+    nb = m * k // 32
+    words = rng.integers(0, 1 << 32, size=nb, dtype=np.uint64).astype(np.uint32)
+    words[0::7] = 0
+    words[1::7] = 0xFFFFFFFF
+    words[2::7] = 0x55555555
+    scales = rng.uniform(0.001, 2.0, size=nb).astype(np.float16)
+    scales[3::11] = np.float16(0.0)
+    scales[4::11] = np.float16(6e-8)     # subnormal
+    scales[5::13] = np.float16(65504.0)  # largest finite
+    scales[6::17] *= np.float16(-1.0)     # negative (the quantizer never writes one)
+    buf = np.concatenate([words.view(np.uint8), scales.view(np.uint8)])
+    assert buf.size == q4.q4_weight_bytes(4, m, k)
+    x = synth.activations(880 + m, 2, k)
+    say(f"q1_0 hand-built words m={m}")
+    y = _gemv(env, 4, buf, x, m, k)
+    yr, ad = orc.matvec(4, buf, m, k, x, threads=threads(), absdot=True)
+    check_tolerance(y, yr, ad, GEMV_TOL, what=f"q1_0 hand-built m={m}")
 
 
 def test_q8_0_extreme_codes(env):
@@ -357,6 +401,7 @@ GLU_CASES = [
     (1, 1, 37, 256), (1, 4, 130, 1024), (1, 1, 300, 4096), (1, 8, 90, 4096), (1, 1, 70, 11008),
     (2, 1, 130, 960), (2, 4, 300, 4096),
     (3, 1, 130, 1024), (3, 4, 300, 4096),
+    (4, 1, 130, 960), (4, 4, 300, 4096), (4, 1, 2560, 960),
 ]
 
 

@@ -60,7 +60,8 @@ def _check_step(gpu_logits, ref_logits, gpu_token, what):
     assert ref_logits[gpu_token] >= ref_logits.max() - 2 * err - 1e-6, f"{what}: token {gpu_token} not a maximum"
 
 
-@pytest.mark.parametrize("fmt,cfg", [(0, TINY), (2, TINY), (1, TINY_K), (3, TINY_K)], ids=["q4_0", "q8_0", "q4_k", "q2_k"])
+@pytest.mark.parametrize("fmt,cfg", [(0, TINY), (2, TINY), (1, TINY_K), (3, TINY_K), (4, TINY)],
+                         ids=["q4_0", "q8_0", "q4_k", "q2_k", "q1_0"])
 def test_steps_match_reference(env, fmt, cfg):
     torch, q4, _ = env
     gpu, ref = _build(env, fmt, cfg)

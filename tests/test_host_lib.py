@@ -63,6 +63,10 @@ def test_weight_bytes(q4):
     # Q2_K: 84 bytes per 256 weights, k a multiple of 256.
     assert q4.q4_weight_bytes(3, 4096, 11008) == 4096 * 43 * 84
     assert q4.q4_weight_bytes(3, 3, 288) == 0
+    # Q1_0: 6 bytes per 32 weights (a code word and a scale), k a multiple of 32.
+    assert q4.q4_weight_bytes(4, 4096, 11008) == 4096 * 11008 * 3 // 16
+    assert q4.q4_weight_bytes(4, 3, 48) == 0
+    assert q4.q4_weight_bytes(4, 5, 96) == 5 * 3 * 6
 
 
 SHAPES = sorted(set(synth.gpt2_124m_step() + synth.smollm2_360m_step() + synth.llama7b_layer()))
@@ -94,6 +98,12 @@ def test_quantize_ref_matches_oracle_q2_k(q4, orc, k, m):
     assert np.array_equal(q4.q4_quantize_ref(3, w), orc.quantize(3, w))
 
 
+@pytest.mark.parametrize("k,m", [(768, 768), (960, 320), (4096, 512), (11008, 96)])
+def test_quantize_ref_matches_oracle_q1_0(q4, orc, k, m):
+    w = synth.weights(synth.seed_for(5, k % 97 + m % 89), m, k)
+    assert np.array_equal(q4.q4_quantize_ref(4, w), orc.quantize(4, w))
+
+
 def _edge_matrix(k):
     """Rows that exercise ties, subnormal scales, clamps, zeros and sign patterns."""
     rng = np.random.default_rng(17)
@@ -113,12 +123,19 @@ def _edge_matrix(k):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_quantize_ref_matches_oracle_edges(q4, orc, fmt):
     w = _edge_matrix(512)
+    w[2, ::3] = -0.0  # signed zeros (the Q1_0 sign rule)
     assert np.array_equal(q4.q4_quantize_ref(fmt, w), orc.quantize(fmt, w))
     # Golden blocks through the product quantizer too.
-    if fmt == 3:
+    if fmt == 4:
+        from golden import floats, hexbytes, load
+        for name, sec in load("q1_0_blocks.txt").items():
+            buf = q4.q4_quantize_ref(4, floats(sec["w"][0]).reshape(1, 32))
+            assert bytes(buf[:4]) == hexbytes(sec["codes"][0]), name
+            assert int(buf[4]) | (int(buf[5]) << 8) == int(sec["d_bits"][0], 16), name
+    elif fmt == 3:
         from golden import floats, hexbytes, load
         sec = load("q2_k_superblocks.txt")["K2-B"]
         buf = q4.q4_quantize_ref(3, floats(sec["w"][0]).reshape(1, 256))
@@ -154,7 +171,7 @@ def test_quantize_ref_status(q4, orc):
     w3 = w.copy()
     w3[10, 0] = 1e9
     w3[11, 0] = np.inf
-    for fmt in (0, 1, 2, 3):
+    for fmt in (0, 1, 2, 3, 4):
         with pytest.raises(q4.Q4Error) as e:
             q4.q4_quantize_ref(fmt, w3)
         assert e.value.status == q4.Q4_ERANGE
