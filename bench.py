@@ -185,10 +185,11 @@ def bench_7b(torch, q4, timer, reps=20):
     import synth
 
     out = {}
-    name = {0: "q4_0", 1: "q4_k", 2: "q8_0", 3: "q2_k"}
-    # Q4_0 at one token (the gate), Q4_K at 1, 4, 8 tokens, and Q8_0 and Q2_K
-    # at one token beside them (the pages compare q8_0, q4_k_m and q2_k).
-    for fmt, ns in ((0, (1,)), (1, (1, 4, 8)), (2, (1,)), (3, (1,))):
+    name = {0: "q4_0", 1: "q4_k", 2: "q8_0", 3: "q2_k", 4: "q1_0"}
+    # Q4_0 at one token (the gate), Q4_K at 1, 4, 8 tokens, and Q8_0, Q2_K and
+    # Q1_0 at one token beside them (the pages compare q8_0, q4_k_m and q2_k,
+    # and name q1_0 as a format added through one dequantization routine).
+    for fmt, ns in ((0, (1,)), (1, (1, 4, 8)), (2, (1,)), (3, (1,)), (4, (1,))):
         layer_t, layer_b = {1: 0.0}, 0
         for k, m in synth.llama7b_layer()[:2] + synth.llama7b_layer()[3:]:
             wq = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(4, k + m), m, k))
@@ -308,7 +309,7 @@ def bench_full_step(torch, q4, timer, fmt=0, steps=256, warmup=8):
     log(f"full step smollm2-360m: {t * 1e6:.1f} us/token, {1 / t:.0f} tokens/s")
     return {"us_per_token": round(t * 1e6, 2), "tokens_per_s": round(1 / t, 1), "launches_per_step": launches,
             "weight_bytes": wbytes, "GB_s_weights": round(wbytes / t / 1e9, 1),
-            "positions": f"{warmup}..{pos - 1}", "format": {0: "Q4_0", 1: "Q4_K", 2: "Q8_0", 3: "Q2_K"}[fmt],
+            "positions": f"{warmup}..{pos - 1}", "format": {0: "Q4_0", 1: "Q4_K", 2: "Q8_0", 3: "Q2_K", 4: "Q1_0"}[fmt],
             "cache": "one weight copy (a generation loop)"}
 
 

@@ -56,6 +56,8 @@ namespace gemv {
 //   Q2_K: the Q4_K choices for rows of fewer than 128 units; longer rows:
 //     32 lanes x 2 rows in 4-wave groups (8-wave groups of one row per lane
 //     at one token for rows of 256 units or more).
+//   Q1_0: the Q4_0 choices, except two rows per lane for one-token LM
+//     heads (m >= 16384, nu <= 32: 8 lanes x 2 rows).
 //   Q8_0: the Q4_0 choices (same unit of 32 weights, twice the bytes),
 //     except one row per lane at one token for rows of 128 units or more
 //     (4 waves; 64 lanes per row for tall products, else 32).
@@ -71,6 +73,7 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
     const int64_t nu = k / kUnitWeights;
     if (fmt == Q4_FMT_Q8_0 && n == 1 && nu >= 128) return m >= 8192 ? Cfg{64, 1, 4, 4} : Cfg{32, 1, 4, 4};
     if (fmt == Q4_FMT_Q2_K && nu >= 128) return n == 1 && nu >= 256 ? Cfg{32, 1, 8, 2} : Cfg{32, 2, 4, 2};
+    if (fmt == Q4_FMT_Q1_0 && n == 1 && nu <= 32 && m >= 16384) return Cfg{8, 2, 1, 8};
     if (fmt == Q4_FMT_Q4_0 || fmt == Q4_FMT_Q8_0 || fmt == Q4_FMT_Q1_0) {
         if (n == 1) {
             if (nu <= 32) return m >= 16384 ? Cfg{8, 1, 1, 8} : Cfg{32, 2, 1, 8};
