@@ -1167,6 +1167,7 @@ int dispatch_glu_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, i
 // and choose_glu().
 #define Q4_GEMV_NORM_CONFIGS(X) \
     X(8, 1, 1)                  \
+    X(8, 2, 1)                  \
     X(16, 1, 1)                 \
     X(16, 1, 4)                 \
     X(32, 1, 4)                 \

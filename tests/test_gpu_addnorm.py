@@ -167,7 +167,8 @@ def test_addnorm_matches_unfused(env):
     check_tolerance(y[None, :], yd.cpu().numpy(), ad, GEMV_TOL, what="fused vs unfused")
 
 
-NORM_GEOMS = [(8, 1, 1), (16, 1, 1), (16, 1, 4), (32, 1, 4), (32, 1, 8), (32, 2, 1), (32, 2, 4), (64, 1, 4)]
+NORM_GEOMS = [(8, 1, 1), (8, 2, 1), (16, 1, 1), (16, 1, 4), (32, 1, 4), (32, 1, 8), (32, 2, 1), (32, 2, 4),
+              (64, 1, 4)]
 NORM_GLU_GEOMS = [(16, 2, 1), (16, 2, 4), (32, 2, 1), (32, 2, 4), (64, 2, 4)]
 
 
