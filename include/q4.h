@@ -215,7 +215,7 @@ int q4_gemv_addnorm_tuned(int fmt, const void *w, const float *x, const float *d
                           const q4_gemv_tuning *tuning, void *hip_stream);
 
 /* Prefill product Y[t][i] = sum_k bf16_rne(w_hat[i][k]) * X[t][k], fp32 out.
- * w: device, quantized as above (Q4_0 or Q4_K), 16-byte aligned; x_bf16: device bf16 bit
+ * w: device, quantized as above (any format), 16-byte aligned; x_bf16: device bf16 bit
  * patterns [n][k], 16-byte aligned; y: device float32 [n][m], 4-byte aligned.
  * n >= 1 (any token count). Weight tiles are dequantized to bf16 into LDS
  * and reused across the token tile by bf16 matrix-core (MFMA) instructions

@@ -5,7 +5,10 @@
 // "integrated dequantization"): for the matrix-vector product of decode, the
 // quantized weights are unpacked and scaled in registers and never written
 // anywhere; the format decoder is a compile-time policy (same section,
-// "extensibility"), so Q4_0 and Q4_K share the kernel body.
+// "extensibility"), so Q4_0, Q4_K, Q8_0, Q2_K and Q1_0 share the kernel body
+// (the notes below describe the 4-bit formats; each policy states its own
+// unit). The same body also serves the gated epilogue (GLU) and the fused
+// residual add + RMSNorm prologue (NORM).
 //
 // gfx950 design:
 //   * Memory bound: each 32-weight unit is one 16-byte nibble load (plus a
