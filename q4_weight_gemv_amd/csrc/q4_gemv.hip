@@ -42,6 +42,22 @@ int device_cus()
     return cus;
 }
 
+int device_lds_optin()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hip_status(hipGetDevice(&dev)) != Q4_OK) return -1;
+    if (dev >= 0 && dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v != 0) return v;
+    }
+    int bytes = 0;
+    if (hipDeviceGetAttribute(&bytes, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess || bytes <= 0)
+        bytes = -1;
+    if (dev >= 0 && dev < 64) cache[dev].store(bytes, std::memory_order_relaxed);
+    return bytes;
+}
+
 namespace gemv {
 
 // Default geometry, from a sweep of every instantiated geometry on gfx950

@@ -42,6 +42,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -682,7 +683,8 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
     const int per_tok = nuc * 4;
     const int total = N * per_tok;
     // it / per_tok as a multiply-high by ceil(2^32 / per_tok): exact while
-    // it * per_tok < 2^32 (it < 8 * per_tok and per_tok <= 4 * 65536/144 here).
+    // it * per_tok < 2^32 (it < N * per_tok and per_tok <= 4 * 163840 / (144 N)
+    // here, the most units one workgroup's LDS holds for N >= 2 tokens).
     const uint32_t inv = N == 1 ? 0u : 0xFFFFFFFFu / static_cast<uint32_t>(per_tok) + 1u;
     auto split_item = [&](int it, int &t, int &rem) {
         if constexpr (N == 1) {
@@ -1096,10 +1098,42 @@ int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStre
     const int nu = k / 32;
     int uc = nu;
     const int bytes_per_unit = N * kLdsBytesPerUnit;
-    if (uc * bytes_per_unit > kMaxLdsBytes) uc = kMaxLdsBytes / bytes_per_unit / 8 * 8;  // chunks of whole super-blocks
+    // Several tokens of a long row exceed the default 64 KiB: rather than
+    // restage the activations chunk by chunk for every tile, take up to the
+    // workgroup's opt-in LDS (160 KiB on gfx950), which holds the whole row
+    // (8 tokens of 4096, 4 of 8960) or larger chunks, at fewer groups per CU.
+    // (64-bit products: a whole row of many tokens can exceed 2^31 bytes.)
+    const int64_t row_bytes = static_cast<int64_t>(nu) * bytes_per_unit;
+    int budget = kMaxLdsBytes;
+    if (!NORM && N >= 2 && row_bytes > kMaxLdsBytes) {
+        const int optin = device_lds_optin();
+        if (optin > kMaxLdsBytes) budget = optin;
+    }
+    if (row_bytes > budget) uc = budget / bytes_per_unit / 8 * 8;  // chunks of whole super-blocks
     if (uc <= 0) return Q4_EUNSUPPORTED;
     if (NORM && uc < nu) return Q4_EUNSUPPORTED;  // the fused norm needs the whole row staged
     const size_t lds = static_cast<size_t>(uc) * bytes_per_unit + (NORM ? 4 * WAVES : 0);
+    if (lds > static_cast<size_t>(kMaxLdsBytes)) {
+        // Above 64 KiB a kernel opts in to its dynamic LDS size, once per device.
+        static std::atomic<int> opted[64];
+        int dev = 0;
+        if (hip_status(hipGetDevice(&dev)) != Q4_OK) return Q4_EHIP;
+        if (dev < 0 || dev >= 64) return Q4_EUNSUPPORTED;
+        if (!opted[dev].load(std::memory_order_acquire)) {
+            int st = hip_status(hipFuncSetAttribute(
+                reinterpret_cast<const void *>(&gemv_kernel<F, N, LPR, R, WAVES, JB, true, GLU, NORM>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, budget));
+            if (st == Q4_OK)
+                st = hip_status(hipFuncSetAttribute(
+                    reinterpret_cast<const void *>(&gemv_kernel<F, N, LPR, R, WAVES, JB, false, GLU, NORM>),
+                    hipFuncAttributeMaxDynamicSharedMemorySize, budget));
+            if (st != Q4_OK) return st;
+            opted[dev].store(1, std::memory_order_release);
+        }
+        // Groups that fit a compute unit's LDS at once.
+        const int fit = budget / static_cast<int>(lds);
+        if (groups_per_cu > fit) groups_per_cu = fit > 0 ? fit : 1;
+    }
     const int ntiles = (m + rows_per_wg - 1) / rows_per_wg;
     const long long cap = static_cast<long long>(cus) * groups_per_cu;
     const unsigned grid = static_cast<unsigned>(ntiles < cap ? ntiles : cap);

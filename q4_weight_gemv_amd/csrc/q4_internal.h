@@ -37,6 +37,10 @@ int launch_gemm(int fmt, const void *w, const uint16_t *x, float *y,
 // Compute units of the current device (cached per device).
 int device_cus();
 
+// Largest dynamic LDS a workgroup of the current device may opt in to, in
+// bytes (cached per device; <= 0 if the runtime does not report it).
+int device_lds_optin();
+
 // Q4_OK for hipSuccess, else Q4_EHIP, after recording e as the calling
 // thread's last HIP error (reported by q4_last_hip_error).
 int hip_status(hipError_t e);
