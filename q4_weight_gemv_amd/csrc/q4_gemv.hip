@@ -68,7 +68,8 @@ namespace gemv {
 //     per lane (LM heads, m >= 16384: 8 lanes x 1 row); nu < 128 -> 4 waves,
 //     64 lanes per row; longer rows -> 4 waves, 32 lanes x 2 rows.
 //   Q4_0, several tokens: 4 waves; 64 lanes per row for 33..127 units, else
-//     32 lanes x 2 rows.
+//     32 lanes x 2 rows; at 6..8 tokens of 128..255 units, 8-wave groups of
+//     one row per lane (the whole row's activations in the opt-in LDS).
 //   Q2_K: the Q4_K choices for rows of fewer than 128 units; longer rows:
 //     32 lanes x 2 rows in 4-wave groups (8-wave groups of one row per lane
 //     at one token for rows of 256 units or more).
@@ -79,10 +80,10 @@ namespace gemv {
 //     (4 waves; 64 lanes per row for tall products, else 32).
 //   Q4_K: 4 waves of 64 lanes per row for 33..127 units. Short rows: 16
 //     lanes per row, one-wave groups at 1..2 tokens, 4 waves at 3..4, and 32
-//     lanes x 2 rows from 5 tokens. Rows of 256 units or more: 8-wave groups
-//     of 32 lanes per row. Rows of 128..255 units: the same 8-wave groups for
-//     tall products at one token and at 2..4 tokens, else 4 waves of 16 lanes
-//     per row.
+//     lanes x 2 rows from 5 tokens. Rows of 256 units or more, and rows of
+//     128..255 units at several tokens: 8-wave groups of 32 lanes per row.
+//     Rows of 128..255 units at one token: the same 8-wave groups for tall
+//     products, else 4 waves of 16 lanes per row.
 Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 {
     (void)cus;
@@ -97,14 +98,14 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
             return Cfg{32, 2, 4, 2};
         }
         if (nu > 32 && nu < 128) return Cfg{64, 1, 4, 4};
+        if (fmt == Q4_FMT_Q4_0 && n >= 6 && nu >= 128 && nu < 256) return Cfg{32, 1, 8, 2};
         return Cfg{32, 2, 4, 2};
     }
     if (nu > 32 && nu < 128) return Cfg{64, 1, 4, 4};
     if (nu <= 32) return n <= 2 ? Cfg{16, 1, 1, 8} : n >= 5 ? Cfg{32, 2, 4, 2} : Cfg{16, 1, 4, 4};
     if (nu >= 256) return Cfg{32, 1, 8, 2};
     if (n == 1) return m >= 8192 ? Cfg{32, 1, 8, 1} : Cfg{16, 1, 4, 4};
-    if (n <= 4) return Cfg{32, 1, 8, 2};
-    return Cfg{16, 1, 4, 4};
+    return Cfg{32, 1, 8, 2};
 }
 
 // The gated product's geometry: the plain product's choice for the stacked
