@@ -208,8 +208,8 @@ int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y,
  * errors, plus Q4_EINVAL for a null or negative tuning and Q4_EUNSUPPORTED for
  * a geometry that is not instantiated for the fused product. Instantiated:
  * (8,1,1) (8,2,1) (16,1,1) (16,1,4) (32,1,4) (32,1,8) (32,2,1) (32,2,4) (64,1,4)
- * with Q4_EPILOGUE_NONE; (16,2,1) (16,2,4) (32,2,1) (32,2,4) (64,2,4) with
- * Q4_EPILOGUE_SILU_MUL. */
+ * with Q4_EPILOGUE_NONE; (16,2,1) (16,2,4) (32,2,1) (32,2,4) (32,2,8) (64,2,4)
+ * with Q4_EPILOGUE_SILU_MUL. */
 int q4_gemv_addnorm_tuned(int fmt, const void *w, const float *x, const float *delta, const float *gain, float eps,
                           float *x_out, float *y, int64_t m, int64_t k, int epilogue,
                           const q4_gemv_tuning *tuning, void *hip_stream);

@@ -113,13 +113,19 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 // same lanes per row, so each gate and up row is summed exactly as the plain
 // product sums it, and one-wave groups only where the plain choice has them.
 // (Eight lanes per row, the plain choice for very tall short-row products,
-// becomes sixteen.)
+// becomes sixteen.) 8-wave plain choices at several tokens keep their 8-wave
+// groups: with the whole row's activations in the opt-in LDS, a 4-wave group
+// would leave one group of 4 waves per CU.
 Cfg choose_glu(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 {
     const Cfg c = choose(fmt, 2 * m, k, n, cus);
     const bool one_wave = c.waves == 1;
     if (c.lpr <= 16) return one_wave ? Cfg{16, 2, 1, 8} : Cfg{16, 2, 4, 4};
-    if (c.lpr == 32) return one_wave ? Cfg{32, 2, 1, 8} : Cfg{32, 2, 4, 2};
+    if (c.lpr == 32) {
+        if (one_wave) return Cfg{32, 2, 1, 8};
+        if (c.waves == 8 && n >= 2) return Cfg{32, 2, 8, 2};
+        return Cfg{32, 2, 4, 2};
+    }
     return Cfg{64, 2, 4, 4};
 }
 

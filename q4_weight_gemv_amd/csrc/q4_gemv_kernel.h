@@ -1187,6 +1187,7 @@ int dispatch_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m
     X(16, 2, 4)                \
     X(32, 2, 1)                \
     X(32, 2, 4)                \
+    X(32, 2, 8)                \
     X(64, 2, 4)
 
 template <class F, int N>

@@ -169,7 +169,7 @@ def test_addnorm_matches_unfused(env):
 
 NORM_GEOMS = [(8, 1, 1), (8, 2, 1), (16, 1, 1), (16, 1, 4), (32, 1, 4), (32, 1, 8), (32, 2, 1), (32, 2, 4),
               (64, 1, 4)]
-NORM_GLU_GEOMS = [(16, 2, 1), (16, 2, 4), (32, 2, 1), (32, 2, 4), (64, 2, 4)]
+NORM_GLU_GEOMS = [(16, 2, 1), (16, 2, 4), (32, 2, 1), (32, 2, 4), (32, 2, 8), (64, 2, 4)]
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
