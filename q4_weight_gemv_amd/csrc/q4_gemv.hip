@@ -69,10 +69,12 @@ namespace gemv {
 //     64 lanes per row; longer rows -> 4 waves, 32 lanes x 2 rows.
 //   Q4_0, several tokens: 4 waves; 64 lanes per row for 33..127 units, else
 //     32 lanes x 2 rows; at 6..8 tokens of 128..255 units, 8-wave groups of
-//     one row per lane (the whole row's activations in the opt-in LDS).
+//     one row per lane (the whole row's activations in the opt-in LDS); the
+//     same for Q8_0 and Q1_0.
 //   Q2_K: the Q4_K choices for rows of fewer than 128 units; longer rows:
 //     32 lanes x 2 rows in 4-wave groups (8-wave groups of one row per lane
-//     at one token for rows of 256 units or more).
+//     at one token for rows of 256 units or more, and at 6..8 tokens for rows
+//     of 128..255 units).
 //   Q1_0: the Q4_0 choices, except two rows per lane for one-token LM
 //     heads (m >= 16384, nu <= 32: 8 lanes x 2 rows).
 //   Q8_0: the Q4_0 choices (same unit of 32 weights, twice the bytes),
@@ -89,7 +91,8 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
     (void)cus;
     const int64_t nu = k / kUnitWeights;
     if (fmt == Q4_FMT_Q8_0 && n == 1 && nu >= 128) return m >= 8192 ? Cfg{64, 1, 4, 4} : Cfg{32, 1, 4, 4};
-    if (fmt == Q4_FMT_Q2_K && nu >= 128) return n == 1 && nu >= 256 ? Cfg{32, 1, 8, 2} : Cfg{32, 2, 4, 2};
+    if (fmt == Q4_FMT_Q2_K && nu >= 128)
+        return (n == 1 && nu >= 256) || (n >= 6 && nu < 256) ? Cfg{32, 1, 8, 2} : Cfg{32, 2, 4, 2};
     if (fmt == Q4_FMT_Q1_0 && n == 1 && nu <= 32 && m >= 16384) return Cfg{8, 2, 1, 8};
     if (fmt == Q4_FMT_Q4_0 || fmt == Q4_FMT_Q8_0 || fmt == Q4_FMT_Q1_0) {
         if (n == 1) {
@@ -98,7 +101,7 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
             return Cfg{32, 2, 4, 2};
         }
         if (nu > 32 && nu < 128) return Cfg{64, 1, 4, 4};
-        if (fmt == Q4_FMT_Q4_0 && n >= 6 && nu >= 128 && nu < 256) return Cfg{32, 1, 8, 2};
+        if (n >= 6 && nu >= 128 && nu < 256) return Cfg{32, 1, 8, 2};
         return Cfg{32, 2, 4, 2};
     }
     if (nu > 32 && nu < 128) return Cfg{64, 1, 4, 4};
