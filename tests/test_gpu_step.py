@@ -60,8 +60,12 @@ def _check_step(gpu_logits, ref_logits, gpu_token, what):
     assert ref_logits[gpu_token] >= ref_logits.max() - 2 * err - 1e-6, f"{what}: token {gpu_token} not a maximum"
 
 
-@pytest.mark.parametrize("fmt,cfg", [(0, TINY), (2, TINY), (1, TINY_K), (3, TINY_K), (4, TINY)],
-                         ids=["q4_0", "q8_0", "q4_k", "q2_k", "q1_0"])
+HD64 = dict(TINY, hidden=256, heads=4, kv_heads=2, head_dim=64, ffn=512)
+HD128 = dict(TINY, hidden=256, heads=2, kv_heads=1, head_dim=128, ffn=512)
+
+
+@pytest.mark.parametrize("fmt,cfg", [(0, TINY), (2, TINY), (1, TINY_K), (3, TINY_K), (4, TINY), (0, HD64), (0, HD128)],
+                         ids=["q4_0", "q8_0", "q4_k", "q2_k", "q1_0", "q4_0-d64", "q4_0-d128"])
 def test_steps_match_reference(env, fmt, cfg):
     torch, q4, _ = env
     gpu, ref = _build(env, fmt, cfg)
@@ -137,3 +141,61 @@ def test_position_past_the_cache_is_refused_on_device(env):
     assert torch.isnan(gpu.buf["att"]).all()
     assert not gpu.buf["k_cache"].any() and not gpu.buf["v_cache"].any()
     assert int(gpu.buf["token"].item()) == 0
+
+
+# Positions on the attention kernel's boundaries: value chunks of 512 / 256 /
+# 128 positions (head_dim 32 / 64 / 128), score blocks of 256, and the last
+# position the scores' LDS holds (8191).
+ATT_POSITIONS = [0, 1, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1000, 4097, 8191]
+
+
+@pytest.mark.parametrize("head_dim,heads,kv_heads", [(32, 8, 2), (64, 4, 2), (128, 2, 1)])
+def test_attention_at_long_positions(env, head_dim, heads, kv_heads):
+    # One layer; the caches hold random rows (keys scaled so the softmax is
+    # far from uniform). After one step at pos, the attention output must be
+    # the float64 attention (oracle.llama) of the step's own q|k|v, rotated to
+    # pos, over those rows with row pos replaced by the new key and value;
+    # and the caches must hold the new rotated key and value at pos.
+    # theta = 1 makes every rotation angle the position itself, exact in
+    # fp32, so the comparison isolates the attention's reductions (fp32
+    # angles pos * theta^(-2i/d) drift by up to ~4e-4 rad at pos 8191, which
+    # alone moves the output by ~1e-3; the step tests cover theta = 1e4).
+    torch, q4, _ = env
+    from oracle import llama
+
+    cfg = dict(TINY, layers=1, hidden=256, heads=heads, kv_heads=kv_heads, head_dim=head_dim, ffn=512,
+               max_pos=8192, theta=1.0)
+    gpu, _ = _build(env, 0, cfg, seed=6100 + head_dim)
+    rng = np.random.default_rng(head_dim)
+    shape = (kv_heads, cfg["max_pos"], head_dim)
+    kc0 = (10.0 * rng.standard_normal(shape)).astype(np.float32)
+    vc0 = rng.standard_normal(shape).astype(np.float32)
+    qn, kvn = heads * head_dim, kv_heads * head_dim
+    for pos in ATT_POSITIONS:
+        gpu.buf["k_cache"].copy_(torch.from_numpy(kc0.reshape(-1)))
+        gpu.buf["v_cache"].copy_(torch.from_numpy(vc0.reshape(-1)))
+        gpu.set(token=11, pos=pos)
+        say(f"attention head_dim={head_dim} pos={pos}")
+        gpu.step()
+        torch.cuda.synchronize()
+        qkv = gpu.buf["qkv"].cpu().numpy().astype(np.float64)
+        q = llama.rope(qkv[:qn], pos, cfg["theta"], head_dim)
+        k = llama.rope(qkv[qn:qn + kvn], pos, cfg["theta"], head_dim).reshape(kv_heads, head_dim)
+        v = qkv[qn + kvn:].reshape(kv_heads, head_dim)
+        kc = kc0.astype(np.float64)
+        vc = vc0.astype(np.float64)
+        kc[:, pos] = k
+        vc[:, pos] = v
+        ref = llama.attention(q, kc, vc, pos, heads).reshape(heads, head_dim)
+        att = gpu.buf["att"].cpu().numpy().astype(np.float64).reshape(heads, head_dim)
+        for h in range(heads):
+            rel = np.linalg.norm(att[h] - ref[h]) / np.linalg.norm(ref[h])
+            assert rel <= 3e-5, (pos, h, rel)
+        kg = gpu.buf["k_cache"].cpu().numpy().reshape(shape)
+        vg = gpu.buf["v_cache"].cpu().numpy().reshape(shape)
+        assert np.allclose(kg[:, pos], k, rtol=1e-5, atol=1e-5 * np.abs(k).max()), pos
+        assert np.array_equal(vg[:, pos], v.astype(np.float32)), pos
+        others = np.ones(cfg["max_pos"], bool)
+        others[pos] = False
+        assert np.array_equal(kg[:, others], kc0[:, others]) and np.array_equal(vg[:, others], vc0[:, others])
+    gpu.close()
