@@ -344,12 +344,16 @@ def test_stacked_projections_equal_separate_products(env, fmt, k, parts):
         r += w.shape[0]
 
 
-@pytest.mark.parametrize("fmt", [0, 1])
-def test_sequence_and_graph_match_single_calls(env, fmt):
+@pytest.mark.parametrize("fmt,n", [(0, 2), (1, 2), (0, 8), (1, 8)])
+def test_sequence_and_graph_match_single_calls(env, fmt, n):
+    # At 8 tokens the 4096- and 11008-long rows stage their activations in
+    # the opt-in LDS (whole row, or chunks larger than 64 KiB).
     torch, q4, _ = env
-    shapes = [(768, 2304), (768, 768), (768, 3072), (3072, 768), (960, 320)] if fmt == 0 else \
-             [(1024, 512), (2560, 960), (4096, 257)]
-    n = 2
+    if n == 8:
+        shapes = [(4096, 300), (11008, 200), (768, 500)]
+    else:
+        shapes = [(768, 2304), (768, 768), (768, 3072), (3072, 768), (960, 320)] if fmt == 0 else \
+                 [(1024, 512), (2560, 960), (4096, 257)]
     ops, refs = [], []
     for i, (k, m) in enumerate(shapes):
         w = synth.weights(800 + i, m, k)
@@ -360,12 +364,12 @@ def test_sequence_and_graph_match_single_calls(env, fmt):
         q4.q4_gemv(fmt, wd, xd, ref, m, k)
         refs.append(ref)
         ops.append((wd, xd, torch.full((n, m), float("nan"), device="cuda"), m, k))
-    say(f"sequence fmt={fmt}")
+    say(f"sequence fmt={fmt} n={n}")
     q4.q4_gemv_sequence(fmt, ops, n)
     torch.cuda.synchronize()
     for (_, _, y, _, _), ref in zip(ops, refs):
         assert torch.equal(y, ref)
-    say(f"graph fmt={fmt}")
+    say(f"graph fmt={fmt} n={n}")
     g = q4.Q4Graph(fmt, ops, n)
     for rep in range(3):
         for (_, _, y, _, _) in ops:

@@ -310,6 +310,21 @@ def test_addnorm_argument_errors(q4):
     assert f(0, None, None, None, None, 1e-5, None, None, 0, 256, 0, None) == q4.Q4_OK  # m = 0: no-op
 
 
+def test_addnorm_tuned_argument_errors(q4):
+    f = q4.raw().q4_gemv_addnorm_tuned
+    W, X, D, G, XO, Y = (A16 * i for i in range(1, 7))
+    bad = q4.q4_gemv_tuning(-1, 0, 0, 0)
+    assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 256, 0, None, None) == q4.Q4_EINVAL          # no tuning
+    assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 256, 0, ctypes.byref(bad), None) == q4.Q4_EINVAL
+    big = q4.q4_gemv_tuning(0, 0, 0, 65)
+    assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 256, 0, ctypes.byref(big), None) == q4.Q4_EINVAL
+    ok = q4.q4_gemv_tuning(0, 0, 0, 0)
+    assert f(0, W, X, D, None, 1e-5, XO, Y, 64, 256, 0, ctypes.byref(ok), None) == q4.Q4_EINVAL  # no gain
+    assert f(0, W, X, D, G, 1e-5, X, Y, 64, 256, 0, ctypes.byref(ok), None) == q4.Q4_EINVAL     # x_out is x
+    assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 14592, 0, ctypes.byref(ok), None) == q4.Q4_EUNSUPPORTED
+    assert f(0, None, None, None, None, 1e-5, None, None, 0, 256, 0, ctypes.byref(ok), None) == q4.Q4_OK
+
+
 def test_sequence_epilogue_field(q4):
     lib = q4.raw()
     ops = (q4.q4_gemv_op * 1)()
