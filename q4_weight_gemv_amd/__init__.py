@@ -247,6 +247,21 @@ def q4_gemv_sequence(fmt: int, ops, n: int, stream=None) -> None:
     _check(_lib.q4_gemv_sequence(fmt, arr, len(ops), n, _stream_ptr(stream)), "q4_gemv_sequence")
 
 
+class Q4Sequence:
+    """A layer stack marshalled once for q4_gemv_sequence: each launch() enqueues
+    the products back-to-back on the stream (no graph), with no per-call
+    argument building on the Python side."""
+
+    def __init__(self, fmt: int, ops, n: int):
+        self._ops = list(ops)  # keep the tensors alive: their pointers are in the array
+        self._arr = _ops_array(self._ops)
+        self._fmt, self._n = fmt, n
+
+    def launch(self, stream=None) -> None:
+        _check(_lib.q4_gemv_sequence(self._fmt, self._arr, len(self._ops), self._n, _stream_ptr(stream)),
+               "q4_gemv_sequence")
+
+
 class Q4Graph:
     """A captured decode step: q4_graph_create / q4_graph_launch / q4_graph_destroy."""
 

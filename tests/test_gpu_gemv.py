@@ -369,6 +369,14 @@ def test_sequence_and_graph_match_single_calls(env, fmt, n):
     torch.cuda.synchronize()
     for (_, _, y, _, _), ref in zip(ops, refs):
         assert torch.equal(y, ref)
+    seq = q4.Q4Sequence(fmt, ops, n)  # marshalled once, launched twice
+    for _ in range(2):
+        for (_, _, y, _, _) in ops:
+            y.fill_(float("nan"))
+        seq.launch()
+        torch.cuda.synchronize()
+        for (_, _, y, _, _), ref in zip(ops, refs):
+            assert torch.equal(y, ref)
     say(f"graph fmt={fmt} n={n}")
     g = q4.Q4Graph(fmt, ops, n)
     for rep in range(3):
