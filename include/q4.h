@@ -176,7 +176,8 @@ int q4_gemv_glu(int fmt, const void *w, const float *x, float *y,
  * x, delta, gain, x_out: device float32 [k], 16-byte aligned; x_out must not
  * overlap x, delta or y (it is written while they are read). y: device
  * float32 [m]. k at most 14560 (the whole row is staged in one workgroup's
- * LDS). Errors as q4_gemv / q4_gemv_glu, plus Q4_EINVAL for a NULL gain, an
+ * LDS). m == 0 is a successful no-op that writes nothing (x_out included).
+ * Errors as q4_gemv / q4_gemv_glu, plus Q4_EINVAL for a NULL gain, an
  * eps that is negative, infinite or NaN, an overlapping x_out or an unknown
  * epilogue, Q4_EALIGN for a misaligned delta, gain or x_out and
  * Q4_EUNSUPPORTED for a longer row. */
