@@ -98,14 +98,17 @@ class Step:
     cold: enough weight copies (>= 512 MiB) that every step reads HBM; warm:
     one copy, replayed (MALL-resident when the step fits in 256 MB)."""
 
-    def __init__(self, torch, q4, shapes, fmt, n, config_id, cold=True):
+    def __init__(self, torch, q4, shapes, fmt, n, config_id, cold=True, quantize=None):
         import synth
 
         # Entries (K, M) or (K, M, gated): a gated product reads 2M weight rows.
+        # `quantize(fmt, w)` makes the weight buffers (the library's host
+        # quantizer unless a caller passes another with the same output).
+        quantize = quantize or q4.q4_quantize_ref
         shapes = [tuple(s) + (0,) * (3 - len(s)) for s in shapes]
         self.shapes, self.fmt, self.n = shapes, fmt, n
         self.bytes = sum(gemv_bytes(q4, fmt, m, k, n, g) for k, m, g in shapes)
-        self.host_w = [q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(config_id, i), (2 if g else 1) * m, k))
+        self.host_w = [quantize(fmt, synth.weights(synth.seed_for(config_id, i), (2 if g else 1) * m, k))
                        for i, (k, m, g) in enumerate(shapes)]
         self.host_x = [synth.activations(synth.seed_for(config_id, i, True), n, k) for i, (k, m, g) in enumerate(shapes)]
         self.xs = [torch.from_numpy(x).cuda() for x in self.host_x]
