@@ -130,6 +130,32 @@ def test_long_context(env):
     gpu.close()
 
 
+def test_smollm2_360m_graph_as_benchmarked(env):
+    # The whole SmolLM2-360M step at full size, as the benchmark's generation
+    # loop runs it: the same seeded float weights (seed 5000), Q4_0, one
+    # captured graph replayed from token 1 at position 0, the tokens chaining
+    # on the device. Every one of the first 40 positions is checked against
+    # the float64 model.
+    torch, q4, _ = env
+    cfg = dict(synth.SMOLLM2_360M)
+    say("smollm2-360m step: building")
+    gpu, ref = _build(env, 0, cfg)
+    gpu.set(token=1, pos=0)
+    say("smollm2-360m step: capture")
+    gpu.capture()
+    token = 1
+    for pos in range(40):
+        gpu.replay()
+        torch.cuda.synchronize()
+        tok = int(gpu.buf["token"].item())
+        ref_lg, _ = ref.step(token, pos)
+        _check_step(gpu.buf["logits"].cpu().numpy().astype(np.float64), ref_lg, tok, f"smollm2 pos {pos}")
+        token = tok
+    say("smollm2-360m step: 40 positions checked")
+    assert int(gpu.buf["pos"].item()) == 40
+    gpu.close()
+
+
 def test_position_past_the_cache_is_refused_on_device(env):
     # pos = max_pos: the attention writes NaN, no cache entry is written, the
     # step completes (no fault), and the selection falls back to token 0.
