@@ -52,6 +52,26 @@ __device__ __forceinline__ float block_max(float v, float *red)
     return s;
 }
 
+// Sum over W consecutive lanes (W = 8, 16 or 32, groups aligned to W), by
+// exchanges in a butterfly: every lane of the group ends with the same total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+template <int W>
+__device__ __forceinline__ float lane_group_sum(float v)
+{
+    static_assert(W == 8 || W == 16 || W == 32, "lane group of 8, 16 or 32");
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp_f<0x141>(v);  // row_half_mirror: lane 7 - i of its 8 (the other quad)
+    if constexpr (W >= 16) v += dpp_f<0x140>(v);  // row_mirror: lane 15 - i of its 16 (the other 8)
+    if constexpr (W >= 32) v += __shfl_xor(v, 16);
+    return v;
+}
+
 // Dequantized weight (r, c) of a quantized m x k matrix, any format (one value;
 // the embedding gather reads one row).
 __device__ float weight_at(int fmt, const uint8_t *w, int64_t m, int64_t k, int64_t r, int64_t c)
@@ -114,14 +134,17 @@ __device__ __forceinline__ void rope_cs(int i, int d, int pos, float log2_theta,
 // then softmax(q . k_t / sqrt(D)) over t <= pos and the weighted sum of values.
 // Caches: [kv_heads][max_pos][D]. A position outside [0, max_pos) writes NaN
 // outputs and touches no cache.
-// The step's q, k and v are loaded alongside the position. Scores: one
-// position per thread, its key row read as D/4 16-byte loads issued together
+// The step's q, k and v are loaded alongside the position. Keys and values
+// are read alike: thread (c, r) holds dimensions 4c..4c+3 of positions r,
+// r + RR, ... (RR = 256 / (D/4)), so each load instruction of a wave reads
+// whole rows, contiguous in the cache; VJ rows per thread are loaded at once
 // (rows past pos read row pos and are dropped; the current position's key
-// comes from LDS, since another workgroup may be writing it to the cache).
-// Values: thread (c, r) holds dimensions 4c..4c+3 of positions r, r + RR, ...
-// (RR = 256 / (D/4)); VJ rows per thread are loaded at once, the first VJ
-// right behind the first key rows so that their latency overlaps the scores
-// and the softmax; the per-thread sums meet in LDS at the end.
+// and value come from LDS, since another workgroup may be writing them to
+// the cache). A score is the sum of its row's D/4 partial dot products,
+// formed across those lanes by a butterfly. The first VJ value rows are
+// loaded with the first key rows so that their latency overlaps the scores
+// and the softmax; the per-thread sums of weighted values meet in LDS at the
+// end.
 template <int D>
 __global__ __launch_bounds__(kThreads) void attention_kernel(const float *__restrict__ qkv, float *__restrict__ kcache,
                                                              float *__restrict__ vcache, const int32_t *__restrict__ posp,
@@ -176,50 +199,47 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const float *__rest
         vc[static_cast<size_t>(pos) * D + tid] = vs[tid];
     }
     const float scale = 1.0f / sqrtf(static_cast<float>(D));
-    const f4 *qv = reinterpret_cast<const f4 *>(qs);
-    const f4 *kl = reinterpret_cast<const f4 *>(ks);
-    auto key_row = [&](int t, f4(&r)[VQ]) {
-        const f4 *row = reinterpret_cast<const f4 *>(kc + static_cast<size_t>(t < pos ? t : pos) * D);
-#pragma unroll
-        for (int j = 0; j < VQ; j++) r[j] = row[j];
-    };
-    float mx = -INFINITY;
-    auto score = [&](int t, const f4(&r)[VQ]) {
-        float s = 0.0f;
-#pragma unroll
-        for (int j = 0; j < VQ; j++) {
-            const f4 qq = qv[j];
-            const f4 kk = t == pos ? kl[j] : r[j];
-            s = fmaf(qq.x, kk.x, s);
-            s = fmaf(qq.y, kk.y, s);
-            s = fmaf(qq.z, kk.z, s);
-            s = fmaf(qq.w, kk.w, s);
-        }
-        if (t <= pos) {
-            s *= scale;
-            scores[t] = s;
-            mx = fmaxf(mx, s);
-        }
-    };
     const int vcol = tid % VQ, vrow0 = tid / VQ;
-    f4 vrows[VJ];
-    auto value_rows = [&](int t0) {
+    // This thread's four dimensions of the query and of the current key.
+    const f4 qq = reinterpret_cast<const f4 *>(qs)[vcol];
+    const f4 kcur = reinterpret_cast<const f4 *>(ks)[vcol];
+    // Rows t0 + vrow0 + j*RR (j < VJ) of a cache, dimensions 4*vcol..+3.
+    auto cache_rows = [&](const float *cache, int t0, f4(&r)[VJ]) {
 #pragma unroll
         for (int j = 0; j < VJ; j++) {
             const int t = t0 + vrow0 + j * RR;
-            vrows[j] = reinterpret_cast<const f4 *>(vc + static_cast<size_t>(t < pos ? t : pos) * D)[vcol];
+            r[j] = reinterpret_cast<const f4 *>(cache + static_cast<size_t>(t < pos ? t : pos) * D)[vcol];
         }
     };
+    float mx = -INFINITY;
+    auto score_rows = [&](int t0, const f4(&r)[VJ]) {
+#pragma unroll
+        for (int j = 0; j < VJ; j++) {
+            if (t0 + j * RR > pos) break;  // the slice's rows all lie past pos (uniform)
+            const int t = t0 + vrow0 + j * RR;
+            const f4 kk = t == pos ? kcur : r[j];
+            float p = qq.x * kk.x;
+            p = fmaf(qq.y, kk.y, p);
+            p = fmaf(qq.z, kk.z, p);
+            p = fmaf(qq.w, kk.w, p);
+            const float sc = lane_group_sum<VQ>(p) * scale;  // every lane of the row
+            if (t <= pos) {
+                if (vcol == 0) scores[t] = sc;
+                mx = fmaxf(mx, sc);
+            }
+        }
+    };
+    f4 vrows[VJ];
     {
-        f4 r[VQ];
-        key_row(tid, r);
-        value_rows(0);
-        score(tid, r);
+        f4 kr[VJ];
+        cache_rows(kc, 0, kr);
+        cache_rows(vc, 0, vrows);
+        score_rows(0, kr);
     }
-    for (int t0 = kThreads; t0 <= pos; t0 += kThreads) {
-        f4 r[VQ];
-        key_row(t0 + tid, r);
-        score(t0 + tid, r);
+    for (int t0 = CH; t0 <= pos; t0 += CH) {
+        f4 kr[VJ];
+        cache_rows(kc, t0, kr);
+        score_rows(t0, kr);
     }
     mx = block_max(mx, red);
     float sum = 0.0f;
@@ -234,6 +254,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const float *__rest
     auto accumulate = [&](int t0) {
 #pragma unroll
         for (int j = 0; j < VJ; j++) {
+            if (t0 + j * RR > pos) break;  // the slice's rows all lie past pos (uniform)
             const int t = t0 + vrow0 + j * RR;
             const float w = scores[t < pos ? t : pos];
             const f4 vv = t == pos ? vcur : vrows[j];
@@ -243,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(const float *__rest
     };
     accumulate(0);
     for (int t0 = CH; t0 <= pos; t0 += CH) {
-        value_rows(t0);
+        cache_rows(vc, t0, vrows);
         accumulate(t0);
     }
     reinterpret_cast<f4 *>(part)[vrow0 * VQ + vcol] = acc;
