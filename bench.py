@@ -135,10 +135,10 @@ class Step:
             g.close()
 
 
-def traffic_from_profile(per_launch_bytes):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "pmc_gemv_gpt2_step.txt")
+def traffic_from_profile(per_launch_bytes, path=None):
+    """HBM bytes per launch from the committed counter summary (or the one at
+    `path`), if it was taken on the current kernel sources (else None)."""
+    path = path or os.path.join(ROOT, "profiles", "pmc_gemv_gpt2_step.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -373,7 +373,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build measures one GPU: run with --gpus 1 (nothing here uses a second GPU)"}))
+        print(json.dumps({"error": "bench.py measures one GPU: run with --gpus 1 (nothing here uses a second GPU)"}))
         sys.exit(2)
 
     import torch
