@@ -18,7 +18,9 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "q4_oracle.c")
-LIB = os.path.join(HERE, "liboracle.so")
+# Q4_ORACLE_LIB names another build of the oracle to load (the mutation tests
+# point it at copies of the source with planted mistakes).
+LIB = os.environ.get("Q4_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 Q4_0 = 0
 Q4_K = 1
@@ -29,15 +31,17 @@ Q1_0 = 4
 OK, EINVAL, ENONFINITE, ERANGE = 0, -1, -4, -5
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (IEEE semantics: no contraction, no fast-math)."""
-    if force or not os.path.exists(LIB):
-        tmp = LIB + ".tmp"
+def build(force: bool = True, src: str | None = None, out: str | None = None) -> str:
+    """Compile the oracle with gcc (IEEE semantics: no contraction, no fast-math):
+    ``src`` (default q4_oracle.c) into ``out`` (default the library loaded here)."""
+    src, out = src or SRC, out or LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
         cmd = ["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
+               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, LIB)
-    return LIB
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
