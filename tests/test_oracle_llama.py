@@ -102,24 +102,26 @@ def _tiny_model(fmt=0, layers=2):
 
 def test_step_is_the_composition_of_its_parts(L):
     # One layer written out by hand from the operators (and numpy's own
-    # sigmoid form of silu) reproduces Model.step; a second step reads the
-    # first step's cache entries.
+    # sigmoid form of silu) reproduces Model.step over three positions, each
+    # step reading the earlier steps' cache entries. The tokens are given,
+    # not chained, and distinct: a model that repeats its input token would
+    # cache the same value at every position, and attention's output would
+    # then not depend on its weights (nor on the keys' rotation).
     import oracle
 
     cfg, bufs = _tiny_model(layers=1)
     m = L.Model(0, cfg, bufs)
-    lg0, t0 = m.step(7, 0)
-    lg1, t1 = m.step(t0, 1)
+    tokens = (7, 11, 3)
+    ref = [m.step(t, pos) for pos, t in enumerate(tokens)]
     c = cfg
     d, H, Hk = c["head_dim"], c["heads"], c["kv_heads"]
     emb = oracle.dequantize(0, bufs["emb"], c["vocab"], c["hidden"]).astype(np.float64)
     W = {n: oracle.dequantize(0, bufs[f"{n}0"], *shape).astype(np.float64) for n, shape in
          (("qkv", (H * d + 2 * Hk * d, c["hidden"])), ("o", (c["hidden"], H * d)),
           ("gu", (2 * c["ffn"], c["hidden"])), ("down", (c["hidden"], c["ffn"])))}
-    kc = np.zeros((Hk, 2, d))
-    vc = np.zeros((Hk, 2, d))
-    tok, logits = 7, None
-    for pos in range(2):
+    kc = np.zeros((Hk, len(tokens), d))
+    vc = np.zeros((Hk, len(tokens), d))
+    for pos, tok in enumerate(tokens):
         x = emb[tok]
         h = x / np.sqrt(np.mean(x * x) + c["eps"]) * bufs["norm_attn0"]
         qkv = W["qkv"] @ h
@@ -132,6 +134,5 @@ def test_step_is_the_composition_of_its_parts(L):
         gate = gu[: c["ffn"]]
         x = x + W["down"] @ (gate * (1.0 / (1.0 + np.exp(-gate))) * gu[c["ffn"]:])
         logits = emb @ (x / np.sqrt(np.mean(x * x) + c["eps"]) * bufs["norm_final"])
-        tok = int(np.argmax(logits))
-        assert np.allclose(logits, (lg0, lg1)[pos], rtol=1e-12, atol=1e-12)
-        assert tok == (t0, t1)[pos]
+        assert np.allclose(logits, ref[pos][0], rtol=1e-12, atol=1e-12), pos
+        assert int(np.argmax(logits)) == ref[pos][1]

@@ -4,13 +4,17 @@ Each case plants one mistake in a copy of the oracle's C source: a wrong
 rounding rule, a dropped or mis-signed term, a wrong index, offset or
 operand, a swapped field. The copy is built with the oracle's own flags and
 the oracle's pin suites (tests/test_oracle_*.py) run against it in a
-subprocess; at least one pin must fail. The pins compare the oracle with
+subprocess; at least one pin must fail. The float64 decode-step reference
+(oracle/llama.py) gets the same treatment: a copy of the oracle package with
+one mistake in it is imported in place of the original, and its pins must
+fail. The pins compare the oracle with
 values fixed from outside it (hand-worked blocks, exact rationals, closed
 forms, library routines), so a mistake that none of them notices would be
 one the oracle could carry into every parity test.
 """
 import glob
 import os
+import shutil
 import subprocess
 import sys
 
@@ -92,4 +96,54 @@ def test_planted_mistake_fails_a_pin(tmp_path, name, old, new):
     src = open(oracle.SRC).read()
     assert src.count(old) == 1, f"{name}: the text to mutate must occur exactly once"
     r = _run_pins(tmp_path, src.replace(old, new))
+    assert r.returncode == 1 and " failed" in r.stdout, f"{name} was not caught:\n{r.stdout[-1500:]}\n{r.stderr[-500:]}"
+
+
+# Mistakes in the float64 decode step (oracle/llama.py).
+LLAMA_MUTANTS = [
+    ("rmsnorm_eps_outside_root", "x / math.sqrt(float(np.mean(x * x)) + eps)",
+     "x / (math.sqrt(float(np.mean(x * x))) + eps)"),
+    ("rope_sign", "out[:, :half] = v[:, :half] * c - v[:, half:] * s", "out[:, :half] = v[:, :half] * c + v[:, half:] * s"),
+    ("rope_frequency", "a = pos * theta ** (-2.0 * i / head_dim)", "a = pos * theta ** (-1.0 * i / head_dim)"),
+    ("attention_scale", "s = k @ q[h] / math.sqrt(d)", "s = k @ q[h] / d"),
+    ("attention_group_map", "k = kcache[h // group, : pos + 1]\n        v = vcache[h // group, : pos + 1]",
+     "k = kcache[h % kv_heads, : pos + 1]\n        v = vcache[h % kv_heads, : pos + 1]"),
+    ("attention_reads_one_past", "k = kcache[h // group, : pos + 1]", "k = kcache[h // group, : pos + 2]"),
+    ("step_mlp_norm_weight", "h2 = rmsnorm(x, L[\"norm_mlp\"], c[\"eps\"])", "h2 = rmsnorm(x, L[\"norm_attn\"], c[\"eps\"])"),
+    ("step_gate_up_swapped", "delta = L[\"down\"] @ (silu(gu[: c[\"ffn\"]]) * gu[c[\"ffn\"]:])",
+     "delta = L[\"down\"] @ (silu(gu[c[\"ffn\"]:]) * gu[: c[\"ffn\"]])"),
+    ("step_value_not_rotated_key", "k = rope(qkv[q_n:q_n + kv_n], pos, c[\"theta\"], d)", "k = qkv[q_n:q_n + kv_n]"),
+]
+
+
+def _run_llama_pins(tmp_path, source):
+    import oracle
+
+    pkg = tmp_path / "oracle"
+    shutil.copytree(os.path.dirname(oracle.SRC), pkg, ignore=shutil.ignore_patterns("__pycache__"))
+    (pkg / "llama.py").write_text(source)
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    env.pop("Q4_ORACLE_LIB", None)
+    where = subprocess.run([sys.executable, "-c", "import oracle.llama as m; print(m.__file__)"], cwd=tmp_path, env=env,
+                           capture_output=True, text=True, timeout=120)
+    assert where.stdout.strip() == str(pkg / "llama.py"), where.stdout + where.stderr  # the copy is what runs
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-m", "not gpu", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", "test_oracle_llama.py")],
+                          cwd=tmp_path, env=env, capture_output=True, text=True, timeout=600)
+
+
+def test_unmutated_llama_copy_passes(tmp_path):
+    import oracle
+
+    r = _run_llama_pins(tmp_path, open(os.path.join(os.path.dirname(oracle.SRC), "llama.py")).read())
+    assert r.returncode == 0, r.stdout[-1500:]
+
+
+@pytest.mark.parametrize("name,old,new", LLAMA_MUTANTS, ids=[m[0] for m in LLAMA_MUTANTS])
+def test_planted_llama_mistake_fails_a_pin(tmp_path, name, old, new):
+    import oracle
+
+    src = open(os.path.join(os.path.dirname(oracle.SRC), "llama.py")).read()
+    assert src.count(old) == 1, f"{name}: the text to mutate must occur exactly once"
+    r = _run_llama_pins(tmp_path, src.replace(old, new))
     assert r.returncode == 1 and " failed" in r.stdout, f"{name} was not caught:\n{r.stdout[-1500:]}\n{r.stderr[-500:]}"
