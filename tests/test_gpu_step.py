@@ -1,8 +1,9 @@
 """GPU parity of the whole decode step (q4_llama_step / the captured graph)
 against the float64 reference oracle.llama.Model.
 
-Small Llama-family models run several chained steps on the device; the oracle
-follows the tokens the device picks, and each step's logits are compared
+Small Llama-family models run several steps on the device (given tokens, or
+chained through the device's own selection, which the oracle then follows);
+each step's logits are compared
 (normwise, and elementwise against the logits' term scale), the device token
 must be a maximum of the reference logits within that error, and the KV cache
 must hold the reference's rotated keys and values. The captured graph
@@ -67,11 +68,15 @@ HD128 = dict(TINY, hidden=256, heads=2, kv_heads=1, head_dim=128, ffn=512)
 @pytest.mark.parametrize("fmt,cfg", [(0, TINY), (2, TINY), (1, TINY_K), (3, TINY_K), (4, TINY), (0, HD64), (0, HD128)],
                          ids=["q4_0", "q8_0", "q4_k", "q2_k", "q1_0", "q4_0-d64", "q4_0-d128"])
 def test_steps_match_reference(env, fmt, cfg):
+    # Six steps with given, distinct tokens: these small random models tend
+    # to repeat their input token, and a cache holding the same value at
+    # every position would hide the attention weights. The device's own
+    # selection and position advance are checked at every step; the chained
+    # generation loop is covered by the graph and long-context tests.
     torch, q4, _ = env
     gpu, ref = _build(env, fmt, cfg)
-    gpu.set(token=7, pos=0)
-    token = 7
-    for pos in range(6):
+    for pos, token in enumerate((7, 11, 3, 250, 42, 99)):
+        gpu.set(token=token, pos=pos)
         say(f"step fmt={fmt} pos={pos}")
         gpu.step()
         torch.cuda.synchronize()
@@ -80,7 +85,6 @@ def test_steps_match_reference(env, fmt, cfg):
         ref_lg, _ = ref.step(token, pos)
         _check_step(lg, ref_lg, tok, f"fmt {fmt} pos {pos}")
         assert int(gpu.buf["pos"].item()) == pos + 1
-        token = tok
     c = cfg
     kc = gpu.buf["k_cache"].cpu().numpy().reshape(c["layers"], c["kv_heads"], c["max_pos"], c["head_dim"])
     vc = gpu.buf["v_cache"].cpu().numpy().reshape(c["layers"], c["kv_heads"], c["max_pos"], c["head_dim"])
@@ -169,9 +173,10 @@ def test_position_past_the_cache_is_refused_on_device(env):
     assert int(gpu.buf["token"].item()) == 0
 
 
-# Positions on the attention kernel's boundaries: value chunks of 512 / 256 /
-# 128 positions (head_dim 32 / 64 / 128), score blocks of 256, and the last
-# position the scores' LDS holds (8191).
+# Positions on the attention kernel's boundaries: rounds of 512 / 256 / 128
+# positions (head_dim 32 / 64 / 128) for keys and values alike, the row
+# slices of 32 / 16 / 8 positions inside them (skipped past pos), and the
+# last position the scores' LDS holds (8191).
 ATT_POSITIONS = [0, 1, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1000, 4097, 8191]
 
 
