@@ -498,7 +498,7 @@ def main():
         if on("gemm"):
             extras["gemm_smollm2_layer"] = bench_gemm(torch, q4, timer, reps=max(2, K // 50))
             extras["gemm_smollm2_layer_fused_qkv_gateup"] = bench_gemm(
-                torch, q4, timer, reps=max(2, K // 50), shapes=[(960, 1600), (960, 960), (960, 5120), (2560, 960)],
+                torch, q4, timer, reps=max(2, K // 50), shapes=synth.smollm2_360m_layer_stacked(),
                 per_matrix=False)
         result["extras"] = extras
 

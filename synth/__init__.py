@@ -137,6 +137,12 @@ def smollm2_360m_layer():
     return [(h, h), (h, 320), (h, 320), (h, h), (h, 2560), (h, 2560), (2560, h)]
 
 
+def smollm2_360m_layer_stacked():
+    """The same layer with q|k|v and gate|up stacked: 4 matrices (prefill GEMM)."""
+    h = 960
+    return [(h, 1600), (h, h), (h, 5120), (2560, h)]
+
+
 def llama7b_layer():
     """7B-class layer as listed: 4096->4096, 4096->11008 (gate, up) and 11008->4096."""
     return [(4096, 4096), (4096, 11008), (4096, 11008), (11008, 4096)]

@@ -83,8 +83,10 @@ def test_parity_small(env, fmt, m, k, n):
     _parity(env, fmt, m, k, n, seed=600 + n)
 
 
-@pytest.mark.parametrize("k,m", sorted(set(synth.smollm2_360m_layer())))
+@pytest.mark.parametrize("k,m", sorted(set(synth.smollm2_360m_layer() + synth.smollm2_360m_layer_stacked())))
 def test_parity_smollm2_layer_512_tokens(env, k, m):
+    # Every matrix the prefill bench times: the layer's seven, and its
+    # stacked q|k|v (960 -> 1600) and gate|up (960 -> 5120).
     _parity(env, 0, m, k, 512, seed=700 + k % 13, rows=sample_rows(m, k, edge=96, rand=64))
 
 
