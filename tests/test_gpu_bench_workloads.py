@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("gpt2_124m", "gpt2_124m_step", 1),           # the headline step: 49 Q4_0 products
     ("smollm2_360m", "smollm2_360m_step", 2),     # 225 products
+    ("smollm2_360m_stacked", "smollm2_360m_step_fused", 2),  # q|k|v and gate|up stacked: 129
     ("smollm2_360m_gated", "smollm2_360m_step_gated", 2),  # q|k|v stacked, gate.up gated: 129
 ]
 
