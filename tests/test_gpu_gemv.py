@@ -415,6 +415,7 @@ GLU_CASES = [
     (3, 1, 130, 1024), (3, 4, 300, 4096),
     (4, 1, 130, 960), (4, 4, 300, 4096), (4, 1, 2560, 960),
     (0, 8, 300, 4096), (1, 4, 300, 4096), (1, 8, 70, 11008),  # 8-wave gated groups
+    (0, 1, 11008, 4096), (1, 1, 11008, 4096), (1, 4, 11008, 4096), (1, 8, 11008, 4096),  # the 7B gate|up as benchmarked
 ]
 
 
