@@ -227,8 +227,13 @@ def q4_gemm_tuned(fmt: int, w, x_bf16, y, m: int, k: int, tile_rows=0, tile_toke
 
 
 def q4_read_probe(buf, sink, groups: int = 2048, stream=None) -> None:
-    """Stream-read a device buffer once (measured HBM ceiling; not a product)."""
-    _check(_lib.q4_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), groups,
+    """Stream-read a device buffer once (measured HBM ceiling; not a product).
+    ``sink`` None: a pure read; else (device, 4-byte elements, at least
+    4 * ``groups`` of them) it receives one XOR fold per wave."""
+    if sink is not None and sink.numel() * sink.element_size() < 16 * groups:
+        raise Q4Error(Q4_EINVAL, "q4_read_probe: sink holds fewer than 4 * `groups` 4-byte words")
+    _check(_lib.q4_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(),
+                              None if sink is None else sink.data_ptr(), groups,
                               _stream_ptr(stream)), "q4_read_probe")
 
 

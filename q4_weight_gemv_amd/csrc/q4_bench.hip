@@ -25,8 +25,17 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4 *__restrict__ p, 
         acc ^= (a ^ b) ^ (c ^ d);
     }
     for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
-    const uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
-    if (v == 0x9E3779B9u) sink[0] = v;
+    uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (!sink) {
+        // A pure read: the fold is consumed here (so the loads stay) and
+        // nothing is stored or exchanged.
+        asm volatile("" ::"v"(v));
+        return;
+    }
+    // Each wave's fold of everything it read, one plain store per wave (no
+    // barrier holds a finished wave, no shared word serializes them).
+    for (int o = 32; o > 0; o >>= 1) v ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o));
+    if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4u + (threadIdx.x >> 6)] = v;
 }
 
 }  // namespace bench
@@ -34,7 +43,7 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4 *__restrict__ p, 
 
 extern "C" int q4_read_probe(const void *p, size_t bytes, uint32_t *sink, int groups, void *hip_stream)
 {
-    if (!p || !sink || bytes == 0 || groups < 1 || groups > 65536) return Q4_EINVAL;
+    if (!p || bytes == 0 || groups < 1 || groups > 65536) return Q4_EINVAL;
     if ((bytes & 15) || (reinterpret_cast<uintptr_t>(p) & 15) || (reinterpret_cast<uintptr_t>(sink) & 3))
         return Q4_EALIGN;
     hipLaunchKernelGGL(q4::bench::read_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0,

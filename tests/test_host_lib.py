@@ -409,6 +409,7 @@ def test_read_probe_argument_errors(q4):
     assert f(None, 1 << 20, A16, 64, None) == q4.Q4_EINVAL
     assert f(A16, 0, A16, 64, None) == q4.Q4_EINVAL
     assert f(A16, 1 << 20, A16, 0, None) == q4.Q4_EINVAL
+    assert f(A16, 1 << 20, A16 + 2, 64, None) == q4.Q4_EALIGN  # sink not 4-byte aligned (NULL is allowed)
     assert f(A16, 1 << 20, A16, 65537, None) == q4.Q4_EINVAL
     assert f(A16 + 8, 1 << 20, A16, 64, None) == q4.Q4_EALIGN
     assert f(A16, (1 << 20) + 8, A16, 64, None) == q4.Q4_EALIGN
