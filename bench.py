@@ -18,10 +18,14 @@ Infinity Cache.
               launched on, timed region / launches), against 8 TB/s HBM.
 
 Also reported in "extras": the 7B-class shapes (Q4_0 at N=1 -- the gate
-shapes -- and Q4_K at N=1/4/8), the SmolLM2-360M step, the prefill GEMM over
-a SmolLM2-360M layer at 512 tokens, launches from a plain stream, and the
-per-launch floor. "cpu_baseline" is the CPU oracle timed on the host cores on
-whole repeats of the same step (bounded to about 10 s).
+shapes -- Q4_K at N=1/4/8, the other formats, and the gated gate|up product),
+the SmolLM2-360M product stacks (plain, stacked, gated), the whole
+SmolLM2-360M decode step as a replayed generation loop, the prefill GEMM over
+a SmolLM2-360M layer at 512 tokens (separate and stacked matrices), warm
+steps, launches from a plain stream, the per-launch floor, and the streaming-
+read ceiling (a pure read, and the same read storing a few bytes per wave).
+"cpu_baseline" is the CPU oracle timed on the host cores on whole repeats of
+the same step (bounded to about 10 s).
 """
 from __future__ import annotations
 
