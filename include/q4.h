@@ -141,7 +141,9 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
  * [2^14, 2^15)), then held as a pair of fp16 values hi + lo (about 2^-23
  * relative) when m < 256, or as one fp16 value (at most 2^-12 relative, so
  * every output is within 2^-12 * sum_k |w_hat[i][k] x[t][k]|) when m >= 256;
- * products and sums are fp32. */
+ * products and sums are fp32. A NaN among token t's activations makes every
+ * y[t][i] NaN, as exact IEEE evaluation does (0 * NaN included); the other
+ * tokens are unaffected. x is otherwise expected finite. */
 int q4_gemv(int fmt, const void *w, const float *x, float *y,
             int64_t m, int64_t k, int64_t n, void *hip_stream);
 

@@ -292,6 +292,31 @@ def test_deterministic(env):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt,m,k,n", [(0, 300, 1024, 1), (0, 100, 960, 4), (1, 300, 1024, 4), (2, 130, 960, 1),
+                                         (3, 130, 1024, 4), (4, 130, 960, 4)])
+def test_nan_activation_makes_its_token_nan(env, fmt, m, k, n):
+    # IEEE arithmetic: a NaN among one token's activations makes every output
+    # of that token NaN (0 * NaN is NaN too), as in the oracle; the other
+    # tokens are unaffected. Outputs start at a finite sentinel, so a NaN
+    # below was written by the kernel.
+    torch, q4, orc = env
+    buf = _quantize_both(q4, orc, fmt, synth.weights(synth.seed_for(1300 + fmt, m), m, k))
+    x = synth.activations(synth.seed_for(1300 + fmt, m, True), n, k)
+    bad = n - 1
+    x[bad, k // 3] = np.nan
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(x).cuda()
+    yd = torch.full((n, m), 12345.0, dtype=torch.float32, device="cuda")
+    say(f"nan activation fmt={fmt} m={m} k={k} n={n}")
+    q4.q4_gemv(fmt, wd, xd, yd, m, k)
+    torch.cuda.synchronize()
+    y = yd.cpu().numpy()
+    yr, ad = orc.matvec(fmt, buf, m, k, x, threads=threads(), absdot=True)
+    assert np.isnan(yr[bad]).all() and np.isnan(y[bad]).all()
+    if n > 1:
+        check_tolerance(y[:bad], yr[:bad], ad[:bad], GEMV_TOL, what=f"fmt={fmt} tokens without the NaN")
+
+
 def test_extreme_activation_scales(env):
     # Per-unit power-of-two scaling: results track x * 2^s exactly for large
     # and tiny s (fp16 alone would overflow at 65504 or flush tiny values).
