@@ -223,7 +223,8 @@ int q4_gemv_addnorm_tuned(int fmt, const void *w, const float *x, const float *d
  * n >= 1 (any token count). Weight tiles are dequantized to bf16 into LDS
  * and reused across the token tile by bf16 matrix-core (MFMA) instructions
  * with fp32 accumulation (Methodology section 3: dequantize into shared
- * memory and reuse for the matrix-matrix product). */
+ * memory and reuse for the matrix-matrix product). A NaN among token t's
+ * activations makes every Y[t][i] NaN; the other tokens are unaffected. */
 int q4_gemm(int fmt, const void *w, const uint16_t *x_bf16, float *y,
             int64_t m, int64_t k, int64_t n, void *hip_stream);
 

@@ -153,6 +153,29 @@ def test_q1_0_hand_built_words(env):
     check_tolerance(y, yb, adb, 1e-4, what="gemm q1_0 hand-built (bf16 W)")
 
 
+@pytest.mark.parametrize("fmt,m,k,n", [(0, 130, 960, 70), (1, 96, 1024, 130), (4, 130, 960, 65)])
+def test_nan_activation_makes_its_token_nan(env, fmt, m, k, n):
+    # A NaN among one token's bf16 activations makes every output of that
+    # token NaN, as in the oracle; the other tokens are unaffected. Outputs
+    # start at a finite sentinel, so a NaN below was written by the kernel.
+    torch, q4, orc = env
+    buf = _quantize_both(q4, orc, fmt, synth.weights(synth.seed_for(1400 + fmt, m), m, k))
+    xb = synth.bf16_bits(synth.activations(synth.seed_for(1400 + fmt, m, True), n, k))
+    bad = n // 2
+    xb[bad, k // 3] = 0x7FC0  # bf16 quiet NaN
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).cuda()
+    yd = torch.full((n, m), 12345.0, dtype=torch.float32, device="cuda")
+    say(f"gemm nan activation fmt={fmt} m={m} k={k} n={n}")
+    q4.q4_gemm(fmt, wd, xd, yd, m, k)
+    torch.cuda.synchronize()
+    y = yd.cpu().numpy()
+    yr, ad = orc.matmul(fmt, buf, m, k, xb, threads=threads(), absdot=True)
+    assert np.isnan(yr[bad]).all() and np.isnan(y[bad]).all()
+    good = [t for t in range(n) if t != bad]
+    check_tolerance(y[good], yr[good], ad[good], GEMM_TOL, what=f"gemm fmt={fmt} tokens without the NaN")
+
+
 def test_gemm_misaligned_and_noop(env):
     torch, q4, _ = env
     w = torch.zeros(4096, dtype=torch.uint8, device="cuda")
