@@ -18,13 +18,19 @@
 //   * No MFMA: the arithmetic intensity is ~3.6 flop/byte.
 //   * VALU budget: a nibble pair is turned into an fp16 pair by one AND:
 //     (w & 0x000F000F) reads as two fp16 subnormals q*2^-24, and
-//     (w & 0x00F000F0) as 16q*2^-24. For Q4_0 one packed fp16 add of
-//     -8*2^-24 (-128*2^-24) makes them (q-8)*2^-24 (16(q-8)*2^-24), still
-//     exact subnormals, so every product (q-8)*x is exact and a zero weight
-//     contributes exactly zero. v_dot2c_f32_f16 multiplies the pairs with fp16
-//     activation pairs and accumulates in fp32. Q4_K keeps unsigned codes and
-//     folds its mins in through precomputed activation sums, one per 16
-//     elements (the format's value is itself that difference of two terms).
+//     (w & 0x00F000F0) as 16q*2^-24. One packed fp16 fma, times 1024 less
+//     8*2^-14 (128*2^-14), makes them (q-8)*2^-14 (16(q-8)*2^-14), exact
+//     normal fp16 values (or zero), so every product (q-8)*x is exact and a
+//     zero weight contributes exactly zero. v_dot2c_f32_f16 multiplies the
+//     pairs with fp16 activation pairs and accumulates in fp32. The codes
+//     are moved out of the fp16 subnormal range on purpose: fed subnormal
+//     operands, v_dot2c_f32_f16 on gfx950 keeps fewer bits of the products
+//     and rounds them down (a measured mean error of -2^-22 of the unit's
+//     term scale per 32-weight unit, the same sign for every row), while
+//     with normal operands it matches a chain of IEEE fp32 fmas. Q4_K keeps
+//     unsigned codes (a packed multiply by 1024) and folds its mins in
+//     through precomputed activation sums, one per 16 elements (the format's
+//     value is itself that difference of two terms).
 //   * Activations are staged once per workgroup into LDS as fp16 pairs in the
 //     order the unpack produces them, each 32-element unit scaled by a power
 //     of two that puts its largest magnitude in [2^14, 2^15): the scaling is
@@ -59,6 +65,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kLo = 0x000F000Fu;  // low nibbles of bytes 0 and 2
 constexpr uint32_t kHi = 0x00F000F0u;  // high nibbles of bytes 0 and 2
 constexpr int kLdsBytesPerUnit = 144;  // 2 x 64 B of fp16 pairs (hi, lo) + 16 B of unit metadata
+// LDS layout of the staged activations, unit-major: (token t, unit ul) owns
+// nine 16-byte slots from xslot(t, ul, uc): the hi and lo fp16 pairs of
+// nibble dword i at 2i and 2i + 1, the unit's metadata at 8. One address per
+// unit, the slots as immediate offsets; consecutive lanes read units 144 B
+// apart, which falls on distinct LDS banks for a 16-byte read.
+constexpr int kLdsSlots = 9;
+__device__ __forceinline__ int xslot(int t, int ul, int uc) { return (t * uc + ul) * kLdsSlots; }
 constexpr int kMaxLdsBytes = 64 * 1024;
 // Products with fewer rows hold activations as hi + lo fp16 pairs; taller
 // ones as a single fp16 each (see launch_one).
@@ -86,16 +99,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
                                              kBufferWord3);
 }
 
-// Descriptor for the bytes [off, bytes) of a buffer: the uniform part of an
-// address goes into the (scalar) base, so the hardware range check, which
-// covers the per-lane offset, still stops at the buffer's end.
-// (Both values are wave-uniform; readfirstlane states that to the compiler,
-// which otherwise may build the descriptor in vector registers and wrap every
-// load in a per-lane loop.)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t sub_rsrc(const uint8_t *p, uint32_t bytes, uint32_t off)
+// A wave-uniform value stated as such (kept in a scalar register): the
+// uniform part of a load's offset goes into the instruction's scalar offset.
+// Only the per-lane offset is range-checked against the descriptor, and a
+// live lane's whole offset lies inside the buffer by construction, so a lane
+// pointed at kNoFetch still reads zeros without a memory request.
+__device__ __forceinline__ uint32_t uniform(uint32_t v)
 {
-    const uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(off < bytes ? off : bytes)));
-    return make_rsrc(p + o, bytes - o);
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
 }
 
 template <int AUX>
@@ -147,16 +158,29 @@ __device__ __forceinline__ uint32_t add_h2(uint32_t a, _Float16 c)
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// Q4_0 codes as signed subnormal pairs: (q-8)*2^-24 for low nibbles,
-// 16(q-8)*2^-24 for high nibbles (exact: integers up to 128 times 2^-24).
+// Masked code bits c*2^-24 (an fp16 subnormal pair, c < 1024) as the normal
+// pair c*2^-14 - OFF*2^-14: one packed fp16 fma, exact (c*2^-14 and the
+// result have at most 11 significant bits and lie in the normal range, or
+// are zero). Every code below carries the factor 2^-14 (kCodeExp), which
+// the unit's metadata scale removes.
+constexpr int kCodeExp = 14;
+template <int OFF>
+__device__ __forceinline__ uint32_t code_pair(uint32_t v)
+{
+    const half2_t h = __builtin_bit_cast(half2_t, v);
+    const _Float16 k = static_cast<_Float16>(1024.0f);
+    const _Float16 o = static_cast<_Float16>(-static_cast<float>(OFF) * 0x1p-14f);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h, half2_t{k, k}, half2_t{o, o}));
+}
+
+// Q4_0 codes as signed normal fp16 pairs: (q-8)*2^-14 for low nibbles,
+// 16(q-8)*2^-14 for high nibbles.
 template <bool LO>
 __device__ __forceinline__ float dot_dword(uint32_t q, u32x4 xh, u32x4 xl, float acc)
 {
-    const _Float16 m8 = static_cast<_Float16>(-0x1p-21f);   // -8 * 2^-24
-    const _Float16 m128 = static_cast<_Float16>(-0x1p-17f); // -128 * 2^-24
     const uint32_t s = q >> 8;
-    const uint32_t p0 = add_h2(q & kLo, m8), p1 = add_h2(q & kHi, m128);
-    const uint32_t p2 = add_h2(s & kLo, m8), p3 = add_h2(s & kHi, m128);
+    const uint32_t p0 = code_pair<8>(q & kLo), p1 = code_pair<128>(q & kHi);
+    const uint32_t p2 = code_pair<8>(s & kLo), p3 = code_pair<128>(s & kHi);
     acc = dot2(p0, xh.x, acc);
     acc = dot2(p1, xh.y, acc);
     acc = dot2(p2, xh.z, acc);
@@ -191,33 +215,34 @@ struct FmtQ4_0 {
     // 16 nibble bytes at (row*nu + u)*16, its scale at scale_plane +
     // (row*nu + u)*2. The lane part goes in the VGPR offset, the uniform part
     // (tile, chunk, batch) in the SGPR offset, jl in the immediate.
-    __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+    __device__ static void load(Regs &g, __amdgpu_buffer_rsrc_t wr, uint32_t scale_plane, uint32_t nu,
                                 uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl, bool live)
     {
-        const uint32_t uni_u = trow * nu + ubase;
+        const uint32_t uni_u = uniform(trow * nu + ubase);
         const uint32_t lane_u = rowrel * nu + li + jl;
-        g.q = load16<kNonTemporal>(sub_rsrc(w, wbytes, uni_u * 16u), live ? lane_u * 16u : kNoFetch, 0);
-        g.d = __builtin_amdgcn_raw_buffer_load_b16(sub_rsrc(w, wbytes, scale_plane + uni_u * 2u),
-                                                   live ? lane_u * 2u : kNoFetch, 0, 0);
+        g.q = load16<kNonTemporal>(wr, live ? lane_u * 16u : kNoFetch, uni_u * 16u);
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(wr, live ? lane_u * 2u : kNoFetch, scale_plane + uni_u * 2u, 0);
     }
-    // Unit metadata: z = 2^(e+24) (unit scale times the fp16-subnormal factor).
+    // Unit metadata: z = 2^(e+14) (the unit's activation scale times the
+    // codes' factor 2^14).
     __device__ static f32x4 meta(float /*gl*/, float /*gh*/, int e)
     {
-        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + 24), 0.0f};
+        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + kCodeExp), 0.0f};
     }
     template <int N, int R, bool LO>
     __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
-                                      const f32x4 *__restrict__ meta, int ul, int uc, uint32_t /*u*/,
+                                      int ul, int uc, uint32_t /*u*/,
                                       float (&acc)[R][N])
     {
 #pragma unroll
         for (int t = 0; t < N; t++) {
-            const f32x4 mt = meta[t * uc + ul];
+            const u32x4 *xu = xs + xslot(t, ul, uc);
+            const f32x4 mt = __builtin_bit_cast(f32x4, xu[8]);
             u32x4 xh[4], xl[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                xh[i] = xs[(t * 8 + 2 * i) * uc + ul];
-                xl[i] = LO ? xs[(t * 8 + 2 * i + 1) * uc + ul] : u32x4{0u, 0u, 0u, 0u};
+                xh[i] = xu[2 * i];
+                xl[i] = LO ? xu[2 * i + 1] : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int r = 0; r < R; r++) {
@@ -265,17 +290,15 @@ struct FmtQ8_0 {
     };
     // Unit (row, u), row = trow + rowrel, u = ubase + li + jl: its 32 code
     // bytes at (row*nu + u)*32, its scale at scale_plane + (row*nu + u)*2.
-    __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+    __device__ static void load(Regs &g, __amdgpu_buffer_rsrc_t wr, uint32_t scale_plane, uint32_t nu,
                                 uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl, bool live)
     {
-        const uint32_t uni_u = trow * nu + ubase;
+        const uint32_t uni_u = uniform(trow * nu + ubase);
         const uint32_t lane_u = rowrel * nu + li + jl;
-        const __amdgpu_buffer_rsrc_t r = sub_rsrc(w, wbytes, uni_u * 32u);
         const uint32_t off = live ? lane_u * 32u : kNoFetch;
-        g.q0 = load16<kNonTemporal>(r, off, 0);
-        g.q1 = load16<kNonTemporal>(r, off + 16u, 0);
-        g.d = __builtin_amdgcn_raw_buffer_load_b16(sub_rsrc(w, wbytes, scale_plane + uni_u * 2u),
-                                                   live ? lane_u * 2u : kNoFetch, 0, 0);
+        g.q0 = load16<kNonTemporal>(wr, off, uni_u * 32u);
+        g.q1 = load16<kNonTemporal>(wr, off + 16u, uni_u * 32u);
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(wr, live ? lane_u * 2u : kNoFetch, scale_plane + uni_u * 2u, 0);
     }
     // Unit metadata: z = 2^e (the unit's activation scale; the codes are
     // integers).
@@ -285,17 +308,18 @@ struct FmtQ8_0 {
     }
     template <int N, int R, bool LO>
     __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
-                                      const f32x4 *__restrict__ meta, int ul, int uc, uint32_t /*u*/,
+                                      int ul, int uc, uint32_t /*u*/,
                                       float (&acc)[R][N])
     {
 #pragma unroll
         for (int t = 0; t < N; t++) {
-            const f32x4 mt = meta[t * uc + ul];
+            const u32x4 *xu = xs + xslot(t, ul, uc);
+            const f32x4 mt = __builtin_bit_cast(f32x4, xu[8]);
             u32x4 xh[4], xl[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                xh[i] = xs[(t * 8 + 2 * i) * uc + ul];
-                xl[i] = LO ? xs[(t * 8 + 2 * i + 1) * uc + ul] : u32x4{0u, 0u, 0u, 0u};
+                xh[i] = xu[2 * i];
+                xl[i] = LO ? xu[2 * i + 1] : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int r = 0; r < R; r++) {
@@ -324,11 +348,12 @@ struct FmtQ8_0 {
 };
 
 // Q1_0: a unit is one block: a 32-bit code word (bit e = element e) and an
-// fp16 scale d in the scale plane. The value (2b - 1) d makes the unit's dot
-// product d (2 A - S), A = sum of the activations whose code is 1, S = the
-// unit's activation sum (from the staging, in the metadata). A is formed by
-// dot2 on the 0/1 codes as exact fp16 subnormals: b * 2^-24 for L elements,
-// 16 b * 2^-24 for H elements (whose staged activations are divided by 16).
+// fp16 scale d in the scale plane. The value is (2b - 1) d: each bit pair,
+// moved to bits (0, 16) for L elements (b*2^-24 as fp16 subnormals) or
+// (4, 20) for H elements (16b*2^-24; their staged activations are divided by
+// 16), becomes the exact normal codes (2b - 1)*2^-14 (16(2b - 1)*2^-14) by
+// one packed fp16 fma (times 2048, less 2^-14 (16*2^-14)), so dot2 forms the
+// unit's sum of (2b - 1) x directly.
 // Pair order as staged: (L, L+2), (H, H+2), (L+1, L+3), (H+1, H+3) with
 // L = 4i, H = L + 16 for item i, i.e. bits 4i.. of the word shifted down.
 struct FmtQ1_0 {
@@ -345,21 +370,29 @@ struct FmtQ1_0 {
     };
     // Unit (row, u), row = trow + rowrel, u = ubase + li + jl: its code word
     // at (row*nu + u)*4, its scale at scale_plane + (row*nu + u)*2.
-    __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+    __device__ static void load(Regs &g, __amdgpu_buffer_rsrc_t wr, uint32_t scale_plane, uint32_t nu,
                                 uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl, bool live)
     {
-        const uint32_t uni_u = trow * nu + ubase;
+        const uint32_t uni_u = uniform(trow * nu + ubase);
         const uint32_t lane_u = rowrel * nu + li + jl;
-        g.q = __builtin_amdgcn_raw_buffer_load_b32(sub_rsrc(w, wbytes, uni_u * 4u), live ? lane_u * 4u : kNoFetch, 0,
-                                                   kNonTemporal);
-        g.d = __builtin_amdgcn_raw_buffer_load_b16(sub_rsrc(w, wbytes, scale_plane + uni_u * 2u),
-                                                   live ? lane_u * 2u : kNoFetch, 0, 0);
+        g.q = __builtin_amdgcn_raw_buffer_load_b32(wr, live ? lane_u * 4u : kNoFetch, uni_u * 4u, kNonTemporal);
+        g.d = __builtin_amdgcn_raw_buffer_load_b16(wr, live ? lane_u * 2u : kNoFetch, scale_plane + uni_u * 2u, 0);
     }
-    // Unit metadata: z = 2^(e+25) (twice the unit scale times the subnormal
-    // factor), w = S (gh arrives multiplied by 16: the H activations' sum).
-    __device__ static f32x4 meta(float gl, float gh, int e)
+    // Unit metadata: z = 2^(e+14) (the unit's activation scale times the
+    // codes' factor 2^14).
+    __device__ static f32x4 meta(float /*gl*/, float /*gh*/, int e)
     {
-        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + 25), __builtin_amdgcn_ldexpf(gl + gh, e)};
+        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + kCodeExp), 0.0f};
+    }
+    // Bits v*2^-24 (v = b or 16b per half) -> exact fp16 pair
+    // (2v - OFF)*2^-14 = 2048 * v*2^-24 - OFF*2^-14.
+    template <int OFF>
+    __device__ static uint32_t sign_pair(uint32_t v)
+    {
+        const half2_t h = __builtin_bit_cast(half2_t, v);
+        const _Float16 k = static_cast<_Float16>(2048.0f);
+        const _Float16 o = static_cast<_Float16>(-static_cast<float>(OFF) * 0x1p-14f);
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h, half2_t{k, k}, half2_t{o, o}));
     }
     // Code pairs of item i from t = word >> 4i: L pairs take bits (0, 2) and
     // (1, 3) to bits (0, 16); H pairs take bits (16, 18) and (17, 19) to
@@ -370,17 +403,18 @@ struct FmtQ1_0 {
     __device__ static uint32_t pair_h1(uint32_t t) { return ((t >> 13) & 0x10u) | ((t << 1) & 0x100000u); }
     template <int N, int R, bool LO>
     __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
-                                      const f32x4 *__restrict__ meta, int ul, int uc, uint32_t /*u*/,
+                                      int ul, int uc, uint32_t /*u*/,
                                       float (&acc)[R][N])
     {
 #pragma unroll
         for (int t = 0; t < N; t++) {
-            const f32x4 mt = meta[t * uc + ul];
+            const u32x4 *xu = xs + xslot(t, ul, uc);
+            const f32x4 mt = __builtin_bit_cast(f32x4, xu[8]);
             u32x4 xh[4], xl[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                xh[i] = xs[(t * 8 + 2 * i) * uc + ul];
-                xl[i] = LO ? xs[(t * 8 + 2 * i + 1) * uc + ul] : u32x4{0u, 0u, 0u, 0u};
+                xh[i] = xu[2 * i];
+                xl[i] = LO ? xu[2 * i + 1] : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int r = 0; r < R; r++) {
@@ -388,7 +422,8 @@ struct FmtQ1_0 {
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     const uint32_t tt = g[r].q >> (4 * i);
-                    const uint32_t p0 = pair_l0(tt), p1 = pair_h0(tt), p2 = pair_l1(tt), p3 = pair_h1(tt);
+                    const uint32_t p0 = sign_pair<1>(pair_l0(tt)), p1 = sign_pair<16>(pair_h0(tt));
+                    const uint32_t p2 = sign_pair<1>(pair_l1(tt)), p3 = sign_pair<16>(pair_h1(tt));
                     a = dot2(p0, xh[i].x, a);
                     a = dot2(p1, xh[i].y, a);
                     a = dot2(p2, xh[i].z, a);
@@ -400,7 +435,7 @@ struct FmtQ1_0 {
                         a = dot2(p3, xl[i].w, a);
                     }
                 }
-                acc[r][t] = __builtin_fmaf(half_lo(g[r].d), __builtin_fmaf(mt.z, a, -mt.w), acc[r][t]);
+                acc[r][t] = __builtin_fmaf(half_lo(g[r].d) * mt.z, a, acc[r][t]);
             }
         }
     }
@@ -411,8 +446,9 @@ struct FmtQ1_0 {
 // bit pairs 2j, 2j+1, the codes of the four runs j = 0..3 of 8 elements
 // 128h + 32j + 8i .. +7; run j lies in sub-block 8h + 2j + (i >= 2). Item j
 // of the unit is run j: L = its first four elements, H = its last four
-// (kHighOffset 4, staged divided by 16). A code pair is the masked bits
-// themselves as fp16 subnormals: q*2^-24 (L) or 16q*2^-24 (H).
+// (kHighOffset 4, staged divided by 16). A code pair is the masked bits (an
+// fp16 subnormal pair) times 1024: q*2^-14 (L) or 16q*2^-14 (H), exact
+// normal fp16 values or zero.
 template <int J>
 __device__ __forceinline__ uint32_t q2_hi_pair(uint32_t b)
 {
@@ -438,30 +474,29 @@ struct FmtQ2_K {
     // 8): super-block (row*ns + u/8); code bytes at 64 per super-block + 8*(u & 7),
     // scale bytes at scale_plane + 16 per super-block + 8h, d and dmin at
     // scale_plane*5/4 + 4 per super-block.
-    __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t scale_plane, uint32_t nu,
+    __device__ static void load(Regs &g, __amdgpu_buffer_rsrc_t wr, uint32_t scale_plane, uint32_t nu,
                                 uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl, bool live)
     {
         const uint32_t ns = nu >> 3;
-        const uint32_t uni_sb = trow * ns + (ubase >> 3);
+        const uint32_t uni_sb = uniform(trow * ns + (ubase >> 3));
         const uint32_t lane_sb = rowrel * ns + (li >> 3) + (jl >> 3);
         const uint32_t dd_plane = scale_plane + scale_plane / 4u;
         g.q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                            sub_rsrc(w, wbytes, uni_sb * 64u),
-                                            live ? lane_sb * 64u + 8u * (li & 7u) : kNoFetch, 0, kNonTemporal));
+                                            wr, live ? lane_sb * 64u + 8u * (li & 7u) : kNoFetch, uni_sb * 64u,
+                                            kNonTemporal));
         g.sc = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                             sub_rsrc(w, wbytes, scale_plane + uni_sb * 16u),
-                                             live ? lane_sb * 16u + 8u * ((li & 7u) >> 2) : kNoFetch, 0, 0));
-        g.dd = __builtin_amdgcn_raw_buffer_load_b32(sub_rsrc(w, wbytes, dd_plane + uni_sb * 4u),
-                                                    live ? lane_sb * 4u : kNoFetch, 0, 0);
+                                             wr, live ? lane_sb * 16u + 8u * ((li & 7u) >> 2) : kNoFetch,
+                                             scale_plane + uni_sb * 16u, 0));
+        g.dd = __builtin_amdgcn_raw_buffer_load_b32(wr, live ? lane_sb * 4u : kNoFetch, dd_plane + uni_sb * 4u, 0);
     }
-    // Unit metadata: z = 2^(e+24), w = 2^e.
+    // Unit metadata: z = 2^(e+14) (the codes carry 2^-14), w = 2^e.
     __device__ static f32x4 meta(float /*gl*/, float /*gh*/, int e)
     {
-        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + 24), __builtin_amdgcn_ldexpf(1.0f, e)};
+        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + kCodeExp), __builtin_amdgcn_ldexpf(1.0f, e)};
     }
     template <int N, int R, bool LO>
     __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
-                                      const f32x4 *__restrict__ meta, int ul, int uc, uint32_t u,
+                                      int ul, int uc, uint32_t u,
                                       float (&acc)[R][N])
     {
         constexpr uint32_t one = 0x3C003C00u, sixteen = 0x4C004C00u;  // fp16 pairs (1, 1) and (16, 16)
@@ -481,13 +516,14 @@ struct FmtQ2_K {
         }
 #pragma unroll
         for (int t = 0; t < N; t++) {
-            const f32x4 mt = meta[t * uc + ul];
+            const u32x4 *xu = xs + xslot(t, ul, uc);
+            const f32x4 mt = __builtin_bit_cast(f32x4, xu[8]);
             u32x4 xh[4], xl[4];
             float sx[4];
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                xh[j] = xs[(t * 8 + 2 * j) * uc + ul];
-                xl[j] = LO ? xs[(t * 8 + 2 * j + 1) * uc + ul] : u32x4{0u, 0u, 0u, 0u};
+                xh[j] = xu[2 * j];
+                xl[j] = LO ? xu[2 * j + 1] : u32x4{0u, 0u, 0u, 0u};
                 // Sum of the run's staged activations (the H ones counted 16 times).
                 float s = dot2(xh[j].x, one, 0.0f);
                 s = dot2(xh[j].y, sixteen, s);
@@ -507,8 +543,10 @@ struct FmtQ2_K {
                 float ts = 0.0f, tm = 0.0f;
                 auto run = [&](auto jc) {
                     constexpr int j = decltype(jc)::value;
-                    const uint32_t p0 = (a >> (2 * j)) & 0x00030003u, p2 = (a >> (2 * j + 8)) & 0x00030003u;
-                    const uint32_t p1 = q2_hi_pair<j>(b), p3 = (b >> (2 * j + 4)) & 0x00300030u;
+                    const uint32_t p0 = code_pair<0>((a >> (2 * j)) & 0x00030003u);
+                    const uint32_t p2 = code_pair<0>((a >> (2 * j + 8)) & 0x00030003u);
+                    const uint32_t p1 = code_pair<0>(q2_hi_pair<j>(b));
+                    const uint32_t p3 = code_pair<0>((b >> (2 * j + 4)) & 0x00300030u);
                     float aj = dot2(p0, xh[j].x, 0.0f);
                     aj = dot2(p1, xh[j].y, aj);
                     aj = dot2(p2, xh[j].z, aj);
@@ -550,25 +588,25 @@ struct FmtQ4_K {
     // Unit u = ubase + li + jl of row trow + rowrel (ubase and jl multiples
     // of 8): super-block (row*ns + u/8) at 144 bytes each, header at its
     // start, slice u & 7 = li & 7 at 16 + 16*(li & 7).
-    __device__ static void load(Regs &g, const uint8_t *w, uint32_t wbytes, uint32_t /*scale_plane*/, uint32_t nu,
+    __device__ static void load(Regs &g, __amdgpu_buffer_rsrc_t wr, uint32_t /*scale_plane*/, uint32_t nu,
                                 uint32_t trow, uint32_t rowrel, uint32_t li, uint32_t ubase, uint32_t jl, bool live)
     {
         const uint32_t ns = nu >> 3;
-        const __amdgpu_buffer_rsrc_t r = sub_rsrc(w, wbytes, (trow * ns + (ubase >> 3)) * 144u);
+        const uint32_t uni_b = uniform((trow * ns + (ubase >> 3)) * 144u);
         const uint32_t lane_b = live ? (rowrel * ns + (li >> 3) + (jl >> 3)) * 144u : kNoFetch;
-        g.h = load16<0>(r, lane_b, 0);
-        g.q = load16<kNonTemporal>(r, lane_b + 16u + ((li & 7u) << 4), 0);
+        g.h = load16<0>(wr, lane_b, uni_b);
+        g.q = load16<kNonTemporal>(wr, lane_b + 16u + ((li & 7u) << 4), uni_b);
     }
     // Unit metadata: x = sum of the 16 low-nibble activations, y = 16 x sum of
     // the 16 pre-divided high-nibble activations (both scaled units),
-    // z = 2^(e+24), w = 2^e.
+    // z = 2^(e+14) (the codes carry 2^-14), w = 2^e.
     __device__ static f32x4 meta(float gl, float gh, int e)
     {
-        return f32x4{gl, gh, __builtin_amdgcn_ldexpf(1.0f, e + 24), __builtin_amdgcn_ldexpf(1.0f, e)};
+        return f32x4{gl, gh, __builtin_amdgcn_ldexpf(1.0f, e + kCodeExp), __builtin_amdgcn_ldexpf(1.0f, e)};
     }
     template <int N, int R, bool LO>
     __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
-                                      const f32x4 *__restrict__ meta, int ul, int uc, uint32_t u,
+                                      int ul, int uc, uint32_t u,
                                       float (&acc)[R][N])
     {
         // Sub-blocks a = 2c (low nibbles) and b = 2c+1 (high nibbles), c = (u & 7) >> 1.
@@ -593,12 +631,13 @@ struct FmtQ4_K {
         }
 #pragma unroll
         for (int t = 0; t < N; t++) {
-            const f32x4 mt = meta[t * uc + ul];
+            const u32x4 *xu = xs + xslot(t, ul, uc);
+            const f32x4 mt = __builtin_bit_cast(f32x4, xu[8]);
             u32x4 xh[4], xl[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                xh[i] = xs[(t * 8 + 2 * i) * uc + ul];
-                xl[i] = LO ? xs[(t * 8 + 2 * i + 1) * uc + ul] : u32x4{0u, 0u, 0u, 0u};
+                xh[i] = xu[2 * i];
+                xl[i] = LO ? xu[2 * i + 1] : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int r = 0; r < R; r++) {
@@ -609,7 +648,8 @@ struct FmtQ4_K {
                 for (int i = 0; i < 4; i++) {
                     const uint32_t qi = i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
                     const uint32_t s = qi >> 8;
-                    const uint32_t p0 = qi & kLo, p1 = qi & kHi, p2 = s & kLo, p3 = s & kHi;
+                    const uint32_t p0 = code_pair<0>(qi & kLo), p1 = code_pair<0>(qi & kHi);
+                    const uint32_t p2 = code_pair<0>(s & kLo), p3 = code_pair<0>(s & kHi);
                     aa = dot2(p0, xh[i].x, aa);
                     ab = dot2(p1, xh[i].y, ab);
                     aa = dot2(p2, xh[i].z, aa);
@@ -676,7 +716,7 @@ struct NormIo {
 // staging waits on one L2 round trip per round, not one per item.
 template <class F, int N, int NT, int P, bool LO, bool NORM, class Issue>
 __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, int nuc, int uc,
-                                      u32x4 *__restrict__ xs, f32x4 *__restrict__ meta, int tid, NormIo &nio,
+                                      u32x4 *__restrict__ xs, int tid, NormIo &nio,
                                       Issue issue)
 {
     static_assert(!NORM || N == 1, "the fused norm is a one-token prologue");
@@ -791,10 +831,10 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
             gh += dpp<0x4E>(gh);
             const f32x4 mv = F::meta(gl, 16.0f * gh, e);
             if (live) {
-                u32x4 *dst = xs + (t * 8 + 2 * i) * uc + ul;
-                dst[0] = vhi;
-                if constexpr (LO) dst[uc] = vlo;
-                if (i == 0) meta[t * uc + ul] = mv;
+                u32x4 *dst = xs + xslot(t, ul, uc);
+                dst[2 * i] = vhi;
+                if constexpr (LO) dst[2 * i + 1] = vlo;
+                if (i == 0) dst[8] = __builtin_bit_cast(u32x4, mv);
             }
         }
     }
@@ -878,8 +918,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     constexpr int NT = 64 * WAVES;
     extern __shared__ u32x4 lds[];
     u32x4 *xs = lds;
-    f32x4 *meta = reinterpret_cast<f32x4 *>(lds + N * 8 * uc);
-    float *wave_ssq = reinterpret_cast<float *>(meta + N * uc);  // NORM: one sum per wave
+    float *wave_ssq = reinterpret_cast<float *>(lds + N * kLdsSlots * uc);  // NORM: one sum per wave
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -898,6 +937,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
         return GLU ? out_in_tile + (r >> 1) * SUBS + (r & 1) * M : out_in_tile + r * SUBS;
     };
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, static_cast<uint32_t>(N) * static_cast<uint32_t>(K) * 4u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, wbytes);
 
     float acc[R][N];
     auto zero_acc = [&]() {
@@ -925,7 +965,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
 #pragma unroll
             for (int r = 0; r < R; r++) {
                 const bool live = li + (j0 + jj) * LPR < nuc && out_row(tile, GLU ? r >> 1 : r) < M;
-                F::load(g[jj][r], w, wbytes, scale_plane, static_cast<uint32_t>(nu), trow,
+                F::load(g[jj][r], wr, scale_plane, static_cast<uint32_t>(nu), trow,
                         static_cast<uint32_t>(wrow_rel(r)), static_cast<uint32_t>(li), ubase,
                         static_cast<uint32_t>(jj * LPR), live);
             }
@@ -934,7 +974,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
 #pragma unroll
         for (int jj = 0; jj < JB; jj++) {
             const int ul = li + (j0 + jj) * LPR;
-            if (ul < nuc) F::template accumulate<N, R, LO>(g[jj], xs, meta, ul, uc, static_cast<uint32_t>(c0 + ul), acc);
+            if (ul < nuc) F::template accumulate<N, R, LO>(g[jj], xs, ul, uc, static_cast<uint32_t>(c0 + ul), acc);
         }
     };
     // 1/rms of the fused norm (set once the staging is complete).
@@ -1032,7 +1072,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
                 ct += gstride;
             }
         };
-        stage<F, N, NT, kStageRound<WAVES>, LO, NORM>(xr, K, 0, nu, uc, xs, meta, tid, nio, [&]() {
+        stage<F, N, NT, kStageRound<WAVES>, LO, NORM>(xr, K, 0, nu, uc, xs, tid, nio, [&]() {
 #pragma unroll
             for (int p = 0; p < D; p++) load_next(gbuf[p]);
         });
@@ -1067,7 +1107,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
             const int jc = (nuc + LPR - 1) / LPR;  // unit slots per lane per row in this chunk
             if (!first) wg_sync<WAVES>();
             first = false;
-            stage<F, N, NT, kStageRound<WAVES>, LO, false>(xr, K, c0, nuc, uc, xs, meta, tid, nio,
+            stage<F, N, NT, kStageRound<WAVES>, LO, false>(xr, K, c0, nuc, uc, xs, tid, nio,
                                                        [&]() { load_batch(ga, tile, 0, c0, nuc); });
             wg_sync<WAVES>();
             // Prefetches are unconditional (a batch past the chunk issues

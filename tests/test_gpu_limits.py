@@ -109,28 +109,18 @@ def test_decode_outputs_just_under_2gib(env):
 
 def test_decode_activations_just_under_2gib(env):
     # 8 tokens of 67,108,832 activations (x 36 KB below 2 GiB), 3 ragged
-    # rows: the staging runs in LDS-sized chunks up to the last unit. The
-    # activations are random in each token's last 2^18 elements (token 7's
-    # reach the buffer's end) and in scattered 32-element blocks, zero
-    # elsewhere: the kernel still stages and streams all of x, and a chunk
-    # read from the wrong place near the 2 GiB edge changes y by its whole
-    # size instead of a few parts in 10^5 of a 67M-term sum. (Random data on
-    # every element would also put the outputs deep in cancellation, about
-    # 10^-3 of their term scale, where the fp32 accumulation's rounding --
-    # measured at about 2^-20 of the term scale, growing with K -- exceeds
-    # the normwise ratio; the elementwise bound holds there with room.)
+    # rows: the staging runs in LDS-sized chunks up to the last unit. Every
+    # activation is random (normal), so every chunk of x up to the buffer's
+    # end enters the sums, and the outputs sit deep in cancellation (about
+    # 1/sqrt(K) of their term scale): the fp32 sums must carry no same-sign
+    # rounding drift to meet the normwise bound there.
     torch, q4, orc = env
     fmt, n, m = 0, 8, 3
     k = (LIMIT - 1) // (4 * n) // 32 * 32
     assert 4 * n * k < LIMIT <= 4 * n * (k + 32)
     buf = _random_buffer(q4, fmt, m, k, 7400)
     rng = np.random.default_rng(7401)
-    x = np.zeros((n, k), np.float32)
-    tail = 1 << 18
-    x[:, k - tail:] = rng.standard_normal((n, tail), dtype=np.float32)
-    for t in range(n):
-        for b in rng.integers(0, k // 32, size=256):
-            x[t, 32 * b:32 * b + 32] = rng.standard_normal(32, dtype=np.float32)
+    x = rng.standard_normal((n, k), dtype=np.float32)
     say(f"limits: activations {4 * n * k} B m={m} k={k} n={n}")
     wd = torch.from_numpy(buf).cuda()
     xd = torch.from_numpy(x).cuda()
