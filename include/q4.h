@@ -131,7 +131,9 @@ size_t q4_weight_bytes(int fmt, int64_t m, int64_t k);
  * all in Q4".) */
 int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, size_t out_bytes);
 
-/* Decode product y[t][i] = sum_k w_hat[i][k] * x[t][k] for t < n, fp32 out.
+/* Decode product y[t][i] = sum_k w_hat[i][k] * x[t][k] for t < n, fp32 out
+ * (Llamas on the Web, technical summary, problem statement: the product of a
+ * matrix in a llama.cpp quantization format with an activation vector).
  * w: device, quantized as above, 16-byte aligned; x: device float32 [n][k],
  * 16-byte aligned; y: device float32 [n][m], 4-byte aligned, fully written.
  * n must be 1..8 (decode batch); m == 0 is a successful no-op.
@@ -139,11 +141,15 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
  * Web, technical summary, Methodology section 3). Each 32-element piece of x
  * is scaled exactly by a power of two (its largest magnitude into
  * [2^14, 2^15)), then held as a pair of fp16 values hi + lo (about 2^-23
- * relative) when m < 256, or as one fp16 value (at most 2^-12 relative, so
- * every output is within 2^-12 * sum_k |w_hat[i][k] x[t][k]|) when m >= 256;
- * products and sums are fp32. A NaN among token t's activations makes every
- * y[t][i] NaN, as exact IEEE evaluation does (0 * NaN included); the other
- * tokens are unaffected. x is otherwise expected finite. */
+ * relative) when m < 256, or as one fp16 value when m >= 256 (round to
+ * nearest: at most 2^-11 relative, so every output is within
+ * 2^-11 * sum_k |w_hat[i][k] x[t][k]| plus the fp32 sums' rounding); the
+ * weight codes are exact fp16 values, products and sums are fp32. A NaN among
+ * token t's activations makes every y[t][i] NaN, as exact IEEE evaluation
+ * does (0 * NaN included); the other tokens are unaffected. x is otherwise
+ * expected finite. One token on a Q4_0 matrix of rows of up to 14560 weights
+ * runs the streaming kernel (see q4_gemv_tuning), everything else the tiled
+ * kernel; both are deterministic. */
 int q4_gemv(int fmt, const void *w, const float *x, float *y,
             int64_t m, int64_t k, int64_t n, void *hip_stream);
 
@@ -156,10 +162,11 @@ int q4_gemv(int fmt, const void *w, const float *x, float *y,
  * i < m:
  *   y[t][i] = silu(g) * u,  g = sum_k w_hat[i][k] x[t][k],
  *   u = sum_k w_hat[m+i][k] x[t][k],  silu(g) = g / (1 + exp(-g)).
- * g and u are summed exactly as q4_gemv sums the rows of the stacked matrix
- * (same arithmetic, same tolerance); the epilogue is fp32. x [n][k] and
- * y [n][m] are device arrays, n is 1..8. Errors as q4_gemv, with the size
- * limits applying to the 2m-row matrix (m below 2^29). */
+ * g and u are summed exactly as the tiled kernel of q4_gemv sums the rows of
+ * the stacked matrix (q4_gemv_tuned with Q4_GEMV_KERNEL_TILED: same
+ * arithmetic, same tolerance); the epilogue is fp32. x [n][k] and y [n][m]
+ * are device arrays, n is 1..8. Errors as q4_gemv, with the size limits
+ * applying to the 2m-row matrix (m below 2^29). */
 int q4_gemv_glu(int fmt, const void *w, const float *x, float *y,
                 int64_t m, int64_t k, int64_t n, void *hip_stream);
 
@@ -186,30 +193,48 @@ int q4_gemv_glu(int fmt, const void *w, const float *x, float *y,
 int q4_gemv_addnorm(int fmt, const void *w, const float *x, const float *delta, const float *gain, float eps,
                     float *x_out, float *y, int64_t m, int64_t k, int epilogue, void *hip_stream);
 
-/* Tile geometry of the decode product. The library picks it per shape; the
- * tuned entry point lets a sweep override it (tile and workgroup sizes are
- * tunable parameters whose defaults come from an empirical sweep: Llamas on
- * the Web, technical summary, Methodology section 2, "tunable parameters").
- * A zero field keeps the library's choice. Instantiated geometries
- * (lanes_per_row, rows_per_lane, waves_per_group): (8,1,1) (8,2,1) (8,4,1)
- * (16,1,1) (16,2,1) (32,1,1) (32,2,1) (64,1,1) (16,1,4) (32,1,4) (32,2,4)
- * (64,1,4) (64,2,4) (64,4,4) (32,1,8); others return Q4_EUNSUPPORTED. */
+/* Kernel and geometry of the decode product. The library picks them per
+ * shape; the tuned entry point lets a sweep override them (tile and
+ * workgroup sizes are tunable parameters whose defaults come from an
+ * empirical sweep: Llamas on the Web, technical summary, Methodology
+ * section 2, "tunable parameters"). A zero field keeps the library's choice.
+ * Two kernels:
+ *   Q4_GEMV_KERNEL_TILED: workgroups stride over tiles of rows, staging the
+ *     activations per workgroup; any n. Instantiated geometries
+ *     (lanes_per_row, rows_per_lane, waves_per_group): (8,1,1) (8,2,1)
+ *     (8,4,1) (16,1,1) (16,2,1) (32,1,1) (32,2,1) (64,1,1) (16,1,4) (32,1,4)
+ *     (32,2,4) (64,1,4) (64,2,4) (64,4,4) (32,1,8).
+ *   Q4_GEMV_KERNEL_STREAM: one token (n = 1), rows of at most 14560 weights;
+ *     each workgroup owns one contiguous range of rows, stages x once and
+ *     keeps `depth` weight slots in flight per lane; rows_per_lane is 1.
+ *     Instantiated (lanes_per_row, waves_per_group, depth): (8,16,2)
+ *     (16,16,2) (16,1,2) (32,1,2) (32,8,2) (32,16,2) (64,4,2) (64,8,2)
+ *     (64,16,2) (64,8,3) (64,16,4).
+ * With kernel Q4_GEMV_KERNEL_AUTO, a tuning that sets any geometry field
+ * names a tiled geometry; one that sets none keeps the library's choice of
+ * kernel. Other geometries return Q4_EUNSUPPORTED. */
+enum { Q4_GEMV_KERNEL_AUTO = 0, Q4_GEMV_KERNEL_TILED = 1, Q4_GEMV_KERNEL_STREAM = 2 };
 typedef struct {
     int lanes_per_row;   /* lanes sharing one weight row: 8, 16, 32 or 64 */
-    int rows_per_lane;   /* rows each lane streams at once: 1, 2 or 4 */
-    int waves_per_group; /* waves per workgroup: 1, 4 or 8 */
+    int rows_per_lane;   /* rows each lane streams at once: 1, 2 or 4 (streaming: 1) */
+    int waves_per_group; /* waves per workgroup */
     int groups_per_cu;   /* workgroups per compute unit the grid is sized for (0..64) */
+    int kernel;          /* Q4_GEMV_KERNEL_* */
+    int depth;           /* streaming kernel: weight slots in flight per lane */
 } q4_gemv_tuning;
 
-/* q4_gemv with an explicit tile geometry; same arguments, layouts, results
- * and errors, plus Q4_EINVAL for a null or negative tuning and
- * Q4_EUNSUPPORTED for a geometry that is not instantiated. */
+/* q4_gemv with an explicit kernel and geometry; same arguments, layouts,
+ * results and errors, plus Q4_EINVAL for a null tuning, a negative field or
+ * an unknown kernel, and Q4_EUNSUPPORTED for a geometry that is not
+ * instantiated or the streaming kernel at n > 1 or beyond its row length. */
 int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y,
                   int64_t m, int64_t k, int64_t n, const q4_gemv_tuning *tuning, void *hip_stream);
 
 /* q4_gemv_addnorm with an explicit tile geometry; same arguments, results and
- * errors, plus Q4_EINVAL for a null or negative tuning and Q4_EUNSUPPORTED for
- * a geometry that is not instantiated for the fused product. Instantiated:
+ * errors, plus Q4_EINVAL for a null tuning, a negative field or an unknown
+ * kernel, and Q4_EUNSUPPORTED for the streaming kernel (the fused product
+ * runs on the tiled kernel) or a geometry that is not instantiated for the
+ * fused product. Instantiated:
  * (8,1,1) (8,2,1) (16,1,1) (16,1,4) (32,1,4) (32,1,8) (32,2,1) (32,2,4) (64,1,4)
  * with Q4_EPILOGUE_NONE; (16,2,1) (16,2,4) (32,2,1) (32,2,4) (32,2,8) (64,2,4)
  * with Q4_EPILOGUE_SILU_MUL. */

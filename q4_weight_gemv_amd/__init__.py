@@ -48,9 +48,15 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 
+Q4_GEMV_KERNEL_AUTO = 0
+Q4_GEMV_KERNEL_TILED = 1
+Q4_GEMV_KERNEL_STREAM = 2
+
+
 class q4_gemv_tuning(ctypes.Structure):
     _fields_ = [("lanes_per_row", ctypes.c_int), ("rows_per_lane", ctypes.c_int),
-                ("waves_per_group", ctypes.c_int), ("groups_per_cu", ctypes.c_int)]
+                ("waves_per_group", ctypes.c_int), ("groups_per_cu", ctypes.c_int),
+                ("kernel", ctypes.c_int), ("depth", ctypes.c_int)]
 
 
 class q4_gemm_tuning(ctypes.Structure):
@@ -193,19 +199,22 @@ def q4_gemv_addnorm_tuned(fmt: int, w, x, delta, gain, eps: float, x_out, y, m: 
 
 
 # The instantiated tile geometries, as the header lists them.
-# Decode: (lanes_per_row, rows_per_lane, waves_per_group).
+# Decode, tiled kernel: (lanes_per_row, rows_per_lane, waves_per_group).
 GEMV_GEOMETRIES = ((8, 1, 1), (8, 2, 1), (8, 4, 1), (16, 1, 1), (16, 2, 1), (32, 1, 1), (32, 2, 1), (64, 1, 1),
                    (16, 1, 4), (32, 1, 4), (32, 2, 4), (64, 1, 4), (64, 2, 4), (64, 4, 4), (32, 1, 8))
+# Decode, one-token streaming kernel: (lanes_per_row, waves_per_group, depth).
+GEMV_STREAM_GEOMETRIES = ((8, 16, 2), (16, 16, 2), (16, 1, 2), (32, 1, 2), (32, 8, 2), (32, 16, 2), (64, 4, 2),
+                          (64, 8, 2), (64, 16, 2), (64, 8, 3), (64, 16, 4))
 # Prefill: (tile_rows, tile_tokens, stage_k).
 GEMM_TILES = ((16, 64, 512), (16, 64, 1024), (32, 64, 256), (32, 64, 512), (32, 64, 1024), (32, 128, 512),
               (64, 64, 256), (64, 64, 512))
 
 
 def q4_gemv_tuned(fmt: int, w, x, y, m: int, k: int, lanes_per_row=0, rows_per_lane=0, waves_per_group=0,
-                  groups_per_cu=0, stream=None) -> None:
-    """q4_gemv with an explicit tile geometry (0 keeps the library's choice)."""
+                  groups_per_cu=0, stream=None, kernel=Q4_GEMV_KERNEL_AUTO, depth=0) -> None:
+    """q4_gemv with an explicit kernel and geometry (0 keeps the library's choice)."""
     n = x.shape[0] if x.dim() == 2 else 1
-    t = q4_gemv_tuning(lanes_per_row, rows_per_lane, waves_per_group, groups_per_cu)
+    t = q4_gemv_tuning(lanes_per_row, rows_per_lane, waves_per_group, groups_per_cu, kernel, depth)
     _check(_lib.q4_gemv_tuned(fmt, w.data_ptr(), x.data_ptr(), y.data_ptr(), m, k, n, ctypes.byref(t),
                               _stream_ptr(stream)), "q4_gemv_tuned")
 

@@ -86,7 +86,34 @@ namespace gemv {
 //     128..255 units at several tokens: 8-wave groups of 32 lanes per row.
 //     Rows of 128..255 units at one token: the same 8-wave groups for tall
 //     products, else 4 waves of 16 lanes per row.
+//   Q4_0, one token, rows of up to kStreamMaxUnits units: the streaming
+//     kernel (two weight slots in flight per lane, one workgroup per compute
+//     unit): short rows (nu <= 32) 32 lanes per row in 8-wave groups, LM
+//     heads (m >= 16384) 8 (nu <= 24) or 16 lanes per row in 16-wave groups;
+//     longer rows 64 lanes per row, 16-wave groups, or two 8-wave groups per
+//     compute unit when the matrix has 8..16 rows of at most 4096 weights per
+//     compute unit (staging x twice per compute unit costs little there).
+Cfg choose_stream(int64_t m, int64_t k, int cus)
+{
+    const int64_t nu = k / kUnitWeights;
+    if (nu <= 32) {
+        if (m >= 16384) return Cfg{nu <= 24 ? 8 : 16, 1, 16, 1, 2};
+        return Cfg{32, 1, 8, 1, 2};
+    }
+    if (nu <= 128 && m >= 8LL * cus && m <= 16LL * cus) return Cfg{64, 1, 8, 2, 2};
+    return Cfg{64, 1, 16, 1, 2};
+}
+
+Cfg choose_tiled(int fmt, int64_t m, int64_t k, int64_t n, int cus);
+
 Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
+{
+    const int64_t nu = k / kUnitWeights;
+    if (fmt == Q4_FMT_Q4_0 && n == 1 && nu <= kStreamMaxUnits) return choose_stream(m, k, cus);
+    return choose_tiled(fmt, m, k, n, cus);
+}
+
+Cfg choose_tiled(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 {
     (void)cus;
     const int64_t nu = k / kUnitWeights;
@@ -119,9 +146,11 @@ Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 // becomes sixteen.) 8-wave plain choices at several tokens keep their 8-wave
 // groups: with the whole row's activations in the opt-in LDS, a 4-wave group
 // would leave one group of 4 waves per CU.
+Cfg choose_tiled(int fmt, int64_t m, int64_t k, int64_t n, int cus);
+
 Cfg choose_glu(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 {
-    const Cfg c = choose(fmt, 2 * m, k, n, cus);
+    const Cfg c = choose_tiled(fmt, 2 * m, k, n, cus);
     const bool one_wave = c.waves == 1;
     if (c.lpr <= 16) return one_wave ? Cfg{16, 2, 1, 8} : Cfg{16, 2, 4, 4};
     if (c.lpr == 32) {
@@ -138,6 +167,17 @@ int dispatch(int fmt, const Cfg &c, const void *w, const float *x, float *y, int
     const auto *wb = static_cast<const uint8_t *>(w);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int mi = static_cast<int>(m), ki = static_cast<int>(k);
+    if (c.depth > 0) {
+        // The streaming kernel: one token, plain product, the whole row staged.
+        if (glu || n != 1 || k / kUnitWeights > kStreamMaxUnits) return Q4_EUNSUPPORTED;
+        switch (fmt) {
+        case Q4_FMT_Q4_0: return dispatch_stream<FmtQ4_0>(c, wb, x, y, mi, ki, s, cus);
+        case Q4_FMT_Q8_0: return dispatch_stream<FmtQ8_0>(c, wb, x, y, mi, ki, s, cus);
+        case Q4_FMT_Q1_0: return dispatch_stream<FmtQ1_0>(c, wb, x, y, mi, ki, s, cus);
+        case Q4_FMT_Q2_K: return dispatch_stream<FmtQ2_K>(c, wb, x, y, mi, ki, s, cus);
+        default: return dispatch_stream<FmtQ4_K>(c, wb, x, y, mi, ki, s, cus);
+        }
+    }
 #define Q4_N_CASE(F, NN)                                                            \
     case NN:                                                                        \
         return glu ? dispatch_glu_cfg<F, NN>(c, wb, x, y, mi, ki, s, cus)           \
@@ -199,7 +239,7 @@ int launch_gemv_addnorm(int fmt, const void *w, const float *x, const Prologue &
 {
     const int cus = device_cus();
     if (cus <= 0) return Q4_EHIP;
-    gemv::Cfg c = glu ? gemv::choose_glu(fmt, m, k, 1, cus) : gemv::choose(fmt, m, k, 1, cus);
+    gemv::Cfg c = glu ? gemv::choose_glu(fmt, m, k, 1, cus) : gemv::choose_tiled(fmt, m, k, 1, cus);
     // The fused norm stages three vectors (x, delta, gain) per workgroup, so
     // short-row gated products take 16 lanes per row in their one-wave groups
     // (twice the rows per group, half the groups staging): 3.7 against 4.9 us
@@ -341,8 +381,11 @@ extern "C" int q4_gemv_addnorm_tuned(int fmt, const void *w, const float *x, con
 {
     if (!tuning) return Q4_EINVAL;
     if (tuning->lanes_per_row < 0 || tuning->rows_per_lane < 0 || tuning->waves_per_group < 0 ||
-        tuning->groups_per_cu < 0 || tuning->groups_per_cu > 64)
+        tuning->groups_per_cu < 0 || tuning->groups_per_cu > 64 || tuning->depth < 0 || tuning->kernel < 0 ||
+        tuning->kernel > Q4_GEMV_KERNEL_STREAM)
         return Q4_EINVAL;
+    // The fused norm runs on the tiled kernel only.
+    if (tuning->kernel == Q4_GEMV_KERNEL_STREAM) return Q4_EUNSUPPORTED;
     return addnorm_entry(fmt, w, x, delta, gain, eps, x_out, y, m, k, epilogue, tuning, hip_stream);
 }
 
@@ -353,15 +396,27 @@ extern "C" int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y, i
     if (st != Q4_OK) return st;
     if (!tuning) return Q4_EINVAL;
     if (tuning->lanes_per_row < 0 || tuning->rows_per_lane < 0 || tuning->waves_per_group < 0 ||
-        tuning->groups_per_cu < 0 || tuning->groups_per_cu > 64)
+        tuning->groups_per_cu < 0 || tuning->groups_per_cu > 64 || tuning->depth < 0 || tuning->kernel < 0 ||
+        tuning->kernel > Q4_GEMV_KERNEL_STREAM)
         return Q4_EINVAL;
+    if (tuning->kernel == Q4_GEMV_KERNEL_STREAM && n > 1) return Q4_EUNSUPPORTED;
     if (m == 0 || n == 0) return Q4_OK;
     const int cus = q4::device_cus();
     if (cus <= 0) return Q4_EHIP;
+    // The kernel: the one-token streaming kernel when asked for, or when the
+    // library would pick it and no tiled geometry field is given; else the
+    // tiled kernel.
+    const bool geometry = tuning->lanes_per_row || tuning->rows_per_lane || tuning->waves_per_group ||
+                          tuning->groups_per_cu;
     q4::gemv::Cfg c = q4::gemv::choose(fmt, m, k, n, cus);
+    if (tuning->kernel == Q4_GEMV_KERNEL_TILED || (tuning->kernel == Q4_GEMV_KERNEL_AUTO && geometry))
+        c = q4::gemv::choose_tiled(fmt, m, k, n, cus);
+    else if (tuning->kernel == Q4_GEMV_KERNEL_STREAM && c.depth == 0)
+        c = q4::gemv::choose_stream(m, k, cus);
     if (tuning->lanes_per_row) c.lpr = tuning->lanes_per_row;
     if (tuning->rows_per_lane) c.r = tuning->rows_per_lane;
     if (tuning->waves_per_group) c.waves = tuning->waves_per_group;
     if (tuning->groups_per_cu) c.groups_per_cu = tuning->groups_per_cu;
+    if (tuning->depth && c.depth) c.depth = tuning->depth;
     return q4::gemv::dispatch(fmt, c, w, x, y, m, k, n, hip_stream, cus);
 }

@@ -714,7 +714,7 @@ struct NormIo {
 // calls issue() (the first weight batch), and only then waits for the
 // activations, so the weight loads are in flight during the staging and the
 // staging waits on one L2 round trip per round, not one per item.
-template <class F, int N, int NT, int P, bool LO, bool NORM, class Issue>
+template <class F, int N, int NT, int P, bool LO, bool NORM, class Issue, bool SKIP_DEAD = false>
 __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, int nuc, int uc,
                                       u32x4 *__restrict__ xs, int tid, NormIo &nio,
                                       Issue issue)
@@ -742,7 +742,15 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
         uint32_t offs[P];
 #pragma unroll
         for (int p = 0; p < P; p++) {
-            // Branch-free: an item past the end lands past N*K and reads zeros.
+            // Lanes past the end land past N*K and read zeros. With SKIP_DEAD
+            // a slot with no live item in the whole workgroup issues no loads
+            // at all (a uniform branch: even a load that fetches nothing costs
+            // the CU's address unit a pass over 64 lanes); without it every
+            // slot's loads are issued, branch-free.
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            a[p] = b[p] = da[p] = db[p] = ga[p] = gb[p] = z;
+            offs[p] = 0u;
+            if (SKIP_DEAD && rb + p * NT >= total) continue;
             int t, rem;
             split_item(base + p * NT, t, rem);
             const uint32_t off = static_cast<uint32_t>(t * K + F::item_base(c0 + (rem >> 2), rem & 3)) * 4u;

@@ -68,12 +68,14 @@ int launch_gemv_addnorm(int fmt, const void *w, const float *x, const Prologue &
 
 namespace gemv {
 
-// Tile geometry of the decode kernel.
+// Geometry of a decode launch: the tiled kernel (depth == 0) or the
+// one-token streaming kernel (depth > 0: slots in flight per lane; r == 1).
 struct Cfg {
     int lpr;            // lanes per row: 8, 16, 32 or 64
     int r;              // rows per lane
-    int waves;          // waves per workgroup: 1, 4 or 8
-    int groups_per_cu;  // resident workgroups per compute unit the grid is sized for
+    int waves;          // waves per workgroup
+    int groups_per_cu;  // workgroups per compute unit the grid is sized for
+    int depth = 0;      // streaming kernel: weight slots in flight per lane
 };
 
 struct FmtQ4_0;
@@ -90,6 +92,13 @@ int dispatch_glu_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, i
 template <class F>
 int dispatch_norm_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus,
                       bool glu, const Prologue &pro);
+// Defined in q4_gemv_stream.hip: the one-token streaming kernel.
+template <class F>
+int dispatch_stream(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus);
+
+// Longest row (in 32-weight units) the streaming kernel takes: the whole row
+// is staged once per workgroup in its LDS (144 bytes per unit, 64 KiB).
+constexpr int64_t kStreamMaxUnits = 455;
 
 }  // namespace gemv
 }  // namespace q4

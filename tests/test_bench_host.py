@@ -29,7 +29,6 @@ def test_gpt2_step_algorithmic_bytes(q4):
     total = sum(bench.gemv_bytes(q4, 0, m, k, 1) for k, m in shapes)
     assert total == sum(m * k * 9 // 16 + 4 * (k + m) for k, m in shapes)
     assert total == 70_280_692
-    assert round(total / len(shapes)) == 1_434_300  # the roofline's bytes per launch
 
 
 def test_batched_and_gated_product_bytes(q4):
@@ -48,23 +47,45 @@ def test_cold_rotation_reads_past_the_caches():
         assert c >= 2 and (c - 1) * nbytes >= 512 << 20, (nbytes, c)
 
 
-def test_traffic_reported_only_for_matching_sources(tmp_path):
+def test_headline_layer_bytes(q4):
+    # The headline step: the 7B-class layer as listed (4096->4096,
+    # 4096->11008 x2, 11008->4096) in Q4_0 at one token.
+    shapes = synth.llama7b_layer()
+    assert shapes == [(4096, 4096), (4096, 11008), (4096, 11008), (11008, 4096)]
+    weights = sum(m * k * 9 // 16 for k, m in shapes)
+    assert weights == 85_524_480
+    assert sum(bench.gemv_bytes(q4, 0, m, k, 1) for k, m in shapes) == weights + 4 * sum(k + m for k, m in shapes)
+    k, m = bench.DOMINANT
+    assert (k, m) in shapes and bench.gemv_bytes(q4, 0, m, k, 1) == 25_362_432 + 4 * (4096 + 11008)
+
+
+def test_profile_figures_reported_only_for_matching_sources(tmp_path):
     h = bench.kernel_source_hash()
     good = tmp_path / "good.txt"
-    good.write_text(f"kernel_source_sha256: {h}\nhbm_bytes_per_launch: 1570923\n")
-    assert bench.traffic_from_profile(1.0, str(good)) == 1570923.0
+    good.write_text(f"kernel_source_sha256: {h}\nhbm_bytes_per_launch: 1570923\nmedian_us: 7.125\n")
+    assert bench.traffic_from_profile(str(good)) == 1570923.0
+    assert bench.trace_median_from_profile(str(good)) == 7.125
     other = "0" * 16 if h != "0" * 16 else "1" * 16
     stale = tmp_path / "stale.txt"
-    stale.write_text(f"kernel_source_sha256: {other}\nhbm_bytes_per_launch: 1570923\n")
-    assert bench.traffic_from_profile(1.0, str(stale)) is None
-    assert bench.traffic_from_profile(1.0, str(tmp_path / "missing.txt")) is None
+    stale.write_text(f"kernel_source_sha256: {other}\nhbm_bytes_per_launch: 1570923\nmedian_us: 7.125\n")
+    assert bench.traffic_from_profile(str(stale)) is None
+    assert bench.trace_median_from_profile(str(stale)) is None
+    assert bench.traffic_from_profile(str(tmp_path / "missing.txt")) is None
 
 
 def test_source_hash_covers_the_headline_kernel():
-    # The headline decode kernel's template and its Q4_0 instantiation units.
-    for f in ("q4_gemv_kernel.h", "q4_gemv.hip", "q4_gemv_q4_0_a.hip", "q4_gemv_q4_0_b.hip"):
+    # The one-token decode kernels (streaming and tiled), their Q4_0
+    # instantiation units and the host code that picks between them.
+    for f in ("q4_gemv_kernel.h", "q4_gemv_stream.h", "q4_gemv.hip", "q4_gemv_stream.hip", "q4_gemv_q4_0_a.hip",
+              "q4_gemv_q4_0_b.hip"):
         assert f in bench.KERNEL_SOURCES
         assert os.path.exists(os.path.join(ROOT, "q4_weight_gemv_amd", "csrc", f))
+
+
+def test_cpu_share_and_host_description():
+    cores, model = bench.host_cpu()
+    assert cores >= 1 and isinstance(model, str) and model
+    assert bench.CPU_SHARE == 16
 
 
 def test_more_than_one_gpu_is_refused():

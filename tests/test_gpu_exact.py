@@ -125,6 +125,32 @@ def test_exact_integer_sums_every_geometry(env, fmt, geom):
     assert np.array_equal(y, yr), np.argwhere(y != yr)[:5]
 
 
+def _stream_geometry_list():
+    import q4_weight_gemv_amd as q4
+
+    return list(q4.GEMV_STREAM_GEOMETRIES)
+
+
+@pytest.mark.parametrize("geom", _stream_geometry_list(), ids=lambda g: f"L{g[0]}W{g[1]}D{g[2]}")
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
+def test_exact_integer_sums_every_stream_geometry(env, fmt, geom):
+    torch, q4, orc = env
+    m, k = 600, 2304
+    rng = np.random.default_rng(fmt * 91 + geom[0] + 10 * geom[1] + 100 * geom[2])
+    buf = _integer_buffer(q4, fmt, m, k, rng)
+    x = rng.integers(-1, 2, size=(1, k)).astype(np.float32)
+    say(f"exact sums fmt={fmt} stream geometry {geom}")
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(x).cuda()
+    yd = torch.full((1, m), float("nan"), dtype=torch.float32, device="cuda")
+    q4.q4_gemv_tuned(fmt, wd, xd, yd, m, k, lanes_per_row=geom[0], waves_per_group=geom[1], groups_per_cu=1,
+                     kernel=q4.Q4_GEMV_KERNEL_STREAM, depth=geom[2])
+    torch.cuda.synchronize()
+    y = yd.cpu().numpy()
+    yr = orc.matvec(fmt, buf, m, k, x, threads=16)
+    assert np.array_equal(y, yr), np.argwhere(y != yr)[:5]
+
+
 # ---- hand-built blocks, one-hot columns ----------------------------------------
 
 # fp16 scales the quantizer never writes, beside ordinary ones.
@@ -176,7 +202,8 @@ def _q4_k_hand_buffer(orc, m, k, rng):
                                      (1, 300, 4096)])
 def test_hand_built_blocks_onehot(env, fmt, m, k):
     # Below and above 256 rows (activations as hi + lo fp16 pairs, or single
-    # fp16 values); k = 4096 at 300 rows takes the one-token streaming kernel.
+    # fp16 values); one token of Q4_0 takes the streaming kernel, several
+    # tokens (and Q4_K) the tiled one.
     torch, q4, orc = env
     rng = np.random.default_rng(31 * m + k + fmt)
     buf = _q4_0_hand_buffer(m, k, rng) if fmt == 0 else _q4_k_hand_buffer(orc, m, k, rng)

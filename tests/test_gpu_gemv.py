@@ -137,6 +137,67 @@ def test_parity_every_geometry(env, fmt, n, geom):
     check_tolerance(yd.cpu().numpy(), yr, ad, GEMV_TOL, what=f"geometry {geom} fmt={fmt} n={n}")
 
 
+def _stream_geometries():
+    import q4_weight_gemv_amd as q4
+
+    return list(q4.GEMV_STREAM_GEOMETRIES)
+
+
+@pytest.mark.parametrize("geom", _stream_geometries(), ids=lambda g: f"L{g[0]}W{g[1]}D{g[2]}")
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("m,k", [(600, 2304), (1000, 768), (37, 11008), (300, 4096)])
+def test_parity_every_stream_geometry(env, fmt, geom, m, k):
+    """Every instantiated geometry of the one-token streaming kernel, every
+    format, through q4_gemv_tuned: ragged rows (a partial last row group and a
+    partial last slot of units), short rows, a long row, and hi + lo versus
+    single fp16 activations (fewer or more than 256 rows)."""
+    torch, q4, orc = env
+    w = synth.weights(synth.seed_for(910 + fmt, m), m, k)
+    x = synth.activations(synth.seed_for(910 + fmt, m, True), 1, k)
+    buf = _quantize_both(q4, orc, fmt, w)
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(x).cuda()
+    yd = torch.full((1, m), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"stream geometry {geom} fmt={fmt} m={m} k={k}")
+    q4.q4_gemv_tuned(fmt, wd, xd, yd, m, k, lanes_per_row=geom[0], waves_per_group=geom[1], groups_per_cu=1,
+                     kernel=q4.Q4_GEMV_KERNEL_STREAM, depth=geom[2])
+    torch.cuda.synchronize()
+    yr, ad = orc.matvec(fmt, buf, m, k, x, threads=threads(), absdot=True)
+    check_tolerance(yd.cpu().numpy(), yr, ad, GEMV_TOL, what=f"stream {geom} fmt={fmt} {m}x{k}")
+
+
+@pytest.mark.parametrize("m,k", [(1, 32), (3, 64), (7, 768), (9, 960), (255, 4096), (256, 4096), (257, 4096),
+                                 (4097, 4096), (2, 14560), (300, 14560), (40, 14592), (5, 1 << 16)])
+def test_parity_q4_0_one_token_edges(env, m, k):
+    # The library's one-token choice at the edges of the streaming kernel:
+    # single rows, fewer rows than a row group, the 256-row switch of the
+    # activation precision, the longest row it stages (14560 weights, 65520
+    # bytes of LDS) and longer rows (the tiled kernel).
+    _parity(env, 0, m, k, 1, seed=330 + m % 11)
+
+
+@pytest.mark.parametrize("gpc", [1, 2, 3, 4, 8])
+def test_stream_groups_per_cu(env, gpc):
+    # Workgroups per compute unit change only how the rows are split, never a
+    # row's arithmetic: every split gives the same bits.
+    torch, q4, orc = env
+    m, k = 2311, 2304
+    buf = q4.q4_quantize_ref(0, synth.weights(921, m, k))
+    x = synth.activations(922, 1, k)
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(x).cuda()
+    outs = []
+    for g in (1, gpc):
+        yd = torch.full((1, m), float("nan"), dtype=torch.float32, device="cuda")
+        q4.q4_gemv_tuned(0, wd, xd, yd, m, k, lanes_per_row=64, waves_per_group=8, groups_per_cu=g,
+                         kernel=q4.Q4_GEMV_KERNEL_STREAM, depth=2)
+        torch.cuda.synchronize()
+        outs.append(yd.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    yr, ad = orc.matvec(0, buf, m, k, x, threads=threads(), absdot=True)
+    check_tolerance(outs[1], yr, ad, GEMV_TOL, what=f"stream gpc={gpc}")
+
+
 SMALL_Q4_K = [(1, 256), (37, 512), (130, 1024), (257, 2560), (300, 4096), (77, 11008), (1025, 768 + 256)]
 
 
@@ -453,7 +514,14 @@ def test_glu_matches_plain_product_of_stacked_matrix(env, fmt, n, m, k):
     buf = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(1100 + fmt, m), 2 * m, k))
     x = synth.activations(synth.seed_for(1100 + fmt, m, True), n, k)
     say(f"glu vs plain fmt={fmt} n={n} m={m} k={k}")
-    yp = _gemv(env, fmt, buf, x, 2 * m, k)
+    # The plain product on the tiled kernel, which the gated product shares
+    # (one token of Q4_0 would otherwise take the streaming kernel).
+    wd = torch.from_numpy(buf).cuda()
+    xd = torch.from_numpy(x).cuda()
+    ypd = torch.full((n, 2 * m), float("nan"), dtype=torch.float32, device="cuda")
+    q4.q4_gemv_tuned(fmt, wd, xd, ypd, 2 * m, k, kernel=q4.Q4_GEMV_KERNEL_TILED)
+    torch.cuda.synchronize()
+    yp = ypd.cpu().numpy()
     yg = _glu(env, fmt, buf, x, m, k)
     ref = _silu_mul64(yp[:, :m], yp[:, m:])
     scale = np.abs(yp[:, :m].astype(np.float64) * yp[:, m:])

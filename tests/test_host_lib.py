@@ -237,6 +237,14 @@ def test_tuned_argument_errors(q4):
     assert f(0, *ok, 64, 256, 9, ctypes.byref(good), None) == q4.Q4_EUNSUPPORTED
     assert f(0, A16 + 4, A16, A16, 64, 256, 1, ctypes.byref(good), None) == q4.Q4_EALIGN
     assert f(0, None, None, None, 0, 256, 1, ctypes.byref(good), None) == q4.Q4_OK
+    # kernel and depth fields: negative or unknown values are refused, and the
+    # streaming kernel takes one token only.
+    for t in (q4.q4_gemv_tuning(0, 0, 0, 0, -1, 0), q4.q4_gemv_tuning(0, 0, 0, 0, 3, 0),
+              q4.q4_gemv_tuning(0, 0, 0, 0, 2, -1)):
+        assert f(0, *ok, 64, 256, 1, ctypes.byref(t), None) == q4.Q4_EINVAL
+    stream = q4.q4_gemv_tuning(0, 0, 0, 0, q4.Q4_GEMV_KERNEL_STREAM, 0)
+    assert f(0, *ok, 64, 256, 2, ctypes.byref(stream), None) == q4.Q4_EUNSUPPORTED
+    assert f(0, None, None, None, 0, 256, 1, ctypes.byref(stream), None) == q4.Q4_OK
 
 
 def test_gemm_tuned_argument_errors(q4):
@@ -323,6 +331,10 @@ def test_addnorm_tuned_argument_errors(q4):
     assert f(0, W, X, D, G, 1e-5, X, Y, 64, 256, 0, ctypes.byref(ok), None) == q4.Q4_EINVAL     # x_out is x
     assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 14592, 0, ctypes.byref(ok), None) == q4.Q4_EUNSUPPORTED
     assert f(0, None, None, None, None, 1e-5, None, None, 0, 256, 0, ctypes.byref(ok), None) == q4.Q4_OK
+    stream = q4.q4_gemv_tuning(0, 0, 0, 0, q4.Q4_GEMV_KERNEL_STREAM, 0)  # the fused norm is tiled only
+    assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 256, 0, ctypes.byref(stream), None) == q4.Q4_EUNSUPPORTED
+    unknown = q4.q4_gemv_tuning(0, 0, 0, 0, 5, 0)
+    assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 256, 0, ctypes.byref(unknown), None) == q4.Q4_EINVAL
 
 
 def test_sequence_epilogue_field(q4):
@@ -382,11 +394,16 @@ def test_geometry_lists_match_header(q4):
     import re
 
     text = open(os.path.join(ROOT, "include", "q4.h")).read()
-    gemv_doc = text[text.index("typedef struct {\n    int lanes_per_row;") - 700:text.index("int lanes_per_row;")]
+    tiled_doc = text[text.index("Q4_GEMV_KERNEL_TILED: workgroups"):text.index("Q4_GEMV_KERNEL_STREAM: one token")]
+    stream_doc = text[text.index("Q4_GEMV_KERNEL_STREAM: one token"):text.index("With kernel Q4_GEMV_KERNEL_AUTO")]
     gemm_doc = text[text.index("/* Tile geometry of the prefill product"):text.index("int tile_rows;")]
     triples = lambda t: tuple(tuple(int(v) for v in m) for m in re.findall(r"\((\d+),(\d+),(\d+)\)", t))
-    assert triples(gemv_doc) == q4.GEMV_GEOMETRIES
+    assert triples(tiled_doc) == q4.GEMV_GEOMETRIES
+    assert triples(stream_doc) == q4.GEMV_STREAM_GEOMETRIES
     assert triples(gemm_doc) == q4.GEMM_TILES
+    src = open(os.path.join(ROOT, "q4_weight_gemv_amd", "csrc", "q4_gemv_stream.hip")).read()
+    listed = tuple(tuple(int(v) for v in m) for m in re.findall(r"X\((\d+), (\d+), (\d+)\)", src))
+    assert listed == q4.GEMV_STREAM_GEOMETRIES
 
 
 def test_binding_loads_torch_runtime_first():
