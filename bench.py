@@ -309,6 +309,52 @@ def bench_7b(torch, q4, timer, reps=20):
     return out
 
 
+def sweep_one_token(torch, q4, timer, reps=10, out=None):
+    """Time every streaming geometry and the library's tiled choice for one
+    token, cold (a graph of one launch per rotating weight copy), at the
+    workload shapes: Q4_0 at every GPT-2-124M, SmolLM2-360M and 7B-class
+    shape; the other formats at the 7B-class and SmolLM2 shapes. One JSON
+    line per measurement (the evidence behind the library's defaults)."""
+    import synth
+
+    name = {0: "q4_0", 1: "q4_k", 2: "q8_0", 3: "q2_k", 4: "q1_0"}
+    small = sorted(set(synth.gpt2_124m_step() + synth.smollm2_360m_step()))
+    big = sorted(set(synth.llama7b_layer()))
+    s = torch.cuda.Stream()
+    for fmt in (0, 1, 2, 3, 4):
+        shapes = small + big if fmt == 0 else sorted(set(synth.smollm2_360m_step())) + big
+        for k, m in shapes:
+            if k % (256 if fmt in (1, 3) else 32):
+                continue
+            wq = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(6, k + m), m, k))
+            copies = [torch.from_numpy(wq).cuda() for _ in range(copies_for(wq.size))]
+            x = torch.from_numpy(synth.activations(synth.seed_for(6, k, True), 1, k)).cuda()
+            y = torch.empty((1, m), device="cuda")
+            nb = gemv_bytes(q4, fmt, m, k, 1)
+            cfgs = [("tiled", dict(kernel=q4.Q4_GEMV_KERNEL_TILED))] + [
+                (f"stream L{g[0]} W{g[1]} D{g[2]}", dict(kernel=q4.Q4_GEMV_KERNEL_STREAM, lanes_per_row=g[0],
+                                                        waves_per_group=g[1], groups_per_cu=gpc, depth=g[2]))
+                for g in q4.GEMV_STREAM_GEOMETRIES for gpc in ((4, 8) if g[1] == 1 else (1, 2) if g[1] <= 8 else (1,))]
+            cfgs = [(f"{label} G{kw.get('groups_per_cu', 0)}" if "stream" in label else label, kw) for label, kw in cfgs]
+            for label, kw in cfgs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.stream(s):
+                    q4.q4_gemv_tuned(fmt, copies[0], x, y, m, k, stream=s, **kw)
+                    torch.cuda.synchronize()
+                    with torch.cuda.graph(g, stream=s):
+                        for c in copies:
+                            q4.q4_gemv_tuned(fmt, c, x, y, m, k, stream=s, **kw)
+                t = timer.region(lambda i: g.replay(), reps, 2) / (reps * len(copies))
+                del g
+                rec = {"format": name[fmt], "shape": f"{k}->{m}", "kernel": label, "us": round(t * 1e6, 3),
+                       "pct_peak": round(100 * nb / t / 1e9 / HBM_PEAK_GBS, 2)}
+                print(json.dumps(rec), flush=True)
+                if out is not None:
+                    out.append(rec)
+            del copies
+            torch.cuda.empty_cache()
+
+
 def bench_gemm(torch, q4, timer, n=512, reps=20, shapes=None, per_matrix=True):
     """Prefill GEMM over the SmolLM2-360M layer's matrices at 512 tokens:
     one graph of the launches, replayed (weights 5.5 MB, L2/MALL-resident);
@@ -468,6 +514,8 @@ def main():
                          "smollm2_fused, smollm2_gated, warm, read_ceiling, full_step, gemm")
     ap.add_argument("--profile-shape", default=None,
                     help="K,M: run only this Q4_0 one-token product, cold, --steps graph replays (for rocprofv3)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every one-token geometry at the workload shapes (one JSON line each) and exit")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 64 MiB device copy (torch) once, as the reference for HBM byte counters")
     args = ap.parse_args()
@@ -498,6 +546,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.sweep:
+        sweep_one_token(torch, q4, timer)
+        return
 
     if args.profile_shape:
         pk, pm = (int(v) for v in args.profile_shape.split(","))

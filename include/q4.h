@@ -12,9 +12,11 @@
  * the caller ahead of time (Methodology section 1, "static allocation").
  *
  * Conventions for every entry point:
- *   - The caller owns every buffer. The library allocates no memory and keeps
- *     no state between calls (the graph handle below is caller-owned state),
- *     so calls are reentrant.
+ *   - The caller owns every buffer. The library allocates no memory. What it
+ *     keeps between calls is read-only per device: cached device attributes
+ *     (compute units, the workgroup LDS limit) and, once per device and
+ *     kernel, the opt-in of kernels that use more than 64 KiB of LDS; the
+ *     graph handles below are caller-owned state. Calls are reentrant.
  *   - Matrices are row-major. W is logically [m][k] (k = input dimension,
  *     m = output dimension), quantized along k. Activations are token-major:
  *     x[n][k], y[n][m].
@@ -96,7 +98,7 @@ enum {
     Q4_OK = 0,
     Q4_EINVAL = -1,       /* bad size, null pointer, k not a whole number of blocks, short buffer */
     Q4_EUNSUPPORTED = -2, /* n outside 1..8 for gemv; unknown format; w, x or y of 2 GiB or more */
-    Q4_EALIGN = -3,       /* w or x not 16-byte aligned, y not 4-byte aligned */
+    Q4_EALIGN = -3,       /* w not 16-byte aligned; x or y not 4-byte aligned */
     Q4_ENONFINITE = -4,   /* NaN or Inf among the weights given to the quantizer */
     Q4_ERANGE = -5,       /* a block scale that rounds to a non-finite fp16 */
     Q4_EHIP = -6          /* the HIP runtime reported a launch or capture error */
@@ -104,7 +106,11 @@ enum {
 
 /* Bytes of the quantized buffer for an m x k matrix; 0 if k is not a
  * positive multiple of the block (32 for Q4_0, Q8_0 and Q1_0, 256 for the K-quants),
- * m < 0, or the format is unknown. Host only; no device work. */
+ * m < 0, or the format is unknown. Host only; no device work. (Q4_0 stores
+ * 16-bit weights in 4 bits per parameter plus a shared fp16 scale per 32:
+ * MicroLLM Lab post, "Seven models, all in Q4", and the block sizes of the
+ * llama.cpp formats the technical summary of Llamas on the Web serves,
+ * problem statement.) */
 size_t q4_weight_bytes(int fmt, int64_t m, int64_t k);
 
 /* Host quantizer: float32 W[m][k] (host memory) -> packed buffer `out`
@@ -135,7 +141,7 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
  * (Llamas on the Web, technical summary, problem statement: the product of a
  * matrix in a llama.cpp quantization format with an activation vector).
  * w: device, quantized as above, 16-byte aligned; x: device float32 [n][k],
- * 16-byte aligned; y: device float32 [n][m], 4-byte aligned, fully written.
+ * 4-byte aligned; y: device float32 [n][m], 4-byte aligned, fully written.
  * n must be 1..8 (decode batch); m == 0 is a successful no-op.
  * Weights are dequantized in registers and never written back (Llamas on the
  * Web, technical summary, Methodology section 3). Each 32-element piece of x
@@ -182,7 +188,8 @@ int q4_gemv_glu(int fmt, const void *w, const float *x, float *y,
  * The kernel stages v * gain and scales each reduced row sum by the fp32
  * factor 1/sqrt(mean(v^2) + eps) (the same value for every row), so the
  * product's tolerance is q4_gemv's, relative to the normalised input.
- * x, delta, gain, x_out: device float32 [k], 16-byte aligned; x_out must not
+ * x: device float32 [k], 4-byte aligned; delta, gain, x_out: device float32
+ * [k], 16-byte aligned; x_out must not
  * overlap x, delta or y (it is written while they are read). y: device
  * float32 [m]. k at most 14560 (the whole row is staged in one workgroup's
  * LDS). m == 0 is a successful no-op that writes nothing (x_out included).
@@ -244,7 +251,7 @@ int q4_gemv_addnorm_tuned(int fmt, const void *w, const float *x, const float *d
 
 /* Prefill product Y[t][i] = sum_k bf16_rne(w_hat[i][k]) * X[t][k], fp32 out.
  * w: device, quantized as above (any format), 16-byte aligned; x_bf16: device bf16 bit
- * patterns [n][k], 16-byte aligned; y: device float32 [n][m], 4-byte aligned.
+ * patterns [n][k], 4-byte aligned; y: device float32 [n][m], 4-byte aligned.
  * n >= 1 (any token count). Weight tiles are dequantized to bf16 into LDS
  * and reused across the token tile by bf16 matrix-core (MFMA) instructions
  * with fp32 accumulation (Methodology section 3: dequantize into shared

@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libq4gemv.so")
+# Q4_GEMV_LIB names another build of the library (the host-sanitizer test
+# tier loads one); by default the in-tree build.
+LIB_PATH = os.environ.get("Q4_GEMV_LIB") or os.path.join(HERE, "libq4gemv.so")
 
 Q4_FMT_Q4_0 = 0
 Q4_FMT_Q4_K = 1

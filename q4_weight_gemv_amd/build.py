@@ -53,32 +53,50 @@ SOURCES = [
 ]
 
 
-def _compile(src: str, kind: str) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+# Host sanitizers for a test build (sanitize="address,undefined"): the host
+# code of every unit is instrumented, the device code is built as usual.
+def _host_sanitizer_flags(sanitize: str | None, device_unit: bool) -> list:
+    if not sanitize:
+        return []
+    if device_unit:
+        return ["-Xarch_host", f"-fsanitize={sanitize}", "-Xarch_host", "-fno-omit-frame-pointer"]
+    return [f"-fsanitize={sanitize}", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, kind: str, obj_dir: str = OBJ, sanitize: str | None = None) -> str:
+    out = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     if kind == "host":
-        cmd = [HIPCC, "-x", "c++"] + COMMON + HOST_ONLY + ["-c", path, "-o", out]
+        cmd = [HIPCC, "-x", "c++"] + COMMON + HOST_ONLY + _host_sanitizer_flags(sanitize, False) + ["-c", path, "-o", out]
     else:
-        cmd = [HIPCC, "-x", "hip"] + COMMON + DEVICE + ["-c", path, "-o", out]
+        cmd = [HIPCC, "-x", "hip"] + COMMON + DEVICE + _host_sanitizer_flags(sanitize, True) + ["-c", path, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, sanitize: str | None = None, out: str | None = None) -> str:
+    """Build the library (``out``, default the in-tree libq4gemv.so). With
+    ``sanitize`` (e.g. "address,undefined") the host code is instrumented and
+    the objects go to their own folder; load such a build by pointing
+    Q4_GEMV_LIB at it, with the sanitizer runtime preloaded."""
+    lib = out or LIB
+    obj_dir = OBJ if not sanitize else os.path.join(ROOT, "_build", "obj_" + sanitize.replace(",", "_"))
+    os.makedirs(obj_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(*s), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(*s, obj_dir=obj_dir, sanitize=sanitize), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp] + objs
+    if sanitize:
+        cmd += ["-Xarch_host", f"-fsanitize={sanitize}", "-shared-libsan"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

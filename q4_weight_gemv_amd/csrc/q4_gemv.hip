@@ -60,10 +60,12 @@ int device_lds_optin()
 
 namespace gemv {
 
-// Default geometry, from a sweep of every instantiated geometry on gfx950
+// Default geometries, from sweeps of every instantiated geometry on gfx950
 // (cold weights, graph-replayed launches) at the decode shapes of the
 // GPT-2-124M and SmolLM2-360M steps and the 7B-class layer, per format and
-// token count. Rows of nu 32-weight units:
+// token count. The tiled kernel (several tokens, the gated and fused-norm
+// products, and one token where the streaming kernel is not chosen), rows
+// of nu 32-weight units:
 //   Q4_0, one token: nu <= 32 -> one-wave groups, 32 lanes per row, two rows
 //     per lane (LM heads, m >= 16384: 8 lanes x 1 row); nu < 128 -> 4 waves,
 //     64 lanes per row; longer rows -> 4 waves, 32 lanes x 2 rows.
@@ -86,21 +88,29 @@ namespace gemv {
 //     128..255 units at several tokens: 8-wave groups of 32 lanes per row.
 //     Rows of 128..255 units at one token: the same 8-wave groups for tall
 //     products, else 4 waves of 16 lanes per row.
-//   Q4_0, one token, rows of up to kStreamMaxUnits units: the streaming
-//     kernel (two weight slots in flight per lane, one workgroup per compute
-//     unit): short rows (nu <= 32) 32 lanes per row in 8-wave groups, LM
-//     heads (m >= 16384) 8 (nu <= 24) or 16 lanes per row in 16-wave groups;
-//     longer rows 64 lanes per row, 16-wave groups, or two 8-wave groups per
-//     compute unit when the matrix has 8..16 rows of at most 4096 weights per
-//     compute unit (staging x twice per compute unit costs little there).
-Cfg choose_stream(int64_t m, int64_t k, int cus)
+//   One token, rows of up to kStreamMaxUnits units, every format: the
+//     streaming kernel (two weight slots in flight per lane), from a sweep of
+//     its geometries and the tiled choice at the workload shapes
+//     (bench.py --sweep; 256 compute units): short rows (nu <= 32) 32 lanes
+//     per row in one 8-wave group per compute unit, LM heads (m >= 16384)
+//     8 (nu <= 24, and Q1_0) or 16 lanes per row in 16-wave groups (Q8_0:
+//     32); longer rows 64 lanes per row: one 8-wave group per compute unit
+//     below 8 rows per compute unit, two from 8 to 16 rows per compute unit
+//     of rows up to 4096 weights (and for every longer Q8_0 row), else one
+//     16-wave group. Q8_0's short rows below LM-head height stay on the
+//     tiled kernel (within 2 % either way).
+Cfg choose_stream(int fmt, int64_t m, int64_t k, int cus)
 {
     const int64_t nu = k / kUnitWeights;
     if (nu <= 32) {
-        if (m >= 16384) return Cfg{nu <= 24 ? 8 : 16, 1, 16, 1, 2};
+        if (m >= 16384) {
+            if (fmt == Q4_FMT_Q8_0) return Cfg{32, 1, 16, 1, 2};
+            return Cfg{nu <= 24 || fmt == Q4_FMT_Q1_0 ? 8 : 16, 1, 16, 1, 2};
+        }
         return Cfg{32, 1, 8, 1, 2};
     }
-    if (nu <= 128 && m >= 8LL * cus && m <= 16LL * cus) return Cfg{64, 1, 8, 2, 2};
+    if (m < 8LL * cus) return Cfg{64, 1, 8, 1, 2};
+    if ((nu <= 128 && m <= 16LL * cus) || fmt == Q4_FMT_Q8_0) return Cfg{64, 1, 8, 2, 2};
     return Cfg{64, 1, 16, 1, 2};
 }
 
@@ -109,7 +119,8 @@ Cfg choose_tiled(int fmt, int64_t m, int64_t k, int64_t n, int cus);
 Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 {
     const int64_t nu = k / kUnitWeights;
-    if (fmt == Q4_FMT_Q4_0 && n == 1 && nu <= kStreamMaxUnits) return choose_stream(m, k, cus);
+    const bool q8_short = fmt == Q4_FMT_Q8_0 && nu <= 32 && m < 16384;
+    if (n == 1 && nu <= kStreamMaxUnits && !q8_short) return choose_stream(fmt, m, k, cus);
     return choose_tiled(fmt, m, k, n, cus);
 }
 
@@ -318,7 +329,11 @@ int check_product_args(int fmt, const void *w, const void *x, const float *y, in
     if (wbytes >= (1ull << 31) || static_cast<uint64_t>(n) * k * 4 >= (1ull << 31) ||
         static_cast<uint64_t>(n) * m * 4 >= (1ull << 31) || m >= (1LL << 30))
         return Q4_EUNSUPPORTED;
-    if ((reinterpret_cast<uintptr_t>(w) & 15) || (reinterpret_cast<uintptr_t>(x) & 15) ||
+    // The weights' 16-byte groups sit on 16-byte boundaries of the buffer.
+    // x is read with 16-byte loads, which gfx950 serves at any 4-byte
+    // alignment (its memory accesses are not alignment-checked beyond the
+    // dword); y is written per element.
+    if ((reinterpret_cast<uintptr_t>(w) & 15) || (reinterpret_cast<uintptr_t>(x) & 3) ||
         (reinterpret_cast<uintptr_t>(y) & 3))
         return Q4_EALIGN;
     return Q4_OK;
@@ -412,7 +427,7 @@ extern "C" int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y, i
     if (tuning->kernel == Q4_GEMV_KERNEL_TILED || (tuning->kernel == Q4_GEMV_KERNEL_AUTO && geometry))
         c = q4::gemv::choose_tiled(fmt, m, k, n, cus);
     else if (tuning->kernel == Q4_GEMV_KERNEL_STREAM && c.depth == 0)
-        c = q4::gemv::choose_stream(m, k, cus);
+        c = q4::gemv::choose_stream(fmt, m, k, cus);
     if (tuning->lanes_per_row) c.lpr = tuning->lanes_per_row;
     if (tuning->rows_per_lane) c.r = tuning->rows_per_lane;
     if (tuning->waves_per_group) c.waves = tuning->waves_per_group;

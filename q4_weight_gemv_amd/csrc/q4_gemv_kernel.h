@@ -148,16 +148,6 @@ __device__ __forceinline__ float half_hi(uint32_t v)
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16)));
 }
 
-// Sum of the 16 products of one dword of nibbles with its four fp16 pairs,
-// hi parts (xh) and lo parts (xl).
-// Pair order: (L, L+2), (H, H+2)/16, (L+1, L+3), (H+1, H+3)/16.
-// Packed fp16 add of a constant pair to an fp16 pair given as bits.
-__device__ __forceinline__ uint32_t add_h2(uint32_t a, _Float16 c)
-{
-    const half2_t r = __builtin_bit_cast(half2_t, a) + half2_t{c, c};
-    return __builtin_bit_cast(uint32_t, r);
-}
-
 // Masked code bits c*2^-24 (an fp16 subnormal pair, c < 1024) as the normal
 // pair c*2^-14 - OFF*2^-14: one packed fp16 fma, exact (c*2^-14 and the
 // result have at most 11 significant bits and lie in the normal range, or
@@ -716,8 +706,7 @@ struct NormIo {
 // staging waits on one L2 round trip per round, not one per item.
 template <class F, int N, int NT, int P, bool LO, bool NORM, class Issue, bool SKIP_DEAD = false>
 __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, int nuc, int uc,
-                                      u32x4 *__restrict__ xs, int tid, NormIo &nio,
-                                      Issue issue)
+                                      u32x4 *__restrict__ xs, int tid, NormIo &nio, Issue issue)
 {
     static_assert(!NORM || N == 1, "the fused norm is a one-token prologue");
     const int per_tok = nuc * 4;
@@ -1152,15 +1141,16 @@ int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStre
     // (8 tokens of 4096, 4 of 8960) or larger chunks, at fewer groups per CU.
     // (64-bit products: a whole row of many tokens can exceed 2^31 bytes.)
     const int64_t row_bytes = static_cast<int64_t>(nu) * bytes_per_unit;
+    const int extra = NORM ? 4 * WAVES : 0;  // the fused norm's per-wave sums of squares
     int budget = kMaxLdsBytes;
-    if (!NORM && N >= 2 && row_bytes > kMaxLdsBytes) {
+    if ((NORM || N >= 2) && row_bytes + extra > kMaxLdsBytes) {
         const int optin = device_lds_optin();
         if (optin > kMaxLdsBytes) budget = optin;
     }
-    if (row_bytes > budget) uc = budget / bytes_per_unit / 8 * 8;  // chunks of whole super-blocks
+    if (row_bytes + extra > budget) uc = (budget - extra) / bytes_per_unit / 8 * 8;  // chunks of whole super-blocks
     if (uc <= 0) return Q4_EUNSUPPORTED;
     if (NORM && uc < nu) return Q4_EUNSUPPORTED;  // the fused norm needs the whole row staged
-    const size_t lds = static_cast<size_t>(uc) * bytes_per_unit + (NORM ? 4 * WAVES : 0);
+    const size_t lds = static_cast<size_t>(uc) * bytes_per_unit + extra;
     if (lds > static_cast<size_t>(kMaxLdsBytes)) {
         // Above 64 KiB a kernel opts in to its dynamic LDS size, once per device.
         static std::atomic<int> opted[64];

@@ -217,3 +217,34 @@ def test_addnorm_noop_and_errors(env):
     assert lib.q4_gemv_addnorm(0, p(w), p(x), None, p(g), 1e-5, p(x), p(y), 4, 32, 0, None) == q4.Q4_EINVAL
     torch.cuda.synchronize()
     assert (y == 5.0).all() and (xo == 7.0).all()
+
+
+@pytest.mark.parametrize("geom,glu", [((32, 1, 4), False), ((32, 1, 8), False), ((64, 1, 4), False),
+                                      ((32, 2, 4), True), ((32, 2, 8), True)])
+def test_addnorm_longest_row(env, geom, glu):
+    # The longest row the fused norm stages (455 units, 14560 weights: 65520
+    # bytes of activations, plus one sum of squares per wave), with 4- and
+    # 8-wave groups: the per-wave sums take the workgroup past 64 KiB, which
+    # the launch covers with the device's opt-in LDS.
+    torch, q4, orc = env
+    fmt, m, k = 0, 300, 14560
+    rows = 2 * m if glu else m
+    buf = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(3600, glu), rows, k))
+    x, delta, gain = _inputs(3601, k)
+    v, h = _normed(x, delta, gain, 1e-5)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    wd, xd, dd, gd = dev(buf), dev(x), dev(delta), dev(gain)
+    xo = torch.full((k,), float("nan"), device="cuda")
+    y = torch.full((m,), float("nan"), device="cuda")
+    epi = q4.Q4_EPILOGUE_SILU_MUL if glu else q4.Q4_EPILOGUE_NONE
+    say(f"addnorm longest row geometry {geom} glu={glu}")
+    q4.q4_gemv_addnorm_tuned(fmt, wd, xd, dd, gd, 1e-5, xo, y, m, k, epi, *geom, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(xo.cpu().numpy(), v)
+    if glu:
+        yr = orc.matvec_silu_mul(fmt, buf, m, k, h[None, :], threads=threads())
+    else:
+        yr = orc.matvec(fmt, buf, m, k, h[None, :], threads=threads())
+    yc = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(yc))
+    assert np.linalg.norm(yc - yr[0]) <= GEMV_TOL * np.linalg.norm(yr[0]), geom

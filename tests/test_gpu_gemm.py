@@ -186,3 +186,23 @@ def test_gemm_misaligned_and_noop(env):
     assert lib.q4_gemm(0, w.data_ptr(), x.data_ptr(), y.data_ptr(), 0, 32, 1, None) == q4.Q4_OK
     torch.cuda.synchronize()
     assert (y == 5.0).all()
+
+
+@pytest.mark.parametrize("fmt,m,k,n", [(0, 300, 960, 64), (1, 130, 1024, 33), (0, 2560, 960, 512)])
+@pytest.mark.parametrize("shift", [2, 4, 6])
+def test_x_four_byte_aligned(env, fmt, m, k, n, shift):
+    # bf16 activations 4, 8 or 12 bytes past a 16-byte boundary: the same bits
+    # as the same values at an aligned address.
+    torch, q4, orc = env
+    buf = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(60 + fmt, m), m, k))
+    xb = synth.bf16_bits(synth.activations(synth.seed_for(60 + fmt, m, True), n, k))
+    ref = _gemm(env, fmt, buf, xb, m, k)
+    store = torch.zeros(n * k + 16, dtype=torch.int16, device="cuda")
+    xd = store[shift:shift + n * k].view(n, k)
+    xd.copy_(torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)))
+    assert xd.data_ptr() % 16 == 2 * shift
+    yd = torch.full((n, m), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"gemm x at +{2 * shift} bytes fmt={fmt} m={m} k={k} n={n}")
+    q4.q4_gemm(fmt, torch.from_numpy(buf).cuda(), xd, yd, m, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(yd.cpu().numpy().view(np.uint32), ref.view(np.uint32))

@@ -331,6 +331,34 @@ def test_zero_rows_and_tokens_are_noops(env):
     assert (y == 7.0).all()
 
 
+@pytest.mark.parametrize("fmt,m,k,n", [(0, 300, 4096, 1), (0, 37, 768, 3), (0, 2049, 768, 1), (1, 300, 4096, 1),
+                                         (1, 130, 1024, 8), (2, 300, 960, 1), (3, 130, 1024, 4), (4, 2049, 768, 1)])
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_x_four_byte_aligned(env, fmt, m, k, n, shift):
+    # x 4, 8 or 12 bytes past a 16-byte boundary is staged with 4-byte loads:
+    # the same bits as the same values at an aligned address, and the
+    # oracle's tolerance (one token: the streaming kernel; several: tiled).
+    torch, q4, orc = env
+    buf = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(1500 + fmt, m), m, k))
+    x = synth.activations(synth.seed_for(1500 + fmt, m, True), n, k)
+    wd = torch.from_numpy(buf).cuda()
+    ref = _gemv(env, fmt, buf, x, m, k)
+    store = torch.zeros(n * k + 8, dtype=torch.float32, device="cuda")
+    xd = store[shift:shift + n * k].view(n, k)
+    xd.copy_(torch.from_numpy(x))
+    assert xd.data_ptr() % 16 == 4 * shift
+    yd = torch.full((n, m), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"x at +{4 * shift} bytes fmt={fmt} m={m} k={k} n={n}")
+    q4.q4_gemv(fmt, wd, xd, yd, m, k)
+    torch.cuda.synchronize()
+    y = yd.cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), ref.view(np.uint32))
+    yr, ad = orc.matvec(fmt, buf, m, k, x, threads=threads(), absdot=True)
+    if fmt in (1, 3):
+        ad = orc.termscale(fmt, buf, m, k, x, threads=threads())
+    check_tolerance(y, yr, ad, GEMV_TOL, what=f"x at +{4 * shift} fmt={fmt}")
+
+
 def test_misaligned_pointer_rejected(env):
     torch, q4, _ = env
     w = torch.zeros(4096, dtype=torch.uint8, device="cuda")
@@ -567,7 +595,7 @@ def test_glu_noop_and_errors(env):
     y = torch.full((8,), 5.0, device="cuda")
     assert lib.q4_gemv_glu(0, w.data_ptr(), x.data_ptr(), y.data_ptr(), 0, 32, 1, None) == q4.Q4_OK
     assert lib.q4_gemv_glu(0, w.data_ptr(), x.data_ptr(), y.data_ptr(), 4, 32, 0, None) == q4.Q4_OK
-    assert lib.q4_gemv_glu(0, w.data_ptr(), x.data_ptr() + 4, y.data_ptr(), 4, 32, 1, None) == q4.Q4_EALIGN
+    assert lib.q4_gemv_glu(0, w.data_ptr(), x.data_ptr() + 2, y.data_ptr(), 4, 32, 1, None) == q4.Q4_EALIGN
     torch.cuda.synchronize()
     assert (y == 5.0).all()
 

@@ -212,8 +212,12 @@ def test_product_argument_errors(q4, entry):
     assert f(0, A16, None, A16, 64, 256, 1, None) == q4.Q4_EINVAL
     assert f(0, A16, A16, None, 64, 256, 1, None) == q4.Q4_EINVAL
     assert f(0, A16 + 2, A16, A16, 64, 256, 1, None) == q4.Q4_EALIGN  # misaligned w
-    assert f(0, A16, A16 + 4, A16, 64, 256, 1, None) == q4.Q4_EALIGN  # misaligned x
+    assert f(0, A16 + 8, A16, A16, 64, 256, 1, None) == q4.Q4_EALIGN  # w must be 16-byte aligned
+    assert f(0, A16, A16 + 2, A16, 64, 256, 1, None) == q4.Q4_EALIGN  # misaligned x
     assert f(0, A16, A16, A16 + 2, 64, 256, 1, None) == q4.Q4_EALIGN  # misaligned y
+    # A 4-byte-aligned x passes validation: the call reaches the HIP runtime,
+    # which on a host without a GPU reports an error.
+    assert f(0, A16, A16 + 4, A16, 64, 256, 1, None) == q4.Q4_EHIP
     assert f(0, None, None, None, 0, 256, 1, None) == q4.Q4_OK        # m == 0: no-op
     assert f(0, None, None, None, 64, 256, 0, None) == q4.Q4_OK       # n == 0: no-op
     assert f(0, *ok, 1 << 30, 1 << 10, 1, None) == q4.Q4_EUNSUPPORTED  # beyond 32-bit offsets
@@ -236,6 +240,7 @@ def test_tuned_argument_errors(q4):
     assert f(0, *ok, 64, 48, 1, ctypes.byref(good), None) == q4.Q4_EINVAL
     assert f(0, *ok, 64, 256, 9, ctypes.byref(good), None) == q4.Q4_EUNSUPPORTED
     assert f(0, A16 + 4, A16, A16, 64, 256, 1, ctypes.byref(good), None) == q4.Q4_EALIGN
+    assert f(0, A16, A16 + 6, A16, 64, 256, 1, ctypes.byref(good), None) == q4.Q4_EALIGN
     assert f(0, None, None, None, 0, 256, 1, ctypes.byref(good), None) == q4.Q4_OK
     # kernel and depth fields: negative or unknown values are refused, and the
     # streaming kernel takes one token only.
@@ -254,6 +259,7 @@ def test_gemm_tuned_argument_errors(q4):
     assert f(0, *ok, 64, 256, 4, ctypes.byref(q4.q4_gemm_tuning(-1, 0, 0)), None) == q4.Q4_EINVAL
     assert f(0, *ok, 64, 48, 4, ctypes.byref(q4.q4_gemm_tuning(0, 0, 0)), None) == q4.Q4_EINVAL
     assert f(0, A16, A16 + 2, A16, 64, 256, 4, ctypes.byref(q4.q4_gemm_tuning(0, 0, 0)), None) == q4.Q4_EALIGN
+    assert f(0, A16 + 4, A16, A16, 64, 256, 4, ctypes.byref(q4.q4_gemm_tuning(0, 0, 0)), None) == q4.Q4_EALIGN
     assert f(0, None, None, None, 0, 256, 4, ctypes.byref(q4.q4_gemm_tuning(0, 0, 0)), None) == q4.Q4_OK
 
 
@@ -261,7 +267,7 @@ def test_sequence_and_graph_argument_errors(q4):
     lib = q4.raw()
     ops = (q4.q4_gemv_op * 2)()
     ops[0] = q4.q4_gemv_op(A16, A16, A16, 64, 256)
-    ops[1] = q4.q4_gemv_op(A16, A16 + 4, A16, 64, 256)  # misaligned x in the second op
+    ops[1] = q4.q4_gemv_op(A16, A16 + 2, A16, 64, 256)  # misaligned x in the second op
     assert lib.q4_gemv_sequence(0, ops, 2, 1, None) == q4.Q4_EALIGN
     assert lib.q4_gemv_sequence(0, None, 2, 1, None) == q4.Q4_EINVAL
     assert lib.q4_gemv_sequence(0, ops, -1, 1, None) == q4.Q4_EINVAL
@@ -301,7 +307,7 @@ def test_addnorm_argument_errors(q4):
     assert f(0, W, X, D, G + 4, 1e-5, XO, Y, 64, 256, 0, None) == q4.Q4_EALIGN     # misaligned gain
     assert f(0, W, X, D + 8, G, 1e-5, XO, Y, 64, 256, 0, None) == q4.Q4_EALIGN     # misaligned delta
     assert f(0, W, X, D, G, 1e-5, XO + 4, Y, 64, 256, 0, None) == q4.Q4_EALIGN     # misaligned x_out
-    assert f(0, W, X + 4, D, G, 1e-5, XO, Y, 64, 256, 0, None) == q4.Q4_EALIGN     # misaligned x
+    assert f(0, W, X + 2, D, G, 1e-5, XO, Y, 64, 256, 0, None) == q4.Q4_EALIGN     # misaligned x
     assert f(0, W, X, D, G, 1e-5, X, Y, 64, 256, 0, None) == q4.Q4_EINVAL          # x_out is x
     assert f(0, W, X, D, G, 1e-5, X + 512, Y, 64, 256, 0, None) == q4.Q4_EINVAL    # x_out overlaps x
     assert f(0, W, X, D, G, 1e-5, D - 16, Y, 64, 256, 0, None) == q4.Q4_EINVAL     # x_out overlaps delta
@@ -342,7 +348,7 @@ def test_sequence_epilogue_field(q4):
     ops = (q4.q4_gemv_op * 1)()
     ops[0] = q4.q4_gemv_op(A16, A16, A16, 64, 256, 7)  # unknown epilogue
     assert lib.q4_gemv_sequence(0, ops, 1, 1, None) == q4.Q4_EINVAL
-    ops[0] = q4.q4_gemv_op(A16, A16 + 4, A16, 64, 256, q4.Q4_EPILOGUE_SILU_MUL)
+    ops[0] = q4.q4_gemv_op(A16, A16 + 2, A16, 64, 256, q4.Q4_EPILOGUE_SILU_MUL)
     assert lib.q4_gemv_sequence(0, ops, 1, 1, None) == q4.Q4_EALIGN
     ops[0] = q4.q4_gemv_op(A16, A16, A16, 1 << 29, 256, q4.Q4_EPILOGUE_SILU_MUL)
     assert lib.q4_gemv_sequence(0, ops, 1, 1, None) == q4.Q4_EUNSUPPORTED
