@@ -153,9 +153,15 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
  * weight codes are exact fp16 values, products and sums are fp32. A NaN among
  * token t's activations makes every y[t][i] NaN, as exact IEEE evaluation
  * does (0 * NaN included); the other tokens are unaffected. x is otherwise
- * expected finite. One token on a Q4_0 matrix of rows of up to 14560 weights
- * runs the streaming kernel (see q4_gemv_tuning), everything else the tiled
- * kernel; both are deterministic. */
+ * expected finite. One token on a matrix of rows of up to 14560 weights
+ * runs the streaming kernel, Q4_K at several tokens on 256 rows or more the
+ * matrix-core kernel (from 2 tokens on rows of up to 2048 weights, from 4 on
+ * rows of up to 8192, from 5 on longer ones), everything else the tiled
+ * kernel (see q4_gemv_tuning); all
+ * are deterministic. The matrix-core kernel scales each 256-element piece of
+ * a token's x (one Q4_K super-block) by a power of two into [2^14, 2^15) and
+ * rounds it to one fp16 value (the same 2^-11 bound); its codes sc*q and
+ * mins are exact fp16 values and its products and sums fp32. */
 int q4_gemv(int fmt, const void *w, const float *x, float *y,
             int64_t m, int64_t k, int64_t n, void *hip_stream);
 
@@ -217,10 +223,15 @@ int q4_gemv_addnorm(int fmt, const void *w, const float *x, const float *delta, 
  *     Instantiated (lanes_per_row, waves_per_group, depth): (8,16,2)
  *     (16,16,2) (16,1,2) (32,1,2) (32,8,2) (32,16,2) (64,4,2) (64,8,2)
  *     (64,16,2) (64,8,3) (64,16,4).
+ *   Q4_GEMV_KERNEL_MATRIX: Q4_K only, n = 1..8: the products on matrix cores
+ *     (v_mfma_f32_16x16x32_f16 on 16-row tiles); one 8-wave workgroup per
+ *     compute unit (times groups_per_cu, the only geometry field it takes;
+ *     the others must be 0) owns a contiguous range of tiles and stages x
+ *     once (in chunks when the row does not fit the LDS).
  * With kernel Q4_GEMV_KERNEL_AUTO, a tuning that sets any geometry field
  * names a tiled geometry; one that sets none keeps the library's choice of
  * kernel. Other geometries return Q4_EUNSUPPORTED. */
-enum { Q4_GEMV_KERNEL_AUTO = 0, Q4_GEMV_KERNEL_TILED = 1, Q4_GEMV_KERNEL_STREAM = 2 };
+enum { Q4_GEMV_KERNEL_AUTO = 0, Q4_GEMV_KERNEL_TILED = 1, Q4_GEMV_KERNEL_STREAM = 2, Q4_GEMV_KERNEL_MATRIX = 3 };
 typedef struct {
     int lanes_per_row;   /* lanes sharing one weight row: 8, 16, 32 or 64 */
     int rows_per_lane;   /* rows each lane streams at once: 1, 2 or 4 (streaming: 1) */
@@ -233,14 +244,16 @@ typedef struct {
 /* q4_gemv with an explicit kernel and geometry; same arguments, layouts,
  * results and errors, plus Q4_EINVAL for a null tuning, a negative field or
  * an unknown kernel, and Q4_EUNSUPPORTED for a geometry that is not
- * instantiated or the streaming kernel at n > 1 or beyond its row length. */
+ * instantiated, the streaming kernel at n > 1 or beyond its row length, or
+ * the matrix-core kernel on a format other than Q4_K or with a geometry field
+ * other than groups_per_cu. */
 int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y,
                   int64_t m, int64_t k, int64_t n, const q4_gemv_tuning *tuning, void *hip_stream);
 
 /* q4_gemv_addnorm with an explicit tile geometry; same arguments, results and
  * errors, plus Q4_EINVAL for a null tuning, a negative field or an unknown
- * kernel, and Q4_EUNSUPPORTED for the streaming kernel (the fused product
- * runs on the tiled kernel) or a geometry that is not instantiated for the
+ * kernel, and Q4_EUNSUPPORTED for the streaming or matrix-core kernel (the
+ * fused product runs on the tiled kernel) or a geometry that is not instantiated for the
  * fused product. Instantiated:
  * (8,1,1) (8,2,1) (16,1,1) (16,1,4) (32,1,4) (32,1,8) (32,2,1) (32,2,4) (64,1,4)
  * with Q4_EPILOGUE_NONE; (16,2,1) (16,2,4) (32,2,1) (32,2,4) (32,2,8) (64,2,4)

@@ -53,6 +53,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 Q4_GEMV_KERNEL_AUTO = 0
 Q4_GEMV_KERNEL_TILED = 1
 Q4_GEMV_KERNEL_STREAM = 2
+Q4_GEMV_KERNEL_MATRIX = 3
 
 
 class q4_gemv_tuning(ctypes.Structure):

@@ -46,6 +46,7 @@ SOURCES = [
     ("q4_gemv_norm_a.hip", "device"),
     ("q4_gemv_norm_b.hip", "device"),
     ("q4_gemv_stream.hip", "device"),
+    ("q4_gemv_mfma.hip", "device"),
     ("q4_gemm.hip", "device"),
     ("q4_stack.hip", "device"),
     ("q4_step.hip", "device"),

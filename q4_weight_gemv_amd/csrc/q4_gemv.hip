@@ -116,8 +116,23 @@ Cfg choose_stream(int fmt, int64_t m, int64_t k, int cus)
 
 Cfg choose_tiled(int fmt, int64_t m, int64_t k, int64_t n, int cus);
 
+// The Q4_K matrix-core kernel from several tokens on, for products of 256
+// rows or more (one fp16 per activation, as the tiled kernel there). From a
+// sweep against the tiled kernel's per-token dot products: faster from 5
+// tokens on, from 4 on rows that fit one workgroup's LDS at once (8192
+// weights), and from 2 on rows of up to 2048 weights.
+bool use_matrix(int fmt, int64_t m, int64_t k, int64_t n)
+{
+    return fmt == Q4_FMT_Q4_K && m >= 256 && (n >= 5 || (n == 4 && k <= 8192) || (n >= 2 && k <= 2048));
+}
+
 Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 {
+    if (use_matrix(fmt, m, k, n)) {
+        Cfg c{0, 0, 0, 1};
+        c.matrix = true;
+        return c;
+    }
     const int64_t nu = k / kUnitWeights;
     const bool q8_short = fmt == Q4_FMT_Q8_0 && nu <= 32 && m < 16384;
     if (n == 1 && nu <= kStreamMaxUnits && !q8_short) return choose_stream(fmt, m, k, cus);
@@ -178,6 +193,11 @@ int dispatch(int fmt, const Cfg &c, const void *w, const float *x, float *y, int
     const auto *wb = static_cast<const uint8_t *>(w);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int mi = static_cast<int>(m), ki = static_cast<int>(k);
+    if (c.matrix) {
+        // The matrix-core kernel: Q4_K, plain product.
+        if (glu || fmt != Q4_FMT_Q4_K) return Q4_EUNSUPPORTED;
+        return dispatch_mfma(wb, x, y, mi, ki, static_cast<int>(n), s, cus, c.groups_per_cu);
+    }
     if (c.depth > 0) {
         // The streaming kernel: one token, plain product, the whole row staged.
         if (glu || n != 1 || k / kUnitWeights > kStreamMaxUnits) return Q4_EUNSUPPORTED;
@@ -397,10 +417,10 @@ extern "C" int q4_gemv_addnorm_tuned(int fmt, const void *w, const float *x, con
     if (!tuning) return Q4_EINVAL;
     if (tuning->lanes_per_row < 0 || tuning->rows_per_lane < 0 || tuning->waves_per_group < 0 ||
         tuning->groups_per_cu < 0 || tuning->groups_per_cu > 64 || tuning->depth < 0 || tuning->kernel < 0 ||
-        tuning->kernel > Q4_GEMV_KERNEL_STREAM)
+        tuning->kernel > Q4_GEMV_KERNEL_MATRIX)
         return Q4_EINVAL;
     // The fused norm runs on the tiled kernel only.
-    if (tuning->kernel == Q4_GEMV_KERNEL_STREAM) return Q4_EUNSUPPORTED;
+    if (tuning->kernel == Q4_GEMV_KERNEL_STREAM || tuning->kernel == Q4_GEMV_KERNEL_MATRIX) return Q4_EUNSUPPORTED;
     return addnorm_entry(fmt, w, x, delta, gain, eps, x_out, y, m, k, epilogue, tuning, hip_stream);
 }
 
@@ -412,22 +432,31 @@ extern "C" int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y, i
     if (!tuning) return Q4_EINVAL;
     if (tuning->lanes_per_row < 0 || tuning->rows_per_lane < 0 || tuning->waves_per_group < 0 ||
         tuning->groups_per_cu < 0 || tuning->groups_per_cu > 64 || tuning->depth < 0 || tuning->kernel < 0 ||
-        tuning->kernel > Q4_GEMV_KERNEL_STREAM)
+        tuning->kernel > Q4_GEMV_KERNEL_MATRIX)
         return Q4_EINVAL;
     if (tuning->kernel == Q4_GEMV_KERNEL_STREAM && n > 1) return Q4_EUNSUPPORTED;
+    // The matrix-core kernel: Q4_K only, and of the geometry fields only
+    // groups_per_cu applies.
+    if (tuning->kernel == Q4_GEMV_KERNEL_MATRIX &&
+        (fmt != Q4_FMT_Q4_K || tuning->lanes_per_row || tuning->rows_per_lane || tuning->waves_per_group ||
+         tuning->depth))
+        return Q4_EUNSUPPORTED;
     if (m == 0 || n == 0) return Q4_OK;
     const int cus = q4::device_cus();
     if (cus <= 0) return Q4_EHIP;
-    // The kernel: the one-token streaming kernel when asked for, or when the
-    // library would pick it and no tiled geometry field is given; else the
-    // tiled kernel.
+    // The kernel: the one asked for; with Q4_GEMV_KERNEL_AUTO the tiled
+    // kernel when a tiled geometry field is given, else the library's choice.
     const bool geometry = tuning->lanes_per_row || tuning->rows_per_lane || tuning->waves_per_group ||
                           tuning->groups_per_cu;
     q4::gemv::Cfg c = q4::gemv::choose(fmt, m, k, n, cus);
-    if (tuning->kernel == Q4_GEMV_KERNEL_TILED || (tuning->kernel == Q4_GEMV_KERNEL_AUTO && geometry))
+    if (tuning->kernel == Q4_GEMV_KERNEL_TILED || (tuning->kernel == Q4_GEMV_KERNEL_AUTO && geometry)) {
         c = q4::gemv::choose_tiled(fmt, m, k, n, cus);
-    else if (tuning->kernel == Q4_GEMV_KERNEL_STREAM && c.depth == 0)
+    } else if (tuning->kernel == Q4_GEMV_KERNEL_STREAM && c.depth == 0) {
         c = q4::gemv::choose_stream(fmt, m, k, cus);
+    } else if (tuning->kernel == Q4_GEMV_KERNEL_MATRIX) {
+        c = q4::gemv::Cfg{0, 0, 0, 1};
+        c.matrix = true;
+    }
     if (tuning->lanes_per_row) c.lpr = tuning->lanes_per_row;
     if (tuning->rows_per_lane) c.r = tuning->rows_per_lane;
     if (tuning->waves_per_group) c.waves = tuning->waves_per_group;

@@ -1,0 +1,372 @@
+// Decode product at several tokens for Q4_K on gfx950's matrix cores.
+//
+// At 2 to 8 tokens the tiled kernel's VALU dot products bound it: every
+// weight pair costs one v_dot2 per token. Here v_mfma_f32_16x16x32_f16 forms
+// the products, so a weight costs its unpacking once, whatever the token
+// count, and the weight stream is the bound again.
+//
+// Format (llama.cpp K-quants, the stretch format of Llamas on the Web,
+// technical summary, Methodology section 3): a 256-weight super-block holds
+// fp16 d and dmin, twelve bytes of 6-bit sub-block scales sc and mins m, and
+// 128 nibble bytes; weight = d * sc * q - dmin * m for its 32-weight sub-block.
+//
+// Per super-block and tile of 16 weight rows, with tokens on the MFMA's A side
+// (16 slots; the unused ones repeat token 0 and are never stored) and weight
+// rows on its B side:
+//   Dq[t][r] = sum_k (sc q)[r][k] * xs[t][k]      eight MFMAs
+//   Dm[t][r] = sum_k m[r][s(k)] * xs[t][k]         eight MFMAs (the sub-block's min, broadcast)
+//   y[t][r] += 2^e[t] * (d[r] Dq[t][r] - dmin[r] Dm[t][r])
+// where xs = x * 2^-e[t] rounded to fp16, e[t] per token and super-block
+// putting its largest magnitude into [2^14, 2^15). sc q (at most 945) and m
+// (at most 63) are exact fp16 values and every product is exact in fp32, so
+// the only roundings are x's to fp16 (at most 2^-11 relative) and the fp32 sums.
+//
+// MFMA 16x16x32 operand layout (wave64): lane l holds A row l%16 (a token)
+// and B column l%16 (a weight row), each at the 8 k slots 8(l/16)..+7; the
+// result D[4(l/16)+i][l%16], i < 4. Within a super-block, MFMA j (0..7) gives
+// lane group g = l/16 the weights of nibble chunk g (bytes 32g..32g+31 of the
+// 128): j < 4 the low nibbles of bytes 8j..8j+7 (sub-block 2g), j >= 4 the
+// high nibbles of bytes 8(j-4)..+7 (sub-block 2g+1); its A lanes hold the same
+// eight k. So each lane loads one contiguous 32-byte chunk per super-block,
+// and the D lane's weight row is its own B row: d, dmin and the scales come
+// from the header it loaded.
+//
+// Work: one workgroup of 8 waves per compute unit owns a contiguous range of
+// 16-row tiles and stages the activations once (in chunks of super-blocks
+// when a long row exceeds the LDS). The 8 waves split every tile's
+// super-blocks; their sums meet in LDS and are added in wave order
+// (deterministic). The next tile's weights are in flight while one is
+// multiplied.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "q4_gemv_kernel.h"
+#include "q4_internal.h"
+
+namespace q4 {
+namespace gemv {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaSbMax = 4;     // most super-blocks per wave per tile and chunk
+constexpr int kStageRounds = 2;   // staging rounds whose activation loads are in flight together
+constexpr int kSbBytes = 144;     // Q4_K super-block
+constexpr int kXRowPad = 16;      // bytes after each token's row of staged activations
+
+// Two nibble codes (bytes B and B+1 of n) as the exact fp16 pair (sc q0, sc q1).
+// A byte permute places each masked byte under the fp16 exponent of 1024:
+// bits 0x64nn are 1024 + nn. A low nibble (nn = q) then takes one packed fma
+// with sc and -1024 sc; a high nibble left in place (nn = 16 q) one with
+// sc/16 and -64 sc. Both are exact: sc/16 is a multiple of 2^-4, every
+// product and the result (an integer below 1024) fit fp16's 11 bits.
+template <int B>
+__device__ __forceinline__ uint32_t scaled_codes(uint32_t n, half2_t sc, half2_t off)
+{
+    constexpr uint32_t sel = B == 0 ? 0x04010400u : 0x04030402u;
+    const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, n, sel));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, sc, off));
+}
+
+// Eight codes from masked dwords a (codes 0..3) and b (4..7).
+__device__ __forceinline__ half8 code8(uint32_t a, uint32_t b, half2_t sc, half2_t off)
+{
+    return __builtin_bit_cast(half8, u32x4{scaled_codes<0>(a, sc, off), scaled_codes<2>(a, sc, off),
+                                           scaled_codes<0>(b, sc, off), scaled_codes<2>(b, sc, off)});
+}
+
+// Maximum over the 8 lanes of each aligned group of 8 (DPP: swap neighbours,
+// swap pairs, mirror the halves of the 8).
+__device__ __forceinline__ float max8(float v)
+{
+    const int b = __builtin_bit_cast(int, v);
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false)));
+    const int c = __builtin_bit_cast(int, v);
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(c, c, 0x4E, 0xF, 0xF, false)));
+    const int d = __builtin_bit_cast(int, v);
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(d, d, 0x141, 0xF, 0xF, false)));
+}
+
+// LDS of a chunk of CS super-blocks:
+//   xs:  [n][CS*256] fp16, rows padded by kXRowPad bytes
+//   scl: [CS][16] fp32 2^e (zero for token slots n..15)
+//   red: [2 tiles][7 waves][64 lanes] f32x4, the waves' sums of a tile
+struct MfmaLds {
+    uint32_t xs, scl, red, total;
+};
+
+__host__ __device__ inline MfmaLds mfma_lds(int n, int cs)
+{
+    MfmaLds l;
+    l.xs = 0;
+    l.scl = static_cast<uint32_t>(n) * (static_cast<uint32_t>(cs) * 512u + kXRowPad);
+    l.red = l.scl + static_cast<uint32_t>(cs) * 64u;
+    l.total = l.red + 2u * (kMfmaWaves - 1) * 64u * 16u;
+    return l;
+}
+
+template <int N, int SBW>
+__global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t *__restrict__ w, uint32_t wbytes,
+                                                                   const float *__restrict__ x, float *__restrict__ y,
+                                                                   int M, int K, int CS)
+{
+    static_assert(N >= 1 && N <= 16 && SBW >= 1 && SBW <= kMfmaSbMax, "shape");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, col = lane & 15;
+    const int ns = K / 256;
+    const MfmaLds L = mfma_lds(N, CS);
+    const uint32_t xrow = static_cast<uint32_t>(CS) * 512u + kXRowPad;
+    const int tiles = (M + 15) / 16;
+    const int t0 = static_cast<int>(static_cast<int64_t>(blockIdx.x) * tiles / gridDim.x);
+    const int t1 = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * tiles / gridDim.x);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, wbytes);
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(x, static_cast<uint32_t>(static_cast<uint64_t>(N) * static_cast<uint64_t>(K) * 4u));
+    const uint32_t row_bytes = static_cast<uint32_t>(ns) * kSbBytes;
+    // This lane's A row in LDS: token col (slots past n repeat token 0).
+    const uint32_t xa = static_cast<uint32_t>(col < N ? col : 0) * xrow + 128u * g;
+
+    struct Set {
+        u32x4 hd[SBW], q0[SBW], q1[SBW];
+    };
+    // Super-blocks [s0, s0 + nsb) of tile t's row for this lane. Every one of
+    // the SBW slots issues its loads (slots past nsb, rows past M and tiles
+    // past t1 fetch nothing), so the number of loads in flight is the same on
+    // every path and each wait covers exactly the loads it needs.
+    auto load = [&](Set &st, int t, int s0, int nsb, int t1) {
+        const int row = t * 16 + col;
+        const bool live = t < t1 && row < M;
+        const uint32_t base = static_cast<uint32_t>(row) * row_bytes;
+#pragma unroll
+        for (int i = 0; i < SBW; i++) {
+            const bool on = live && i < nsb;
+            const uint32_t sbo = uniform(static_cast<uint32_t>(s0 + (i < nsb ? i : 0)) * kSbBytes);
+            st.hd[i] = load16<0>(wr, on ? base : kNoFetch, sbo);
+            st.q0[i] = load16<kNonTemporal>(wr, on ? base + 16u + 32u * g : kNoFetch, sbo);
+            st.q1[i] = load16<kNonTemporal>(wr, on ? base + 32u + 32u * g : kNoFetch, sbo);
+        }
+    };
+    // Tile t over the chunk's super-blocks [s0, s0 + nsb) (cb: the chunk's
+    // first super-block): this wave's sums, then the workgroup's in wave
+    // order; wave 0 writes y (first chunk) or adds to it (later chunks).
+    auto tile = [&](const Set &st, int t, int s0, int nsb, int cb) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < SBW; i++) {
+            if (i < nsb) {
+                const int sbl = s0 + i - cb;
+                const u32x4 h = st.hd[i];
+                // Sub-blocks 2g and 2g+1: their 6-bit fields sit in bytes
+                // 2(g&1) and 2(g&1)+1 of the scale words.
+                const uint32_t sh = (g & 1) << 4;
+                const bool upper = g >= 2;
+                const uint32_t w0 = h.y >> sh, w1 = h.z >> sh, w2 = h.w >> sh;
+                const uint32_t sca = upper ? ((w2 & 15u) | (((w0 >> 6) & 3u) << 4)) : (w0 & 63u);
+                const uint32_t scb = upper ? (((w2 >> 8) & 15u) | (((w0 >> 14) & 3u) << 4)) : ((w0 >> 8) & 63u);
+                const uint32_t ma = upper ? (((w2 >> 4) & 15u) | (((w1 >> 6) & 3u) << 4)) : (w1 & 63u);
+                const uint32_t mb = upper ? (((w2 >> 12) & 15u) | (((w1 >> 14) & 3u) << 4)) : ((w1 >> 8) & 63u);
+                const _Float16 fa = static_cast<_Float16>(static_cast<float>(sca));
+                const _Float16 fb = static_cast<_Float16>(static_cast<float>(scb));
+                // Low nibbles: sc and -1024 sc; high nibbles in place: sc/16 and -64 sc.
+                const _Float16 fb16 = fb * static_cast<_Float16>(0.0625f);
+                const _Float16 oa = fa * static_cast<_Float16>(-1024.0f), ob = fb * static_cast<_Float16>(-64.0f);
+                const half2_t sc_a = {fa, fa}, sc_b = {fb16, fb16};
+                const half2_t off_a = {oa, oa}, off_b = {ob, ob};
+                const _Float16 ha = static_cast<_Float16>(static_cast<float>(ma));
+                const _Float16 hb = static_cast<_Float16>(static_cast<float>(mb));
+                const half8 bm_a = half8{ha, ha, ha, ha, ha, ha, ha, ha}, bm_b = half8{hb, hb, hb, hb, hb, hb, hb, hb};
+                const uint32_t qw[8] = {st.q0[i].x, st.q0[i].y, st.q0[i].z, st.q0[i].w,
+                                        st.q1[i].x, st.q1[i].y, st.q1[i].z, st.q1[i].w};
+                const uint8_t *xp = lds + xa + static_cast<uint32_t>(sbl) * 512u;
+                f32x4 dq = {0.0f, 0.0f, 0.0f, 0.0f}, dm = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const uint32_t qa = qw[2 * (j & 3)], qb = qw[2 * (j & 3) + 1];
+                    const half8 bw = j < 4 ? code8(qa & 0x0F0F0F0Fu, qb & 0x0F0F0F0Fu, sc_a, off_a)
+                                           : code8(qa & 0xF0F0F0F0u, qb & 0xF0F0F0F0u, sc_b, off_b);
+                    const half8 ax = *reinterpret_cast<const half8 *>(xp + 2 * (32 * (j >> 2) + 8 * (j & 3)));
+                    dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bw, dq, 0, 0, 0);
+                    dm = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, j < 4 ? bm_a : bm_b, dm, 0, 0, 0);
+                }
+                const f32x4 sc4 = *reinterpret_cast<const f32x4 *>(lds + L.scl + (sbl * 16 + 4 * g) * 4);
+                const float d = half_lo(h.x), dmin = half_hi(h.x);
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    acc[r] = __builtin_fmaf(sc4[r], __builtin_fmaf(d, dq[r], -(dmin * dm[r])), acc[r]);
+            }
+        }
+        f32x4 *red = reinterpret_cast<f32x4 *>(lds + L.red) + (t & 1) * (kMfmaWaves - 1) * 64;
+        if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int v = 1; v < kMfmaWaves; v++) acc += red[(v - 1) * 64 + lane];
+            const int row = t * 16 + col;
+            if (row < M) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int tok = 4 * g + r;
+                    if (tok < N) {
+                        float *dst = y + static_cast<size_t>(tok) * M + row;
+                        *dst = cb == 0 ? acc[r] : *dst + acc[r];
+                    }
+                }
+            }
+        }
+    };
+
+    // Staging: 8 lanes per (token, super-block); load i of the 8 lanes reads
+    // the 128 bytes of sub-block i's activations 4i.. (one cache line per
+    // load and group), so lane l holds elements 32i + 4l .. +3 for i < 8.
+    // kStageRounds rounds of 64 pairs per batch of loads.
+    const int l8 = tid & 7;
+    f32x4 v[kStageRounds][8];
+    auto stage_load = [&](int p0, int pairs, int cb, int csz) {
+#pragma unroll
+        for (int rr = 0; rr < kStageRounds; rr++) {
+            const int p = p0 + rr * 8 * kMfmaWaves;
+            const int t = p / csz, sbl = p % csz;
+            const uint32_t off = p < pairs ? (static_cast<uint32_t>(t) * K + static_cast<uint32_t>(cb + sbl) * 256u +
+                                              4u * l8) * 4u
+                                           : kNoFetch;
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                v[rr][i] = __builtin_bit_cast(f32x4, load16<0>(xr, off == kNoFetch ? kNoFetch : off + 128u * i, 0));
+        }
+    };
+    auto stage_convert = [&](int p0, int pairs, int csz) {
+#pragma unroll
+        for (int rr = 0; rr < kStageRounds; rr++) {
+            const int p = p0 + rr * 8 * kMfmaWaves;
+            if (p < pairs) {
+                const int t = p / csz, sbl = p % csz;
+                float mx = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[rr][i].x), fabsf(v[rr][i].y)),
+                                         fmaxf(fabsf(v[rr][i].z), fabsf(v[rr][i].w))));
+                mx = max8(mx);
+                // Largest magnitude into [2^14, 2^15): scale by 2^(14 - floor(log2(mx))).
+                const int ex = static_cast<int>((__builtin_bit_cast(uint32_t, mx) >> 23) & 255u) - 127;
+                const int shift = mx == 0.0f ? 0 : 14 - ex;
+                uint8_t *dst = lds + L.xs + t * xrow + (sbl * 256 + 4 * l8) * 2;
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const f32x4 a = v[rr][i];
+                    const half2_t h01 = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.x, shift)),
+                                         static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.y, shift))};
+                    const half2_t h23 = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.z, shift)),
+                                         static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.w, shift))};
+                    *reinterpret_cast<u32x2 *>(dst + 64 * i) =
+                        u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+                }
+                if (l8 == 0)
+                    *reinterpret_cast<float *>(lds + L.scl + (sbl * 16 + t) * 4) = __builtin_amdgcn_ldexpf(1.0f, -shift);
+            }
+        }
+    };
+
+    Set sa, sb;
+    for (int cb = 0; cb < ns; cb += CS) {
+        const int csz = ns - cb < CS ? ns - cb : CS;
+        // This wave's share of the chunk: super-blocks [s0, s0 + nsb).
+        const int s0 = cb + wave * csz / kMfmaWaves, nsb = cb + (wave + 1) * csz / kMfmaWaves - s0;
+        const int pairs = N * csz;
+        const int p0 = tid >> 3;
+        if (cb > 0) __syncthreads();  // every wave is done with the previous chunk's activations
+        // The first staging batch's loads go out ahead of the first tile's
+        // weights: its conversion then waits for them alone, while the
+        // weights' longer trip from HBM overlaps the staging.
+        stage_load(p0, pairs, cb, csz);
+        load(sa, t0, s0, nsb, t1);
+        stage_convert(p0, pairs, csz);
+        for (int q = p0 + 8 * kMfmaWaves * kStageRounds; q < pairs; q += 8 * kMfmaWaves * kStageRounds) {
+            stage_load(q, pairs, cb, csz);
+            stage_convert(q, pairs, csz);
+        }
+        for (int i = tid; i < 16 * csz; i += 64 * kMfmaWaves)
+            if (i % 16 >= N) *reinterpret_cast<float *>(lds + L.scl + i * 4) = 0.0f;
+        __syncthreads();
+
+        // ---- the tiles, two register sets: the next tile's loads in flight
+        for (int t = t0; t < t1; t += 2) {
+            load(sb, t + 1, s0, nsb, t1);
+            tile(sa, t, s0, nsb, cb);
+            load(sa, t + 2, s0, nsb, t1);
+            if (t + 1 < t1) tile(sb, t + 1, s0, nsb, cb);
+        }
+    }
+}
+
+template <int N, int SBW>
+int launch_mfma_sbw(const uint8_t *w, const float *x, float *y, int m, int k, int cs, size_t lds, int budget,
+                    hipStream_t s, int cus, int groups_per_cu)
+{
+    if (lds > static_cast<size_t>(kMaxLdsBytes)) {
+        static std::atomic<int> opted[64];
+        int dev = 0;
+        if (hip_status(hipGetDevice(&dev)) != Q4_OK) return Q4_EHIP;
+        if (dev < 0 || dev >= 64) return Q4_EUNSUPPORTED;
+        if (!opted[dev].load(std::memory_order_acquire)) {
+            const int st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_q4k_kernel<N, SBW>),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize, budget));
+            if (st != Q4_OK) return st;
+            opted[dev].store(1, std::memory_order_release);
+        }
+    }
+    const int tiles = (m + 15) / 16;
+    const int cap = cus * (groups_per_cu > 0 ? groups_per_cu : 1);
+    const unsigned grid = static_cast<unsigned>(tiles < cap ? tiles : cap);
+    const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(Q4_FMT_Q4_K, m, k));
+    hipLaunchKernelGGL((mfma_q4k_kernel<N, SBW>), dim3(grid), dim3(64 * kMfmaWaves), lds, s, w, wbytes, x, y, m, k, cs);
+    return hip_status(hipGetLastError());
+}
+
+template <int N>
+int launch_mfma(const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus, int groups_per_cu)
+{
+    const int ns = k / 256;
+    // Chunks of at most 8 kMfmaSbMax super-blocks (four per wave per tile)
+    // whose staged activations fit the LDS (the opt-in size above 64 KiB).
+    int budget = kMaxLdsBytes;
+    const int optin = device_lds_optin();
+    int cs = ns < kMfmaWaves * kMfmaSbMax ? ns : kMfmaWaves * kMfmaSbMax;
+    if (mfma_lds(N, cs).total > static_cast<uint32_t>(budget) && optin > budget) budget = optin;
+    while (cs > 1 && mfma_lds(N, cs).total > static_cast<uint32_t>(budget)) cs--;
+    if (mfma_lds(N, cs).total > static_cast<uint32_t>(budget)) return Q4_EUNSUPPORTED;
+    const int chunks = (ns + cs - 1) / cs;
+    cs = (ns + chunks - 1) / chunks;  // even chunks
+    const size_t lds = mfma_lds(N, cs).total;
+    // Super-blocks per wave and tile: the chunk split over the 8 waves.
+    switch ((cs + kMfmaWaves - 1) / kMfmaWaves) {
+    case 1: return launch_mfma_sbw<N, 1>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
+    case 2: return launch_mfma_sbw<N, 2>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
+    case 3: return launch_mfma_sbw<N, 3>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
+    default: return launch_mfma_sbw<N, 4>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
+    }
+}
+
+int dispatch_mfma(const uint8_t *w, const float *x, float *y, int m, int k, int n, hipStream_t s, int cus,
+                  int groups_per_cu)
+{
+    switch (n) {
+    case 1: return launch_mfma<1>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 2: return launch_mfma<2>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 3: return launch_mfma<3>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 4: return launch_mfma<4>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 5: return launch_mfma<5>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 6: return launch_mfma<6>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 7: return launch_mfma<7>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 8: return launch_mfma<8>(w, x, y, m, k, s, cus, groups_per_cu);
+    default: return Q4_EUNSUPPORTED;
+    }
+}
+
+}  // namespace gemv
+}  // namespace q4

@@ -68,14 +68,16 @@ int launch_gemv_addnorm(int fmt, const void *w, const float *x, const Prologue &
 
 namespace gemv {
 
-// Geometry of a decode launch: the tiled kernel (depth == 0) or the
-// one-token streaming kernel (depth > 0: slots in flight per lane; r == 1).
+// Geometry of a decode launch: the tiled kernel (depth == 0), the one-token
+// streaming kernel (depth > 0: slots in flight per lane; r == 1), or the
+// several-token Q4_K matrix-core kernel (matrix; only groups_per_cu applies).
 struct Cfg {
     int lpr;            // lanes per row: 8, 16, 32 or 64
     int r;              // rows per lane
     int waves;          // waves per workgroup
     int groups_per_cu;  // workgroups per compute unit the grid is sized for
     int depth = 0;      // streaming kernel: weight slots in flight per lane
+    bool matrix = false;
 };
 
 struct FmtQ4_0;
@@ -95,6 +97,11 @@ int dispatch_norm_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, 
 // Defined in q4_gemv_stream.hip: the one-token streaming kernel.
 template <class F>
 int dispatch_stream(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus);
+
+// Defined in q4_gemv_mfma.hip: the Q4_K decode product on matrix cores, any
+// token count 1..8.
+int dispatch_mfma(const uint8_t *w, const float *x, float *y, int m, int k, int n, hipStream_t s, int cus,
+                  int groups_per_cu);
 
 // Longest row (in 32-weight units) the streaming kernel takes: the whole row
 // is staged once per workgroup in its LDS (144 bytes per unit, 64 KiB).

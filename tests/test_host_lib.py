@@ -244,12 +244,23 @@ def test_tuned_argument_errors(q4):
     assert f(0, None, None, None, 0, 256, 1, ctypes.byref(good), None) == q4.Q4_OK
     # kernel and depth fields: negative or unknown values are refused, and the
     # streaming kernel takes one token only.
-    for t in (q4.q4_gemv_tuning(0, 0, 0, 0, -1, 0), q4.q4_gemv_tuning(0, 0, 0, 0, 3, 0),
+    for t in (q4.q4_gemv_tuning(0, 0, 0, 0, -1, 0), q4.q4_gemv_tuning(0, 0, 0, 0, 4, 0),
               q4.q4_gemv_tuning(0, 0, 0, 0, 2, -1)):
         assert f(0, *ok, 64, 256, 1, ctypes.byref(t), None) == q4.Q4_EINVAL
     stream = q4.q4_gemv_tuning(0, 0, 0, 0, q4.Q4_GEMV_KERNEL_STREAM, 0)
     assert f(0, *ok, 64, 256, 2, ctypes.byref(stream), None) == q4.Q4_EUNSUPPORTED
     assert f(0, None, None, None, 0, 256, 1, ctypes.byref(stream), None) == q4.Q4_OK
+    # The matrix-core kernel: Q4_K only, and groups_per_cu its only geometry field.
+    matrix = q4.q4_gemv_tuning(0, 0, 0, 0, q4.Q4_GEMV_KERNEL_MATRIX, 0)
+    assert f(0, *ok, 64, 256, 4, ctypes.byref(matrix), None) == q4.Q4_EUNSUPPORTED
+    for t in (q4.q4_gemv_tuning(32, 0, 0, 0, q4.Q4_GEMV_KERNEL_MATRIX, 0),
+              q4.q4_gemv_tuning(0, 2, 0, 0, q4.Q4_GEMV_KERNEL_MATRIX, 0),
+              q4.q4_gemv_tuning(0, 0, 8, 0, q4.Q4_GEMV_KERNEL_MATRIX, 0),
+              q4.q4_gemv_tuning(0, 0, 0, 0, q4.Q4_GEMV_KERNEL_MATRIX, 2)):
+        assert f(1, *ok, 64, 256, 4, ctypes.byref(t), None) == q4.Q4_EUNSUPPORTED
+    assert f(1, None, None, None, 0, 256, 4, ctypes.byref(matrix), None) == q4.Q4_OK
+    assert f(1, None, None, None, 0, 256, 4,
+             ctypes.byref(q4.q4_gemv_tuning(0, 0, 0, 2, q4.Q4_GEMV_KERNEL_MATRIX, 0)), None) == q4.Q4_OK
 
 
 def test_gemm_tuned_argument_errors(q4):
@@ -339,6 +350,8 @@ def test_addnorm_tuned_argument_errors(q4):
     assert f(0, None, None, None, None, 1e-5, None, None, 0, 256, 0, ctypes.byref(ok), None) == q4.Q4_OK
     stream = q4.q4_gemv_tuning(0, 0, 0, 0, q4.Q4_GEMV_KERNEL_STREAM, 0)  # the fused norm is tiled only
     assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 256, 0, ctypes.byref(stream), None) == q4.Q4_EUNSUPPORTED
+    matrix = q4.q4_gemv_tuning(0, 0, 0, 0, q4.Q4_GEMV_KERNEL_MATRIX, 0)
+    assert f(1, W, X, D, G, 1e-5, XO, Y, 64, 256, 0, ctypes.byref(matrix), None) == q4.Q4_EUNSUPPORTED
     unknown = q4.q4_gemv_tuning(0, 0, 0, 0, 5, 0)
     assert f(0, W, X, D, G, 1e-5, XO, Y, 64, 256, 0, ctypes.byref(unknown), None) == q4.Q4_EINVAL
 
