@@ -355,6 +355,73 @@ def sweep_one_token(torch, q4, timer, reps=10, out=None):
             torch.cuda.empty_cache()
 
 
+def sweep_tokens(torch, q4, timer, reps=10):
+    """Q4_K decode products at 2..8 tokens: the tiled kernel (the library's
+    tiled choice) against the matrix-core kernel (one and two workgroups per
+    compute unit) and the library's default, cold, at the 7B-class shapes and
+    two others (short and long rows). One JSON line per measurement (the
+    evidence behind the library's choice of kernel)."""
+    import synth
+
+    shapes = sorted(set(synth.llama7b_layer())) + [(2048, 8192), (8192, 2048)]
+    s = torch.cuda.Stream()
+    for k, m in shapes:
+        wq = q4.q4_quantize_ref(1, synth.weights(synth.seed_for(6, k + m), m, k))
+        copies = [torch.from_numpy(wq).cuda() for _ in range(copies_for(wq.size))]
+        for n in range(2, 9):
+            x = torch.from_numpy(synth.activations(synth.seed_for(6, k + n, True), n, k)).cuda()
+            y = torch.empty((n, m), device="cuda")
+            nb = gemv_bytes(q4, 1, m, k, n)
+            for label, kw in (("tiled", dict(kernel=q4.Q4_GEMV_KERNEL_TILED)),
+                              ("matrix G1", dict(kernel=q4.Q4_GEMV_KERNEL_MATRIX, groups_per_cu=1)),
+                              ("matrix G2", dict(kernel=q4.Q4_GEMV_KERNEL_MATRIX, groups_per_cu=2)),
+                              ("library", dict())):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.stream(s):
+                    q4.q4_gemv_tuned(1, copies[0], x, y, m, k, stream=s, **kw)
+                    torch.cuda.synchronize()
+                    with torch.cuda.graph(g, stream=s):
+                        for c in copies:
+                            q4.q4_gemv_tuned(1, c, x, y, m, k, stream=s, **kw)
+                t = timer.region(lambda i: g.replay(), reps, 2) / (reps * len(copies))
+                del g
+                print(json.dumps({"format": "q4_k", "shape": f"{k}->{m}", "tokens": n, "kernel": label,
+                                  "us": round(t * 1e6, 3), "pct_peak": round(100 * nb / t / 1e9 / HBM_PEAK_GBS, 2)}),
+                      flush=True)
+        del copies
+        torch.cuda.empty_cache()
+
+
+def sweep_gemm(torch, q4, timer, n=512, reps=10):
+    """Every instantiated prefill tile against the library's choice at the
+    SmolLM2-360M layer shapes x 512 tokens, Q4_0 (graphs of 20 launches per
+    tile). One JSON line per measurement."""
+    import synth
+
+    s = torch.cuda.Stream()
+    for k, m in sorted(set(synth.smollm2_360m_layer())):
+        wq = torch.from_numpy(q4.q4_quantize_ref(0, synth.weights(synth.seed_for(7, k + m), m, k))).cuda()
+        xb = torch.from_numpy(synth.bf16_bits(synth.activations(synth.seed_for(7, k, True), n, k)).view(np.int16)).cuda()
+        y = torch.empty((n, m), device="cuda")
+        for label, tile in [("library", None)] + [(f"{t[0]}x{t[1]}x{t[2]}", t) for t in q4.GEMM_TILES]:
+            def launch():
+                if tile is None:
+                    q4.q4_gemm(0, wq, xb, y, m, k, stream=s)
+                else:
+                    q4.q4_gemm_tuned(0, wq, xb, y, m, k, tile[0], tile[1], tile[2], stream=s)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                launch()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=s):
+                    for _ in range(20):
+                        launch()
+            t = timer.region(lambda i: g.replay(), reps, 2) / (reps * 20)
+            del g
+            print(json.dumps({"format": "q4_0", "shape": f"{k}->{m}", "tokens": n, "tile": label,
+                              "us": round(t * 1e6, 3), "TFLOP_s": round(2 * n * m * k / t / 1e12, 1)}), flush=True)
+
+
 def bench_gemm(torch, q4, timer, n=512, reps=20, shapes=None, per_matrix=True):
     """Prefill GEMM over the SmolLM2-360M layer's matrices at 512 tokens:
     one graph of the launches, replayed (weights 5.5 MB, L2/MALL-resident);
@@ -516,6 +583,10 @@ def main():
                     help="K,M: run only this Q4_0 one-token product, cold, --steps graph replays (for rocprofv3)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every one-token geometry at the workload shapes (one JSON line each) and exit")
+    ap.add_argument("--sweep-tokens", action="store_true",
+                    help="time the tiled and matrix-core kernels for Q4_K at 2..8 tokens (JSON lines), then exit")
+    ap.add_argument("--sweep-gemm", action="store_true",
+                    help="time every prefill tile at the SmolLM2-360M layer x 512 tokens (JSON lines), then exit")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 64 MiB device copy (torch) once, as the reference for HBM byte counters")
     args = ap.parse_args()
@@ -549,6 +620,12 @@ def main():
 
     if args.sweep:
         sweep_one_token(torch, q4, timer)
+        return
+    if args.sweep_tokens:
+        sweep_tokens(torch, q4, timer)
+        return
+    if args.sweep_gemm:
+        sweep_gemm(torch, q4, timer)
         return
 
     if args.profile_shape:
@@ -585,6 +662,11 @@ def main():
         nb = gemv_bytes(q4, 0, m, k, 1)
         per_shape[f"{k}to{m}"] = {"us": round(tp * 1e6, 3), "GB_s": round(nb / tp / 1e9, 1),
                                   "pct_peak": round(100 * nb / tp / 1e9 / HBM_PEAK_GBS, 1)}
+        # the committed kernel trace of this shape (one process per shape), if current
+        med = trace_median_from_profile(os.path.join(ROOT, "profiles", f"trace_gemv_q4_0_{k}x{m}.md"))
+        if med is not None:
+            per_shape[f"{k}to{m}"]["trace_median_us"] = med
+            per_shape[f"{k}to{m}"]["trace_pct_peak"] = round(100 * nb / (med * 1e3) / HBM_PEAK_GBS, 1)
     traffic = traffic_from_profile()
     median_us = trace_median_from_profile()
     log(f"dominant {dk}->{dm}: {t_dom * 1e6:.3f} us/launch, {achieved:.1f} GB/s")

@@ -39,8 +39,9 @@
 //     scaled activation is held as an unevaluated sum hi + lo of two fp16
 //     values (lo = fp16(x - hi)), about 2^-23 relative, so every product term
 //     is as accurate as fp32 arithmetic (the second half costs a second dot2
-//     per pair); taller products keep hi only (2^-12 relative per activation,
-//     so each output is within 2^-12 * sum_k |w_ik x_k|), which halves the dot
+//     per pair); taller products keep hi only (round to nearest: at most
+//     2^-11 relative per activation, so each output is within
+//     2^-11 * sum_k |w_ik x_k| plus the fp32 sums' rounding), which halves the dot
 //     issues, the activation LDS reads and most of the staging work.
 //   * Workgroups of one wave for short rows need no s_barrier (LDS order
 //     within a wave suffices); longer rows share the staging across 4 waves.
@@ -1178,7 +1179,7 @@ int launch_one(const uint8_t *w, const float *x, float *y, int m, int k, hipStre
     const int64_t wrows = GLU ? 2 * static_cast<int64_t>(m) : m;
     const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(F::kFormat, wrows, k));
     // Activations as hi + lo fp16 pairs (about 2^-23 relative) for short
-    // matrices, as one fp16 each (2^-12 relative, half the dot issues, LDS
+    // matrices, as one fp16 each (2^-11 relative, half the dot issues, LDS
     // reads and staging work) once there are kLoRowLimit rows or more
     // (weight rows: a gated product rounds like the plain product of its
     // stacked matrix).
