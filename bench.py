@@ -198,6 +198,25 @@ def trace_median_from_profile(path=None):
                           "median_us")
 
 
+def gemm_mfma_busy_from_profile(path=None):
+    """MFMA busy (% of the dense bf16 rate) per prefill matrix of the SmolLM2
+    layer, from the committed counter summary, if it was taken on the current
+    prefill source (else None)."""
+    path = path or os.path.join(ROOT, "profiles", "gemm_smollm2_layer_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256:\s*(\w+)", text)
+    with open(os.path.join(ROOT, "q4_weight_gemv_amd", "csrc", "q4_gemm.hip"), "rb") as fh:
+        cur = hashlib.sha256(fh.read()).hexdigest()[:16]
+    if not m or m.group(1) != cur:
+        return None
+    out = {}
+    for k, mm, pct in re.findall(r"^\| (\d+)->(\d+) [^|]*(?:\\\|[^|]*)*\|.*?\| ([0-9.]+) % \|", text, re.M):
+        out[f"{k}to{mm}"] = float(pct)
+    return out or None
+
+
 def host_cpu():
     """(cores this process may run on, CPU model) of the host."""
     try:
@@ -774,6 +793,9 @@ def main():
             extras["smollm2_full_decode_step"] = bench_full_step(torch, q4, timer)
         if on("gemm"):
             extras["gemm_smollm2_layer"] = bench_gemm(torch, q4, timer, reps=max(2, K // 50))
+            busy = gemm_mfma_busy_from_profile()
+            if busy is not None:
+                extras["gemm_smollm2_layer"]["mfma_busy_pct_by_counters"] = busy
             extras["gemm_smollm2_layer_fused_qkv_gateup"] = bench_gemm(
                 torch, q4, timer, reps=max(2, K // 50), shapes=synth.smollm2_360m_layer_stacked(),
                 per_matrix=False)
