@@ -278,17 +278,20 @@ def cpu_baseline(step, what, budget_s=10.0, budget_1core_s=6.0):
     }
 
 
-def product_time(torch, q4, timer, fmt, k, m, n=1, reps=20, seed_config=4):
+def product_time(torch, q4, timer, fmt, k, m, n=1, reps=20, seed_config=4, gated=False):
     """Average launch time (s) of one decode product, cold: a graph of one
     launch per rotating weight copy, replayed, timed with HIP events on the
-    stream the graph is launched on."""
+    stream the graph is launched on. gated: the gated product of a 2m-row
+    matrix (m outputs)."""
     import synth
 
-    wq = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(seed_config, k + m), m, k))
+    rows = 2 * m if gated else m
+    wq = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(seed_config, k + rows), rows, k))
     copies = [torch.from_numpy(wq).cuda() for _ in range(copies_for(wq.size))]
     x = torch.from_numpy(synth.activations(synth.seed_for(seed_config, k, True), n, k)).cuda()
     y = torch.empty((n, m), device="cuda")
-    g = q4.Q4Graph(fmt, [(c, x, y, m, k) for c in copies], n)
+    ep = q4.Q4_EPILOGUE_SILU_MUL if gated else q4.Q4_EPILOGUE_NONE
+    g = q4.Q4Graph(fmt, [(c, x, y, m, k, ep) for c in copies], n)
     t = timer.region(lambda i: g.launch(), reps, 3) / (reps * len(copies))
     g.close()
     del copies
@@ -324,6 +327,17 @@ def bench_7b(torch, q4, timer, reps=20):
         out[key] = {"us": round(layer_t * 1e6, 2), "GB_s": round(layer_b / layer_t / 1e9, 1),
                     "pct_peak": round(100 * layer_b / layer_t / 1e9 / HBM_PEAK_GBS, 1),
                     "note": "sum of the products' separate per-launch times"}
+        torch.cuda.empty_cache()
+    # The gate and up projections as one gated product (4096 -> 2 x 11008,
+    # silu(g) * u): Q4_0 at one token, Q4_K at 1, 4 and 8.
+    for fmt, ns in ((0, (1,)), (1, (1, 4, 8))):
+        for n in ns:
+            t = product_time(torch, q4, timer, fmt, 4096, 11008, n, reps, gated=True)
+            nb = gemv_bytes(q4, fmt, 11008, 4096, n, gated=1)
+            key = f"{name[fmt]}_gated_4096to2x11008_n{n}"
+            out[key] = {"us": round(t * 1e6, 3), "GB_s": round(nb / t / 1e9, 1),
+                        "pct_peak": round(100 * nb / t / 1e9 / HBM_PEAK_GBS, 1)}
+            log(f"{key}: {t * 1e6:.2f} us {nb / t / 1e9:.0f} GB/s")
         torch.cuda.empty_cache()
     return out
 

@@ -174,9 +174,11 @@ int q4_gemv(int fmt, const void *w, const float *x, float *y,
  * i < m:
  *   y[t][i] = silu(g) * u,  g = sum_k w_hat[i][k] x[t][k],
  *   u = sum_k w_hat[m+i][k] x[t][k],  silu(g) = g / (1 + exp(-g)).
- * g and u are summed exactly as the tiled kernel of q4_gemv sums the rows of
- * the stacked matrix (q4_gemv_tuned with Q4_GEMV_KERNEL_TILED: same
- * arithmetic, same tolerance); the epilogue is fp32. x [n][k] and y [n][m]
+ * g and u are summed exactly as q4_gemv_tuned sums the rows of the stacked
+ * matrix with the kernel the gated product shares (same arithmetic, same
+ * tolerance): the matrix-core kernel for Q4_K where q4_gemv would pick it for
+ * the stacked matrix and the row has at most 4096 weights, else the tiled
+ * kernel (Q4_GEMV_KERNEL_TILED); the epilogue is fp32. x [n][k] and y [n][m]
  * are device arrays, n is 1..8. Errors as q4_gemv, with the size limits
  * applying to the 2m-row matrix (m below 2^29). */
 int q4_gemv_glu(int fmt, const void *w, const float *x, float *y,

@@ -176,6 +176,13 @@ Cfg choose_tiled(int fmt, int64_t m, int64_t k, int64_t n, int cus);
 
 Cfg choose_glu(int fmt, int64_t m, int64_t k, int64_t n, int cus)
 {
+    // The matrix-core kernel where the plain product of the stacked matrix
+    // would take it and the row fits its gated form (16 super-blocks).
+    if (use_matrix(fmt, 2 * m, k, n) && k <= 4096) {
+        Cfg c{0, 0, 0, 1};
+        c.matrix = true;
+        return c;
+    }
     const Cfg c = choose_tiled(fmt, 2 * m, k, n, cus);
     const bool one_wave = c.waves == 1;
     if (c.lpr <= 16) return one_wave ? Cfg{16, 2, 1, 8} : Cfg{16, 2, 4, 4};
@@ -194,9 +201,9 @@ int dispatch(int fmt, const Cfg &c, const void *w, const float *x, float *y, int
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int mi = static_cast<int>(m), ki = static_cast<int>(k);
     if (c.matrix) {
-        // The matrix-core kernel: Q4_K, plain product.
-        if (glu || fmt != Q4_FMT_Q4_K) return Q4_EUNSUPPORTED;
-        return dispatch_mfma(wb, x, y, mi, ki, static_cast<int>(n), s, cus, c.groups_per_cu);
+        // The matrix-core kernel: Q4_K, plain or gated.
+        if (fmt != Q4_FMT_Q4_K) return Q4_EUNSUPPORTED;
+        return dispatch_mfma(wb, x, y, mi, ki, static_cast<int>(n), s, cus, c.groups_per_cu, glu);
     }
     if (c.depth > 0) {
         // The streaming kernel: one token, plain product, the whole row staged.

@@ -31,6 +31,11 @@
 // and the D lane's weight row is its own B row: d, dmin and the scales come
 // from the header it loaded.
 //
+// The gated product (silu(W_gate x) * (W_up x), gate rows then up rows of
+// one 2M-row matrix) runs the same way with a gate and an up row per lane,
+// sharing the activation fragments, and applies the epilogue in fp32; its
+// g and u are the stacked matrix's rows as the plain form sums them.
+//
 // Work: one workgroup of 8 waves per compute unit owns a contiguous range of
 // 16-row tiles and stages the activations once (in chunks of super-blocks
 // when a long row exceeds the LDS). The 8 waves split every tile's
@@ -92,27 +97,31 @@ __device__ __forceinline__ float max8(float v)
 // LDS of a chunk of CS super-blocks:
 //   xs:  [n][CS*256] fp16, rows padded by kXRowPad bytes
 //   scl: [CS][16] fp32 2^e (zero for token slots n..15)
-//   red: [2 tiles][7 waves][64 lanes] f32x4, the waves' sums of a tile
+//   red: [2 tiles][gate, up][7 waves][64 lanes] f32x4, the waves' sums of a tile
 struct MfmaLds {
     uint32_t xs, scl, red, total;
 };
 
-__host__ __device__ inline MfmaLds mfma_lds(int n, int cs)
+__host__ __device__ inline MfmaLds mfma_lds(int n, int cs, bool glu = false)
 {
     MfmaLds l;
     l.xs = 0;
     l.scl = static_cast<uint32_t>(n) * (static_cast<uint32_t>(cs) * 512u + kXRowPad);
     l.red = l.scl + static_cast<uint32_t>(cs) * 64u;
-    l.total = l.red + 2u * (kMfmaWaves - 1) * 64u * 16u;
+    l.total = l.red + 2u * (glu ? 2u : 1u) * (kMfmaWaves - 1) * 64u * 16u;
     return l;
 }
 
-template <int N, int SBW>
+// GLU: the gated product. The weights have 2M rows (gate rows, then up
+// rows); each tile's lanes load gate row r and up row M + r, the same
+// activation fragments feed both, and y = silu(g) * u (one chunk only).
+template <int N, int SBW, bool GLU>
 __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t *__restrict__ w, uint32_t wbytes,
                                                                    const float *__restrict__ x, float *__restrict__ y,
                                                                    int M, int K, int CS)
 {
     static_assert(N >= 1 && N <= 16 && SBW >= 1 && SBW <= kMfmaSbMax, "shape");
+    constexpr int NR = GLU ? 2 : 1;  // weight rows per output row
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -120,7 +129,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, col = lane & 15;
     const int ns = K / 256;
-    const MfmaLds L = mfma_lds(N, CS);
+    const MfmaLds L = mfma_lds(N, CS, GLU);
     const uint32_t xrow = static_cast<uint32_t>(CS) * 512u + kXRowPad;
     const int tiles = (M + 15) / 16;
     const int t0 = static_cast<int>(static_cast<int64_t>(blockIdx.x) * tiles / gridDim.x);
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     const uint32_t xa = static_cast<uint32_t>(col < N ? col : 0) * xrow + 128u * g;
 
     struct Set {
-        u32x4 hd[SBW], q0[SBW], q1[SBW];
+        u32x4 hd[NR][SBW], q0[NR][SBW], q1[NR][SBW];
     };
     // Super-blocks [s0, s0 + nsb) of tile t's row for this lane. Every one of
     // the SBW slots issues its loads (slots past nsb, rows past M and tiles
@@ -142,71 +151,113 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     auto load = [&](Set &st, int t, int s0, int nsb, int t1) {
         const int row = t * 16 + col;
         const bool live = t < t1 && row < M;
-        const uint32_t base = static_cast<uint32_t>(row) * row_bytes;
 #pragma unroll
-        for (int i = 0; i < SBW; i++) {
-            const bool on = live && i < nsb;
-            const uint32_t sbo = uniform(static_cast<uint32_t>(s0 + (i < nsb ? i : 0)) * kSbBytes);
-            st.hd[i] = load16<0>(wr, on ? base : kNoFetch, sbo);
-            st.q0[i] = load16<kNonTemporal>(wr, on ? base + 16u + 32u * g : kNoFetch, sbo);
-            st.q1[i] = load16<kNonTemporal>(wr, on ? base + 32u + 32u * g : kNoFetch, sbo);
+        for (int w = 0; w < NR; w++) {
+            const uint32_t base = static_cast<uint32_t>(row + w * M) * row_bytes;
+#pragma unroll
+            for (int i = 0; i < SBW; i++) {
+                const bool on = live && i < nsb;
+                const uint32_t sbo = uniform(static_cast<uint32_t>(s0 + (i < nsb ? i : 0)) * kSbBytes);
+                st.hd[w][i] = load16<0>(wr, on ? base : kNoFetch, sbo);
+                st.q0[w][i] = load16<kNonTemporal>(wr, on ? base + 16u + 32u * g : kNoFetch, sbo);
+                st.q1[w][i] = load16<kNonTemporal>(wr, on ? base + 32u + 32u * g : kNoFetch, sbo);
+            }
         }
     };
     // Tile t over the chunk's super-blocks [s0, s0 + nsb) (cb: the chunk's
     // first super-block): this wave's sums, then the workgroup's in wave
     // order; wave 0 writes y (first chunk) or adds to it (later chunks).
+    // One weight row's super-block decoded for the MFMAs: code scales and
+    // offsets of its two sub-blocks, their mins broadcast, d and dmin.
+    struct Dec {
+        half2_t sc_a, off_a, sc_b, off_b;
+        half8 bm_a, bm_b;
+        float d, dmin;
+    };
+    auto decode = [&](const u32x4 &h) {
+        // Sub-blocks 2g and 2g+1: their 6-bit fields sit in bytes
+        // 2(g&1) and 2(g&1)+1 of the scale words.
+        const uint32_t sh = (g & 1) << 4;
+        const bool upper = g >= 2;
+        const uint32_t w0 = h.y >> sh, w1 = h.z >> sh, w2 = h.w >> sh;
+        const uint32_t sca = upper ? ((w2 & 15u) | (((w0 >> 6) & 3u) << 4)) : (w0 & 63u);
+        const uint32_t scb = upper ? (((w2 >> 8) & 15u) | (((w0 >> 14) & 3u) << 4)) : ((w0 >> 8) & 63u);
+        const uint32_t ma = upper ? (((w2 >> 4) & 15u) | (((w1 >> 6) & 3u) << 4)) : (w1 & 63u);
+        const uint32_t mb = upper ? (((w2 >> 12) & 15u) | (((w1 >> 14) & 3u) << 4)) : ((w1 >> 8) & 63u);
+        const _Float16 fa = static_cast<_Float16>(static_cast<float>(sca));
+        const _Float16 fb = static_cast<_Float16>(static_cast<float>(scb));
+        // Low nibbles: sc and -1024 sc; high nibbles in place: sc/16 and -64 sc.
+        const _Float16 fb16 = fb * static_cast<_Float16>(0.0625f);
+        const _Float16 oa = fa * static_cast<_Float16>(-1024.0f), ob = fb * static_cast<_Float16>(-64.0f);
+        const _Float16 ha = static_cast<_Float16>(static_cast<float>(ma));
+        const _Float16 hb = static_cast<_Float16>(static_cast<float>(mb));
+        Dec e;
+        e.sc_a = half2_t{fa, fa};
+        e.off_a = half2_t{oa, oa};
+        e.sc_b = half2_t{fb16, fb16};
+        e.off_b = half2_t{ob, ob};
+        e.bm_a = half8{ha, ha, ha, ha, ha, ha, ha, ha};
+        e.bm_b = half8{hb, hb, hb, hb, hb, hb, hb, hb};
+        e.d = half_lo(h.x);
+        e.dmin = half_hi(h.x);
+        return e;
+    };
+    // Tile t over the chunk's super-blocks [s0, s0 + nsb) (cb: the chunk's
+    // first super-block): this wave's sums, then the workgroup's in wave
+    // order; wave 0 writes y (first chunk) or adds to it (later chunks).
     auto tile = [&](const Set &st, int t, int s0, int nsb, int cb) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 acc[NR];
+#pragma unroll
+        for (int w = 0; w < NR; w++) acc[w] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < SBW; i++) {
             if (i < nsb) {
                 const int sbl = s0 + i - cb;
-                const u32x4 h = st.hd[i];
-                // Sub-blocks 2g and 2g+1: their 6-bit fields sit in bytes
-                // 2(g&1) and 2(g&1)+1 of the scale words.
-                const uint32_t sh = (g & 1) << 4;
-                const bool upper = g >= 2;
-                const uint32_t w0 = h.y >> sh, w1 = h.z >> sh, w2 = h.w >> sh;
-                const uint32_t sca = upper ? ((w2 & 15u) | (((w0 >> 6) & 3u) << 4)) : (w0 & 63u);
-                const uint32_t scb = upper ? (((w2 >> 8) & 15u) | (((w0 >> 14) & 3u) << 4)) : ((w0 >> 8) & 63u);
-                const uint32_t ma = upper ? (((w2 >> 4) & 15u) | (((w1 >> 6) & 3u) << 4)) : (w1 & 63u);
-                const uint32_t mb = upper ? (((w2 >> 12) & 15u) | (((w1 >> 14) & 3u) << 4)) : ((w1 >> 8) & 63u);
-                const _Float16 fa = static_cast<_Float16>(static_cast<float>(sca));
-                const _Float16 fb = static_cast<_Float16>(static_cast<float>(scb));
-                // Low nibbles: sc and -1024 sc; high nibbles in place: sc/16 and -64 sc.
-                const _Float16 fb16 = fb * static_cast<_Float16>(0.0625f);
-                const _Float16 oa = fa * static_cast<_Float16>(-1024.0f), ob = fb * static_cast<_Float16>(-64.0f);
-                const half2_t sc_a = {fa, fa}, sc_b = {fb16, fb16};
-                const half2_t off_a = {oa, oa}, off_b = {ob, ob};
-                const _Float16 ha = static_cast<_Float16>(static_cast<float>(ma));
-                const _Float16 hb = static_cast<_Float16>(static_cast<float>(mb));
-                const half8 bm_a = half8{ha, ha, ha, ha, ha, ha, ha, ha}, bm_b = half8{hb, hb, hb, hb, hb, hb, hb, hb};
-                const uint32_t qw[8] = {st.q0[i].x, st.q0[i].y, st.q0[i].z, st.q0[i].w,
-                                        st.q1[i].x, st.q1[i].y, st.q1[i].z, st.q1[i].w};
+                Dec e[NR];
+                uint32_t qw[NR][8];
+#pragma unroll
+                for (int w = 0; w < NR; w++) {
+                    e[w] = decode(st.hd[w][i]);
+                    const u32x4 a0 = st.q0[w][i], a1 = st.q1[w][i];
+                    qw[w][0] = a0.x, qw[w][1] = a0.y, qw[w][2] = a0.z, qw[w][3] = a0.w;
+                    qw[w][4] = a1.x, qw[w][5] = a1.y, qw[w][6] = a1.z, qw[w][7] = a1.w;
+                }
                 const uint8_t *xp = lds + xa + static_cast<uint32_t>(sbl) * 512u;
-                f32x4 dq = {0.0f, 0.0f, 0.0f, 0.0f}, dm = {0.0f, 0.0f, 0.0f, 0.0f};
+                f32x4 dq[NR], dm[NR];
+#pragma unroll
+                for (int w = 0; w < NR; w++) dq[w] = dm[w] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
-                    const uint32_t qa = qw[2 * (j & 3)], qb = qw[2 * (j & 3) + 1];
-                    const half8 bw = j < 4 ? code8(qa & 0x0F0F0F0Fu, qb & 0x0F0F0F0Fu, sc_a, off_a)
-                                           : code8(qa & 0xF0F0F0F0u, qb & 0xF0F0F0F0u, sc_b, off_b);
                     const half8 ax = *reinterpret_cast<const half8 *>(xp + 2 * (32 * (j >> 2) + 8 * (j & 3)));
-                    dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bw, dq, 0, 0, 0);
-                    dm = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, j < 4 ? bm_a : bm_b, dm, 0, 0, 0);
+#pragma unroll
+                    for (int w = 0; w < NR; w++) {
+                        const uint32_t qa = qw[w][2 * (j & 3)], qb = qw[w][2 * (j & 3) + 1];
+                        const half8 bw = j < 4 ? code8(qa & 0x0F0F0F0Fu, qb & 0x0F0F0F0Fu, e[w].sc_a, e[w].off_a)
+                                               : code8(qa & 0xF0F0F0F0u, qb & 0xF0F0F0F0u, e[w].sc_b, e[w].off_b);
+                        dq[w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bw, dq[w], 0, 0, 0);
+                        dm[w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, j < 4 ? e[w].bm_a : e[w].bm_b, dm[w], 0, 0, 0);
+                    }
                 }
                 const f32x4 sc4 = *reinterpret_cast<const f32x4 *>(lds + L.scl + (sbl * 16 + 4 * g) * 4);
-                const float d = half_lo(h.x), dmin = half_hi(h.x);
 #pragma unroll
-                for (int r = 0; r < 4; r++)
-                    acc[r] = __builtin_fmaf(sc4[r], __builtin_fmaf(d, dq[r], -(dmin * dm[r])), acc[r]);
+                for (int w = 0; w < NR; w++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        acc[w][r] = __builtin_fmaf(sc4[r], __builtin_fmaf(e[w].d, dq[w][r], -(e[w].dmin * dm[w][r])),
+                                                   acc[w][r]);
             }
         }
-        f32x4 *red = reinterpret_cast<f32x4 *>(lds + L.red) + (t & 1) * (kMfmaWaves - 1) * 64;
-        if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
+        f32x4 *red = reinterpret_cast<f32x4 *>(lds + L.red) + (t & 1) * NR * (kMfmaWaves - 1) * 64;
+        if (wave > 0) {
+#pragma unroll
+            for (int w = 0; w < NR; w++) red[(w * (kMfmaWaves - 1) + wave - 1) * 64 + lane] = acc[w];
+        }
         __syncthreads();
         if (wave == 0) {
 #pragma unroll
-            for (int v = 1; v < kMfmaWaves; v++) acc += red[(v - 1) * 64 + lane];
+            for (int w = 0; w < NR; w++)
+#pragma unroll
+                for (int v = 1; v < kMfmaWaves; v++) acc[w] += red[(w * (kMfmaWaves - 1) + v - 1) * 64 + lane];
             const int row = t * 16 + col;
             if (row < M) {
 #pragma unroll
@@ -214,7 +265,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
                     const int tok = 4 * g + r;
                     if (tok < N) {
                         float *dst = y + static_cast<size_t>(tok) * M + row;
-                        *dst = cb == 0 ? acc[r] : *dst + acc[r];
+                        if constexpr (GLU)
+                            *dst = silu_mul(acc[0][r], acc[1][r]);
+                        else
+                            *dst = cb == 0 ? acc[0][r] : *dst + acc[0][r];
                     }
                 }
             }
@@ -304,17 +358,20 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     }
 }
 
-template <int N, int SBW>
+template <int N, int SBW, bool GLU>
 int launch_mfma_sbw(const uint8_t *w, const float *x, float *y, int m, int k, int cs, size_t lds, int budget,
                     hipStream_t s, int cus, int groups_per_cu)
 {
+    if constexpr (GLU && SBW > 2) {
+        return Q4_EUNSUPPORTED;  // the gated product keeps two rows' loads in flight: at most 2 per wave
+    } else {
     if (lds > static_cast<size_t>(kMaxLdsBytes)) {
         static std::atomic<int> opted[64];
         int dev = 0;
         if (hip_status(hipGetDevice(&dev)) != Q4_OK) return Q4_EHIP;
         if (dev < 0 || dev >= 64) return Q4_EUNSUPPORTED;
         if (!opted[dev].load(std::memory_order_acquire)) {
-            const int st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_q4k_kernel<N, SBW>),
+            const int st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_q4k_kernel<N, SBW, GLU>),
                                                           hipFuncAttributeMaxDynamicSharedMemorySize, budget));
             if (st != Q4_OK) return st;
             opted[dev].store(1, std::memory_order_release);
@@ -323,49 +380,62 @@ int launch_mfma_sbw(const uint8_t *w, const float *x, float *y, int m, int k, in
     const int tiles = (m + 15) / 16;
     const int cap = cus * (groups_per_cu > 0 ? groups_per_cu : 1);
     const unsigned grid = static_cast<unsigned>(tiles < cap ? tiles : cap);
-    const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(Q4_FMT_Q4_K, m, k));
-    hipLaunchKernelGGL((mfma_q4k_kernel<N, SBW>), dim3(grid), dim3(64 * kMfmaWaves), lds, s, w, wbytes, x, y, m, k, cs);
+    const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(Q4_FMT_Q4_K, GLU ? 2LL * m : m, k));
+    hipLaunchKernelGGL((mfma_q4k_kernel<N, SBW, GLU>), dim3(grid), dim3(64 * kMfmaWaves), lds, s, w, wbytes, x, y, m,
+                       k, cs);
     return hip_status(hipGetLastError());
+    }
 }
 
-template <int N>
+template <int N, bool GLU>
 int launch_mfma(const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus, int groups_per_cu)
 {
     const int ns = k / 256;
     // Chunks of at most 8 kMfmaSbMax super-blocks (four per wave per tile)
     // whose staged activations fit the LDS (the opt-in size above 64 KiB).
+    // The gated product takes rows of at most 16 super-blocks, in one chunk.
+    if (GLU && ns > 2 * kMfmaWaves) return Q4_EUNSUPPORTED;
     int budget = kMaxLdsBytes;
     const int optin = device_lds_optin();
     int cs = ns < kMfmaWaves * kMfmaSbMax ? ns : kMfmaWaves * kMfmaSbMax;
-    if (mfma_lds(N, cs).total > static_cast<uint32_t>(budget) && optin > budget) budget = optin;
-    while (cs > 1 && mfma_lds(N, cs).total > static_cast<uint32_t>(budget)) cs--;
-    if (mfma_lds(N, cs).total > static_cast<uint32_t>(budget)) return Q4_EUNSUPPORTED;
+    if (mfma_lds(N, cs, GLU).total > static_cast<uint32_t>(budget) && optin > budget) budget = optin;
+    while (cs > 1 && mfma_lds(N, cs, GLU).total > static_cast<uint32_t>(budget)) cs--;
+    if (mfma_lds(N, cs, GLU).total > static_cast<uint32_t>(budget)) return Q4_EUNSUPPORTED;
+    if (GLU && cs < ns) return Q4_EUNSUPPORTED;
     const int chunks = (ns + cs - 1) / cs;
     cs = (ns + chunks - 1) / chunks;  // even chunks
-    const size_t lds = mfma_lds(N, cs).total;
+    const size_t lds = mfma_lds(N, cs, GLU).total;
     // Super-blocks per wave and tile: the chunk split over the 8 waves.
     switch ((cs + kMfmaWaves - 1) / kMfmaWaves) {
-    case 1: return launch_mfma_sbw<N, 1>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
-    case 2: return launch_mfma_sbw<N, 2>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
-    case 3: return launch_mfma_sbw<N, 3>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
-    default: return launch_mfma_sbw<N, 4>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
+    case 1: return launch_mfma_sbw<N, 1, GLU>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
+    case 2: return launch_mfma_sbw<N, 2, GLU>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
+    case 3: return launch_mfma_sbw<N, 3, GLU>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
+    default: return launch_mfma_sbw<N, 4, GLU>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
+    }
+}
+
+template <bool GLU>
+int dispatch_mfma_glu(const uint8_t *w, const float *x, float *y, int m, int k, int n, hipStream_t s, int cus,
+                      int groups_per_cu)
+{
+    switch (n) {
+    case 1: return launch_mfma<1, GLU>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 2: return launch_mfma<2, GLU>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 3: return launch_mfma<3, GLU>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 4: return launch_mfma<4, GLU>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 5: return launch_mfma<5, GLU>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 6: return launch_mfma<6, GLU>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 7: return launch_mfma<7, GLU>(w, x, y, m, k, s, cus, groups_per_cu);
+    case 8: return launch_mfma<8, GLU>(w, x, y, m, k, s, cus, groups_per_cu);
+    default: return Q4_EUNSUPPORTED;
     }
 }
 
 int dispatch_mfma(const uint8_t *w, const float *x, float *y, int m, int k, int n, hipStream_t s, int cus,
-                  int groups_per_cu)
+                  int groups_per_cu, bool glu)
 {
-    switch (n) {
-    case 1: return launch_mfma<1>(w, x, y, m, k, s, cus, groups_per_cu);
-    case 2: return launch_mfma<2>(w, x, y, m, k, s, cus, groups_per_cu);
-    case 3: return launch_mfma<3>(w, x, y, m, k, s, cus, groups_per_cu);
-    case 4: return launch_mfma<4>(w, x, y, m, k, s, cus, groups_per_cu);
-    case 5: return launch_mfma<5>(w, x, y, m, k, s, cus, groups_per_cu);
-    case 6: return launch_mfma<6>(w, x, y, m, k, s, cus, groups_per_cu);
-    case 7: return launch_mfma<7>(w, x, y, m, k, s, cus, groups_per_cu);
-    case 8: return launch_mfma<8>(w, x, y, m, k, s, cus, groups_per_cu);
-    default: return Q4_EUNSUPPORTED;
-    }
+    return glu ? dispatch_mfma_glu<true>(w, x, y, m, k, n, s, cus, groups_per_cu)
+               : dispatch_mfma_glu<false>(w, x, y, m, k, n, s, cus, groups_per_cu);
 }
 
 }  // namespace gemv

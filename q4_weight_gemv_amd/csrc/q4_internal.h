@@ -99,9 +99,10 @@ template <class F>
 int dispatch_stream(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus);
 
 // Defined in q4_gemv_mfma.hip: the Q4_K decode product on matrix cores, any
-// token count 1..8.
+// token count 1..8; glu: the gated product of a 2m-row matrix (rows of at
+// most 4096 weights).
 int dispatch_mfma(const uint8_t *w, const float *x, float *y, int m, int k, int n, hipStream_t s, int cus,
-                  int groups_per_cu);
+                  int groups_per_cu, bool glu = false);
 
 // Longest row (in 32-weight units) the streaming kernel takes: the whole row
 // is staged once per workgroup in its LDS (144 bytes per unit, 64 KiB).

@@ -522,9 +522,20 @@ def _silu_mul64(g, u):
     return g / (1.0 + np.exp(-g)) * np.asarray(u, np.float64)
 
 
+def _glu_plain_kernel(q4, fmt, n, m, k):
+    """The kernel whose plain product of the stacked 2m-row matrix the gated
+    product reproduces (q4.h, q4_gemv_glu): the matrix-core kernel for Q4_K
+    where q4_gemv would pick it for the stacked matrix and the row has at most
+    4096 weights, else the tiled kernel."""
+    matrix = (fmt == 1 and 2 * m >= 256 and k <= 4096 and
+              (n >= 5 or (n == 4 and k <= 8192) or (n >= 2 and k <= 2048)))
+    return q4.Q4_GEMV_KERNEL_MATRIX if matrix else q4.Q4_GEMV_KERNEL_TILED
+
+
 GLU_CASES = [
     (0, 1, 37, 96), (0, 3, 130, 960), (0, 1, 1280, 960), (0, 8, 200, 2560), (0, 1, 300, 4096), (0, 2, 70, 11008),
     (1, 1, 37, 256), (1, 4, 130, 1024), (1, 1, 300, 4096), (1, 8, 90, 4096), (1, 1, 70, 11008),
+    (1, 2, 200, 2048), (1, 3, 130, 512), (1, 5, 300, 4096), (1, 8, 300, 4096),  # the matrix-core gated form
     (2, 1, 130, 960), (2, 4, 300, 4096),
     (3, 1, 130, 1024), (3, 4, 300, 4096),
     (4, 1, 130, 960), (4, 4, 300, 4096), (4, 1, 2560, 960),
@@ -542,12 +553,12 @@ def test_glu_matches_plain_product_of_stacked_matrix(env, fmt, n, m, k):
     buf = q4.q4_quantize_ref(fmt, synth.weights(synth.seed_for(1100 + fmt, m), 2 * m, k))
     x = synth.activations(synth.seed_for(1100 + fmt, m, True), n, k)
     say(f"glu vs plain fmt={fmt} n={n} m={m} k={k}")
-    # The plain product on the tiled kernel, which the gated product shares
-    # (one token of Q4_0 would otherwise take the streaming kernel).
+    # The plain product on the kernel the gated product shares (one token of
+    # Q4_0 would otherwise take the streaming kernel).
     wd = torch.from_numpy(buf).cuda()
     xd = torch.from_numpy(x).cuda()
     ypd = torch.full((n, 2 * m), float("nan"), dtype=torch.float32, device="cuda")
-    q4.q4_gemv_tuned(fmt, wd, xd, ypd, 2 * m, k, kernel=q4.Q4_GEMV_KERNEL_TILED)
+    q4.q4_gemv_tuned(fmt, wd, xd, ypd, 2 * m, k, kernel=_glu_plain_kernel(q4, fmt, n, m, k))
     torch.cuda.synchronize()
     yp = ypd.cpu().numpy()
     yg = _glu(env, fmt, buf, x, m, k)
