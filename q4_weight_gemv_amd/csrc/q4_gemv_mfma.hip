@@ -94,20 +94,22 @@ __device__ __forceinline__ float max8(float v)
     return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(d, d, 0x141, 0xF, 0xF, false)));
 }
 
-// LDS of a chunk of CS super-blocks:
-//   xs:  [n][CS*256] fp16, rows padded by kXRowPad bytes
-//   scl: [CS][16] fp32 2^e (zero for token slots n..15)
-//   red: [2 tiles][gate, up][7 waves][64 lanes] f32x4, the waves' sums of a tile
+// LDS. Wave v stages and reads its own columns v*SBW .. v*SBW + SBW - 1 (its
+// super-blocks of the current chunk), so no wave waits for another's staging:
+//   xs:  [n][8 SBW columns * 256] fp16, rows padded by kXRowPad bytes
+//   scl: [8 SBW columns][16] fp32 2^e (zero for token slots n..15)
+//   red: [2][gate, up][7 waves][64 lanes] f32x4, the waves' sums of a tile
 struct MfmaLds {
     uint32_t xs, scl, red, total;
 };
 
-__host__ __device__ inline MfmaLds mfma_lds(int n, int cs, bool glu = false)
+__host__ __device__ inline MfmaLds mfma_lds(int n, int sbw, bool glu = false)
 {
+    const uint32_t cols = static_cast<uint32_t>(kMfmaWaves) * static_cast<uint32_t>(sbw);
     MfmaLds l;
     l.xs = 0;
-    l.scl = static_cast<uint32_t>(n) * (static_cast<uint32_t>(cs) * 512u + kXRowPad);
-    l.red = l.scl + static_cast<uint32_t>(cs) * 64u;
+    l.scl = static_cast<uint32_t>(n) * (cols * 512u + kXRowPad);
+    l.red = l.scl + cols * 64u;
     l.total = l.red + 2u * (glu ? 2u : 1u) * (kMfmaWaves - 1) * 64u * 16u;
     return l;
 }
@@ -115,13 +117,15 @@ __host__ __device__ inline MfmaLds mfma_lds(int n, int cs, bool glu = false)
 // GLU: the gated product. The weights have 2M rows (gate rows, then up
 // rows); each tile's lanes load gate row r and up row M + r, the same
 // activation fragments feed both, and y = silu(g) * u (one chunk only).
-template <int N, int SBW, bool GLU>
+// ONE: every workgroup owns exactly one tile (the grid is the tile count).
+template <int N, int SBW, bool GLU, bool ONE>
 __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t *__restrict__ w, uint32_t wbytes,
                                                                    const float *__restrict__ x, float *__restrict__ y,
                                                                    int M, int K, int CS)
 {
     static_assert(N >= 1 && N <= 16 && SBW >= 1 && SBW <= kMfmaSbMax, "shape");
     constexpr int NR = GLU ? 2 : 1;  // weight rows per output row
+    constexpr uint32_t xrow = kMfmaWaves * SBW * 512u + kXRowPad;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -129,8 +133,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, col = lane & 15;
     const int ns = K / 256;
-    const MfmaLds L = mfma_lds(N, CS, GLU);
-    const uint32_t xrow = static_cast<uint32_t>(CS) * 512u + kXRowPad;
+    const MfmaLds L = mfma_lds(N, SBW, GLU);
+    const uint32_t wcol = static_cast<uint32_t>(wave) * SBW;  // this wave's first LDS column
     const int tiles = (M + 15) / 16;
     const int t0 = static_cast<int>(static_cast<int64_t>(blockIdx.x) * tiles / gridDim.x);
     const int t1 = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * tiles / gridDim.x);
@@ -139,16 +143,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
         make_rsrc(x, static_cast<uint32_t>(static_cast<uint64_t>(N) * static_cast<uint64_t>(K) * 4u));
     const uint32_t row_bytes = static_cast<uint32_t>(ns) * kSbBytes;
     // This lane's A row in LDS: token col (slots past n repeat token 0).
-    const uint32_t xa = static_cast<uint32_t>(col < N ? col : 0) * xrow + 128u * g;
+    const uint32_t xa = static_cast<uint32_t>(col < N ? col : 0) * xrow + wcol * 512u + 128u * g;
 
     struct Set {
         u32x4 hd[NR][SBW], q0[NR][SBW], q1[NR][SBW];
     };
     // Super-blocks [s0, s0 + nsb) of tile t's row for this lane. Every one of
     // the SBW slots issues its loads (slots past nsb, rows past M and tiles
-    // past t1 fetch nothing), so the number of loads in flight is the same on
-    // every path and each wait covers exactly the loads it needs.
-    auto load = [&](Set &st, int t, int s0, int nsb, int t1) {
+    // past t1 fetch nothing), so a set is always the same number of loads and
+    // each wait covers exactly the loads it needs.
+    auto load = [&](Set &st, int t, int s0, int nsb) {
         const int row = t * 16 + col;
         const bool live = t < t1 && row < M;
 #pragma unroll
@@ -164,9 +168,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
             }
         }
     };
-    // Tile t over the chunk's super-blocks [s0, s0 + nsb) (cb: the chunk's
-    // first super-block): this wave's sums, then the workgroup's in wave
-    // order; wave 0 writes y (first chunk) or adds to it (later chunks).
     // One weight row's super-block decoded for the MFMAs: code scales and
     // offsets of its two sub-blocks, their mins broadcast, d and dmin.
     struct Dec {
@@ -202,17 +203,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
         e.dmin = half_hi(h.x);
         return e;
     };
-    // Tile t over the chunk's super-blocks [s0, s0 + nsb) (cb: the chunk's
-    // first super-block): this wave's sums, then the workgroup's in wave
-    // order; wave 0 writes y (first chunk) or adds to it (later chunks).
-    auto tile = [&](const Set &st, int t, int s0, int nsb, int cb) {
-        f32x4 acc[NR];
-#pragma unroll
-        for (int w = 0; w < NR; w++) acc[w] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // This wave's sums over its nsb super-blocks of one tile (the set's
+    // weights against its own LDS columns), added to acc.
+    auto partial = [&](const Set &st, int nsb, f32x4(&acc)[NR]) {
 #pragma unroll
         for (int i = 0; i < SBW; i++) {
             if (i < nsb) {
-                const int sbl = s0 + i - cb;
                 Dec e[NR];
                 uint32_t qw[NR][8];
 #pragma unroll
@@ -222,7 +218,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
                     qw[w][0] = a0.x, qw[w][1] = a0.y, qw[w][2] = a0.z, qw[w][3] = a0.w;
                     qw[w][4] = a1.x, qw[w][5] = a1.y, qw[w][6] = a1.z, qw[w][7] = a1.w;
                 }
-                const uint8_t *xp = lds + xa + static_cast<uint32_t>(sbl) * 512u;
+                const uint8_t *xp = lds + xa + static_cast<uint32_t>(i) * 512u;
                 f32x4 dq[NR], dm[NR];
 #pragma unroll
                 for (int w = 0; w < NR; w++) dq[w] = dm[w] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -238,7 +234,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
                         dm[w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, j < 4 ? e[w].bm_a : e[w].bm_b, dm[w], 0, 0, 0);
                     }
                 }
-                const f32x4 sc4 = *reinterpret_cast<const f32x4 *>(lds + L.scl + (sbl * 16 + 4 * g) * 4);
+                const f32x4 sc4 = *reinterpret_cast<const f32x4 *>(lds + L.scl + ((wcol + i) * 16 + 4 * g) * 4);
 #pragma unroll
                 for (int w = 0; w < NR; w++)
 #pragma unroll
@@ -247,7 +243,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
                                                    acc[w][r]);
             }
         }
-        f32x4 *red = reinterpret_cast<f32x4 *>(lds + L.red) + (t & 1) * NR * (kMfmaWaves - 1) * 64;
+    };
+    // Tile t's sums of the workgroup, added in wave order through LDS
+    // buffer buf (consecutive calls alternate buffers, so one barrier per
+    // call suffices); wave 0 writes y, or adds to it (a later chunk).
+    auto finish = [&](f32x4(&acc)[NR], int t, bool add, int buf) {
+        f32x4 *red = reinterpret_cast<f32x4 *>(lds + L.red) + buf * NR * (kMfmaWaves - 1) * 64;
         if (wave > 0) {
 #pragma unroll
             for (int w = 0; w < NR; w++) red[(w * (kMfmaWaves - 1) + wave - 1) * 64 + lane] = acc[w];
@@ -268,94 +269,206 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
                         if constexpr (GLU)
                             *dst = silu_mul(acc[0][r], acc[1][r]);
                         else
-                            *dst = cb == 0 ? acc[0][r] : *dst + acc[0][r];
+                            *dst = add ? *dst + acc[0][r] : acc[0][r];
                     }
                 }
             }
         }
     };
 
-    // Staging: 8 lanes per (token, super-block); load i of the 8 lanes reads
-    // the 128 bytes of sub-block i's activations 4i.. (one cache line per
-    // load and group), so lane l holds elements 32i + 4l .. +3 for i < 8.
-    // kStageRounds rounds of 64 pairs per batch of loads.
-    const int l8 = tid & 7;
+    // Staging of this wave's share [s0, s0 + nsb) of a chunk: pair p = t + N i
+    // (token t, super-block s0 + i), 8 lanes per pair and 8 pairs per round.
+    // Load j of a pair's 8 lanes reads the 128 bytes of sub-block j's
+    // activations 4j.. (one cache line per load and pair), so lane l holds
+    // elements 32j + 4l .. +3 for j < 8. kStageRounds rounds per batch.
+    const int l8 = lane & 7, pj = lane >> 3;
     f32x4 v[kStageRounds][8];
-    auto stage_load = [&](int p0, int pairs, int cb, int csz) {
+    auto stage_load = [&](int r0, int s0, int np) {
 #pragma unroll
         for (int rr = 0; rr < kStageRounds; rr++) {
-            const int p = p0 + rr * 8 * kMfmaWaves;
-            const int t = p / csz, sbl = p % csz;
-            const uint32_t off = p < pairs ? (static_cast<uint32_t>(t) * K + static_cast<uint32_t>(cb + sbl) * 256u +
-                                              4u * l8) * 4u
-                                           : kNoFetch;
+            const int r = r0 + rr;
+            if (8 * r >= np) {
+                // No live pair in this round (uniform): no loads. The registers
+                // are still set, so no earlier batch's values stay live.
 #pragma unroll
-            for (int i = 0; i < 8; i++)
-                v[rr][i] = __builtin_bit_cast(f32x4, load16<0>(xr, off == kNoFetch ? kNoFetch : off + 128u * i, 0));
+                for (int j = 0; j < 8; j++) v[rr][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                continue;
+            }
+            const int p = 8 * r + pj;
+            const int t = p % N, i = p / N;
+            const uint32_t off = p < np ? (static_cast<uint32_t>(t) * K + static_cast<uint32_t>(s0 + i) * 256u +
+                                           4u * l8) * 4u
+                                        : kNoFetch;
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                v[rr][j] = __builtin_bit_cast(f32x4, load16<0>(xr, off == kNoFetch ? kNoFetch : off + 128u * j, 0));
         }
     };
-    auto stage_convert = [&](int p0, int pairs, int csz) {
+    auto stage_convert = [&](int r0, int np) {
 #pragma unroll
         for (int rr = 0; rr < kStageRounds; rr++) {
-            const int p = p0 + rr * 8 * kMfmaWaves;
-            if (p < pairs) {
-                const int t = p / csz, sbl = p % csz;
+            const int p = 8 * (r0 + rr) + pj;
+            if (p < np) {
+                const int t = p % N, i = p / N;
                 float mx = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; i++)
-                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[rr][i].x), fabsf(v[rr][i].y)),
-                                         fmaxf(fabsf(v[rr][i].z), fabsf(v[rr][i].w))));
+                for (int j = 0; j < 8; j++)
+                    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[rr][j].x), fabsf(v[rr][j].y)),
+                                         fmaxf(fabsf(v[rr][j].z), fabsf(v[rr][j].w))));
                 mx = max8(mx);
                 // Largest magnitude into [2^14, 2^15): scale by 2^(14 - floor(log2(mx))).
                 const int ex = static_cast<int>((__builtin_bit_cast(uint32_t, mx) >> 23) & 255u) - 127;
                 const int shift = mx == 0.0f ? 0 : 14 - ex;
-                uint8_t *dst = lds + L.xs + t * xrow + (sbl * 256 + 4 * l8) * 2;
+                uint8_t *dst = lds + L.xs + t * xrow + ((wcol + i) * 256 + 4 * l8) * 2;
 #pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    const f32x4 a = v[rr][i];
+                for (int j = 0; j < 8; j++) {
+                    const f32x4 a = v[rr][j];
                     const half2_t h01 = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.x, shift)),
                                          static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.y, shift))};
                     const half2_t h23 = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.z, shift)),
                                          static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.w, shift))};
-                    *reinterpret_cast<u32x2 *>(dst + 64 * i) =
+                    *reinterpret_cast<u32x2 *>(dst + 64 * j) =
                         u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
                 }
                 if (l8 == 0)
-                    *reinterpret_cast<float *>(lds + L.scl + (sbl * 16 + t) * 4) = __builtin_amdgcn_ldexpf(1.0f, -shift);
+                    *reinterpret_cast<float *>(lds + L.scl + ((wcol + i) * 16 + t) * 4) =
+                        __builtin_amdgcn_ldexpf(1.0f, -shift);
             }
         }
     };
+    // Batches after the first.
+    auto stage_rest = [&](int s0, int np) {
+        for (int r0 = kStageRounds; 8 * r0 < np; r0 += kStageRounds) {
+            stage_load(r0, s0, np);
+            stage_convert(r0, np);
+        }
+    };
+    // This wave's share of the chunk starting at super-block cb.
+    auto share = [&](int cb, int &s0, int &nsb) {
+        const int csz = ns - cb < CS ? ns - cb : CS;
+        s0 = cb + wave * csz / kMfmaWaves;
+        nsb = cb + (wave + 1) * csz / kMfmaWaves - s0;
+    };
+
+    // Token slots n..15 scale to zero in this wave's columns (never stored).
+    for (int e = lane; e < 16 * SBW; e += 64)
+        if ((e & 15) >= N) *reinterpret_cast<float *>(lds + L.scl + (wcol * 16 + e) * 4) = 0.0f;
 
     Set sa, sb;
-    for (int cb = 0; cb < ns; cb += CS) {
-        const int csz = ns - cb < CS ? ns - cb : CS;
-        // This wave's share of the chunk: super-blocks [s0, s0 + nsb).
-        const int s0 = cb + wave * csz / kMfmaWaves, nsb = cb + (wave + 1) * csz / kMfmaWaves - s0;
-        const int pairs = N * csz;
-        const int p0 = tid >> 3;
-        if (cb > 0) __syncthreads();  // every wave is done with the previous chunk's activations
-        // The first staging batch's loads go out ahead of the first tile's
-        // weights: its conversion then waits for them alone, while the
-        // weights' longer trip from HBM overlaps the staging.
-        stage_load(p0, pairs, cb, csz);
-        load(sa, t0, s0, nsb, t1);
-        stage_convert(p0, pairs, csz);
-        for (int q = p0 + 8 * kMfmaWaves * kStageRounds; q < pairs; q += 8 * kMfmaWaves * kStageRounds) {
-            stage_load(q, pairs, cb, csz);
-            stage_convert(q, pairs, csz);
-        }
-        for (int i = tid; i < 16 * csz; i += 64 * kMfmaWaves)
-            if (i % 16 >= N) *reinterpret_cast<float *>(lds + L.scl + i * 4) = 0.0f;
-        __syncthreads();
+    int s0, nsb;
+    share(0, s0, nsb);
+    // The first staging batch's loads go out ahead of the first tile's
+    // weights: its conversion then waits for them alone, while the weights'
+    // longer trip from HBM overlaps the staging.
+    stage_load(0, s0, N * nsb);
+    load(sa, t0, s0, nsb);
+    stage_convert(0, N * nsb);
+    stage_rest(s0, N * nsb);
 
-        // ---- the tiles, two register sets: the next tile's loads in flight
-        for (int t = t0; t < t1; t += 2) {
-            load(sb, t + 1, s0, nsb, t1);
-            tile(sa, t, s0, nsb, cb);
-            load(sa, t + 2, s0, nsb, t1);
-            if (t + 1 < t1) tile(sb, t + 1, s0, nsb, cb);
+    if constexpr (ONE) {
+        // One tile: the sums carry over the chunks and meet once. The next
+        // chunk's weights are in flight while one chunk is multiplied (its
+        // activations are staged after, from L2). Each path is straight-line
+        // and issues a fixed number of weight loads, so every wait covers
+        // exactly the loads it needs.
+        f32x4 acc[NR];
+#pragma unroll
+        for (int w = 0; w < NR; w++) acc[w] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int cb = 0;;) {
+            if (cb + CS >= ns) {
+                partial(sa, nsb, acc);
+                break;
+            }
+            int s1, n1;
+            share(cb + CS, s1, n1);
+            load(sb, t0, s1, n1);
+            partial(sa, nsb, acc);
+            stage_load(0, s1, N * n1);
+            stage_convert(0, N * n1);
+            stage_rest(s1, N * n1);
+            cb += CS, s0 = s1, nsb = n1;
+            if (cb + CS >= ns) {
+                partial(sb, nsb, acc);
+                break;
+            }
+            share(cb + CS, s1, n1);
+            load(sa, t0, s1, n1);
+            partial(sb, nsb, acc);
+            stage_load(0, s1, N * n1);
+            stage_convert(0, N * n1);
+            stage_rest(s1, N * n1);
+            cb += CS, s0 = s1, nsb = n1;
+        }
+        finish(acc, t0, false, 0);
+    } else {
+    // Several tiles: per chunk, the tiles with the next one's weights in
+    // flight; a later chunk adds to y. Past the last tile no loads are
+    // issued (a load that fetches nothing still costs the address unit a
+    // pass over the wave); each path is straight-line, so its waits stay
+    // exact.
+    int buf = 0;
+    auto one = [&](const Set &st, int t, bool add) {
+        f32x4 acc[NR];
+#pragma unroll
+        for (int w = 0; w < NR; w++) acc[w] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        partial(st, nsb, acc);
+        finish(acc, t, add, buf);
+        buf ^= 1;
+    };
+    for (int cb = 0; cb < ns; cb += CS) {
+        if (cb > 0) {
+            share(cb, s0, nsb);
+            stage_load(0, s0, N * nsb);
+            load(sa, t0, s0, nsb);
+            stage_convert(0, N * nsb);
+            stage_rest(s0, N * nsb);
+        }
+        if constexpr (GLU) {
+            // Two rows per lane: the straight-line paths below would keep more
+            // registers live than the wave has, so past the last tile the
+            // gated form issues loads that fetch nothing.
+            for (int t = t0; t < t1; t += 2) {
+                load(sb, t + 1, s0, nsb);
+                one(sa, t, cb > 0);
+                load(sa, t + 2, s0, nsb);
+                if (t + 1 < t1) one(sb, t + 1, cb > 0);
+            }
+        } else {
+            for (int t = t0; t < t1; t += 2) {
+                if (t + 1 >= t1) {
+                    one(sa, t, cb > 0);
+                    break;
+                }
+                load(sb, t + 1, s0, nsb);
+                one(sa, t, cb > 0);
+                if (t + 2 >= t1) {
+                    one(sb, t + 1, cb > 0);
+                    break;
+                }
+                load(sa, t + 2, s0, nsb);
+                one(sb, t + 1, cb > 0);
+            }
         }
     }
+    }
+}
+
+// The LDS opt-in above 64 KiB, once per kernel and device.
+template <int N, int SBW, bool GLU, bool ONE>
+int opt_in_lds(size_t lds, int budget)
+{
+    if (lds <= static_cast<size_t>(kMaxLdsBytes)) return Q4_OK;
+    static std::atomic<int> opted[64];
+    int dev = 0;
+    if (hip_status(hipGetDevice(&dev)) != Q4_OK) return Q4_EHIP;
+    if (dev < 0 || dev >= 64) return Q4_EUNSUPPORTED;
+    if (!opted[dev].load(std::memory_order_acquire)) {
+        const int st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_q4k_kernel<N, SBW, GLU, ONE>),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, budget));
+        if (st != Q4_OK) return st;
+        opted[dev].store(1, std::memory_order_release);
+    }
+    return Q4_OK;
 }
 
 template <int N, int SBW, bool GLU>
@@ -365,25 +478,23 @@ int launch_mfma_sbw(const uint8_t *w, const float *x, float *y, int m, int k, in
     if constexpr (GLU && SBW > 2) {
         return Q4_EUNSUPPORTED;  // the gated product keeps two rows' loads in flight: at most 2 per wave
     } else {
-    if (lds > static_cast<size_t>(kMaxLdsBytes)) {
-        static std::atomic<int> opted[64];
-        int dev = 0;
-        if (hip_status(hipGetDevice(&dev)) != Q4_OK) return Q4_EHIP;
-        if (dev < 0 || dev >= 64) return Q4_EUNSUPPORTED;
-        if (!opted[dev].load(std::memory_order_acquire)) {
-            const int st = hip_status(hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_q4k_kernel<N, SBW, GLU>),
-                                                          hipFuncAttributeMaxDynamicSharedMemorySize, budget));
+        const int tiles = (m + 15) / 16;
+        const int cap = cus * (groups_per_cu > 0 ? groups_per_cu : 1);
+        const unsigned grid = static_cast<unsigned>(tiles < cap ? tiles : cap);
+        const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(Q4_FMT_Q4_K, GLU ? 2LL * m : m, k));
+        // One tile per workgroup when the tiles fit the grid.
+        if (static_cast<int>(grid) == tiles) {
+            const int st = opt_in_lds<N, SBW, GLU, true>(lds, budget);
             if (st != Q4_OK) return st;
-            opted[dev].store(1, std::memory_order_release);
+            hipLaunchKernelGGL((mfma_q4k_kernel<N, SBW, GLU, true>), dim3(grid), dim3(64 * kMfmaWaves), lds, s, w,
+                               wbytes, x, y, m, k, cs);
+        } else {
+            const int st = opt_in_lds<N, SBW, GLU, false>(lds, budget);
+            if (st != Q4_OK) return st;
+            hipLaunchKernelGGL((mfma_q4k_kernel<N, SBW, GLU, false>), dim3(grid), dim3(64 * kMfmaWaves), lds, s, w,
+                               wbytes, x, y, m, k, cs);
         }
-    }
-    const int tiles = (m + 15) / 16;
-    const int cap = cus * (groups_per_cu > 0 ? groups_per_cu : 1);
-    const unsigned grid = static_cast<unsigned>(tiles < cap ? tiles : cap);
-    const uint32_t wbytes = static_cast<uint32_t>(q4_weight_bytes(Q4_FMT_Q4_K, GLU ? 2LL * m : m, k));
-    hipLaunchKernelGGL((mfma_q4k_kernel<N, SBW, GLU>), dim3(grid), dim3(64 * kMfmaWaves), lds, s, w, wbytes, x, y, m,
-                       k, cs);
-    return hip_status(hipGetLastError());
+        return hip_status(hipGetLastError());
     }
 }
 
@@ -392,21 +503,23 @@ int launch_mfma(const uint8_t *w, const float *x, float *y, int m, int k, hipStr
 {
     const int ns = k / 256;
     // Chunks of at most 8 kMfmaSbMax super-blocks (four per wave per tile)
-    // whose staged activations fit the LDS (the opt-in size above 64 KiB).
+    // whose staged activations fit the LDS (the opt-in size above 64 KiB):
+    // SBW, the most super-blocks per wave, sets the LDS columns.
     // The gated product takes rows of at most 16 super-blocks, in one chunk.
     if (GLU && ns > 2 * kMfmaWaves) return Q4_EUNSUPPORTED;
     int budget = kMaxLdsBytes;
     const int optin = device_lds_optin();
-    int cs = ns < kMfmaWaves * kMfmaSbMax ? ns : kMfmaWaves * kMfmaSbMax;
-    if (mfma_lds(N, cs, GLU).total > static_cast<uint32_t>(budget) && optin > budget) budget = optin;
-    while (cs > 1 && mfma_lds(N, cs, GLU).total > static_cast<uint32_t>(budget)) cs--;
-    if (mfma_lds(N, cs, GLU).total > static_cast<uint32_t>(budget)) return Q4_EUNSUPPORTED;
-    if (GLU && cs < ns) return Q4_EUNSUPPORTED;
-    const int chunks = (ns + cs - 1) / cs;
-    cs = (ns + chunks - 1) / chunks;  // even chunks
-    const size_t lds = mfma_lds(N, cs, GLU).total;
-    // Super-blocks per wave and tile: the chunk split over the 8 waves.
-    switch ((cs + kMfmaWaves - 1) / kMfmaWaves) {
+    int sbw = (ns + kMfmaWaves - 1) / kMfmaWaves;
+    if (sbw > kMfmaSbMax) sbw = kMfmaSbMax;
+    if (mfma_lds(N, sbw, GLU).total > static_cast<uint32_t>(budget) && optin > budget) budget = optin;
+    while (sbw > 1 && mfma_lds(N, sbw, GLU).total > static_cast<uint32_t>(budget)) sbw--;
+    if (mfma_lds(N, sbw, GLU).total > static_cast<uint32_t>(budget)) return Q4_EUNSUPPORTED;
+    const int chunks = (ns + kMfmaWaves * sbw - 1) / (kMfmaWaves * sbw);
+    if (GLU && chunks > 1) return Q4_EUNSUPPORTED;
+    const int cs = (ns + chunks - 1) / chunks;  // even chunks
+    sbw = (cs + kMfmaWaves - 1) / kMfmaWaves;
+    const size_t lds = mfma_lds(N, sbw, GLU).total;
+    switch (sbw) {
     case 1: return launch_mfma_sbw<N, 1, GLU>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
     case 2: return launch_mfma_sbw<N, 2, GLU>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
     case 3: return launch_mfma_sbw<N, 3, GLU>(w, x, y, m, k, cs, lds, budget, s, cus, groups_per_cu);
