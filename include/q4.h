@@ -155,8 +155,8 @@ int q4_quantize_ref(int fmt, const float *w, int64_t m, int64_t k, void *out, si
  * does (0 * NaN included); the other tokens are unaffected. x is otherwise
  * expected finite. One token on a matrix of rows of up to 14560 weights
  * runs the streaming kernel, Q4_K at several tokens on 256 rows or more the
- * matrix-core kernel (from 2 tokens on rows of up to 2048 weights, from 4 on
- * rows of up to 8192, from 5 on longer ones), everything else the tiled
+ * matrix-core kernel (from 3 tokens on, and at 2 tokens on rows of up to
+ * 2048 weights), everything else the tiled
  * kernel (see q4_gemv_tuning); all
  * are deterministic. The matrix-core kernel scales each 256-element piece of
  * a token's x (one Q4_K super-block) by a power of two into [2^14, 2^15) and

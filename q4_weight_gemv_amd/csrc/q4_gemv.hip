@@ -118,12 +118,12 @@ Cfg choose_tiled(int fmt, int64_t m, int64_t k, int64_t n, int cus);
 
 // The Q4_K matrix-core kernel from several tokens on, for products of 256
 // rows or more (one fp16 per activation, as the tiled kernel there). From a
-// sweep against the tiled kernel's per-token dot products: faster from 5
-// tokens on, from 4 on rows that fit one workgroup's LDS at once (8192
-// weights), and from 2 on rows of up to 2048 weights.
+// sweep against the tiled kernel's per-token dot products: faster from 3
+// tokens on at every measured shape, plain and gated; at 2 tokens only on
+// rows of up to 2048 weights.
 bool use_matrix(int fmt, int64_t m, int64_t k, int64_t n)
 {
-    return fmt == Q4_FMT_Q4_K && m >= 256 && (n >= 5 || (n == 4 && k <= 8192) || (n >= 2 && k <= 2048));
+    return fmt == Q4_FMT_Q4_K && m >= 256 && (n >= 3 || (n == 2 && k <= 2048));
 }
 
 Cfg choose(int fmt, int64_t m, int64_t k, int64_t n, int cus)

@@ -527,8 +527,7 @@ def _glu_plain_kernel(q4, fmt, n, m, k):
     product reproduces (q4.h, q4_gemv_glu): the matrix-core kernel for Q4_K
     where q4_gemv would pick it for the stacked matrix and the row has at most
     4096 weights, else the tiled kernel."""
-    matrix = (fmt == 1 and 2 * m >= 256 and k <= 4096 and
-              (n >= 5 or (n == 4 and k <= 8192) or (n >= 2 and k <= 2048)))
+    matrix = fmt == 1 and 2 * m >= 256 and k <= 4096 and (n >= 3 or (n == 2 and k <= 2048))
     return q4.Q4_GEMV_KERNEL_MATRIX if matrix else q4.Q4_GEMV_KERNEL_TILED
 
 

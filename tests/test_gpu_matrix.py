@@ -1,7 +1,7 @@
 """GPU parity of the several-token Q4_K decode product on matrix cores.
 
 The kernel (q4_gemv_tuned with Q4_GEMV_KERNEL_MATRIX; the library's choice for
-Q4_K at 4-8 tokens on 256 rows or more) forms the products with
+Q4_K at 3-8 tokens on 256 rows or more) forms the products with
 v_mfma_f32_16x16x32_f16 from exact fp16 codes and one fp16 per activation.
 Checked against the oracle:
 * outputs within 2e-3 (normwise and elementwise) for 1..8 tokens, ragged row
