@@ -57,7 +57,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaSbMax = 4;     // most super-blocks per wave per tile and chunk
-constexpr int kStageRounds = 2;   // staging rounds whose activation loads are in flight together
 constexpr int kSbBytes = 144;     // Q4_K super-block
 constexpr int kXRowPad = 16;      // bytes after each token's row of staged activations
 
@@ -152,7 +151,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     // the SBW slots issues its loads (slots past nsb, rows past M and tiles
     // past t1 fetch nothing), so a set is always the same number of loads and
     // each wait covers exactly the loads it needs.
-    auto load = [&](Set &st, int t, int s0, int nsb) {
+    auto load = [&](Set &st, int t, int s0, int nsb) __attribute__((always_inline)) {
         const int row = t * 16 + col;
         const bool live = t < t1 && row < M;
 #pragma unroll
@@ -175,7 +174,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
         half8 bm_a, bm_b;
         float d, dmin;
     };
-    auto decode = [&](const u32x4 &h) {
+    auto decode = [&](const u32x4 &h) __attribute__((always_inline)) {
         // Sub-blocks 2g and 2g+1: their 6-bit fields sit in bytes
         // 2(g&1) and 2(g&1)+1 of the scale words.
         const uint32_t sh = (g & 1) << 4;
@@ -205,7 +204,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     };
     // This wave's sums over its nsb super-blocks of one tile (the set's
     // weights against its own LDS columns), added to acc.
-    auto partial = [&](const Set &st, int nsb, f32x4(&acc)[NR]) {
+    auto partial = [&](const Set &st, int nsb, f32x4(&acc)[NR]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < SBW; i++) {
             if (i < nsb) {
@@ -247,7 +246,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     // Tile t's sums of the workgroup, added in wave order through LDS
     // buffer buf (consecutive calls alternate buffers, so one barrier per
     // call suffices); wave 0 writes y, or adds to it (a later chunk).
-    auto finish = [&](f32x4(&acc)[NR], int t, bool add, int buf) {
+    auto finish = [&](f32x4(&acc)[NR], int t, bool add, int buf) __attribute__((always_inline)) {
         f32x4 *red = reinterpret_cast<f32x4 *>(lds + L.red) + buf * NR * (kMfmaWaves - 1) * 64;
         if (wave > 0) {
 #pragma unroll
@@ -280,12 +279,15 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     // (token t, super-block s0 + i), 8 lanes per pair and 8 pairs per round.
     // Load j of a pair's 8 lanes reads the 128 bytes of sub-block j's
     // activations 4j.. (one cache line per load and pair), so lane l holds
-    // elements 32j + 4l .. +3 for j < 8. kStageRounds rounds per batch.
+    // elements 32j + 4l .. +3 for j < 8. R rounds per batch: a wave's whole
+    // share in one batch where the registers allow (up to 3 rounds, 2 at
+    // four super-blocks per wave).
+    constexpr int R = SBW >= 4 ? 2 : ((N * SBW + 7) / 8 < 3 ? (N * SBW + 7) / 8 : 3);
     const int l8 = lane & 7, pj = lane >> 3;
-    f32x4 v[kStageRounds][8];
-    auto stage_load = [&](int r0, int s0, int np) {
+    f32x4 v[R][8];
+    auto stage_load = [&](int r0, int s0, int np) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rr = 0; rr < kStageRounds; rr++) {
+        for (int rr = 0; rr < R; rr++) {
             const int r = r0 + rr;
             if (8 * r >= np) {
                 // No live pair in this round (uniform): no loads. The registers
@@ -304,9 +306,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
                 v[rr][j] = __builtin_bit_cast(f32x4, load16<0>(xr, off == kNoFetch ? kNoFetch : off + 128u * j, 0));
         }
     };
-    auto stage_convert = [&](int r0, int np) {
+    auto stage_convert = [&](int r0, int np) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rr = 0; rr < kStageRounds; rr++) {
+        for (int rr = 0; rr < R; rr++) {
             const int p = 8 * (r0 + rr) + pj;
             if (p < np) {
                 const int t = p % N, i = p / N;
@@ -337,14 +339,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
         }
     };
     // Batches after the first.
-    auto stage_rest = [&](int s0, int np) {
-        for (int r0 = kStageRounds; 8 * r0 < np; r0 += kStageRounds) {
+    auto stage_rest = [&](int s0, int np) __attribute__((always_inline)) {
+        for (int r0 = R; 8 * r0 < np; r0 += R) {
             stage_load(r0, s0, np);
             stage_convert(r0, np);
         }
     };
     // This wave's share of the chunk starting at super-block cb.
-    auto share = [&](int cb, int &s0, int &nsb) {
+    auto share = [&](int cb, int &s0, int &nsb) __attribute__((always_inline)) {
         const int csz = ns - cb < CS ? ns - cb : CS;
         s0 = cb + wave * csz / kMfmaWaves;
         nsb = cb + (wave + 1) * csz / kMfmaWaves - s0;
@@ -368,9 +370,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     if constexpr (ONE) {
         // One tile: the sums carry over the chunks and meet once. The next
         // chunk's weights are in flight while one chunk is multiplied (its
-        // activations are staged after, from L2). Each path is straight-line
-        // and issues a fixed number of weight loads, so every wait covers
-        // exactly the loads it needs.
+        // activations are staged after, from L2; in flight across the
+        // multiply they would not fit the registers). Each path is
+        // straight-line and issues a fixed number of weight loads, so every
+        // wait covers exactly the loads it needs.
         f32x4 acc[NR];
 #pragma unroll
         for (int w = 0; w < NR; w++) acc[w] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mfma_q4k_kernel(const uint8_t
     // pass over the wave); each path is straight-line, so its waits stay
     // exact.
     int buf = 0;
-    auto one = [&](const Set &st, int t, bool add) {
+    auto one = [&](const Set &st, int t, bool add) __attribute__((always_inline)) {
         f32x4 acc[NR];
 #pragma unroll
         for (int w = 0; w < NR; w++) acc[w] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
