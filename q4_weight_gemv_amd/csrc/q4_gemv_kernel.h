@@ -164,44 +164,19 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t v)
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(h, half2_t{k, k}, half2_t{o, o}));
 }
 
-// Offset codes: one AND-OR places a masked nibble pair under the fp16
-// exponent of 1024 (bits 0x6400), giving the exact normal pair 1024 + q for
-// low nibbles and 1024 + 16q for high ones. The offsets are removed once per
-// unit from the staged activations' own sums, which halves the VALU work per
-// weight pair against code_pair (an AND-OR instead of an AND and a packed
-// fma). Used where each activation is a single fp16 value: the offset term
-// is about 2^10 times the code term, so its fp32 rounding costs about 2^-19
-// of a unit's term scale, far below the fp16 activation's 2^-12 but not
-// below the 2^-23 that hi + lo pairs keep.
-constexpr uint32_t kOffsetExp = 0x64006400u;
-__device__ __forceinline__ uint32_t offset_pair(uint32_t v, uint32_t mask) { return (v & mask) | kOffsetExp; }
-
-// Trait: the format decodes offset codes when activations are single fp16
-// values (F::kOffsetCodes), with the unit's offset term in its metadata.
-template <class F, class = void>
-struct offset_codes : std::false_type {};
-template <class F>
-struct offset_codes<F, std::void_t<decltype(F::kOffsetCodes)>> : std::integral_constant<bool, F::kOffsetCodes> {};
-
 // Q4_0 codes as signed normal fp16 pairs: (q-8)*2^-14 for low nibbles,
-// 16(q-8)*2^-14 for high nibbles (hi + lo activations); as offset codes
-// 1024 + q and 1024 + 16q (single fp16 activations).
+// 16(q-8)*2^-14 for high nibbles.
 template <bool LO>
 __device__ __forceinline__ float dot_dword(uint32_t q, u32x4 xh, u32x4 xl, float acc)
 {
     const uint32_t s = q >> 8;
-    if constexpr (!LO) {
-        acc = dot2(offset_pair(q, kLo), xh.x, acc);
-        acc = dot2(offset_pair(q, kHi), xh.y, acc);
-        acc = dot2(offset_pair(s, kLo), xh.z, acc);
-        acc = dot2(offset_pair(s, kHi), xh.w, acc);
-    } else {
-        const uint32_t p0 = code_pair<8>(q & kLo), p1 = code_pair<128>(q & kHi);
-        const uint32_t p2 = code_pair<8>(s & kLo), p3 = code_pair<128>(s & kHi);
-        acc = dot2(p0, xh.x, acc);
-        acc = dot2(p1, xh.y, acc);
-        acc = dot2(p2, xh.z, acc);
-        acc = dot2(p3, xh.w, acc);
+    const uint32_t p0 = code_pair<8>(q & kLo), p1 = code_pair<128>(q & kHi);
+    const uint32_t p2 = code_pair<8>(s & kLo), p3 = code_pair<128>(s & kHi);
+    acc = dot2(p0, xh.x, acc);
+    acc = dot2(p1, xh.y, acc);
+    acc = dot2(p2, xh.z, acc);
+    acc = dot2(p3, xh.w, acc);
+    if constexpr (LO) {
         acc = dot2(p0, xl.x, acc);
         acc = dot2(p1, xl.y, acc);
         acc = dot2(p2, xl.z, acc);
@@ -219,7 +194,6 @@ struct FmtQ4_0 {
     static constexpr int kFormat = Q4_FMT_Q4_0;
     static constexpr int kHighOffset = 16;
     static constexpr int kBatchUnits = 4;  // units (x rows) per lane per batch: 4 x 20 B in flight
-    static constexpr bool kOffsetCodes = true;
     __device__ static int unit_base(int u) { return u << 5; }
     __device__ static int item_base(int u, int i) { return unit_base(u) + 4 * i; }
     __device__ static uint32_t scale_plane(uint64_t rows, uint64_t k) { return static_cast<uint32_t>(rows * k / 2u); }
@@ -246,14 +220,6 @@ struct FmtQ4_0 {
     {
         return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + kCodeExp), 0.0f};
     }
-    // Offset-code metadata, from the sums of the staged fp16 values: gl over
-    // the 16 low-nibble activations, gh16 = 16 x the sum of the 16
-    // pre-divided high-nibble ones. The unit's offset term is
-    // (1024 + 8) gl + (1024 + 128) gh16 / 16; z = 2^e (no code factor).
-    __device__ static f32x4 meta_offset(float gl, float gh16, int e)
-    {
-        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e), __builtin_fmaf(1032.0f, gl, 72.0f * gh16)};
-    }
     template <int N, int R, bool LO>
     __device__ static void accumulate(const Regs (&g)[R], const u32x4 *__restrict__ xs,
                                       int ul, int uc, uint32_t /*u*/,
@@ -276,7 +242,6 @@ struct FmtQ4_0 {
                 a = dot_dword<LO>(g[r].q.y, xh[1], xl[1], a);
                 a = dot_dword<LO>(g[r].q.z, xh[2], xl[2], a);
                 a = dot_dword<LO>(g[r].q.w, xh[3], xl[3], a);
-                if constexpr (!LO) a -= mt.w;  // the offset codes' term
                 acc[r][t] = __builtin_fmaf(half_lo(g[r].d) * mt.z, a, acc[r][t]);
             }
         }
@@ -409,14 +374,6 @@ struct FmtQ1_0 {
     __device__ static f32x4 meta(float /*gl*/, float /*gh*/, int e)
     {
         return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e + kCodeExp), 0.0f};
-    }
-    // Offset-code metadata, from the sums of the staged fp16 values: gl over
-    // the 16 low-nibble activations, gh16 = 16 x the sum of the 16
-    // pre-divided high-nibble ones. The unit's offset term is
-    // (1024 + 8) gl + (1024 + 128) gh16 / 16; z = 2^e (no code factor).
-    __device__ static f32x4 meta_offset(float gl, float gh16, int e)
-    {
-        return f32x4{0.0f, 0.0f, __builtin_amdgcn_ldexpf(1.0f, e), __builtin_fmaf(1032.0f, gl, 72.0f * gh16)};
     }
     // Bits v*2^-24 (v = b or 16b per half) -> exact fp16 pair
     // (2v - OFF)*2^-14 = 2048 * v*2^-24 - OFF*2^-14.
@@ -864,22 +821,13 @@ __device__ __forceinline__ void stage(__amdgpu_buffer_rsrc_t xr, int K, int c0, 
                                     pack_h2(sh1.hi, sh3.hi)};
             const u32x4 vlo = u32x4{pack_h2(sl0.lo, sl2.lo), pack_h2(sh0.lo, sh2.lo), pack_h2(sl1.lo, sl3.lo),
                                     pack_h2(sh1.lo, sh3.lo)};
-            // Offset codes need the sums of the values the products see (the
-            // staged fp16 values); the other formats' sums are of the exact
-            // scaled activations.
-            constexpr bool kOff = offset_codes<F>::value && !LO;
-            const auto fh = [](_Float16 v) { return static_cast<float>(v); };
-            float gl = kOff ? (fh(sl0.hi) + fh(sl1.hi)) + (fh(sl2.hi) + fh(sl3.hi)) : (l0 + l1) + (l2 + l3);
-            float gh = kOff ? (fh(sh0.hi) + fh(sh1.hi)) + (fh(sh2.hi) + fh(sh3.hi)) : (h0 + h1) + (h2 + h3);
+            float gl = (l0 + l1) + (l2 + l3);
+            float gh = (h0 + h1) + (h2 + h3);
             gl += dpp<0xB1>(gl);
             gh += dpp<0xB1>(gh);
             gl += dpp<0x4E>(gl);
             gh += dpp<0x4E>(gh);
-            f32x4 mv;
-            if constexpr (kOff)
-                mv = F::meta_offset(gl, 16.0f * gh, e);
-            else
-                mv = F::meta(gl, 16.0f * gh, e);
+            const f32x4 mv = F::meta(gl, 16.0f * gh, e);
             if (live) {
                 u32x4 *dst = xs + xslot(t, ul, uc);
                 dst[2 * i] = vhi;
