@@ -440,6 +440,35 @@ def test_extreme_activation_q4_k(env):
     check_tolerance(y, yr, orc.termscale(1, buf, m, k, x), GEMV_TOL, what="q4_k outlier")
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("n", [1, 3])
+def test_outlier_activation_single_fp16_path(env, fmt, n):
+    # Products of 256 rows or more hold one fp16 per activation (the tests
+    # above use 96 rows, the hi + lo form). An outlier sets its unit's
+    # power-of-two scale, leaving the unit's other activations about 2^-20 of
+    # it; where the outlier meets a zero weight (Q4_0 code 8) its term must
+    # contribute exactly nothing, or the rounding of a running sum that holds
+    # it swamps the unit's small terms. Each row's error is bounded against
+    # its term magnitudes (about 15 % of the rows have code 8 at an outlier).
+    from gpu_common import GEMV_TOL, check_tolerance
+
+    torch, q4, orc = env
+    m, k = 320, 1024
+    buf = q4.q4_quantize_ref(fmt, synth.weights(75 + fmt, m, k))
+    x = synth.activations(77, 3, k)
+    x[0, 5] = 1e6
+    x[1, 700] = -3e4
+    x[2, ::97] = 1e5  # an outlier in each of eleven units
+    x = x[:n]
+    say(f"outlier activation single fp16 fmt={fmt} n={n}")
+    y = _gemv(env, fmt, buf, x, m, k)
+    if fmt == 0:
+        yr, scale = orc.matvec(fmt, buf, m, k, x, absdot=True)
+    else:
+        yr, scale = orc.matvec(fmt, buf, m, k, x), orc.termscale(fmt, buf, m, k, x)
+    check_tolerance(y, yr, scale, GEMV_TOL, what=f"outlier fmt={fmt} n={n}")
+
+
 @pytest.mark.parametrize("fmt,k,parts", [(0, 960, (960, 320, 320)), (0, 960, (2560, 2560)), (1, 1024, (512, 256, 256))])
 def test_stacked_projections_equal_separate_products(env, fmt, k, parts):
     # Shared-input projections (q|k|v, gate|up) row-stacked into one matrix:
