@@ -379,6 +379,24 @@ typedef struct {            /* device buffers, all caller-owned (16-byte aligned
 int q4_llama_step(int fmt, const q4_llama_config *cfg, const void *emb, const float *norm_final,
                   const q4_llama_layer *layers, const q4_llama_state *state, void *hip_stream);
 
+/* q4_llama_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The same step, kernels and results, except that the intermediate vectors
+ * (state->qkv, att, delta, act: ignored here, may be null) live in a static
+ * device array of the library: 65536 floats (256 KiB) per GPU, held until the
+ * process ends. Each vector takes its length rounded up to a multiple of 16
+ * floats; a configuration needing more than 65536 in total
+ * ((heads + 2 kv_heads) * head_dim + heads * head_dim + hidden + ffn, so
+ * rounded) returns Q4_EUNSUPPORTED with nothing enqueued. Other arguments and
+ * errors as q4_llama_step. Calls no allocating routine; the array's address is
+ * looked up on the first call on each device (Q4_EHIP if that fails). The
+ * array keeps the last call's contents and nothing in it must start at zero
+ * (every vector is written before it is read within a step). Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or a graph that captured this call replayed beside another) race. */
+int q4_llama_step_noalloc(int fmt, const q4_llama_config *cfg, const void *emb, const float *norm_final,
+                          const q4_llama_layer *layers, const q4_llama_state *state, void *hip_stream);
+
 /* The same step captured once into a HIP graph; each launch runs one step. */
 typedef struct q4_llama_graph q4_llama_graph;
 int q4_llama_graph_create(int fmt, const q4_llama_config *cfg, const void *emb, const float *norm_final,

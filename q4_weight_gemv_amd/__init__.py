@@ -110,6 +110,8 @@ _SIGS = {
     "q4_graph_destroy": (ctypes.c_int, [_vp]),
     "q4_llama_step": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_llama_config), _vp, _vp,
                                       ctypes.POINTER(q4_llama_layer), ctypes.POINTER(q4_llama_state), _vp]),
+    "q4_llama_step_noalloc": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_llama_config), _vp, _vp,
+                                              ctypes.POINTER(q4_llama_layer), ctypes.POINTER(q4_llama_state), _vp]),
     "q4_llama_graph_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(q4_llama_config), _vp, _vp,
                                               ctypes.POINTER(q4_llama_layer), ctypes.POINTER(q4_llama_state), _vp,
                                               ctypes.POINTER(_vp)]),
@@ -355,6 +357,14 @@ class LlamaStep:
         _check(_lib.q4_llama_step(self.fmt, ctypes.byref(self._cfg), self.w["emb"].data_ptr(),
                                   self.w["norm_final"].data_ptr(), self._layers, ctypes.byref(self._state),
                                   _stream_ptr(stream)), "q4_llama_step")
+
+    def step_noalloc(self, stream=None) -> None:
+        """The same step through q4_llama_step_noalloc (intermediate vectors in
+        the library's static device array; this object's qkv, att, delta and
+        act buffers are not used)."""
+        _check(_lib.q4_llama_step_noalloc(self.fmt, ctypes.byref(self._cfg), self.w["emb"].data_ptr(),
+                                          self.w["norm_final"].data_ptr(), self._layers, ctypes.byref(self._state),
+                                          _stream_ptr(stream)), "q4_llama_step_noalloc")
 
     def capture(self, stream=None) -> None:
         h = ctypes.c_void_p(None)

@@ -16,6 +16,7 @@
 // one, so a captured step replays as a generation loop with no host work.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <new>
@@ -433,6 +434,44 @@ struct q4_llama_graph {
     hipGraphExec_t exec = nullptr;
 };
 
+// Workspace of q4_llama_step_noalloc: the step's intermediate vectors (q|k|v,
+// attention output, delta, gated activation) in a file-scope device array.
+// Each GPU holds its own copy until the process ends; host code reaches it
+// only through the device address that hipGetSymbolAddress returns for the
+// current device (the array's name on the host is not a device address).
+constexpr int64_t kStepScratchFloats = 65536;  // 256 KiB per GPU
+static __device__ __align__(256) float scratch[kStepScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<float *> scratch_dev[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up on the first call on
+// that device (with it current) and kept.
+int step_scratch(float **out)
+{
+    int dev = 0;
+    int st = q4::hip_status(hipGetDevice(&dev));
+    if (st != Q4_OK) return st;
+    if (dev < 0 || dev >= kMaxDevices) return Q4_EUNSUPPORTED;
+    float *p = scratch_dev[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *a = nullptr;
+        st = q4::hip_status(hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)));
+        if (st != Q4_OK) return st;
+        if (!a) return Q4_EHIP;
+        p = static_cast<float *>(a);
+        scratch_dev[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return Q4_OK;
+}
+
+int64_t round16(int64_t n) { return n > 0 ? (n + 15) / 16 * 16 : 0; }
+
+}  // namespace
+
 extern "C" {
 
 int q4_llama_step(int fmt, const q4_llama_config *cfg, const void *emb, const float *norm_final,
@@ -479,6 +518,30 @@ int q4_llama_graph_create(int fmt, const q4_llama_config *cfg, const void *emb, 
     }
     *graph_out = g;
     return Q4_OK;
+}
+
+int q4_llama_step_noalloc(int fmt, const q4_llama_config *cfg, const void *emb, const float *norm_final,
+                          const q4_llama_layer *layers, const q4_llama_state *state, void *hip_stream)
+{
+    if (!cfg || !state) return Q4_EINVAL;
+    float *base = nullptr;
+    int st = step_scratch(&base);
+    if (st != Q4_OK) return st;
+    // Each vector starts on a 64-byte boundary of the array.
+    const int64_t qn = static_cast<int64_t>(cfg->heads) * cfg->head_dim;
+    const int64_t qkv_n = (static_cast<int64_t>(cfg->heads) + 2LL * cfg->kv_heads) * cfg->head_dim;
+    const int64_t o_att = round16(qkv_n), o_delta = o_att + round16(qn), o_act = o_delta + round16(cfg->hidden);
+    const int64_t need = o_act + round16(cfg->ffn);
+    q4_llama_state ws = *state;
+    const bool fits = need <= kStepScratchFloats;
+    ws.qkv = base;
+    ws.att = base + (fits ? o_att : 0);
+    ws.delta = base + (fits ? o_delta : 0);
+    ws.act = base + (fits ? o_act : 0);
+    st = check_step(fmt, cfg, emb, norm_final, layers, &ws);
+    if (st != Q4_OK) return st;
+    if (!fits) return Q4_EUNSUPPORTED;
+    return enqueue_step(fmt, cfg, emb, norm_final, layers, &ws, static_cast<hipStream_t>(hip_stream));
 }
 
 int q4_llama_graph_launch(q4_llama_graph *graph, void *hip_stream)
