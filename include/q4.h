@@ -13,10 +13,13 @@
  *
  * Conventions for every entry point:
  *   - The caller owns every buffer. The library allocates no memory. What it
- *     keeps between calls is read-only per device: cached device attributes
- *     (compute units, the workgroup LDS limit) and, once per device and
- *     kernel, the opt-in of kernels that use more than 64 KiB of LDS; the
- *     graph handles below are caller-owned state. Calls are reentrant.
+ *     keeps between calls per device: cached device attributes (compute
+ *     units, the workgroup LDS limit), once per device and kernel the opt-in
+ *     of kernels that use more than 64 KiB of LDS, and the device address of
+ *     the static 256 KiB array that q4_llama_step_noalloc works in (loaded
+ *     with the library's code, written only by that call); the graph handles
+ *     below are caller-owned state. Calls are reentrant, except that calls of
+ *     q4_llama_step_noalloc that overlap on one GPU share its array.
  *   - Matrices are row-major. W is logically [m][k] (k = input dimension,
  *     m = output dimension), quantized along k. Activations are token-major:
  *     x[n][k], y[n][m].
