@@ -392,7 +392,9 @@ int q4_llama_step(int fmt, const q4_llama_config *cfg, const void *emb, const fl
  * ((heads + 2 kv_heads) * head_dim + heads * head_dim + hidden + ffn, so
  * rounded) returns Q4_EUNSUPPORTED with nothing enqueued. Other arguments and
  * errors as q4_llama_step. Calls no allocating routine; the array's address is
- * looked up on the first call on each device (Q4_EHIP if that fails). The
+ * looked up on the first call on each device (Q4_EHIP if that fails), so a
+ * caller that captures the call into a HIP graph makes one call on that
+ * device outside capture first. The
  * array keeps the last call's contents and nothing in it must start at zero
  * (every vector is written before it is read within a step). Every call on one
  * GPU shares that GPU's array: calls that overlap on one GPU (on different
