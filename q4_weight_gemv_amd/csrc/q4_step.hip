@@ -524,23 +524,31 @@ int q4_llama_step_noalloc(int fmt, const q4_llama_config *cfg, const void *emb, 
                           const q4_llama_layer *layers, const q4_llama_state *state, void *hip_stream)
 {
     if (!cfg || !state) return Q4_EINVAL;
-    float *base = nullptr;
-    int st = step_scratch(&base);
-    if (st != Q4_OK) return st;
     // Each vector starts on a 64-byte boundary of the array.
     const int64_t qn = static_cast<int64_t>(cfg->heads) * cfg->head_dim;
     const int64_t qkv_n = (static_cast<int64_t>(cfg->heads) + 2LL * cfg->kv_heads) * cfg->head_dim;
     const int64_t o_att = round16(qkv_n), o_delta = o_att + round16(qn), o_act = o_delta + round16(cfg->hidden);
     const int64_t need = o_act + round16(cfg->ffn);
-    q4_llama_state ws = *state;
     const bool fits = need <= kStepScratchFloats;
-    ws.qkv = base;
-    ws.att = base + (fits ? o_att : 0);
-    ws.delta = base + (fits ? o_delta : 0);
-    ws.act = base + (fits ? o_act : 0);
-    st = check_step(fmt, cfg, emb, norm_final, layers, &ws);
+    // Every argument is validated before any HIP call: the workspace
+    // pointers are checked at their offsets from a stand-in base with the
+    // array's alignment (checking reads no memory), then rebased onto the
+    // device's copy of the array.
+    auto place = [&](q4_llama_state &ws, float *base) {
+        ws.qkv = base;
+        ws.att = base + (fits ? o_att : 0);
+        ws.delta = base + (fits ? o_delta : 0);
+        ws.act = base + (fits ? o_act : 0);
+    };
+    q4_llama_state ws = *state;
+    place(ws, reinterpret_cast<float *>(static_cast<uintptr_t>(256)));
+    int st = check_step(fmt, cfg, emb, norm_final, layers, &ws);
     if (st != Q4_OK) return st;
     if (!fits) return Q4_EUNSUPPORTED;
+    float *base = nullptr;
+    st = step_scratch(&base);
+    if (st != Q4_OK) return st;
+    place(ws, base);
     return enqueue_step(fmt, cfg, emb, norm_final, layers, &ws, static_cast<hipStream_t>(hip_stream));
 }
 

@@ -395,6 +395,33 @@ def test_llama_step_argument_errors(q4):
     assert ok(cfg, st3) == q4.Q4_EALIGN
     st4 = q4.q4_llama_state(*([A16] * 7 + [A16 + 8] + [A16] * 3))              # misaligned key cache
     assert ok(cfg, st4) == q4.Q4_EALIGN
+    # The allocation-free step validates the same way before any HIP call; its
+    # state's workspace pointers are ignored (null here), and a model whose
+    # intermediate vectors exceed its 65536-float array is refused.
+    g = lib.q4_llama_step_noalloc
+    st0 = q4.q4_llama_state(*([A16] * 2 + [None] * 4 + [A16] * 5))
+    ok0 = lambda c=cfg, s=st0: g(0, ctypes.byref(c), A16, A16, layers, ctypes.byref(s), None)  # noqa: E731
+    assert g(0, None, A16, A16, layers, ctypes.byref(st0), None) == q4.Q4_EINVAL
+    assert g(0, ctypes.byref(cfg), A16, A16, layers, None, None) == q4.Q4_EINVAL
+    assert g(9, ctypes.byref(cfg), A16, A16, layers, ctypes.byref(st0), None) == q4.Q4_EUNSUPPORTED
+    for c, code in ((q4.q4_llama_config(2, 128, 4, 3, 32, 256, 384, 16, 1e4, 1e-5), q4.Q4_EINVAL),
+                    (q4.q4_llama_config(2, 128, 4, 2, 48, 256, 384, 16, 1e4, 1e-5), q4.Q4_EUNSUPPORTED),
+                    (q4.q4_llama_config(2, 100, 4, 2, 32, 256, 384, 16, 1e4, 1e-5), q4.Q4_EINVAL)):
+        assert ok0(c) == code
+    st5 = q4.q4_llama_state(*([A16] * 10 + [None]))                            # no position buffer
+    assert ok0(cfg, st5) == q4.Q4_EINVAL
+    st6 = q4.q4_llama_state(*([A16] * 7 + [A16 + 8] + [A16] * 3))              # misaligned key cache
+    assert ok0(cfg, st6) == q4.Q4_EALIGN
+    # Distinct buffers pass every other check; an ffn of 65536 floats alone
+    # exceeds the array (a fitting model would go on to the device lookup).
+    a = lambda i: A16 + (i << 16)  # noqa: E731
+    lay = (q4.q4_llama_layer * 2)()
+    for i in range(2):
+        lay[i] = q4.q4_llama_layer(a(1), a(2), a(3), a(4), a(5), a(6))
+    sd = q4.q4_llama_state(a(10), a(11), None, None, None, None, a(16), a(17), a(18), a(19), a(20))
+    for ffn in (65536, 131072):
+        big = q4.q4_llama_config(2, 128, 4, 2, 32, ffn, 384, 16, 1e4, 1e-5)
+        assert g(0, ctypes.byref(big), a(30), a(31), lay, ctypes.byref(sd), None) == q4.Q4_EUNSUPPORTED
     h = ctypes.c_void_p(None)
     assert lib.q4_llama_graph_create(0, None, A16, A16, layers, ctypes.byref(st), None, ctypes.byref(h)) == q4.Q4_EINVAL
     assert h.value is None
