@@ -71,3 +71,38 @@ def test_noalloc_step_refuses_a_model_beyond_its_array(env):
     torch.cuda.synchronize()
     assert int(big.buf["pos"].item()) == 0  # nothing was enqueued
     assert not torch.any(big.buf["k_cache"])
+
+
+def test_noalloc_step_under_caller_graph_capture(env):
+    # The callers it is for: one call on the device outside capture (the
+    # array's address is looked up then), then the step captured into the
+    # caller's own graph (torch's, on its capture stream) and replayed as a
+    # generation loop: every replay, with eager work and synchronizations
+    # between them, equals q4_llama_step on an identical model bit for bit.
+    torch, q4 = env
+    cfg = SMALLER
+    w = _weights(torch, q4, cfg, 7300)
+    first = q4.LlamaStep(0, cfg, w)
+    first.set(token=1, pos=0)
+    first.step_noalloc()
+    ref = q4.LlamaStep(0, cfg, w)
+    got = q4.LlamaStep(0, cfg, w)
+    ref.set(token=9, pos=0)
+    got.set(token=9, pos=0)
+    torch.cuda.synchronize()
+    say("noalloc step under caller capture")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        got.step_noalloc()
+    torch.cuda.synchronize()
+    # Capture enqueues nothing to run: the state is as set.
+    assert int(got.buf["pos"].item()) == 0
+    for pos in range(4):
+        ref.step()
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = torch.randn(1000, device="cuda").sum().item()  # eager work between replays
+        for name in ("logits", "token", "pos", "x", "h", "k_cache", "v_cache"):
+            assert torch.equal(ref.buf[name], got.buf[name]), (pos, name)
+    assert int(got.buf["pos"].item()) == 4
+    del graph
