@@ -30,6 +30,9 @@ Q1_0), the prefill GEMM over a SmolLM2-360M layer at 512 tokens (separate and
 stacked matrices), warm steps, launches from a plain stream, the per-launch
 floor, and the streaming-read ceiling (a pure read, and the same read storing
 a few bytes per wave).
+The GPT-2 step and the whole SmolLM2-360M step also carry "device_busy": the
+sum of their kernels' traced durations per step from the committed rocprofv3
+summary (when taken on the current kernel sources) and the tokens/s it gives.
 "cpu_baseline" is the CPU oracle timed on the host cores on whole repeats of
 the headline step (bounded to about 10 s).
 
@@ -196,6 +199,24 @@ def trace_median_from_profile(path=None):
     committed kernel trace, if it was taken on the current kernel sources."""
     return _profile_field(path or os.path.join(ROOT, "profiles", "trace_gemv_q4_0_4096x11008.md"),
                           "median_us")
+
+
+def kernel_us_per_step_from_profile(path):
+    """Device time per step (its kernels' mean traced durations summed) from a
+    committed kernel trace summary, if taken on the current kernel sources."""
+    return _profile_field(path, "kernel_us_per_step")
+
+
+def device_busy(name, path=None):
+    """The "device_busy" record of a step from its committed trace
+    (profiles/<name>), or None. The profiler stretches short kernels, so the
+    figure bounds the step's device-busy time from above (it can exceed the
+    unprofiled wall time)."""
+    us = kernel_us_per_step_from_profile(path or os.path.join(ROOT, "profiles", name))
+    if us is None:
+        return None
+    return {"kernel_us_per_step": us, "tokens_per_s": round(1e6 / us, 1), "from": f"profiles/{name}",
+            "note": "sum of traced kernel durations per step; traced short kernels run long"}
 
 
 def gemm_mfma_busy_from_profile(path=None):
@@ -760,6 +781,9 @@ def main():
                                    "GB_s": round(gpt2.bytes / tg / 1e9, 1), "products": len(gpt2.shapes),
                                    "avg_launch_us": round(tg / len(gpt2.shapes) * 1e6, 3),
                                    "cache": f"cold: {len(gpt2.copies)} copies", "launch": "HIP graph"}
+            busy = device_busy("trace_gemv_gpt2_step.md")
+            if busy is not None:
+                extras["gpt2_step"]["device_busy"] = busy
             log(f"gpt2 step: {tg * 1e6:.1f} us")
             if on("plain"):
                 n_plain = max(20, K // 10)
@@ -805,6 +829,9 @@ def main():
             extras["read_ceiling"] = bench_read_ceiling(torch, q4, timer)
         if on("full_step"):
             extras["smollm2_full_decode_step"] = bench_full_step(torch, q4, timer)
+            busy = device_busy("step_smollm2_kernel_trace.md")
+            if busy is not None:
+                extras["smollm2_full_decode_step"]["device_busy"] = busy
         if on("gemm"):
             extras["gemm_smollm2_layer"] = bench_gemm(torch, q4, timer, reps=max(2, K // 50))
             busy = gemm_mfma_busy_from_profile()

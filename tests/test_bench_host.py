@@ -71,6 +71,11 @@ def test_profile_figures_reported_only_for_matching_sources(tmp_path):
     assert bench.traffic_from_profile(str(stale)) is None
     assert bench.trace_median_from_profile(str(stale)) is None
     assert bench.traffic_from_profile(str(tmp_path / "missing.txt")) is None
+    good.write_text(f"kernel_source_sha256: {h}\nkernel_us_per_step: 125.0\n")
+    stale.write_text(f"kernel_source_sha256: {other}\nkernel_us_per_step: 125.0\n")
+    busy = bench.device_busy("good.txt", str(good))
+    assert busy["kernel_us_per_step"] == 125.0 and busy["tokens_per_s"] == 8000.0
+    assert bench.device_busy("stale.txt", str(stale)) is None
 
 
 def test_source_hash_covers_the_headline_kernel():
