@@ -36,9 +36,10 @@ summary (when taken on the current kernel sources) and the tokens/s it gives.
 "cpu_baseline" is the CPU oracle timed on the host cores on whole repeats of
 the headline step (bounded to about 10 s).
 
---profile-shape K,M runs only that Q4_0 one-token product (a graph of launches
-on rotating copies, --steps replays) for rocprofv3 runs, one shape per process
-so that each trace holds one shape.
+--profile-shape K,M runs only that product (Q4_0 at one token unless
+--profile-fmt / --profile-tokens say otherwise; a graph of launches on rotating
+copies, --steps replays) for rocprofv3 runs, one shape per process so that each
+trace holds one shape.
 """
 from __future__ import annotations
 
@@ -635,6 +636,9 @@ def main():
                          "smollm2_fused, smollm2_gated, warm, read_ceiling, full_step, gemm")
     ap.add_argument("--profile-shape", default=None,
                     help="K,M: run only this Q4_0 one-token product, cold, --steps graph replays (for rocprofv3)")
+    ap.add_argument("--profile-fmt", type=int, default=0,
+                    help="with --profile-shape: the format (0 Q4_0, 1 Q4_K, 2 Q8_0, 3 Q2_K, 4 Q1_0)")
+    ap.add_argument("--profile-tokens", type=int, default=1, help="with --profile-shape: tokens (1..8)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every one-token geometry at the workload shapes (one JSON line each) and exit")
     ap.add_argument("--sweep-tokens", action="store_true",
@@ -684,10 +688,13 @@ def main():
 
     if args.profile_shape:
         pk, pm = (int(v) for v in args.profile_shape.split(","))
-        t = product_time(torch, q4, timer, 0, pk, pm, 1, reps=K)
-        nb = gemv_bytes(q4, 0, pm, pk, 1)
-        print(json.dumps({"profile_shape": f"{pk}->{pm}", "format": "Q4_0", "tokens": 1, "us_per_launch": round(t * 1e6, 3),
-                          "GB_s": round(nb / t / 1e9, 1), "kernel_source_sha256": kernel_source_hash()}), flush=True)
+        pf, pn = args.profile_fmt, args.profile_tokens
+        t = product_time(torch, q4, timer, pf, pk, pm, pn, reps=K)
+        nb = gemv_bytes(q4, pf, pm, pk, pn)
+        names = {0: "Q4_0", 1: "Q4_K", 2: "Q8_0", 3: "Q2_K", 4: "Q1_0"}
+        print(json.dumps({"profile_shape": f"{pk}->{pm}", "format": names.get(pf, str(pf)), "tokens": pn,
+                          "us_per_launch": round(t * 1e6, 3), "GB_s": round(nb / t / 1e9, 1),
+                          "kernel_source_sha256": kernel_source_hash()}), flush=True)
         return
 
     shapes = synth.llama7b_layer()
