@@ -257,9 +257,10 @@ int q4_gemv_tuned(int fmt, const void *w, const float *x, float *y,
 
 /* q4_gemv_addnorm with an explicit tile geometry; same arguments, results and
  * errors, plus Q4_EINVAL for a null tuning, a negative field or an unknown
- * kernel, and Q4_EUNSUPPORTED for the streaming or matrix-core kernel (the
- * fused product runs on the tiled kernel) or a geometry that is not instantiated for the
- * fused product. Instantiated:
+ * kernel, and Q4_EUNSUPPORTED for the streaming or matrix-core kernel (a tuned
+ * fused product runs on the tiled kernel; the untuned plain form takes the
+ * streaming kernel where the plain one-token product does) or a geometry that
+ * is not instantiated for the fused product. Instantiated:
  * (8,1,1) (8,2,1) (16,1,1) (16,1,4) (32,1,4) (32,1,8) (32,2,1) (32,2,4) (64,1,4)
  * with Q4_EPILOGUE_NONE; (16,2,1) (16,2,4) (32,2,1) (32,2,4) (32,2,8) (64,2,4)
  * with Q4_EPILOGUE_SILU_MUL. */

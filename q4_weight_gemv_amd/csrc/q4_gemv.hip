@@ -277,6 +277,23 @@ int launch_gemv_addnorm(int fmt, const void *w, const float *x, const Prologue &
 {
     const int cus = device_cus();
     if (cus <= 0) return Q4_EHIP;
+    const auto *wb = static_cast<const uint8_t *>(w);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int mi = static_cast<int>(m), ki = static_cast<int>(k);
+    // The plain form takes the streaming kernel wherever the plain one-token
+    // product does (the library's choice, not a tuned geometry).
+    if (!glu && !tuning) {
+        const gemv::Cfg cs = gemv::choose(fmt, m, k, 1, cus);
+        if (cs.depth && !cs.matrix) {
+            switch (fmt) {
+            case Q4_FMT_Q4_0: return gemv::dispatch_stream_norm<gemv::FmtQ4_0>(cs, wb, x, y, mi, ki, s, cus, pro);
+            case Q4_FMT_Q8_0: return gemv::dispatch_stream_norm<gemv::FmtQ8_0>(cs, wb, x, y, mi, ki, s, cus, pro);
+            case Q4_FMT_Q1_0: return gemv::dispatch_stream_norm<gemv::FmtQ1_0>(cs, wb, x, y, mi, ki, s, cus, pro);
+            case Q4_FMT_Q2_K: return gemv::dispatch_stream_norm<gemv::FmtQ2_K>(cs, wb, x, y, mi, ki, s, cus, pro);
+            default: return gemv::dispatch_stream_norm<gemv::FmtQ4_K>(cs, wb, x, y, mi, ki, s, cus, pro);
+            }
+        }
+    }
     gemv::Cfg c = glu ? gemv::choose_glu(fmt, m, k, 1, cus) : gemv::choose_tiled(fmt, m, k, 1, cus);
     // The fused norm stages three vectors (x, delta, gain) per workgroup, so
     // short-row gated products take 16 lanes per row in their one-wave groups
@@ -289,9 +306,6 @@ int launch_gemv_addnorm(int fmt, const void *w, const float *x, const Prologue &
         if (tuning->waves_per_group) c.waves = tuning->waves_per_group;
         if (tuning->groups_per_cu) c.groups_per_cu = tuning->groups_per_cu;
     }
-    const auto *wb = static_cast<const uint8_t *>(w);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int mi = static_cast<int>(m), ki = static_cast<int>(k);
     switch (fmt) {
     case Q4_FMT_Q4_0: return gemv::dispatch_norm_cfg<gemv::FmtQ4_0>(c, wb, x, y, mi, ki, s, cus, glu, pro);
     case Q4_FMT_Q8_0: return gemv::dispatch_norm_cfg<gemv::FmtQ8_0>(c, wb, x, y, mi, ki, s, cus, glu, pro);

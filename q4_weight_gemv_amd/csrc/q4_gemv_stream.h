@@ -22,7 +22,11 @@
 //     lanes (about 16 cycles for a 16-byte load), and at these sizes those
 //     passes, not HBM, decided the time;
 //   * the per-format decode (load and accumulate) is the tiled kernel's
-//     policy, with one row per lane (R = 1) and one token.
+//     policy, with one row per lane (R = 1) and one token;
+//   * NORM: the fused residual add + RMSNorm prologue of q4_gemv_addnorm
+//     (the staging forms v = x + delta, stages v * gain, sums v^2, and
+//     workgroup 0 writes v out; each reduced row is scaled by
+//     1/sqrt(mean(v^2) + eps), as in the tiled kernel).
 #pragma once
 
 #include <utility>
@@ -45,10 +49,10 @@ __device__ __forceinline__ void static_switch(int v, std::integer_sequence<int, 
 template <int WAVES>
 constexpr int kStreamStageRound = WAVES == 1 ? 4 : WAVES <= 4 ? 6 : WAVES <= 8 ? 3 : 2;
 
-template <class F, int LPR, int WAVES, int D, bool LO>
+template <class F, int LPR, int WAVES, int D, bool LO, bool NORM = false>
 __global__ __launch_bounds__(64 * WAVES) void stream_kernel(const uint8_t *__restrict__ w, uint32_t wbytes,
                                                             const float *__restrict__ x, float *__restrict__ y,
-                                                            int M, int K, int rows_per_group)
+                                                            int M, int K, int rows_per_group, Prologue pro)
 {
     constexpr int SUBS = 64 / LPR;
     constexpr int NT = 64 * WAVES;
@@ -92,6 +96,7 @@ __global__ __launch_bounds__(64 * WAVES) void stream_kernel(const uint8_t *__res
     };
     float acc[1][1] = {{0.0f}};
     int cp = 0, c_rg = wave, c_s = 0;
+    float rn = 1.0f;  // NORM: 1/rms of the staged row
     // Compute one position; at the end of a row group reduce it and store.
     // The store is issued at every position (dropped by its out-of-range
     // offset except at a row group's end) so that the compiler's wait counts
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(64 * WAVES) void stream_kernel(const uint8_t *__res
         const bool end = c_s == slots - 1;
         const int row = row0 + c_rg * SUBS + sub;
         float v = 0.0f;
-        if (end) v = row_reduce<LPR>(acc[0][0]);
+        if (end) v = row_reduce<LPR>(acc[0][0]) * rn;
         const bool live = end && li == 0 && row < row_end && cp < total;
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), yr,
                                               live ? static_cast<uint32_t>(row) * 4u : kNoFetch, 0, 0);
@@ -115,13 +120,33 @@ __global__ __launch_bounds__(64 * WAVES) void stream_kernel(const uint8_t *__res
     };
 
     NormIo nio{xr, xr, xr, 0.0f};
+    if constexpr (NORM) {
+        const uint32_t kb = static_cast<uint32_t>(K) * 4u;
+        nio.delta = make_rsrc(pro.delta, pro.delta ? kb : 0u);
+        nio.gain = make_rsrc(pro.gain, kb);
+        nio.out = make_rsrc(pro.x_out, pro.x_out && blockIdx.x == 0 ? kb : 0u);
+    }
     auto issue = [&]() {
 #pragma unroll
         for (int p = 0; p < D; p++) load_next(buf[p]);
     };
-    stage<F, 1, NT, kStreamStageRound<WAVES>, LO, false, decltype(issue), true>(xr, K, 0, nu, nu, xs, tid, nio,
-                                                                              issue);
+    stage<F, 1, NT, kStreamStageRound<WAVES>, LO, NORM, decltype(issue), true>(xr, K, 0, nu, nu, xs, tid, nio,
+                                                                             issue);
+    // NORM: one sum of squares per wave, after the staged row in LDS.
+    [[maybe_unused]] float *wave_ssq = reinterpret_cast<float *>(lds + kLdsSlots * nu);
+    if constexpr (NORM) {
+        const float sq = row_reduce<64>(nio.ssq);
+        if (lane == 0) wave_ssq[wave] = sq;
+    }
     wg_sync<WAVES>();
+    if constexpr (NORM) {
+        // Every workgroup sums the same items in the same order, so every
+        // row sees the same factor.
+        float sq = 0.0f;
+#pragma unroll
+        for (int v = 0; v < WAVES; v++) sq += wave_ssq[v];
+        rn = 1.0f / __builtin_sqrtf(sq / static_cast<float>(K) + pro.eps);
+    }
     if (total == 0) return;  // uniform across the wave; no barrier follows
     // Steady state: the exit is checked before each load, so every load
     // issued here fetches a real slot (a load that fetches nothing still
@@ -151,13 +176,14 @@ drain:
 
 // Launch: groups_per_cu workgroups per compute unit over the rows, each a
 // contiguous range of a multiple of SUBS rows. m is the number of rows.
-template <class F, int LPR, int WAVES, int D>
+template <class F, int LPR, int WAVES, int D, bool NORM = false>
 int launch_stream(const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t stream, int cus,
-                  int groups_per_cu)
+                  int groups_per_cu, const Prologue &pro = Prologue{})
 {
     constexpr int SUBS = 64 / LPR;
     const int nu = k / kUnitWeights;
-    const size_t lds = static_cast<size_t>(nu) * kLdsBytesPerUnit;
+    // The staged row, plus (NORM) one float per wave for the sums of squares.
+    const size_t lds = static_cast<size_t>(nu) * kLdsBytesPerUnit + (NORM ? 16u * ((WAVES + 3) / 4) : 0u);
     if (lds > static_cast<size_t>(kMaxLdsBytes)) {
         const int optin = device_lds_optin();
         if (optin <= 0 || lds > static_cast<size_t>(optin)) return Q4_EUNSUPPORTED;
@@ -167,11 +193,11 @@ int launch_stream(const uint8_t *w, const float *x, float *y, int m, int k, hipS
         if (dev < 0 || dev >= 64) return Q4_EUNSUPPORTED;
         if (!opted[dev].load(std::memory_order_acquire)) {
             int st = hip_status(hipFuncSetAttribute(
-                reinterpret_cast<const void *>(&stream_kernel<F, LPR, WAVES, D, true>),
+                reinterpret_cast<const void *>(&stream_kernel<F, LPR, WAVES, D, true, NORM>),
                 hipFuncAttributeMaxDynamicSharedMemorySize, optin));
             if (st == Q4_OK)
                 st = hip_status(hipFuncSetAttribute(
-                    reinterpret_cast<const void *>(&stream_kernel<F, LPR, WAVES, D, false>),
+                    reinterpret_cast<const void *>(&stream_kernel<F, LPR, WAVES, D, false, NORM>),
                     hipFuncAttributeMaxDynamicSharedMemorySize, optin));
             if (st != Q4_OK) return st;
             opted[dev].store(1, std::memory_order_release);
@@ -185,11 +211,11 @@ int launch_stream(const uint8_t *w, const float *x, float *y, int m, int k, hipS
     // Activations as hi + lo fp16 pairs for matrices of fewer than kLoRowLimit
     // rows, as single fp16 values for taller ones (as the tiled kernel).
     if (m < kLoRowLimit)
-        hipLaunchKernelGGL((stream_kernel<F, LPR, WAVES, D, true>), dim3(grid), dim3(64 * WAVES), lds, stream, w,
-                           wbytes, x, y, m, k, static_cast<int>(rpg));
+        hipLaunchKernelGGL((stream_kernel<F, LPR, WAVES, D, true, NORM>), dim3(grid), dim3(64 * WAVES), lds, stream, w,
+                           wbytes, x, y, m, k, static_cast<int>(rpg), pro);
     else
-        hipLaunchKernelGGL((stream_kernel<F, LPR, WAVES, D, false>), dim3(grid), dim3(64 * WAVES), lds, stream, w,
-                           wbytes, x, y, m, k, static_cast<int>(rpg));
+        hipLaunchKernelGGL((stream_kernel<F, LPR, WAVES, D, false, NORM>), dim3(grid), dim3(64 * WAVES), lds, stream,
+                           w, wbytes, x, y, m, k, static_cast<int>(rpg), pro);
     return hip_status(hipGetLastError());
 }
 

@@ -94,9 +94,13 @@ int dispatch_glu_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, i
 template <class F>
 int dispatch_norm_cfg(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus,
                       bool glu, const Prologue &pro);
-// Defined in q4_gemv_stream.hip: the one-token streaming kernel.
+// Defined in q4_gemv_stream.hip: the one-token streaming kernel, plain and
+// with the fused residual add + RMSNorm prologue.
 template <class F>
 int dispatch_stream(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s, int cus);
+template <class F>
+int dispatch_stream_norm(const Cfg &c, const uint8_t *w, const float *x, float *y, int m, int k, hipStream_t s,
+                         int cus, const Prologue &pro);
 
 // Defined in q4_gemv_mfma.hip: the Q4_K decode product on matrix cores, any
 // token count 1..8; glu: the gated product of a 2m-row matrix (rows of at
