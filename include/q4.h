@@ -411,7 +411,9 @@ int q4_llama_graph_create(int fmt, const q4_llama_config *cfg, const void *emb, 
 int q4_llama_graph_launch(q4_llama_graph *graph, void *hip_stream);
 int q4_llama_graph_destroy(q4_llama_graph *graph);
 
-/* Static string for a status code. */
+/* Static string for a status code (the C ABI's own error reporting, not a
+ * step of the method, so no passage defines it; an unknown code gets a
+ * generic string). */
 const char *q4_strerror(int status);
 
 /* Name of the HIP error behind the calling thread's most recent Q4_EHIP

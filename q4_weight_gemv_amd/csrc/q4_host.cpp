@@ -346,7 +346,7 @@ const char *q4_strerror(int status)
     case Q4_OK: return "ok";
     case Q4_EINVAL: return "invalid argument (size, null pointer, block multiple or buffer length)";
     case Q4_EUNSUPPORTED: return "unsupported (format, token count, or size beyond 32-bit offsets)";
-    case Q4_EALIGN: return "misaligned pointer (w and x need 16 bytes, y 4 bytes)";
+    case Q4_EALIGN: return "misaligned pointer (w needs 16 bytes, activations and outputs 4, norm vectors and caches 16)";
     case Q4_ENONFINITE: return "non-finite weight given to the quantizer";
     case Q4_ERANGE: return "block scale overflows fp16";
     case Q4_EHIP: return "HIP runtime error";
