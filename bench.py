@@ -714,7 +714,7 @@ def main():
     # four launches, the most time), timed alone the same way.
     dk, dm = DOMINANT
     per_launch_bytes = gemv_bytes(q4, 0, dm, dk, 1)
-    reps_dom = max(20, K // 10)
+    reps_dom = max(100, K // 10)  # a stable average, whatever K the headline times
     t_dom = product_time(torch, q4, timer, 0, dk, dm, 1, reps=reps_dom)
     achieved = per_launch_bytes / t_dom / 1e9
     per_shape = {}
